@@ -1,0 +1,32 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def read_golden(name):
+    """key -> value (int when it parses, else float, else str) from tests/golden/<name>."""
+    out = {}
+    with open(os.path.join(ROOT, "tests", "golden", name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, val = line.split(None, 1)
+            val = val.strip()
+            for conv in (int, float):
+                try:
+                    val = conv(val)
+                    break
+                except ValueError:
+                    pass
+            out[key] = val
+    return out
