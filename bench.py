@@ -1,0 +1,276 @@
+"""Throughput of one paged decode step on one MI355X.
+
+A step is the whole hot path over one batch: append one new token per sequence
+(kv_append, slots planned on the host by the library's block pool), then
+single-token decode attention over every sequence's paged KV cache
+(paged_decode_attn: cascade pass over shared blocks when a plan has any,
+split-K partial attention over each row's own blocks, partial merge).  Host
+planning (append plan, cascade plan) is timed separately and reported.
+
+Default workload: the Llama-3-8B-shaped decode layer (64 sequences, lengths
+uniform in [512, 4096], Hq=32, Hkv=8, d=128, bf16 K/V, 16-token blocks,
+random placement).  ``--config 1..5`` selects the other synthetic workloads.
+
+Prints one JSON line.  ``value`` = effective unique-KV GB/s of the step: the
+distinct K/V bytes the step must read plus q, output and table bytes, divided
+by the measured step time (inputs resident in HBM, back-to-back steps).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cascade", action="store_true", help="decode every row on its own (no shared-prefix pass)")
+    ap.add_argument("--cold-iters", type=int, default=10,
+                    help="extra steps each preceded by a 1 GiB write that evicts L2 and MALL (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle baseline (0 = skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def unique_bytes(bt, lens, w):
+    """Distinct K/V bytes one decode reads: valid tokens of every distinct block referenced."""
+    per_block = {}
+    for b in range(len(lens)):
+        n = int(lens[b])
+        nb = -(-n // w.block_size)
+        for j in range(nb):
+            valid = min(w.block_size, n - j * w.block_size)
+            blk = int(bt[b, j])
+            per_block[blk] = max(per_block.get(blk, 0), valid)
+    return sum(per_block.values()) * w.bytes_per_token
+
+
+def host_rows(q_bits, k_pages, v_pages, bt, lens, rows):
+    """Host copies of the inputs the given decode rows read (their blocks, renumbered)."""
+    import torch
+
+    bs = k_pages.shape[1]
+    ids = []
+    for r in rows:
+        ids.extend(int(x) for x in bt[r, : -(-int(lens[r]) // bs)])
+    uniq = sorted(set(ids)) or [0]
+    remap = {b: i for i, b in enumerate(uniq)}
+    idx = torch.tensor(uniq, dtype=torch.int64, device=k_pages.device)
+    k = k_pages.index_select(0, idx).cpu().numpy().view(np.uint16)
+    v = v_pages.index_select(0, idx).cpu().numpy().view(np.uint16)
+    sbt = np.full((len(rows), bt.shape[1]), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        nb = -(-int(lens[r]) // bs)
+        sbt[i, :nb] = [remap[int(x)] for x in bt[r, :nb]]
+    qb = q_bits[list(rows)].cpu().numpy().view(np.uint16)
+    return k, v, sbt, np.asarray([lens[r] for r in rows], dtype=np.int32), qb
+
+
+def cpu_baseline(w, q_bits, k_pages, v_pages, bt, lens, seconds):
+    """Time the fp64 oracle on as many rows as fit in the budget (one BLAS thread)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    rows_done = 0
+    tokens = 0
+    t_total = 0.0
+    order = list(range(len(lens)))
+    with threadpool_limits(limits=1):
+        for b in order:
+            k, v, sbt, sl, qb = host_rows(q_bits, k_pages, v_pages, bt, lens, [b])
+            t0 = time.perf_counter()
+            oracle.ref_decode(qb, k, v, sbt, sl, w.scale, w.dtype)
+            t_total += time.perf_counter() - t0
+            rows_done += 1
+            tokens += int(lens[b])
+            if t_total >= seconds:
+                break
+    gbs = tokens * w.bytes_per_token / t_total / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} of {len(lens)} decode rows ({tokens} tokens, all {w.num_q_heads} query heads), "
+                      f"{t_total:.1f} s of fp64 numpy on one host thread; queries/s = {rows_done / t_total:.2f}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+              "(the path shards by rows / heads with no exchange, but nothing here launches more than one GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_21_amd as pkv
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.get(args.config)
+    print(f"[bench] workload {w.number} {w.name}: {w.description}", file=sys.stderr, flush=True)
+
+    # ---- set-up (not timed): pages, pool, the step's append plan, tables, cascade plan
+    k_pages, v_pages = workloads.make_pages(w, device=dev)
+    pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(pool, w.build_ops)
+    step = w.steps[0]
+    t0 = time.perf_counter()
+    slots, cows = pool.plan_append(step.append_rows)
+    plan_append_us = (time.perf_counter() - t0) * 1e6
+    bt, lens = pool.export_tables(step.decode_rows, w.max_blocks)
+    t0 = time.perf_counter()
+    plan = None if args.no_cascade else pkv.CascadePlan(bt, lens, w.num_q_heads, w.num_kv_heads)
+    plan_build_us = (time.perf_counter() - t0) * 1e6
+    if plan is not None:
+        plan.upload(device=dev)
+    n_nodes = plan.num_nodes if plan is not None else 0
+
+    q = workloads.make_q(w, 0, device=dev)
+    k_new, v_new = workloads.make_new_tokens(w, 0, device=dev)
+    slot_d = torch.from_numpy(slots).to(dev)
+    cow = np.asarray(cows, dtype=np.int32).reshape(-1, 3)
+    cow_d = [torch.from_numpy(np.ascontiguousarray(cow[:, i])).to(dev) for i in range(3)] if len(cow) else [None] * 3
+    bt_d = torch.from_numpy(bt).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    max_len = int(lens.max())
+    ws = torch.empty(max(pkv.decode_workspace_bytes(len(lens), w.num_q_heads, w.num_kv_heads, w.head_dim, max_len,
+                                                    plan), 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((len(lens), w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step():
+        pkv.kv_append(k_pages, v_pages, k_new, v_new, slot_d, cow_d[0], cow_d[1], cow_d[2], dtype=w.dtype,
+                      stream=stream)
+        pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, max_len, scale=w.scale, plan=plan, workspace=ws,
+                              out=out, dtype=w.dtype, stream=stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    # ---- timed region 1: K back-to-back steps (the reported value)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / max(args.steps, 1)
+
+    # ---- timed region 2: the same K steps with per-kernel HIP events (library timing, same stream)
+    pkv.timing_reset()
+    pkv.timing_enable(True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    pkv.timing_enable(False)
+    ms_per_step_instrumented = ev0.elapsed_time(ev1) / max(args.steps, 1)
+    kern = {}
+    for name in ("append", "decode_split", "merge", "cascade"):
+        total, count = pkv.timing_read(name)
+        kern[name] = {"avg_us": round(total / count * 1e3, 3) if count else 0.0, "launches": count}
+
+    # ---- cold steps: evict L2 / MALL with a 1 GiB write before each step
+    cold = []
+    if args.cold_iters > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for _ in range(args.cold_iters):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            one_step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        del flush
+
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(3)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: {args.copy_calibration_mib} MiB read + written", file=sys.stderr)
+
+    # ---- bytes
+    B = len(lens)
+    kv_unique = unique_bytes(bt, lens, w)
+    kv_logical = int(lens.sum()) * w.bytes_per_token
+    q_bytes = B * w.num_q_heads * w.head_dim * 2
+    o_bytes = B * w.num_q_heads * w.head_dim * 4
+    tbl_bytes = bt.nbytes + lens.nbytes
+    U = kv_unique + q_bytes + o_bytes + tbl_bytes
+    value = U / (ms_per_step * 1e-3) / 1e9
+
+    # roofline of the dominant kernel: split-K decode; algorithmic bytes = the K/V of every row's own
+    # (not shared) tokens plus q, per launch
+    if plan is not None:
+        own_tokens = sum(int(lens[b]) - plan.row(b)[0] for b in range(B))
+    else:
+        own_tokens = int(lens.sum())
+    split_bytes = own_tokens * w.bytes_per_token + q_bytes
+    t_split = kern["decode_split"]["avg_us"] * 1e-6
+    achieved = split_bytes / t_split / 1e9 if t_split > 0 else 0.0
+    roofline = {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": kern["decode_split"]["avg_us"]}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, q, k_pages, v_pages, bt, lens, args.cpu_seconds)
+
+    res = {
+        "metric": "paged decode attn: effective KV GB/s, % of HBM peak, decode queries/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "batch": B, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "mean_seq_len": round(float(lens.mean()), 1), "max_seq_len": max_len, "accumulate": "f32",
+                   "cascade": plan is not None, "shared_nodes": n_nodes, "parallelism": "single GPU"},
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "decode_queries_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "bytes": {"kv_unique": kv_unique, "kv_logical": kv_logical, "q": q_bytes, "out": o_bytes,
+                  "tables": tbl_bytes, "step_total_U": U},
+        "kernels": kern,
+        "ms_per_step_instrumented": round(ms_per_step_instrumented, 5),
+        "cold_ms_per_step_median": round(float(np.median(cold)), 5) if cold else None,
+        "host_us": {"plan_append": round(plan_append_us, 1), "plan_build": round(plan_build_us, 1)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

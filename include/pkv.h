@@ -1,0 +1,263 @@
+/*
+ * pkv.h - paged KV cache with shared-prefix decode attention for AMD gfx950 (C ABI).
+ *
+ * Two device operations and the host bookkeeping that feeds them:
+ *
+ *   pkv_kv_append          write each new token's K/V into the slot named by a slot
+ *                          mapping, after copying the valid rows of shared,
+ *                          partly filled tail blocks (copy-on-write).
+ *   pkv_paged_decode_attn  one query token per sequence attends to the sequence's
+ *                          cached K/V through its block table (grouped-query heads);
+ *                          optional cascade plan: blocks shared by several sequences
+ *                          are read once for all of them.
+ *
+ *   pkv_pool_* / pkv_seq_* host block pool with reference counts, fork, append
+ *                          planning (slots + copy-on-write list) and free.
+ *   pkv_plan_*             host cascade planner: finds the blocks that several block
+ *                          tables share and lays out the shared-prefix work.
+ *
+ * Sources.  "The Reasoning Engine Meltdown" (atozofsoftwareengineering.blog):
+ * §2.1 defines attention, softmax(Q K^T / sqrt(d_k)) V, the decode step (the new
+ * query attends to all cached keys and values) and the KV-size formula
+ * 2*L*H*d_h*S*P; §5 the page table with reference counts, zero-copy fork,
+ * copy-on-write and free-on-zero; §6 the manager's API and error conventions.
+ * "Dismantling the Memory Wall" (blog.bako.co): section "PagedAttention: The
+ * Virtual Memory Analogy for GPUs" fixes 16-token blocks and the block table
+ * (token t is in logical block t / block_size); section "Copy-on-Write and
+ * Advanced Decoding Strategies" the sharing of prompt blocks among beams with a
+ * new block only on divergence; section "RadixAttention" the longest shared
+ * prefix reused across requests, which the cascade pass exploits.
+ *
+ * Conventions for every function:
+ *   - Status codes are returned synchronously; on any non-OK status
+ *     pkv_last_error() holds a message (thread-local, valid until the next call
+ *     on the same thread).  Nothing is changed when a call fails.
+ *   - Device pointers are caller-owned device memory (e.g. torch tensors).  The
+ *     device calls enqueue work on `stream` (a hipStream_t; NULL = the default
+ *     stream), never synchronize and never allocate device memory.
+ *   - Pools and plans are library-owned host objects; destroy them explicitly.
+ *     They are not thread-safe: one thread at a time per object.
+ *   - dtype: PKV_F16 (IEEE binary16) or PKV_BF16; q, K and V share it.
+ *   - Page layout: k_pages and v_pages are [num_blocks][block_size][num_kv_heads]
+ *     [head_dim] elements, row-major; token slot s is block s / block_size, row
+ *     s % block_size.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,     /* bad argument: null pointer, negative size, inconsistent shape */
+  PKV_ERR_OOM = -2,         /* block pool exhausted; the pool is unchanged */
+  PKV_ERR_NOT_FOUND = -3,   /* unknown sequence id where one is required (fork parent, append) */
+  PKV_ERR_UNSUPPORTED = -4, /* dtype / head_dim / block_size / group not built into the library */
+  PKV_ERR_HIP = -5,         /* the HIP runtime reported an error while enqueueing */
+  PKV_ERR_WORKSPACE = -6    /* workspace smaller than pkv_decode_workspace_bytes() */
+} pkv_status;
+
+typedef enum { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef struct pkv_pool pkv_pool;
+typedef struct pkv_plan pkv_plan;
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Device operation 1: append new tokens' K/V (with copy-on-write).
+ *
+ * Defined by "The Reasoning Engine Meltdown", §5 (writes land only in pages the
+ * writer owns; a shared page is copied first) and "Dismantling the Memory Wall",
+ * "Copy-on-Write and Advanced Decoding Strategies" (a branch gets its own block
+ * when it diverges).  The copies and slots come from pkv_plan_append().
+ *
+ * Effect, in this order as far as the result is concerned:
+ *   1. for c in [0, num_cow): rows [0, cow_rows[c]) of block cow_src[c] are copied
+ *      to block cow_dst[c], for K and V, all heads;
+ *   2. for i in [0, num_tokens): if slot_mapping[i] >= 0, token slot
+ *      slot_mapping[i] of k_pages / v_pages is set to k_new[i] / v_new[i].
+ * One launch does both: a plan from pkv_plan_append() never makes step 2 write a
+ * row that step 1 reads or writes, so the two cannot race.  Slots < 0 are
+ * skipped (padding); slots >= num_blocks*block_size and copies naming blocks
+ * outside [0, num_blocks) or rows outside [0, block_size] are skipped by the
+ * device (never written), so a bad plan cannot write out of bounds.
+ *
+ *   k_pages, v_pages  device, [num_blocks][block_size][num_kv_heads][head_dim], dtype
+ *   k_new, v_new      device, [num_tokens][num_kv_heads][head_dim], dtype
+ *   slot_mapping      device, int64 [num_tokens]
+ *   cow_src, cow_dst, cow_rows  device, int32 [num_cow] (may be NULL when num_cow == 0)
+ * Requirements: num_kv_heads*head_dim*2 bytes a multiple of 16; 16-byte aligned
+ * pointers.  Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ * ---------------------------------------------------------------------------------------- */
+pkv_status pkv_kv_append(void* k_pages, void* v_pages, int64_t num_blocks, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                         const void* k_new, const void* v_new, int32_t num_tokens,
+                         const int64_t* slot_mapping,
+                         const int32_t* cow_src, const int32_t* cow_dst, const int32_t* cow_rows,
+                         int32_t num_cow, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Device operation 2: single-token decode attention over a paged KV cache.
+ *
+ * Defined by "The Reasoning Engine Meltdown", §2.1 (softmax(Q K^T / sqrt(d_k)) V;
+ * the decode query attends to all cached K_{1:t}, V_{1:t}) and "Dismantling the
+ * Memory Wall", "PagedAttention ..." (token t of row b is row t % block_size of
+ * physical block block_tables[b][t / block_size]).
+ *
+ *   out[b][h][:] = sum_t softmax_t(scale * <q[b][h], K_b[t][h / group]>) * V_b[t][h / group]
+ *
+ * over t in [0, seq_lens[b]), group = num_q_heads / num_kv_heads (query head h
+ * reads KV head h / group).  A row with seq_lens[b] == 0 gets out = 0.  Table
+ * entries past ceil(seq_lens[b] / block_size) are never read.
+ *
+ *   q             device, [batch][num_q_heads][head_dim], dtype
+ *   k_pages/v_pages  device, [num_blocks][block_size][num_kv_heads][head_dim], dtype
+ *   block_tables  device, int32 [batch][max_blocks_per_seq]
+ *   seq_lens      device, int32 [batch]
+ *   max_seq_len   host int >= every seq_lens[b] (sizes the split grid; lengths above it
+ *                 are clamped to it, and to max_blocks_per_seq*block_size, on the device)
+ *   scale         softmax scale (1/sqrt(head_dim) for standard attention)
+ *   plan          NULL: every row is decoded on its own (split-K over its tokens).
+ *                 Non-NULL: a cascade plan built by pkv_plan_build() from the same
+ *                 block tables and lengths and uploaded with pkv_plan_upload(); the
+ *                 shared blocks are then read once per KV head for all rows sharing
+ *                 them, and each row's own remainder is decoded split-K.
+ *   workspace     device scratch of at least pkv_decode_workspace_bytes(...) bytes
+ *                 (fp32 partial results); contents on entry are ignored.
+ *   out           device, float32 [batch][num_q_heads][head_dim]
+ * Supported: block_size 16; head_dim 64 or 128; group in {1, 2, 4, 8}.  Block ids
+ * outside [0, num_blocks) are not read (their tokens are dropped).
+ * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ * ---------------------------------------------------------------------------------------- */
+pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t dtype,
+                                 const void* k_pages, const void* v_pages, int64_t num_blocks,
+                                 int32_t block_size,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                 const pkv_plan* plan, void* workspace, size_t workspace_bytes,
+                                 float* out, void* stream);
+
+/* Bytes of device workspace pkv_paged_decode_attn needs for these sizes (and plan,
+ * which may be NULL).  Returns 0 for invalid arguments (see pkv_last_error). */
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_seq_len, const pkv_plan* plan);
+
+/* ------------------------------------------------------------------------------------------
+ * Host block pool ("The Reasoning Engine Meltdown", §5 and §6).
+ *
+ * Blocks have reference counts.  The free list is a FIFO seeded by `free_order`
+ * (a permutation of [0, num_blocks), NULL for 0, 1, 2, ...): allocation takes
+ * from the front, freed blocks go to the back, in table order.  Sequence ids are
+ * arbitrary int64 keys.  Not thread-safe.
+ * ---------------------------------------------------------------------------------------- */
+
+/* Returns NULL on invalid arguments (free_order not a permutation, sizes <= 0). */
+pkv_pool* pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* New root sequence of num_tokens tokens: ceil(num_tokens/block_size) blocks with
+ * count 1.  PKV_ERR_OOM (nothing changed) if too few blocks are free;
+ * PKV_ERR_INVALID if seq exists or num_tokens < 0. */
+pkv_status pkv_seq_alloc(pkv_pool* pool, int64_t seq, int32_t num_tokens);
+
+/* child gets a copy of parent's block table (a partly filled last block included)
+ * and the same length; every block's count goes up by one; no KV data moves.
+ * PKV_ERR_NOT_FOUND for an unknown parent, PKV_ERR_INVALID if child exists. */
+pkv_status pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t child);
+
+/* Drop the sequence: counts go down in table order, a block reaching 0 goes to
+ * the back of the free list.  An unknown id is a no-op (PKV_OK). */
+pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq);
+
+/* Append one token to each of seqs[0..n) in that order (a sequence at most once).
+ * For each: pos = len; j = pos / block_size; off = pos % block_size;
+ *   off == 0                 -> a new block is appended to the table;
+ *   off > 0, count(t[j]) > 1 -> copy-on-write: a new block Y gets rows [0, off) of
+ *                               t[j] (one entry of the cow_* outputs), count(t[j])
+ *                               drops by one, t[j] = Y;
+ *   slot_out[i] = t[j]*block_size + off; len += 1.
+ * The batch is all-or-nothing: PKV_ERR_OOM with nothing changed if the free list
+ * cannot cover it.  cow_src/cow_dst/cow_rows need room for n entries; *num_cow
+ * receives the count.  PKV_ERR_NOT_FOUND for an unknown id. */
+pkv_status pkv_plan_append(pkv_pool* pool, const int64_t* seqs, int32_t n, int64_t* slot_out,
+                           int32_t* cow_src, int32_t* cow_dst, int32_t* cow_rows, int32_t* num_cow);
+
+/* Write the block tables ([n][max_blocks], padded with -1) and lengths of seqs. */
+pkv_status pkv_export_tables(const pkv_pool* pool, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                             int32_t* tables_out, int32_t* lens_out);
+
+int32_t pkv_seq_len(const pkv_pool* pool, int64_t seq);     /* -1 if unknown */
+int32_t pkv_refcount(const pkv_pool* pool, int32_t block);  /* -1 if out of range */
+int32_t pkv_free_count(const pkv_pool* pool);
+int32_t pkv_num_seqs(const pkv_pool* pool);
+/* Copy up to cap free-list entries, front first; returns the free count. */
+int32_t pkv_free_list(const pkv_pool* pool, int32_t* out, int32_t cap);
+
+/* ------------------------------------------------------------------------------------------
+ * Cascade planner ("Dismantling the Memory Wall", "RadixAttention": a prefix tree
+ * of shared token sequences whose KV is referenced, not copied; "The Reasoning
+ * Engine Meltdown", §5: branches point at the same physical pages).
+ *
+ * From host copies of the block tables and lengths, build a trie over (logical
+ * block index, physical block id).  Every maximal run of *full* blocks that the
+ * same set of >= min_members rows shares becomes a node; each row's blocks after
+ * its last node are its private remainder.  The decode then reads each node's
+ * blocks once per KV head for all of its rows (matrix-core pass) and writes one
+ * partial result per (row, head, node), merged with the remainder's partials.
+ * ---------------------------------------------------------------------------------------- */
+
+/* Returns NULL on invalid arguments (see pkv_last_error).  min_members >= 2. */
+pkv_plan* pkv_plan_build(const int32_t* block_tables, const int32_t* seq_lens, int32_t batch,
+                         int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t min_members);
+void pkv_plan_destroy(pkv_plan* plan);
+
+/* Bytes of device memory the plan's tables need. */
+size_t pkv_plan_device_bytes(const pkv_plan* plan);
+
+/* Copy the plan's tables into caller-owned device memory `device_buf` (at least
+ * pkv_plan_device_bytes bytes) on `stream` and bind it to the plan.  The copy is
+ * ordered on `stream`; later decode calls on other streams must be ordered
+ * after it by the caller. */
+pkv_status pkv_plan_upload(pkv_plan* plan, void* device_buf, size_t bytes, void* stream);
+
+/* Plan inspection (host): number of shared nodes, shared tokens summed over
+ * nodes, tokens each row reads through nodes. */
+int32_t pkv_plan_num_nodes(const pkv_plan* plan);
+/* For node i: number of blocks, number of member rows; copies its block ids and
+ * member rows into the given arrays when non-NULL (sized by the returned counts). */
+pkv_status pkv_plan_node(const pkv_plan* plan, int32_t node, int32_t* num_blocks, int32_t* num_members,
+                         int32_t* blocks_out, int32_t* members_out);
+/* For row b: tokens covered by its nodes (its remainder starts there) and the
+ * number of nodes on its path. */
+pkv_status pkv_plan_row(const pkv_plan* plan, int32_t row, int32_t* shared_tokens, int32_t* depth);
+
+/* ------------------------------------------------------------------------------------------
+ * Kernel timing (for measurement).  When enabled, every kernel launch of the
+ * library is bracketed with HIP events on its own stream; pkv_timing_read()
+ * synchronizes those events and returns the summed duration and count per
+ * kernel since the last reset.  Kernel ids: 0 append, 1 split-K decode,
+ * 2 partial merge, 3 cascade.  Costs two event records per launch when on.
+ * ---------------------------------------------------------------------------------------- */
+enum { PKV_KERNEL_APPEND = 0, PKV_KERNEL_DECODE_SPLIT = 1, PKV_KERNEL_MERGE = 2, PKV_KERNEL_CASCADE = 3,
+       PKV_NUM_KERNELS = 4 };
+pkv_status pkv_timing_enable(int32_t on);
+pkv_status pkv_timing_reset(void);
+pkv_status pkv_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,408 @@
+"""Python binding for libpkv: paged KV cache append and shared-prefix decode attention on gfx950.
+
+Argument marshalling only.  Every step of the path (block-table gather,
+split-K attention, cascade pass, partial merge, append / copy-on-write, block
+pool and cascade planning) runs in the native library ``libpkv.so`` built from
+``csrc/``; PyTorch only provides device memory and streams.  Importing this
+package fails loudly if the library has not been built
+(``python -m paged_kv_cache_21_amd.build``); there is no fallback.
+
+The names mirror the C ABI in ``include/pkv.h``.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "PkvError", "PkvInvalid", "PkvOOM", "PkvNotFound", "PkvUnsupported", "PkvWorkspaceError", "PkvHipError",
+    "kv_append", "paged_decode_attn", "decode_workspace_bytes", "BlockPool", "CascadePlan",
+    "timing_enable", "timing_reset", "timing_read", "KERNELS", "lib", "LIB_PATH", "version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_NOT_FOUND, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP, PKV_ERR_WORKSPACE = (
+    0, -1, -2, -3, -4, -5, -6)
+PKV_F16, PKV_BF16 = 0, 1
+KERNELS = {"append": 0, "decode_split": 1, "merge": 2, "cascade": 3}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class PkvInvalid(PkvError, ValueError):
+    pass
+
+
+class PkvOOM(PkvError, MemoryError):
+    pass
+
+
+class PkvNotFound(PkvError, KeyError):
+    pass
+
+
+class PkvUnsupported(PkvError, NotImplementedError):
+    pass
+
+
+class PkvWorkspaceError(PkvError, ValueError):
+    pass
+
+
+class PkvHipError(PkvError):
+    pass
+
+
+_ERRORS = {PKV_ERR_INVALID: PkvInvalid, PKV_ERR_OOM: PkvOOM, PKV_ERR_NOT_FOUND: PkvNotFound,
+           PKV_ERR_UNSUPPORTED: PkvUnsupported, PKV_ERR_HIP: PkvHipError, PKV_ERR_WORKSPACE: PkvWorkspaceError}
+
+_c = ctypes
+_vp, _i32, _i64, _sz, _f32 = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_size_t, _c.c_float
+
+_SIGNATURES = {
+    "pkv_last_error": (_c.c_char_p, []),
+    "pkv_version": (_c.c_char_p, []),
+    "pkv_kv_append": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp]),
+    "pkv_paged_decode_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32,
+                                     _f32, _vp, _vp, _sz, _vp, _vp]),
+    "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_pool_create": (_vp, [_i32, _i32, _vp]),
+    "pkv_pool_destroy": (None, [_vp]),
+    "pkv_seq_alloc": (_i32, [_vp, _i64, _i32]),
+    "pkv_seq_fork": (_i32, [_vp, _i64, _i64]),
+    "pkv_seq_free": (_i32, [_vp, _i64]),
+    "pkv_plan_append": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "pkv_export_tables": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "pkv_seq_len": (_i32, [_vp, _i64]),
+    "pkv_refcount": (_i32, [_vp, _i32]),
+    "pkv_free_count": (_i32, [_vp]),
+    "pkv_num_seqs": (_i32, [_vp]),
+    "pkv_free_list": (_i32, [_vp, _vp, _i32]),
+    "pkv_plan_build": (_vp, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_plan_destroy": (None, [_vp]),
+    "pkv_plan_device_bytes": (_sz, [_vp]),
+    "pkv_plan_upload": (_i32, [_vp, _vp, _sz, _vp]),
+    "pkv_plan_num_nodes": (_i32, [_vp]),
+    "pkv_plan_node": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp]),
+    "pkv_plan_row": (_i32, [_vp, _i32, _vp, _vp]),
+    "pkv_timing_enable": (_i32, [_i32]),
+    "pkv_timing_reset": (_i32, []),
+    "pkv_timing_read": (_i32, [_i32, _vp, _vp]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_21_amd.build` "
+                          "(hipcc, gfx950). There is no fallback implementation.")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+_lib = _load()
+
+
+def lib():
+    """The loaded ctypes handle of libpkv.so."""
+    return _lib
+
+
+def version():
+    return _lib.pkv_version().decode()
+
+
+def _check(status):
+    if status != PKV_OK:
+        msg = _lib.pkv_last_error().decode(errors="replace")
+        raise _ERRORS.get(status, PkvError)(status, msg)
+
+
+def _ptr(x):
+    """Device / host address of a torch tensor or numpy array (None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return x.data_ptr()
+
+
+def _dtype_code(t, dtype):
+    import torch
+
+    if dtype is not None:
+        return {"f16": PKV_F16, "bf16": PKV_BF16, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}[dtype]
+    if t.dtype == torch.float16:
+        return PKV_F16
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise ValueError("pass dtype='f16'|'bf16' for bit-pattern (int16) tensors")
+
+
+def _stream(stream, like):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream(like.device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _require(cond, msg):
+    if not cond:
+        raise PkvInvalid(PKV_ERR_INVALID, msg)
+
+
+# ---------------------------------------------------------------------------
+# device operations
+
+
+def kv_append(k_pages, v_pages, k_new, v_new, slot_mapping, cow_src=None, cow_dst=None, cow_rows=None,
+              dtype=None, stream=None):
+    """Copy-on-write the listed block prefixes, then write k_new[i]/v_new[i] to slot slot_mapping[i].
+
+    k_pages, v_pages: [num_blocks, block_size, Hkv, d] device tensors (fp16/bf16, or int16 bits with
+    ``dtype``); k_new, v_new: [N, Hkv, d]; slot_mapping int64 [N]; cow_* int32 [n_cow] (device).
+    """
+    _require(k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "k_pages/v_pages must be equal 4-D tensors")
+    _require(k_pages.is_contiguous() and v_pages.is_contiguous(), "pages must be contiguous")
+    nblk, bs, hkv, d = k_pages.shape
+    n = int(slot_mapping.numel())
+    _require(tuple(k_new.shape) == (n, hkv, d) and tuple(v_new.shape) == (n, hkv, d), "k_new/v_new must be [N, Hkv, d]")
+    _require(k_new.is_contiguous() and v_new.is_contiguous() and slot_mapping.is_contiguous(), "inputs must be contiguous")
+    import torch
+
+    _require(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
+    n_cow = 0 if cow_src is None else int(cow_src.numel())
+    if n_cow:
+        _require(cow_src.dtype == cow_dst.dtype == cow_rows.dtype == torch.int32, "cow arrays must be int32")
+        _require(cow_dst.numel() == n_cow and cow_rows.numel() == n_cow, "cow arrays must have equal length")
+    _check(_lib.pkv_kv_append(_ptr(k_pages), _ptr(v_pages), nblk, bs, hkv, d, _dtype_code(k_pages, dtype),
+                              _ptr(k_new), _ptr(v_new), n, _ptr(slot_mapping),
+                              _ptr(cow_src) if n_cow else None, _ptr(cow_dst) if n_cow else None,
+                              _ptr(cow_rows) if n_cow else None, n_cow, _stream(stream, k_pages)))
+
+
+def decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan=None):
+    n = _lib.pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                        plan._handle if plan is not None else None)
+    if n == 0 and batch > 0:
+        msg = _lib.pkv_last_error().decode()
+        if msg:
+            raise PkvInvalid(PKV_ERR_INVALID, msg)
+    return int(n)
+
+
+def paged_decode_attn(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len, scale=None, plan=None,
+                      workspace=None, out=None, dtype=None, stream=None):
+    """o[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the row's seq_lens[b] tokens (fp32 output).
+
+    q: [B, Hq, d]; pages [num_blocks, 16, Hkv, d]; block_tables int32 [B, max_blocks];
+    seq_lens int32 [B] (all device tensors).  ``plan``: an uploaded CascadePlan or None.
+    ``workspace``: a device tensor of at least decode_workspace_bytes(...) bytes (allocated if None).
+    """
+    import torch
+
+    _require(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "bad q / page ranks")
+    _require(q.is_contiguous() and k_pages.is_contiguous() and v_pages.is_contiguous(), "inputs must be contiguous")
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables and lengths must be int32")
+    _require(block_tables.is_contiguous() and seq_lens.is_contiguous(), "tables and lengths must be contiguous")
+    B, hq, d = q.shape
+    nblk, bs, hkv, dk = k_pages.shape
+    _require(dk == d, "head_dim of q and pages differ")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == B and seq_lens.numel() == B, "bad table shape")
+    max_blocks = int(block_tables.shape[1])
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    hplan = plan._handle if plan is not None else None
+    need = decode_workspace_bytes(B, hq, hkv, d, int(max_seq_len), plan)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, hq, d), "bad out tensor")
+    _check(_lib.pkv_paged_decode_attn(_ptr(q), B, hq, hkv, d, _dtype_code(q, dtype), _ptr(k_pages), _ptr(v_pages),
+                                      nblk, bs, _ptr(block_tables), max_blocks, _ptr(seq_lens), int(max_seq_len),
+                                      float(scale), hplan, _ptr(workspace), ws_bytes, _ptr(out),
+                                      _stream(stream, q)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# host block pool
+
+
+class BlockPool:
+    """Reference-counted block pool with fork / copy-on-write append / free (runs in libpkv)."""
+
+    def __init__(self, num_blocks, block_size=16, free_order=None):
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(free_order, dtype=np.int32)
+            _require(order.shape == (num_blocks,), "free_order must have num_blocks entries")
+        self._order = order
+        h = _lib.pkv_pool_create(int(num_blocks), int(block_size), _ptr(order))
+        if not h:
+            raise PkvInvalid(PKV_ERR_INVALID, _lib.pkv_last_error().decode())
+        self._handle = h
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h:
+            _lib.pkv_pool_destroy(h)
+            self._handle = None
+
+    def alloc(self, seq, num_tokens):
+        _check(_lib.pkv_seq_alloc(self._handle, int(seq), int(num_tokens)))
+
+    def fork(self, parent, child):
+        _check(_lib.pkv_seq_fork(self._handle, int(parent), int(child)))
+
+    def free(self, seq):
+        _check(_lib.pkv_seq_free(self._handle, int(seq)))
+
+    def plan_append(self, seqs):
+        """Returns (slots int64 [n], cows int32 [n_cow, 3] of (src, dst, rows))."""
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        slots = np.empty(n, dtype=np.int64)
+        src = np.empty(max(n, 1), dtype=np.int32)
+        dst = np.empty(max(n, 1), dtype=np.int32)
+        rows = np.empty(max(n, 1), dtype=np.int32)
+        ncow = np.zeros(1, dtype=np.int32)
+        _check(_lib.pkv_plan_append(self._handle, _ptr(s), n, _ptr(slots), _ptr(src), _ptr(dst), _ptr(rows),
+                                    _ptr(ncow)))
+        k = int(ncow[0])
+        return slots, np.stack([src[:k], dst[:k], rows[:k]], axis=1)
+
+    def export_tables(self, seqs, max_blocks):
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        bt = np.empty((s.shape[0], max_blocks), dtype=np.int32)
+        lens = np.empty(s.shape[0], dtype=np.int32)
+        _check(_lib.pkv_export_tables(self._handle, _ptr(s), s.shape[0], int(max_blocks), _ptr(bt), _ptr(lens)))
+        return bt, lens
+
+    def table(self, seq):
+        n = self.length(seq)
+        if n < 0:
+            raise PkvNotFound(PKV_ERR_NOT_FOUND, f"sequence {seq} does not exist")
+        nb = -(-n // self.block_size)
+        bt, _ = self.export_tables([seq], max(nb, 1))
+        return [int(x) for x in bt[0, :nb]]
+
+    def length(self, seq):
+        return int(_lib.pkv_seq_len(self._handle, int(seq)))
+
+    def refcount(self, block):
+        return int(_lib.pkv_refcount(self._handle, int(block)))
+
+    def free_count(self):
+        return int(_lib.pkv_free_count(self._handle))
+
+    def num_seqs(self):
+        return int(_lib.pkv_num_seqs(self._handle))
+
+    def free_list(self):
+        n = self.free_count()
+        out = np.empty(max(n, 1), dtype=np.int32)
+        _lib.pkv_free_list(self._handle, _ptr(out), n)
+        return [int(x) for x in out[:n]]
+
+    def __contains__(self, seq):
+        return self.length(seq) >= 0
+
+
+# ---------------------------------------------------------------------------
+# cascade plan
+
+
+class CascadePlan:
+    """Shared-prefix plan built on the host from block tables and lengths (numpy int32)."""
+
+    def __init__(self, block_tables, seq_lens, num_q_heads, num_kv_heads, block_size=16, min_members=2):
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        _require(bt.ndim == 2 and sl.shape == (bt.shape[0],), "block_tables [B, max_blocks], seq_lens [B]")
+        h = _lib.pkv_plan_build(_ptr(bt), _ptr(sl), bt.shape[0], bt.shape[1], int(block_size), int(num_q_heads),
+                                int(num_kv_heads), int(min_members))
+        if not h:
+            raise PkvInvalid(PKV_ERR_INVALID, _lib.pkv_last_error().decode())
+        self._handle = h
+        self.batch = bt.shape[0]
+        self.device_buffer = None
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h:
+            _lib.pkv_plan_destroy(h)
+            self._handle = None
+
+    @property
+    def device_bytes(self):
+        return int(_lib.pkv_plan_device_bytes(self._handle))
+
+    def upload(self, device="cuda", stream=None, buffer=None):
+        """Copy the plan's tables to device memory (a torch buffer it keeps) and bind them."""
+        import torch
+
+        n = self.device_bytes
+        if buffer is None:
+            buffer = torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+        _check(_lib.pkv_plan_upload(self._handle, _ptr(buffer), buffer.numel(), _stream(stream, buffer)))
+        self.device_buffer = buffer
+        return self
+
+    @property
+    def num_nodes(self):
+        return int(_lib.pkv_plan_num_nodes(self._handle))
+
+    def node(self, i):
+        """(block ids, member rows) of shared node i."""
+        nb = np.zeros(1, dtype=np.int32)
+        nm = np.zeros(1, dtype=np.int32)
+        _check(_lib.pkv_plan_node(self._handle, int(i), _ptr(nb), _ptr(nm), None, None))
+        blocks = np.empty(max(int(nb[0]), 1), dtype=np.int32)
+        members = np.empty(max(int(nm[0]), 1), dtype=np.int32)
+        _check(_lib.pkv_plan_node(self._handle, int(i), None, None, _ptr(blocks), _ptr(members)))
+        return blocks[: int(nb[0])].copy(), members[: int(nm[0])].copy()
+
+    def row(self, b):
+        """(shared tokens, depth) of row b."""
+        st = np.zeros(1, dtype=np.int32)
+        dp = np.zeros(1, dtype=np.int32)
+        _check(_lib.pkv_plan_row(self._handle, int(b), _ptr(st), _ptr(dp)))
+        return int(st[0]), int(dp[0])
+
+
+# ---------------------------------------------------------------------------
+# timing
+
+
+def timing_enable(on=True):
+    _check(_lib.pkv_timing_enable(1 if on else 0))
+
+
+def timing_reset():
+    _check(_lib.pkv_timing_reset())
+
+
+def timing_read(kernel):
+    """(total milliseconds, launches) for kernel name or id since the last reset."""
+    k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    ms = np.zeros(1, dtype=np.float64)
+    cnt = np.zeros(1, dtype=np.int64)
+    _check(_lib.pkv_timing_read(k, _ptr(ms), _ptr(cnt)))
+    return float(ms[0]), int(cnt[0])

@@ -1,0 +1,333 @@
+// C-ABI entry points for the device operations: argument checks on the host,
+// workspace layout, kernel dispatch, optional per-kernel event timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "host_common.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace pkv {
+
+namespace {
+thread_local std::string g_error;
+}
+
+void set_error_message(const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+}
+
+void clear_error() { g_error.clear(); }
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// kernel timing
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  struct Pending {
+    int kernel;
+    hipEvent_t start, stop;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> spare;
+  double total_ms[PKV_NUM_KERNELS] = {};
+  int64_t count[PKV_NUM_KERNELS] = {};
+};
+
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+hipEvent_t take_event(Timing& t) {
+  if (!t.spare.empty()) {
+    hipEvent_t e = t.spare.back();
+    t.spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+pkv_status launch(int kernel, const char* what, hipStream_t stream, F&& f) {
+  Timing& t = timing();
+  hipEvent_t start = nullptr, stop = nullptr;
+  if (t.on) {
+    std::lock_guard<std::mutex> lk(t.mu);
+    start = take_event(t);
+    stop = take_event(t);
+    if (start) (void)hipEventRecord(start, stream);
+  }
+  const hipError_t err = f();
+  if (t.on && start && stop) {
+    (void)hipEventRecord(stop, stream);
+    std::lock_guard<std::mutex> lk(t.mu);
+    t.pending.push_back({kernel, start, stop});
+  }
+  if (err != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+  return PKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// split-K sizing shared by the workspace query and the decode call
+
+struct DecodeLayout {
+  int32_t split_len;
+  int32_t max_splits;
+  int32_t slots;
+  size_t acc_bytes;
+  size_t ml_offset;
+  size_t bytes;
+};
+
+// The split length targets a few thousand single-wave work units (the chip runs
+// ~2-3 thousand of them at once): short enough to fill 256 CUs when rows are
+// few, long enough that per-unit overhead (q load, partial write and re-read)
+// stays a few percent of the K/V bytes.
+DecodeLayout decode_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_seq_len, const pkv_plan* plan) {
+  DecodeLayout L{};
+  const int32_t min_shared = [&] {
+    if (!plan || plan->batch == 0) return 0;
+    int32_t m = plan->row_info[0];
+    for (int32_t b = 1; b < plan->batch; ++b) m = std::min(m, plan->row_info[2 * b]);
+    return m;
+  }();
+  const int64_t span = std::max<int64_t>(0, static_cast<int64_t>(max_seq_len) - min_shared);
+  const int64_t pairs = static_cast<int64_t>(batch) * num_kv_heads;
+  auto units = [&](int64_t s) { return pairs * ((span + s - 1) / s); };
+  int32_t split = 256;
+  while (split < 8192 && units(split) > 16384) split *= 2;
+  while (split > 64 && units(split) < 2048) split /= 2;
+  L.split_len = split;
+  L.max_splits = static_cast<int32_t>((span + split - 1) / split);
+  L.slots = L.max_splits + (plan ? plan->max_depth : 0);
+  const size_t recs = static_cast<size_t>(batch) * L.slots * num_q_heads;
+  L.acc_bytes = recs * head_dim * sizeof(float);
+  L.ml_offset = (L.acc_bytes + 255) & ~static_cast<size_t>(255);
+  L.bytes = L.ml_offset + recs * sizeof(float2);
+  return L;
+}
+
+bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+}  // namespace
+}  // namespace pkv
+
+using pkv::fail;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return pkv::g_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+pkv_status pkv_kv_append(void* k_pages, void* v_pages, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t dtype, const void* k_new, const void* v_new, int32_t num_tokens,
+                         const int64_t* slot_mapping, const int32_t* cow_src, const int32_t* cow_dst,
+                         const int32_t* cow_rows, int32_t num_cow, void* stream) {
+  pkv::clear_error();
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_kv_append: dtype %d", dtype);
+  if (num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_tokens < 0 || num_cow < 0)
+    return fail(PKV_ERR_INVALID, "pkv_kv_append: negative or zero size");
+  const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if ((row_elems * 2) % 16 != 0 || row_elems > (1 << 24))
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_kv_append: num_kv_heads*head_dim*2 must be a multiple of 16 bytes");
+  if (num_tokens > 0 && (!k_pages || !v_pages || !k_new || !v_new || !slot_mapping))
+    return fail(PKV_ERR_INVALID, "pkv_kv_append: null pointer");
+  if (num_cow > 0 && (!k_pages || !v_pages || !cow_src || !cow_dst || !cow_rows))
+    return fail(PKV_ERR_INVALID, "pkv_kv_append: null copy-on-write pointer");
+  if (!pkv::aligned16(k_pages) || !pkv::aligned16(v_pages) || !pkv::aligned16(k_new) || !pkv::aligned16(v_new))
+    return fail(PKV_ERR_INVALID, "pkv_kv_append: page and token pointers must be 16-byte aligned");
+  if (static_cast<int64_t>(num_tokens) + num_cow > 0x7fffffff) return fail(PKV_ERR_INVALID, "pkv_kv_append: too many work items");
+  pkv::AppendArgs a{static_cast<uint16_t*>(k_pages), static_cast<uint16_t*>(v_pages), num_blocks, block_size,
+                    static_cast<int32_t>(row_elems), static_cast<const uint16_t*>(k_new),
+                    static_cast<const uint16_t*>(v_new), num_tokens, slot_mapping, cow_src, cow_dst, cow_rows, num_cow};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return pkv::launch(PKV_KERNEL_APPEND, "kv_append", s, [&] { return pkv::launch_kv_append(a, s); });
+}
+
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_seq_len, const pkv_plan* plan) {
+  pkv::clear_error();
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
+      num_q_heads % num_kv_heads != 0) {
+    fail(PKV_ERR_INVALID, "pkv_decode_workspace_bytes: invalid sizes");
+    return 0;
+  }
+  if (plan && plan->batch != batch) {
+    fail(PKV_ERR_INVALID, "pkv_decode_workspace_bytes: plan built for batch %d, not %d", plan->batch, batch);
+    return 0;
+  }
+  return pkv::decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan).bytes;
+}
+
+pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
+                                 int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                 const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out,
+                                 void* stream) {
+  pkv::clear_error();
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn: dtype %d", dtype);
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
+      max_seq_len < 0)
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: negative or zero size");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: num_q_heads %d not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn: head_dim %d (built: 64, 128)", head_dim);
+  if (block_size != 16) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn: block_size %d (built: 16)", block_size);
+  if (!pkv::supported_group(group))
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn: GQA group %d (built: 1, 2, 4, 8)", group);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: scale is not finite");
+  if (plan) {
+    if (plan->batch != batch || plan->group != group || plan->num_kv_heads != num_kv_heads ||
+        plan->block_size != block_size || plan->max_blocks != max_blocks_per_seq)
+      return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: plan was built for different shapes");
+    if (!plan->device) return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: plan not uploaded (pkv_plan_upload)");
+  }
+  const pkv::DecodeLayout L = pkv::decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan);
+  if (batch == 0) return PKV_OK;
+  if (!q || !k_pages || !v_pages || !block_tables || !seq_lens || !out)
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: null pointer");
+  if (!pkv::aligned16(q) || !pkv::aligned16(k_pages) || !pkv::aligned16(v_pages) || !pkv::aligned16(out))
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: q, pages and out must be 16-byte aligned");
+  if (workspace_bytes < L.bytes || (L.bytes > 0 && !workspace))
+    return fail(PKV_ERR_WORKSPACE, "pkv_paged_decode_attn: workspace of %zu bytes, %zu needed", workspace_bytes,
+                L.bytes);
+  if (!pkv::aligned16(workspace)) return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: workspace must be 16-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* acc = static_cast<float*>(workspace);
+  float2* ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + L.ml_offset);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const int32_t* row_info = plan ? plan->device + plan->off_row_info : nullptr;
+
+  if (plan && plan->num_items() > 0) {
+    pkv::CascadeArgs c{static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k_pages),
+                       static_cast<const uint16_t*>(v_pages),
+                       plan->device + plan->off_items,
+                       plan->device + plan->off_nodes,
+                       plan->device + plan->off_blocks,
+                       plan->device + plan->off_members,
+                       acc,
+                       ml,
+                       num_blocks,
+                       plan->num_items(),
+                       num_q_heads,
+                       num_kv_heads,
+                       L.slots,
+                       scale_log2};
+    pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
+                                [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
+    if (st != PKV_OK) return st;
+  }
+  if (L.max_splits > 0) {
+    pkv::SplitArgs sa{static_cast<const uint16_t*>(q),
+                      static_cast<const uint16_t*>(k_pages),
+                      static_cast<const uint16_t*>(v_pages),
+                      block_tables,
+                      seq_lens,
+                      row_info,
+                      acc,
+                      ml,
+                      num_blocks,
+                      batch,
+                      num_q_heads,
+                      num_kv_heads,
+                      max_blocks_per_seq,
+                      max_seq_len,
+                      L.split_len,
+                      L.max_splits,
+                      L.slots,
+                      scale_log2};
+    pkv_status st = pkv::launch(PKV_KERNEL_DECODE_SPLIT, "decode_split", s,
+                                [&] { return pkv::launch_decode_split(dtype, head_dim, group, sa, s); });
+    if (st != PKV_OK) return st;
+  }
+  pkv::MergeArgs ma{seq_lens, row_info, acc, ml, out, batch, num_q_heads, max_blocks_per_seq, max_seq_len,
+                    L.split_len, L.slots};
+  return pkv::launch(PKV_KERNEL_MERGE, "merge", s, [&] { return pkv::launch_merge(head_dim, ma, s); });
+}
+
+pkv_status pkv_plan_upload(pkv_plan* plan, void* device_buf, size_t bytes, void* stream) {
+  pkv::clear_error();
+  if (!plan || !device_buf) return fail(PKV_ERR_INVALID, "pkv_plan_upload: null argument");
+  const size_t need = plan->image.size() * sizeof(int32_t);
+  if (bytes < need) return fail(PKV_ERR_INVALID, "pkv_plan_upload: buffer of %zu bytes, %zu needed", bytes, need);
+  const hipError_t e = hipMemcpyAsync(device_buf, plan->image.data(), need, hipMemcpyHostToDevice,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_plan_upload: %s", hipGetErrorString(e));
+  plan->device = static_cast<const int32_t*>(device_buf);
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_enable(int32_t on) {
+  pkv::clear_error();
+  auto& t = pkv::timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.on = on != 0;
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_reset(void) {
+  pkv::clear_error();
+  auto& t = pkv::timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& p : t.pending) {
+    (void)hipEventSynchronize(p.stop);
+    t.spare.push_back(p.start);
+    t.spare.push_back(p.stop);
+  }
+  t.pending.clear();
+  for (int k = 0; k < PKV_NUM_KERNELS; ++k) {
+    t.total_ms[k] = 0;
+    t.count[k] = 0;
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  pkv::clear_error();
+  if (kernel < 0 || kernel >= PKV_NUM_KERNELS) return fail(PKV_ERR_INVALID, "pkv_timing_read: kernel id %d", kernel);
+  auto& t = pkv::timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& p : t.pending) {
+    hipError_t e = hipEventSynchronize(p.stop);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.start, p.stop);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_timing_read: %s", hipGetErrorString(e));
+    t.total_ms[p.kernel] += ms;
+    t.count[p.kernel] += 1;
+    t.spare.push_back(p.start);
+    t.spare.push_back(p.stop);
+  }
+  t.pending.clear();
+  if (total_ms) *total_ms = t.total_ms[kernel];
+  if (launches) *launches = t.count[kernel];
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,287 @@
+// Shared-prefix ("cascade") decode pass on the gfx950 matrix cores.
+//
+// When many rows' block tables point at the same physical blocks — branches of
+// one search tree forked from a common prefix ("The Reasoning Engine Meltdown",
+// §5: children point at the parent's pages; "Dismantling the Memory Wall",
+// "RadixAttention": one cached copy of a shared prefix serves every request
+// that matches it) — the rows' queries against that prefix form a dense
+// product: Q_n [rows x d] against K_n [tokens x d].  This pass reads each
+// shared block once per KV head and work item and evaluates it for up to 64
+// query rows at a time with MFMA:
+//
+//   S^T = K_n Q_n^T        (v_mfma_f32_16x16x32, K from LDS as the A operand,
+//                           the queries held in registers as the B operand)
+//   online softmax down each column of S^T (one column per query row)
+//   O^T += V_n^T P^T       (V staged transposed in LDS as the A operand; P^T comes
+//                           straight out of the S^T accumulator layout)
+//
+// P is fed to the matrix core as two 16-bit terms, p = p_hi + p_lo, so the
+// product keeps ~16 bits of the fp32 weights rather than 8.
+//
+// Each (row, query head) gets one partial (m, l, acc) per shared node, in the
+// same log2-scaled form as the split-K partials, and the merge kernel combines
+// them with the row's own remainder.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pkv {
+
+namespace {
+
+template <class DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c);
+
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<BF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
+  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
+
+}  // namespace
+
+// Work-group: 4 waves, 64 query rows (16 per wave).  Row rho of a node is
+// (member rho / G, query head hkv*G + rho % G).  Tokens are processed in chunks
+// of 32 (two blocks): the work-group stages K [32 x D] and V^T [D x 32] in LDS,
+// each wave evaluates its 16 rows.
+//
+// MFMA 16x16x32 operand layout used (lane l, element j of 8): A row l % 16,
+// k = 8*(l / 16) + j; B column l % 16, same k; accumulator element j of lane l
+// is (row 4*(l / 16) + j, column l % 16).  A contraction index may be permuted
+// freely as long as A and B agree; the PV product uses the token order the S^T
+// accumulator leaves in each lane.
+template <class DT, int D, int G>
+__global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
+  constexpr int KPITCH = D + 8;  // K row pitch in LDS (elements); the pad spreads rows over banks
+  constexpr int VPITCH = 18;     // V^T row pitch in LDS (32-bit words = 2 tokens each; 16 used)
+  constexpr int NKS = D / 32;    // k-steps of the QK product
+  constexpr int NDT = D / 16;    // 16-wide d tiles of the PV product
+  constexpr int KVEC = 32 * D / 8;             // 16-byte vectors per K chunk
+  constexpr int KVEC_PER_THREAD = KVEC / 256;  // 1 (D=64) or 2 (D=128)
+  static_assert(KVEC_PER_THREAD >= 1, "unsupported head_dim");
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[32 * KPITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t vt_lds[D * VPITCH];
+
+  const int item = blockIdx.x;
+  const int node = a.items[3 * item];
+  if (node < 0) return;  // padding item (uniform for the work-group)
+  const int hkv = a.items[3 * item + 1];
+  const int row0 = a.items[3 * item + 2];
+  const int blk_off = a.nodes[4 * node + 0];
+  const int nblk = a.nodes[4 * node + 1];
+  const int mem_off = a.nodes[4 * node + 2];
+  const int nmem = a.nodes[4 * node + 3];
+  const int R = nmem * G;
+  const int Hkv = a.num_kv_heads;
+  const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lrow = lane & 15;  // MFMA row / column index
+  const int lgrp = lane >> 4;  // MFMA k group
+  const int my_row = row0 + wave * 16 + lrow;
+  const bool wave_active = row0 + wave * 16 < R;
+
+  // queries of this lane's row, as B operands
+  u32x4 qb[NKS];
+  int my_b = -1, my_slot = 0, my_h = 0;
+  if (my_row < R) {
+    const int member = my_row / G;
+    my_b = a.node_members[2 * (mem_off + member)];
+    my_slot = a.node_members[2 * (mem_off + member) + 1];
+    my_h = hkv * G + my_row % G;
+    const uint16_t* qp = a.q + (static_cast<int64_t>(my_b) * a.num_q_heads + my_h) * D + lgrp * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qb[ks] = ld16(qp + ks * 32);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
+  }
+
+  float m = kNegInf, lsum = 0.f;
+  f32x4 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // global -> register staging of one chunk
+  u32x4 kreg[KVEC_PER_THREAD];
+  u32x4 vreg0, vreg1;
+  const int vpair = tid & 15;  // tokens 2*vpair, 2*vpair+1
+  const int vcol = tid >> 4;   // 8-element column group
+  const bool vthread = vcol < D / 8;
+
+  auto block_id = [&](int j) -> int {
+    if (j >= nblk) return -1;
+    const int id = a.node_blocks[blk_off + j];
+    return (id >= 0 && static_cast<int64_t>(id) < a.num_blocks) ? id : -1;
+  };
+  auto load_chunk = [&](int ch) {
+    const int id0 = block_id(2 * ch), id1 = block_id(2 * ch + 1);
+#pragma unroll
+    for (int i = 0; i < KVEC_PER_THREAD; ++i) {
+      const int vi = tid + 256 * i;
+      const int tok = vi / (D / 8);
+      const int col = vi % (D / 8);
+      const int id = tok < 16 ? id0 : id1;
+      kreg[i] = id >= 0 ? ld16(a.k_pages + (static_cast<int64_t>(id) * 16 + (tok & 15)) * tok_stride +
+                               static_cast<int64_t>(hkv) * D + col * 8)
+                        : u32x4{0, 0, 0, 0};
+    }
+    if (vthread) {
+      const int t0 = 2 * vpair;
+      const int id = t0 < 16 ? id0 : id1;
+      if (id >= 0) {
+        const uint16_t* vp = a.v_pages + (static_cast<int64_t>(id) * 16 + (t0 & 15)) * tok_stride +
+                             static_cast<int64_t>(hkv) * D + vcol * 8;
+        vreg0 = ld16(vp);
+        vreg1 = ld16(vp + tok_stride);
+      } else {
+        vreg0 = u32x4{0, 0, 0, 0};
+        vreg1 = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  const int nchunks = (nblk + 1) / 2;
+  if (nchunks > 0) load_chunk(0);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const bool valid0 = block_id(2 * ch) >= 0;
+    const bool valid1 = block_id(2 * ch + 1) >= 0;
+    __syncthreads();  // every wave is done reading the previous chunk
+#pragma unroll
+    for (int i = 0; i < KVEC_PER_THREAD; ++i) {
+      const int vi = tid + 256 * i;
+      const int tok = vi / (D / 8);
+      const int col = vi % (D / 8);
+      *reinterpret_cast<u32x4*>(&k_lds[tok * KPITCH + col * 8]) = kreg[i];
+    }
+    if (vthread) {
+      const uint32_t w0[4] = {vreg0.x, vreg0.y, vreg0.z, vreg0.w};
+      const uint32_t w1[4] = {vreg1.x, vreg1.y, vreg1.z, vreg1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // element 2e and 2e+1 of the column group, for tokens 2*vpair (low) and 2*vpair+1 (high)
+        vt_lds[(vcol * 8 + 2 * e) * VPITCH + vpair] =
+            pack2(static_cast<uint16_t>(w0[e] & 0xffff), static_cast<uint16_t>(w1[e] & 0xffff));
+        vt_lds[(vcol * 8 + 2 * e + 1) * VPITCH + vpair] =
+            pack2(static_cast<uint16_t>(w0[e] >> 16), static_cast<uint16_t>(w1[e] >> 16));
+      }
+    }
+    __syncthreads();
+    if (ch + 1 < nchunks) load_chunk(ch + 1);  // in flight while this chunk is evaluated
+
+    if (wave_active) {
+      // S^T tiles: st[tt][j] = score of token 16*tt + 4*lgrp + j for this lane's row
+      f32x4 st[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(&k_lds[(tt * 16 + lrow) * KPITCH + ks * 32 + lgrp * 8]);
+          c = mfma16x16x32<DT>(kv, qb[ks], c);
+        }
+        st[tt] = c;
+      }
+      float sv[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sv[j] = valid0 ? st[0][j] * a.scale_log2 : kNegInf;
+        sv[4 + j] = valid1 ? st[1][j] * a.scale_log2 : kNegInf;
+      }
+      float cmax = sv[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sv[j]);
+      cmax = fmaxf(cmax, shfl_xor_f32(cmax, 16));
+      cmax = fmaxf(cmax, shfl_xor_f32(cmax, 32));
+      const float mn = fmaxf(m, cmax);
+      if (mn > m) {
+        const float alpha = exp2_diff(m, mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        m = mn;
+      }
+      uint16_t ph[8], pl[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = m == kNegInf ? 0.f : fast_exp2(sv[j] - m);
+        lsum += p;
+        ph[j] = DT::from_float(p);
+        pl[j] = DT::from_float(p - DT::to_float(ph[j]));
+      }
+      const u32x4 bh = u32x4{pack2(ph[0], ph[1]), pack2(ph[2], ph[3]), pack2(ph[4], ph[5]), pack2(ph[6], ph[7])};
+      const u32x4 bl = u32x4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])};
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t* vrow = &vt_lds[(dt * 16 + lrow) * VPITCH];
+        const uint2 t0 = *reinterpret_cast<const uint2*>(vrow + 2 * lgrp);      // tokens 4*lgrp .. +3
+        const uint2 t1 = *reinterpret_cast<const uint2*>(vrow + 8 + 2 * lgrp);  // tokens 16 + 4*lgrp .. +3
+        const u32x4 av = u32x4{t0.x, t0.y, t1.x, t1.y};
+        o[dt] = mfma16x16x32<DT>(av, bh, o[dt]);
+        o[dt] = mfma16x16x32<DT>(av, bl, o[dt]);
+      }
+    }
+  }
+
+  // every lane group holds part of the row's weight sum
+  lsum += shfl_xor_f32(lsum, 16);
+  lsum += shfl_xor_f32(lsum, 32);
+  if (my_row < R) {
+    const int64_t rec = (static_cast<int64_t>(my_b) * a.slots + my_slot) * a.num_q_heads + my_h;
+    float* dst = a.acc + rec * D + lgrp * 4;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<float4*>(dst + dt * 16) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (lgrp == 0) a.ml[rec] = make_float2(m, lsum);
+  }
+}
+
+namespace {
+
+template <class DT, int D, int G>
+hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
+  if (a.num_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL((cascade_kernel<DT, D, G>), dim3(static_cast<unsigned>(a.num_items)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class DT, int D>
+hipError_t launch_cascade_g(int group, const CascadeArgs& a, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_cascade_t<DT, D, 1>(a, stream);
+    case 2: return launch_cascade_t<DT, D, 2>(a, stream);
+    case 4: return launch_cascade_t<DT, D, 4>(a, stream);
+    case 8: return launch_cascade_t<DT, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class DT>
+hipError_t launch_cascade_d(int head_dim, int group, const CascadeArgs& a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_cascade_g<DT, 64>(group, a, stream);
+    case 128: return launch_cascade_g<DT, 128>(group, a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cascade(int dtype, int head_dim, int group, const CascadeArgs& a, hipStream_t stream) {
+  return dtype == 1 ? launch_cascade_d<BF16>(head_dim, group, a, stream)
+                    : launch_cascade_d<F16>(head_dim, group, a, stream);
+}
+
+}  // namespace pkv

@@ -1,0 +1,113 @@
+// Device helpers for the gfx950 kernels: 16-bit float formats, wave64 lane
+// exchanges, the partial-result layout shared by the decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------------------
+// 16-bit storage formats.  A 32-bit word holds two consecutive elements, the
+// lower-addressed one in the low half.
+
+struct BF16 {
+  typedef bf16x8 vec8;
+  // low / high element of a packed pair as fp32 (bf16 is the top half of an fp32)
+  static __device__ __forceinline__ float lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+  // acc + a.lo*b.lo + a.hi*b.hi (products of two bf16 values are exact in fp32)
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc,
+                                           false);
+  }
+  // round-to-nearest-even fp32 -> 16-bit pattern
+  static __device__ __forceinline__ uint16_t from_float(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  }
+  static __device__ __forceinline__ float to_float(uint16_t h) {
+    return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
+  }
+};
+
+struct F16 {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ float lo(uint32_t w) {
+    return static_cast<float>(__builtin_bit_cast(f16x2, w).x);
+  }
+  static __device__ __forceinline__ float hi(uint32_t w) {
+    return static_cast<float>(__builtin_bit_cast(f16x2, w).y);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+  }
+  static __device__ __forceinline__ uint16_t from_float(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+  static __device__ __forceinline__ float to_float(uint16_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Lane exchanges inside a wave64.
+
+// DPP move with the given control (row_mask/bank_mask all lanes, bound_ctrl on).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
+}
+
+constexpr int kDppQuadXor1 = 0xb1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4e;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within each 16
+
+// Sum over groups of N consecutive lanes (N in 1, 2, 4, 8, 16); every lane of a
+// group ends with the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_f32<kDppQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp_f32<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp_f32<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_f32<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
+  const int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp2(a - b) with exp2(-inf - anything) = 0 (an empty running state has m = -inf)
+__device__ __forceinline__ float exp2_diff(float a, float b) { return a == kNegInf ? 0.f : fast_exp2(a - b); }
+
+// 16-byte global load / store helpers
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// Partial results.  Every (row b, partial slot p, query head h) owns
+//   acc[((b * P + p) * Hq + h) * D + 0 .. D)   fp32, un-normalised sum_t 2^(s_t - m) v_t
+//   ml [ (b * P + p) * Hq + h ]               (m, l): running max (log2 units) and sum_t 2^(s_t - m)
+// Slots [0, depth_b) hold the shared-prefix nodes on row b's path, slots
+// [depth_b, depth_b + n_splits_b) the split-K chunks of its own remainder.
+
+struct PartialLayout {
+  float* acc;
+  float2* ml;
+  int32_t slots;  // P
+};
+
+}  // namespace pkv

@@ -1,0 +1,91 @@
+// Kernel launch interface between the C-ABI dispatch (capi.cpp) and the HIP
+// translation units.  Plain structs of pointers and sizes; no HIP types beyond
+// hipStream_t / hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendArgs {
+  uint16_t* k_pages;
+  uint16_t* v_pages;
+  int64_t num_blocks;
+  int32_t block_size;
+  int32_t row_elems;  // num_kv_heads * head_dim
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int32_t num_tokens;
+  const int64_t* slot_mapping;
+  const int32_t* cow_src;
+  const int32_t* cow_dst;
+  const int32_t* cow_rows;
+  int32_t num_cow;
+};
+
+// Split-K decode over each row's own tokens [shared_tokens_b, len_b).
+struct SplitArgs {
+  const uint16_t* q;
+  const uint16_t* k_pages;
+  const uint16_t* v_pages;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* row_info;  // [batch][2] = (shared tokens, depth) from a cascade plan, or null
+  float* acc;
+  float2* ml;
+  int64_t num_blocks;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks;
+  int32_t max_seq_len;
+  int32_t split_len;
+  int32_t max_splits;
+  int32_t slots;
+  float scale_log2;
+};
+
+// Merge of all partials of a row into the normalised output.
+struct MergeArgs {
+  const int32_t* seq_lens;
+  const int32_t* row_info;
+  const float* acc;
+  const float2* ml;
+  float* out;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t max_blocks;
+  int32_t max_seq_len;
+  int32_t split_len;
+  int32_t slots;
+};
+
+// Shared-prefix (cascade) pass over the plan's work items.
+struct CascadeArgs {
+  const uint16_t* q;
+  const uint16_t* k_pages;
+  const uint16_t* v_pages;
+  const int32_t* items;         // [num_items][3] = (node, kv head, first tile row); node < 0: idle
+  const int32_t* nodes;         // [num_nodes][4] = (block offset, num blocks, member offset, num members)
+  const int32_t* node_blocks;   // physical block ids
+  const int32_t* node_members;  // [..][2] = (row, partial slot)
+  float* acc;
+  float2* ml;
+  int64_t num_blocks;
+  int32_t num_items;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t slots;
+  float scale_log2;
+};
+
+constexpr int kCascadeRowsPerItem = 64;  // 4 waves x 16 rows
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+// dtype: 0 f16, 1 bf16.  Returns hipErrorInvalidValue for shapes not built.
+hipError_t launch_decode_split(int dtype, int head_dim, int group, const SplitArgs& a, hipStream_t stream);
+hipError_t launch_merge(int head_dim, const MergeArgs& a, hipStream_t stream);
+hipError_t launch_cascade(int dtype, int head_dim, int group, const CascadeArgs& a, hipStream_t stream);
+
+}  // namespace pkv
