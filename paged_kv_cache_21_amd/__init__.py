@@ -15,6 +15,11 @@ import os
 
 import numpy as np
 
+# torch ships its own HIP runtime.  Importing it first makes libpkv.so bind to
+# that same, already loaded runtime (same soname) instead of pulling a second
+# HIP/HSA runtime into the process, which would then see no device.
+import torch  # noqa: F401
+
 __all__ = [
     "PkvError", "PkvInvalid", "PkvOOM", "PkvNotFound", "PkvUnsupported", "PkvWorkspaceError", "PkvHipError",
     "kv_append", "paged_decode_attn", "decode_workspace_bytes", "BlockPool", "CascadePlan",

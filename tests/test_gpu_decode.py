@@ -183,18 +183,15 @@ def test_identical_histories_identical_outputs(pkv):
     torch = __import__("torch")
     w = workloads.get(1)
     pool, k_pages, v_pages, bt, lens, q = setup_workload(w)
-    # row 1 := row 0's tables (shared blocks); row 2 := copies of row 0's blocks in unused blocks
-    used = set(int(x) for x in bt[bt >= 0])
-    free = [b for b in range(w.num_blocks) if b not in used]
     nb = -(-int(lens[0]) // 16)
-    assert len(free) >= nb
-    bt = bt.copy()
-    bt[1] = bt[0]
+    # append nb fresh blocks to the pool and put copies of row 0's blocks there
+    extra = torch.arange(w.num_blocks, w.num_blocks + nb, dtype=torch.int64)
     src = torch.tensor(bt[0, :nb].astype(np.int64)).cuda()
-    dst = torch.tensor(np.array(free[:nb], dtype=np.int64)).cuda()
-    k_pages[dst] = k_pages[src]
-    v_pages[dst] = v_pages[src]
-    bt[2, :nb] = free[:nb]
+    k_pages = torch.cat([k_pages, k_pages[src]]).contiguous()
+    v_pages = torch.cat([v_pages, v_pages[src]]).contiguous()
+    bt = bt.copy()
+    bt[1] = bt[0]  # row 1: the very same blocks (shared)
+    bt[2, :nb] = extra.numpy()  # row 2: byte-identical copies
     lens = lens.copy()
     lens[1] = lens[2] = lens[0]
     q[1] = q[0]
