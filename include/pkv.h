@@ -135,8 +135,10 @@ pkv_status pkv_kv_append(void* k_pages, void* v_pages, int64_t num_blocks, int32
  *   workspace     device scratch of at least pkv_decode_workspace_bytes(...) bytes
  *                 (fp32 partial results); contents on entry are ignored.
  *   out           device, float32 [batch][num_q_heads][head_dim]
- * Supported: block_size 16; head_dim 64 or 128; group in {1, 2, 4, 8}.  Block ids
- * outside [0, num_blocks) are not read (their tokens are dropped).
+ * Supported: block_size 16; head_dim 64 or 128; group in {1, 2, 4, 8}; num_blocks >= 1
+ * when batch > 0.  Block ids outside [0, num_blocks) are never dereferenced: their
+ * tokens get zero weight (block 0 is read in their place, so a block 0 holding
+ * non-finite values could still reach the output).
  * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
  * ---------------------------------------------------------------------------------------- */
 pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

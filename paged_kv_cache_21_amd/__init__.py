@@ -26,7 +26,8 @@ __all__ = [
     "timing_enable", "timing_reset", "timing_read", "KERNELS", "lib", "LIB_PATH", "version",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+# PKV_LIBRARY may point at another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_NOT_FOUND, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP, PKV_ERR_WORKSPACE = (
     0, -1, -2, -3, -4, -5, -6)

@@ -89,19 +89,22 @@ pkv_status launch(int kernel, const char* what, hipStream_t stream, F&& f) {
 // ---------------------------------------------------------------------------
 // split-K sizing shared by the workspace query and the decode call
 
+// Smallest share of blocks a wave of the split kernel takes; bounds the number
+// of partials a (row, KV head) segment can produce.
+#ifndef PKV_MIN_CHUNK
+#define PKV_MIN_CHUNK 8
+#endif
+
 struct DecodeLayout {
-  int32_t split_len;
-  int32_t max_splits;
-  int32_t slots;
-  size_t acc_bytes;
-  size_t ml_offset;
+  int32_t slots;       // partial slots per row: cascade nodes + split pieces
+  size_t ml_offset;    // bytes
+  size_t counts_offset;
   size_t bytes;
 };
 
-// The split length targets a few thousand single-wave work units (the chip runs
-// ~2-3 thousand of them at once): short enough to fill 256 CUs when rows are
-// few, long enough that per-unit overhead (q load, partial write and re-read)
-// stays a few percent of the K/V bytes.
+// Workspace: fp32 partials acc [batch][slots][Hq][D], (m, l) pairs [batch][slots][Hq],
+// partial counts int32 [batch][Hkv].  A (row, head) segment of n blocks is cut
+// into at most ceil(n / PKV_MIN_CHUNK) + 1 pieces by the split kernel.
 DecodeLayout decode_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t max_seq_len, const pkv_plan* plan) {
   DecodeLayout L{};
@@ -112,18 +115,14 @@ DecodeLayout decode_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_he
     return m;
   }();
   const int64_t span = std::max<int64_t>(0, static_cast<int64_t>(max_seq_len) - min_shared);
-  const int64_t pairs = static_cast<int64_t>(batch) * num_kv_heads;
-  auto units = [&](int64_t s) { return pairs * ((span + s - 1) / s); };
-  int32_t split = 256;
-  while (split < 8192 && units(split) > 16384) split *= 2;
-  while (split > 64 && units(split) < 2048) split /= 2;
-  L.split_len = split;
-  L.max_splits = static_cast<int32_t>((span + split - 1) / split);
-  L.slots = L.max_splits + (plan ? plan->max_depth : 0);
+  const int64_t max_nb = (span + 15) / 16;
+  const int64_t pieces = max_nb > 0 ? (max_nb + PKV_MIN_CHUNK - 1) / PKV_MIN_CHUNK + 1 : 0;
+  L.slots = static_cast<int32_t>(pieces + (plan ? plan->max_depth : 0));
   const size_t recs = static_cast<size_t>(batch) * L.slots * num_q_heads;
-  L.acc_bytes = recs * head_dim * sizeof(float);
-  L.ml_offset = (L.acc_bytes + 255) & ~static_cast<size_t>(255);
-  L.bytes = L.ml_offset + recs * sizeof(float2);
+  const size_t acc_bytes = recs * head_dim * sizeof(float);
+  L.ml_offset = (acc_bytes + 255) & ~static_cast<size_t>(255);
+  L.counts_offset = (L.ml_offset + recs * sizeof(float2) + 255) & ~static_cast<size_t>(255);
+  L.bytes = L.counts_offset + static_cast<size_t>(batch) * num_kv_heads * sizeof(int32_t);
   return L;
 }
 
@@ -209,6 +208,7 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
   }
   const pkv::DecodeLayout L = pkv::decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan);
   if (batch == 0) return PKV_OK;
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: the pool must hold at least one block");
   if (!q || !k_pages || !v_pages || !block_tables || !seq_lens || !out)
     return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: null pointer");
   if (!pkv::aligned16(q) || !pkv::aligned16(k_pages) || !pkv::aligned16(v_pages) || !pkv::aligned16(out))
@@ -244,7 +244,9 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
     if (st != PKV_OK) return st;
   }
-  if (L.max_splits > 0) {
+  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.counts_offset);
+  if (L.slots > (plan ? plan->max_depth : 0)) {
+    const int waves = pkv::decode_split_waves(dtype, head_dim, group);
     pkv::SplitArgs sa{static_cast<const uint16_t*>(q),
                       static_cast<const uint16_t*>(k_pages),
                       static_cast<const uint16_t*>(v_pages),
@@ -253,22 +255,23 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
                       row_info,
                       acc,
                       ml,
+                      counts,
                       num_blocks,
                       batch,
                       num_q_heads,
                       num_kv_heads,
                       max_blocks_per_seq,
                       max_seq_len,
-                      L.split_len,
-                      L.max_splits,
                       L.slots,
+                      PKV_MIN_CHUNK,
+                      waves,
                       scale_log2};
     pkv_status st = pkv::launch(PKV_KERNEL_DECODE_SPLIT, "decode_split", s,
                                 [&] { return pkv::launch_decode_split(dtype, head_dim, group, sa, s); });
     if (st != PKV_OK) return st;
   }
-  pkv::MergeArgs ma{seq_lens, row_info, acc, ml, out, batch, num_q_heads, max_blocks_per_seq, max_seq_len,
-                    L.split_len, L.slots};
+  pkv::MergeArgs ma{seq_lens, row_info, counts, acc, ml, out, batch, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                    max_seq_len, L.slots};
   return pkv::launch(PKV_KERNEL_MERGE, "merge", s, [&] { return pkv::launch_merge(head_dim, ma, s); });
 }
 

@@ -18,19 +18,106 @@
 namespace pkv {
 
 // ---------------------------------------------------------------------------
-// Split-K partial attention.
+// Split-K partial attention with persistent, evenly loaded waves.
 //
-// One wave per work unit (row b, KV head, chunk s of split_len tokens).  The
-// group's G query heads share every K/V load.  Lanes are split into 64/LPT
-// "token rows" of LPT lanes: each token row reads one token's K (and V) row of
-// head_dim elements as LPT x (D/LPT) contiguous bytes with 16-byte loads, so a
-// wave-wide load instruction covers 64/LPT whole tokens.  The q.k dot product
-// is a per-lane dot2 chain plus a DPP sum over the LPT lanes; each token row
-// keeps its own online-softmax state, and the token rows are merged once at
-// the end of the unit with lane shuffles.  The next block's K/V loads are
-// issued before the current block is consumed.
+// The work is every row's own blocks for every KV head, in the order
+// (row, KV head, block); a grid of W waves (as many as the chip holds at once)
+// cuts it into W equal contiguous ranges, so all waves finish together and no
+// wave ever waits for a new work-group to be dispatched.  A wave streams its
+// range block by block, crossing from one (row, head) segment to the next
+// without draining its load pipeline; at the end of each segment piece it
+// writes one partial (m, l, acc) for the G query heads of that KV head.
+//
+// Inside a wave: lanes form 64/LPT "token rows" of LPT lanes; a token row reads
+// one token's K (and V) row of head_dim elements as LPT x (D/LPT) contiguous
+// bytes with 16-byte loads, so a wave-wide load covers 64/LPT whole tokens.  The
+// G query heads share every load.  q.k is a per-lane dot2 chain plus a DPP sum
+// over the LPT lanes; each token row keeps its own online-softmax state, merged
+// across token rows with lane shuffles when a segment piece ends.  The K/V
+// loads of the next block are issued before the current one is consumed.
+// Block ids outside [0, num_blocks) are never dereferenced: block 0 is read in
+// their place and the block's scores are masked to -inf.
+
+namespace {
+
+// A position in the (row, KV head, block) work order.
+struct Cursor {
+  int b;        // row
+  int h;        // KV head
+  int j;        // block within the row's own blocks
+  int nb;       // own blocks of the row
+  int blk0;     // logical block index where the row's own part starts
+  int depth;    // partials the cascade pass wrote for this row
+  int len;      // row length (tokens)
+  int64_t seg;  // index of block 0 of segment (b, h) in the work order
+};
+
+struct RowInfo {
+  int nb, blk0, depth, len;
+};
+
+__device__ __forceinline__ RowInfo load_row(const SplitArgs& a, int b) {
+  int len = a.seq_lens[b];
+  len = min(len, a.max_seq_len);
+  len = min(len, a.max_blocks * 16);
+  int begin = 0, depth = 0;
+  if (a.row_info) {
+    begin = a.row_info[2 * b];
+    depth = a.row_info[2 * b + 1];
+  }
+  RowInfo r;
+  r.nb = len > begin ? (len - begin + 15) >> 4 : 0;
+  r.blk0 = begin >> 4;
+  r.depth = depth;
+  r.len = len;
+  return r;
+}
+
+__device__ __forceinline__ void set_row(Cursor& c, const RowInfo& r) {
+  c.nb = r.nb;
+  c.blk0 = r.blk0;
+  c.depth = r.depth;
+  c.len = r.len;
+}
+
+// next block in the work order (the caller guarantees one exists)
+__device__ __forceinline__ void advance(Cursor& c, const SplitArgs& a) {
+  if (++c.j < c.nb) return;
+  c.j = 0;
+  c.seg += c.nb;
+  if (++c.h < a.num_kv_heads) return;
+  c.h = 0;
+  do {
+    ++c.b;
+    set_row(c, load_row(a, c.b));
+  } while (c.nb == 0);
+}
+
+// inclusive prefix sum over the wave
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int y = __builtin_amdgcn_ds_bpermute((lane - d) << 2, x);
+    x += lane >= d ? y : 0;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) x += __builtin_amdgcn_ds_bpermute((__lane_id() ^ d) << 2, x);
+  return x;
+}
+
+}  // namespace
+
+#ifndef PKV_SPLIT_WAVES_PER_EU
+#define PKV_SPLIT_WAVES_PER_EU 1
+#endif
+
 template <class DT, int D, int G, int LPT>
-__global__ __launch_bounds__(64) void decode_split_kernel(SplitArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
   constexpr int ROWS = 64 / LPT;      // token rows per wave
   constexpr int VPL = D / (8 * LPT);  // 16-byte vectors per token per lane
   constexpr int TPB = 16 / ROWS;      // tokens per lane per 16-token block
@@ -40,200 +127,284 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitArgs a) {
   const int r = lane / LPT;
   const int c = lane % LPT;
   const int Hkv = a.num_kv_heads;
-  const int hkv = blockIdx.x % Hkv;
-  const int rest = blockIdx.x / Hkv;
-  const int b = rest % a.batch;
-  const int s = rest / a.batch;
+  const int w = blockIdx.x;
 
-  int len = a.seq_lens[b];
-  len = min(len, a.max_seq_len);
-  len = min(len, a.max_blocks * 16);
-  int begin = 0, depth = 0;
-  if (a.row_info) {
-    begin = a.row_info[2 * b];
-    depth = a.row_info[2 * b + 1];
+  // ---- this wave's range of the work order
+  int64_t total = 0;
+  for (int base = 0; base < a.batch; base += 64) {
+    const int b = base + lane;
+    const int nb = b < a.batch ? load_row(a, b).nb : 0;
+    total += wave_sum(nb);
   }
-  const int t0 = begin + s * a.split_len;  // multiple of 16
-  if (t0 >= len) return;
-  const int t1 = min(t0 + a.split_len, len);
+  total *= Hkv;
+  const int64_t chunk = max(static_cast<int64_t>(a.min_chunk), (total + a.num_waves - 1) / a.num_waves);
+  const int64_t start = static_cast<int64_t>(w) * chunk;
+  if (start >= total) return;
+  const int count = static_cast<int>(min(chunk, total - start));
+
+  // ---- locate the start: first row whose cumulative work passes `start`
+  Cursor cur;
+  {
+    int64_t run = 0;
+    for (int base = 0;; base += 64) {
+      const int b = base + lane;
+      const int u = b < a.batch ? load_row(a, b).nb * Hkv : 0;
+      const int incl = wave_inclusive_scan(u);
+      const uint64_t hit = __ballot(run + incl > start);
+      if (hit) {
+        const int k = __builtin_ctzll(hit);
+        const int64_t row_start = run + __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(u, k);
+        cur.b = base + k;
+        set_row(cur, load_row(a, cur.b));
+        const int off = static_cast<int>(start - row_start);
+        cur.h = off / cur.nb;
+        cur.j = off - cur.h * cur.nb;
+        cur.seg = row_start + static_cast<int64_t>(cur.h) * cur.nb;
+        break;
+      }
+      run += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  Cursor pre = cur;  // position of the next block to load
 
   const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;  // elements between consecutive tokens
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  const int64_t lane_off = static_cast<int64_t>(r) * tok_stride + c * 8;
 
-  // q of the G heads, restricted to this lane's dims: vector v holds dims (v*LPT + c)*8 .. +8
-  u32x4 qv[G][VPL];
+  auto block_id = [&](const Cursor& p) -> int {
+    return a.block_tables[static_cast<int64_t>(p.b) * a.max_blocks + p.blk0 + p.j];
+  };
+  auto load_q = [&](const Cursor& p, u32x4(&qq)[G][VPL]) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint16_t* qh = a.q + (static_cast<int64_t>(b) * a.num_q_heads + hkv * G + h) * D;
+    for (int g = 0; g < G; ++g) {
+      const uint16_t* qh = a.q + (static_cast<int64_t>(p.b) * a.num_q_heads + p.h * G + g) * D + c * 8;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) qv[h][v] = ld16(qh + (v * LPT + c) * 8);
-  }
-
-  float m[G], l[G], acc[G][VPL * 8];
+      for (int v = 0; v < VPL; ++v) qq[g][v] = ld16(qh + v * LPT * 8);
+    }
+  };
+  auto load_block = [&](const Cursor& p, u32x4(&kk)[TPB][VPL], u32x4(&vv)[TPB][VPL]) -> bool {
+    const int id = block_id(p);
+    const bool ok = id >= 0 && static_cast<int64_t>(id) < a.num_blocks;
+    const int64_t off = static_cast<int64_t>(ok ? id : 0) * 16 * tok_stride + static_cast<int64_t>(p.h) * D + lane_off;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < VPL * 8; ++e) acc[h][e] = 0.f;
-  }
-
-  const int jb_first = t0 >> 4;
-  const int jb_last = (t1 - 1) >> 4;
-
-  u32x4 kc[TPB][VPL], vc[TPB][VPL];
-  bool ok_c;
-  auto load_block = [&](int jb, u32x4(&kk)[TPB][VPL], u32x4(&vv)[TPB][VPL]) -> bool {
-    const int phys = bt[jb];
-    const bool ok = phys >= 0 && static_cast<int64_t>(phys) < a.num_blocks;
-    const int64_t base = ok ? (static_cast<int64_t>(phys) * 16) * tok_stride + static_cast<int64_t>(hkv) * D : 0;
-#pragma unroll
-    for (int i = 0; i < TPB; ++i) {
+    for (int t = 0; t < TPB; ++t) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int64_t off = base + static_cast<int64_t>(r + i * ROWS) * tok_stride + (v * LPT + c) * 8;
-        if (ok) {
-          kk[i][v] = ld16(a.k_pages + off);
-          vv[i][v] = ld16(a.v_pages + off);
-        } else {
-          kk[i][v] = u32x4{0, 0, 0, 0};
-          vv[i][v] = u32x4{0, 0, 0, 0};
-        }
+        const int64_t o = off + static_cast<int64_t>(t * ROWS) * tok_stride + v * LPT * 8;
+        kk[t][v] = ld16_stream(a.k_pages + o);
+        vv[t][v] = ld16_stream(a.v_pages + o);
       }
     }
     return ok;
   };
 
-  ok_c = load_block(jb_first, kc, vc);
-  for (int jb = jb_first; jb <= jb_last; ++jb) {
-    u32x4 kn[TPB][VPL], vn[TPB][VPL];
-    bool ok_n = false;
-    if (jb < jb_last) ok_n = load_block(jb + 1, kn, vn);
+  u32x4 qv[G][VPL], qn[G][VPL];
+  load_q(cur, qv);
+  float m[G], l[G], acc[G][VPL * 8];
+  auto reset_state = [&]() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = kNegInf;
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VPL * 8; ++e) acc[g][e] = 0.f;
+    }
+  };
+  reset_state();
 
-    // scores of this lane's tokens for the G heads
+  auto consume_block = [&](bool ok, const u32x4(&kk)[TPB][VPL], const u32x4(&vv)[TPB][VPL]) {
     float sc[TPB][G];
 #pragma unroll
-    for (int i = 0; i < TPB; ++i) {
+    for (int t = 0; t < TPB; ++t) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int g = 0; g < G; ++g) {
         float x = 0.f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          x = DT::dot2(kc[i][v].x, qv[h][v].x, x);
-          x = DT::dot2(kc[i][v].y, qv[h][v].y, x);
-          x = DT::dot2(kc[i][v].z, qv[h][v].z, x);
-          x = DT::dot2(kc[i][v].w, qv[h][v].w, x);
+          x = DT::dot2(kk[t][v].x, qv[g][v].x, x);
+          x = DT::dot2(kk[t][v].y, qv[g][v].y, x);
+          x = DT::dot2(kk[t][v].z, qv[g][v].z, x);
+          x = DT::dot2(kk[t][v].w, qv[g][v].w, x);
         }
-        sc[i][h] = x;
+        sc[t][g] = x;
       }
     }
+    // sum over the LPT lanes of each token row, one DPP step at a time across all
+    // TPB*G independent sums (keeps the DPP read-after-write hazards hidden)
+    if constexpr (LPT >= 2) {
 #pragma unroll
-    for (int i = 0; i < TPB; ++i) {
-      const int tok = jb * 16 + r + i * ROWS;
-      const bool valid = ok_c && tok < t1;
+      for (int t = 0; t < TPB; ++t)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float x = group_sum<LPT>(sc[i][h]) * a.scale_log2;
-        sc[i][h] = valid ? x : kNegInf;
+        for (int g = 0; g < G; ++g) sc[t][g] += dpp_f32<kDppQuadXor1>(sc[t][g]);
+    }
+    if constexpr (LPT >= 4) {
+#pragma unroll
+      for (int t = 0; t < TPB; ++t)
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[t][g] += dpp_f32<kDppQuadXor2>(sc[t][g]);
+    }
+    if constexpr (LPT >= 8) {
+#pragma unroll
+      for (int t = 0; t < TPB; ++t)
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[t][g] += dpp_f32<kDppRowHalfMirror>(sc[t][g]);
+    }
+    if constexpr (LPT >= 16) {
+#pragma unroll
+      for (int t = 0; t < TPB; ++t)
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[t][g] += dpp_f32<kDppRowMirror>(sc[t][g]);
+    }
+#pragma unroll
+    for (int t = 0; t < TPB; ++t)
+#pragma unroll
+      for (int g = 0; g < G; ++g) sc[t][g] *= a.scale_log2;
+    const int tok0 = (cur.blk0 + cur.j) * 16;
+    if (!ok || tok0 + 16 > cur.len) {  // uniform: only a row's last block can be partial
+#pragma unroll
+      for (int t = 0; t < TPB; ++t) {
+        const bool valid = ok && tok0 + r + t * ROWS < cur.len;
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[t][g] = valid ? sc[t][g] : kNegInf;
       }
     }
-
     // online softmax, per token row
     float mx[G];
     bool grow = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      mx[h] = m[h];
+    for (int g = 0; g < G; ++g) {
+      mx[g] = m[g];
 #pragma unroll
-      for (int i = 0; i < TPB; ++i) mx[h] = fmaxf(mx[h], sc[i][h]);
-      grow |= mx[h] > m[h];
+      for (int t = 0; t < TPB; ++t) mx[g] = fmaxf(mx[g], sc[t][g]);
+      grow |= mx[g] > m[g];
     }
     if (__any(grow)) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float alpha = mx[h] > m[h] ? exp2_diff(m[h], mx[h]) : 1.f;
-        l[h] *= alpha;
+      for (int g = 0; g < G; ++g) {
+        const float alpha = mx[g] > m[g] ? exp2_diff(m[g], mx[g]) : 1.f;
+        l[g] *= alpha;
 #pragma unroll
-        for (int e = 0; e < VPL * 8; ++e) acc[h][e] *= alpha;
-        m[h] = mx[h];
+        for (int e = 0; e < VPL * 8; ++e) acc[g][e] *= alpha;
+        m[g] = mx[g];
       }
     }
 #pragma unroll
-    for (int i = 0; i < TPB; ++i) {
+    for (int t = 0; t < TPB; ++t) {
       float vf[VPL * 8];
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        vf[v * 8 + 0] = DT::lo(vc[i][v].x);
-        vf[v * 8 + 1] = DT::hi(vc[i][v].x);
-        vf[v * 8 + 2] = DT::lo(vc[i][v].y);
-        vf[v * 8 + 3] = DT::hi(vc[i][v].y);
-        vf[v * 8 + 4] = DT::lo(vc[i][v].z);
-        vf[v * 8 + 5] = DT::hi(vc[i][v].z);
-        vf[v * 8 + 6] = DT::lo(vc[i][v].w);
-        vf[v * 8 + 7] = DT::hi(vc[i][v].w);
+        vf[v * 8 + 0] = DT::lo(vv[t][v].x);
+        vf[v * 8 + 1] = DT::hi(vv[t][v].x);
+        vf[v * 8 + 2] = DT::lo(vv[t][v].y);
+        vf[v * 8 + 3] = DT::hi(vv[t][v].y);
+        vf[v * 8 + 4] = DT::lo(vv[t][v].z);
+        vf[v * 8 + 5] = DT::hi(vv[t][v].z);
+        vf[v * 8 + 6] = DT::lo(vv[t][v].w);
+        vf[v * 8 + 7] = DT::hi(vv[t][v].w);
       }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = m[h] == kNegInf ? 0.f : fast_exp2(sc[i][h] - m[h]);
-        l[h] += p;
+      for (int g = 0; g < G; ++g) {
+        // m[g] is -inf only while every score so far is -inf; the finite floor keeps
+        // 2^(-inf - m) = 0 without a branch
+        const float p = fast_exp2(sc[t][g] - fmaxf(m[g], -3.0e38f));
+        l[g] += p;
 #pragma unroll
-        for (int e = 0; e < VPL * 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        for (int e = 0; e < VPL * 8; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
       }
     }
+  };
 
-    if (jb < jb_last) {
+  // merge the token rows and store this segment piece's partial
+  auto finish_segment = [&]() {
 #pragma unroll
-      for (int i = 0; i < TPB; ++i) {
+    for (int dist = LPT; dist < 64; dist *= 2) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mo = shfl_xor_f32(m[g], dist);
+        const float lo_ = shfl_xor_f32(l[g], dist);
+        const float mn = fmaxf(m[g], mo);
+        const float fa = exp2_diff(m[g], mn);
+        const float fb = exp2_diff(mo, mn);
+        l[g] = l[g] * fa + lo_ * fb;
+#pragma unroll
+        for (int e = 0; e < VPL * 8; ++e) {
+          const float ao = shfl_xor_f32(acc[g][e], dist);
+          acc[g][e] = acc[g][e] * fa + ao * fb;
+        }
+        m[g] = mn;
+      }
+    }
+    const int64_t first_wave = cur.seg / chunk;
+    const int k = static_cast<int>(w - first_wave);
+    if (r == 0) {
+      const int slot = cur.depth + k;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int64_t rec = (static_cast<int64_t>(cur.b) * a.slots + slot) * a.num_q_heads + cur.h * G + g;
+        float* dst = a.acc + rec * D;
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          kc[i][v] = kn[i][v];
-          vc[i][v] = vn[i][v];
+          float4* d4 = reinterpret_cast<float4*>(dst + (v * LPT + c) * 8);
+          d4[0] = make_float4(acc[g][v * 8 + 0], acc[g][v * 8 + 1], acc[g][v * 8 + 2], acc[g][v * 8 + 3]);
+          d4[1] = make_float4(acc[g][v * 8 + 4], acc[g][v * 8 + 5], acc[g][v * 8 + 6], acc[g][v * 8 + 7]);
+        }
+        if (c == 0) a.ml[rec] = make_float2(m[g], l[g]);
+      }
+    }
+    if (k == 0 && lane == 0) {
+      const int64_t last_wave = (cur.seg + cur.nb - 1) / chunk;
+      a.counts[static_cast<int64_t>(cur.b) * Hkv + cur.h] = static_cast<int>(last_wave - first_wave + 1);
+    }
+  };
+
+  // one step: prefetch block i+1 (when `more`), consume block i, move on
+  u32x4 ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL];
+  bool ok_a = load_block(pre, ka, va), ok_b = false;
+  bool q_pending = false;
+  auto step = [&](int i, bool ok_cur, const u32x4(&kc)[TPB][VPL], const u32x4(&vc)[TPB][VPL],
+                  u32x4(&kn)[TPB][VPL], u32x4(&vn)[TPB][VPL], bool& ok_next) {
+    const bool more = i + 1 < count;
+    if (more) {
+      const int old_seg_h = pre.h, old_b = pre.b;
+      advance(pre, a);
+      if (pre.h != old_seg_h || pre.b != old_b) {
+        load_q(pre, qn);
+        q_pending = true;
+      }
+    }
+    // unconditional (after the last block it re-reads that block, an L2 hit) so
+    // the wait counts stay the same on every path
+    ok_next = load_block(pre, kn, vn);
+    consume_block(ok_cur, kc, vc);
+    if (!more || cur.j + 1 == cur.nb) {
+      finish_segment();
+      if (more) {
+        advance(cur, a);
+        reset_state();
+        if (q_pending) {
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) qv[g][v] = qn[g][v];
+          q_pending = false;
         }
       }
-      ok_c = ok_n;
+    } else {
+      ++cur.j;
     }
+  };
+  int i = 0;
+  for (; i + 1 < count; i += 2) {
+    step(i, ok_a, ka, va, kb, vb, ok_b);
+    step(i + 1, ok_b, kb, vb, ka, va, ok_a);
   }
-
-  // merge the token rows (lanes c, c+LPT, c+2LPT, ... hold the same dims)
-#pragma unroll
-  for (int dist = LPT; dist < 64; dist *= 2) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = shfl_xor_f32(m[h], dist);
-      const float lo_ = shfl_xor_f32(l[h], dist);
-      const float mn = fmaxf(m[h], mo);
-      const float fa = exp2_diff(m[h], mn);
-      const float fb = exp2_diff(mo, mn);
-      l[h] = l[h] * fa + lo_ * fb;
-#pragma unroll
-      for (int e = 0; e < VPL * 8; ++e) {
-        const float ao = shfl_xor_f32(acc[h][e], dist);
-        acc[h][e] = acc[h][e] * fa + ao * fb;
-      }
-      m[h] = mn;
-    }
-  }
-
-  if (r == 0) {
-    const int slot = depth + s;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int64_t rec = (static_cast<int64_t>(b) * a.slots + slot) * a.num_q_heads + hkv * G + h;
-      float* dst = a.acc + rec * D;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        float4* d4 = reinterpret_cast<float4*>(dst + (v * LPT + c) * 8);
-        d4[0] = make_float4(acc[h][v * 8 + 0], acc[h][v * 8 + 1], acc[h][v * 8 + 2], acc[h][v * 8 + 3]);
-        d4[1] = make_float4(acc[h][v * 8 + 4], acc[h][v * 8 + 5], acc[h][v * 8 + 6], acc[h][v * 8 + 7]);
-      }
-      if (c == 0) a.ml[rec] = make_float2(m[h], l[h]);
-    }
-  }
+  if (i < count) step(i, ok_a, ka, va, kb, vb, ok_b);
 }
 
 // ---------------------------------------------------------------------------
 // Merge: one wave per (row, query head) combines the row's node partials and
-// split partials; rows with no tokens get 0.
+// split partials; rows with no tokens get 0.  Lane p reads partial p's (m, l),
+// the wave reduces the max and the weight sum, then every lane accumulates its
+// D/64 output dims over the partials with independent loads.
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   constexpr int DPL = D / 64;
@@ -248,24 +419,42 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     begin = a.row_info[2 * b];
     depth = a.row_info[2 * b + 1];
   }
-  const int nsplit = len > begin ? (len - begin + a.split_len - 1) / a.split_len : 0;
+  const int hkv = h / (a.num_q_heads / a.num_kv_heads);
+  const int nsplit = len > begin ? a.counts[static_cast<int64_t>(b) * a.num_kv_heads + hkv] : 0;
   const int np = min(depth + nsplit, a.slots);
   const int64_t rec0 = static_cast<int64_t>(b) * a.slots * a.num_q_heads + h;
+  const int64_t rstride = a.num_q_heads;
 
-  float M = kNegInf;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, a.ml[rec0 + static_cast<int64_t>(p) * a.num_q_heads].x);
-  float L = 0.f;
   float o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const int64_t rec = rec0 + static_cast<int64_t>(p) * a.num_q_heads;
-    const float2 ml = a.ml[rec];
-    const float w = exp2_diff(ml.x, M);
-    L = fmaf(w, ml.y, L);
-    const float* src = a.acc + rec * D + lane * DPL;
+  float L = 0.f;
+  float M = kNegInf;
+  // running merge over chunks of 64 partials
+  for (int p0 = 0; p0 < np; p0 += 64) {
+    const int p = p0 + lane;
+    float2 ml = make_float2(kNegInf, 0.f);
+    if (p < np) ml = a.ml[rec0 + p * rstride];
+    float cm = ml.x;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = fmaf(w, src[e], o[e]);
+    for (int dist = 1; dist < 64; dist *= 2) cm = fmaxf(cm, shfl_xor_f32(cm, dist));
+    const float Mn = fmaxf(M, cm);
+    const float fold = exp2_diff(M, Mn);
+    const float wgt = exp2_diff(ml.x, Mn);
+    float lw = wgt * ml.y;
+#pragma unroll
+    for (int dist = 1; dist < 64; dist *= 2) lw += shfl_xor_f32(lw, dist);
+    L = L * fold + lw;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] *= fold;
+    M = Mn;
+    const int n = min(64, np - p0);
+    for (int k = 0; k < n; ++k) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), k));
+      const float* src = a.acc + (rec0 + (p0 + k) * rstride) * D + lane * DPL;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wk, src[e], o[e]);
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   float* dst = a.out + (static_cast<int64_t>(b) * a.num_q_heads + h) * D + lane * DPL;
@@ -326,13 +515,38 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
 
 namespace {
 
+// Lanes per token: 16 for head_dim 128 (8 dims per lane), 8 for head_dim 64.
+#ifndef PKV_LPT_D128
+#define PKV_LPT_D128 16
+#endif
+
+template <class DT, int D, int G>
+constexpr auto split_kernel_ptr() {
+  return &decode_split_kernel<DT, D, G, D == 128 ? PKV_LPT_D128 : 8>;
+}
+
+template <class DT, int D, int G>
+int split_waves_t() {
+  // resident waves of this instance on the current device, cached per device
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_ptr<DT, D, G>(), 64, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 8;
+  cache[dev] = cus * per_cu;
+  return cache[dev];
+}
+
 template <class DT, int D, int G>
 hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
-  constexpr int LPT = D == 128 ? 16 : 8;
-  const int64_t grid = static_cast<int64_t>(a.batch) * a.num_kv_heads * a.max_splits;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_split_kernel<DT, D, G, LPT>), dim3(static_cast<unsigned>(grid)), dim3(64), 0, stream, a);
+  if (a.num_waves <= 0 || a.batch <= 0) return hipSuccess;
+  constexpr int LPT = D == 128 ? PKV_LPT_D128 : 8;
+  hipLaunchKernelGGL((decode_split_kernel<DT, D, G, LPT>), dim3(static_cast<unsigned>(a.num_waves)), dim3(64), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -356,7 +570,27 @@ hipError_t launch_split_d(int head_dim, int group, const SplitArgs& a, hipStream
   }
 }
 
+template <class DT, int D>
+int waves_g(int group) {
+  switch (group) {
+    case 1: return split_waves_t<DT, D, 1>();
+    case 2: return split_waves_t<DT, D, 2>();
+    case 4: return split_waves_t<DT, D, 4>();
+    case 8: return split_waves_t<DT, D, 8>();
+    default: return 0;
+  }
+}
+
+template <class DT>
+int waves_d(int head_dim, int group) {
+  return head_dim == 128 ? waves_g<DT, 128>(group) : head_dim == 64 ? waves_g<DT, 64>(group) : 0;
+}
+
 }  // namespace
+
+int decode_split_waves(int dtype, int head_dim, int group) {
+  return dtype == 1 ? waves_d<BF16>(head_dim, group) : waves_d<F16>(head_dim, group);
+}
 
 hipError_t launch_decode_split(int dtype, int head_dim, int group, const SplitArgs& a, hipStream_t stream) {
   return dtype == 1 ? launch_split_d<BF16>(head_dim, group, a, stream) : launch_split_d<F16>(head_dim, group, a, stream);

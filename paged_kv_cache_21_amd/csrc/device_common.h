@@ -97,6 +97,18 @@ __device__ __forceinline__ float exp2_diff(float a, float b) { return a == kNegI
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Loads of K/V that are read once per call.
+#ifndef PKV_NT_LOADS
+#define PKV_NT_LOADS 1
+#endif
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+#if PKV_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return ld16(p);
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // Partial results.  Every (row b, partial slot p, query head h) owns
 //   acc[((b * P + p) * Hq + h) * D + 0 .. D)   fp32, un-normalised sum_t 2^(s_t - m) v_t

@@ -24,7 +24,15 @@ struct AppendArgs {
   int32_t num_cow;
 };
 
-// Split-K decode over each row's own tokens [shared_tokens_b, len_b).
+// Split-K decode over each row's own tokens [shared_tokens_b, len_b), with the
+// work spread evenly over a fixed number of persistent waves.
+//
+// Work order: rows b, then KV heads, then the row's own blocks j; a row-head
+// "segment" (b, h) holds n_b = ceil((len_b - shared_b) / 16) blocks.  With T the
+// total number of blocks and W waves, wave w takes blocks [w*c, (w+1)*c),
+// c = max(min_chunk, ceil(T / W)).  Partial k of segment (b, h) comes from wave
+// floor(S_bh / c) + k (S_bh = the segment's first index) and goes to partial slot
+// depth_b + k; the wave that starts a segment also stores its partial count.
 struct SplitArgs {
   const uint16_t* q;
   const uint16_t* k_pages;
@@ -34,15 +42,16 @@ struct SplitArgs {
   const int32_t* row_info;  // [batch][2] = (shared tokens, depth) from a cascade plan, or null
   float* acc;
   float2* ml;
+  int32_t* counts;  // [batch][num_kv_heads] partials per segment (written for non-empty segments)
   int64_t num_blocks;
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t max_blocks;
   int32_t max_seq_len;
-  int32_t split_len;
-  int32_t max_splits;
   int32_t slots;
+  int32_t min_chunk;  // c >= min_chunk bounds the partials per segment
+  int32_t num_waves;  // W
   float scale_log2;
 };
 
@@ -50,14 +59,15 @@ struct SplitArgs {
 struct MergeArgs {
   const int32_t* seq_lens;
   const int32_t* row_info;
+  const int32_t* counts;
   const float* acc;
   const float2* ml;
   float* out;
   int32_t batch;
   int32_t num_q_heads;
+  int32_t num_kv_heads;
   int32_t max_blocks;
   int32_t max_seq_len;
-  int32_t split_len;
   int32_t slots;
 };
 
@@ -85,6 +95,8 @@ constexpr int kCascadeRowsPerItem = 64;  // 4 waves x 16 rows
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // dtype: 0 f16, 1 bf16.  Returns hipErrorInvalidValue for shapes not built.
 hipError_t launch_decode_split(int dtype, int head_dim, int group, const SplitArgs& a, hipStream_t stream);
+// Waves the split kernel runs as for these shapes on the current device (all resident at once).
+int decode_split_waves(int dtype, int head_dim, int group);
 hipError_t launch_merge(int head_dim, const MergeArgs& a, hipStream_t stream);
 hipError_t launch_cascade(int dtype, int head_dim, int group, const CascadeArgs& a, hipStream_t stream);
 
