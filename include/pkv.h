@@ -241,8 +241,11 @@ int32_t pkv_plan_num_nodes(const pkv_plan* plan);
  * member rows into the given arrays when non-NULL (sized by the returned counts). */
 pkv_status pkv_plan_node(const pkv_plan* plan, int32_t node, int32_t* num_blocks, int32_t* num_members,
                          int32_t* blocks_out, int32_t* members_out);
+/* Token pieces node i is cut into (each piece is a separate work item and a
+ * separate partial per member row and query head); -1 for a bad index. */
+int32_t pkv_plan_node_pieces(const pkv_plan* plan, int32_t node);
 /* For row b: tokens covered by its nodes (its remainder starts there) and the
- * number of nodes on its path. */
+ * number of partial slots its nodes use (the sum of their pieces). */
 pkv_status pkv_plan_row(const pkv_plan* plan, int32_t row, int32_t* shared_tokens, int32_t* depth);
 
 /* ------------------------------------------------------------------------------------------

@@ -5,7 +5,7 @@ split-K attention, cascade pass, partial merge, append / copy-on-write, block
 pool and cascade planning) runs in the native library ``libpkv.so`` built from
 ``csrc/``; PyTorch only provides device memory and streams.  Importing this
 package fails loudly if the library has not been built
-(``python -m paged_kv_cache_21_amd.build``); there is no fallback.
+(``python paged_kv_cache_21_amd/build.py``); there is no fallback.
 
 The names mirror the C ABI in ``include/pkv.h``.
 """
@@ -97,6 +97,7 @@ _SIGNATURES = {
     "pkv_plan_num_nodes": (_i32, [_vp]),
     "pkv_plan_node": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp]),
     "pkv_plan_row": (_i32, [_vp, _i32, _vp, _vp]),
+    "pkv_plan_node_pieces": (_i32, [_vp, _i32]),
     "pkv_timing_enable": (_i32, [_i32]),
     "pkv_timing_reset": (_i32, []),
     "pkv_timing_read": (_i32, [_i32, _vp, _vp]),
@@ -105,7 +106,7 @@ _SIGNATURES = {
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_21_amd.build` "
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_21_amd/build.py` "
                           "(hipcc, gfx950). There is no fallback implementation.")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
@@ -385,8 +386,15 @@ class CascadePlan:
         _check(_lib.pkv_plan_node(self._handle, int(i), None, None, _ptr(blocks), _ptr(members)))
         return blocks[: int(nb[0])].copy(), members[: int(nm[0])].copy()
 
+    def node_pieces(self, i):
+        """Token pieces node i is split into (one partial slot each)."""
+        n = int(_lib.pkv_plan_node_pieces(self._handle, int(i)))
+        if n < 0:
+            raise PkvInvalid(PKV_ERR_INVALID, f"bad node index {i}")
+        return n
+
     def row(self, b):
-        """(shared tokens, depth) of row b."""
+        """(shared tokens, partial slots used by the row's nodes) of row b."""
         st = np.zeros(1, dtype=np.int32)
         dp = np.zeros(1, dtype=np.int32)
         _check(_lib.pkv_plan_row(self._handle, int(b), _ptr(st), _ptr(dp)))

@@ -49,10 +49,13 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
 
 }  // namespace
 
-// Work-group: 4 waves, 64 query rows (16 per wave).  Row rho of a node is
-// (member rho / G, query head hkv*G + rho % G).  Tokens are processed in chunks
-// of 32 (two blocks): the work-group stages K [32 x D] and V^T [D x 32] in LDS,
-// each wave evaluates its 16 rows.
+// Work-group: 4 waves, 64 query rows (16 per wave), one token piece of one
+// node for one KV head.  Row rho of a node is (member rho / G, query head
+// hkv*G + rho % G).  Tokens are processed in chunks of 32 (two blocks): the
+// work-group stages K [32 x D] and V^T [D x 32] in LDS, each wave evaluates its
+// 16 rows.  Pipeline: two LDS buffers and a two-chunk register ring, so chunk
+// c is evaluated while chunk c+1 is written to the other LDS buffer and chunks
+// c+2, c+3 are in flight from memory; one barrier per chunk.
 //
 // MFMA 16x16x32 operand layout used (lane l, element j of 8): A row l % 16,
 // k = 8*(l / 16) + j; B column l % 16, same k; accumulator element j of lane l
@@ -69,18 +72,22 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
   constexpr int KVEC_PER_THREAD = KVEC / 256;  // 1 (D=64) or 2 (D=128)
   static_assert(KVEC_PER_THREAD >= 1, "unsupported head_dim");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[32 * KPITCH];
-  __shared__ __attribute__((aligned(16))) uint32_t vt_lds[D * VPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][32 * KPITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t vt_lds[2][D * VPITCH];
 
   const int item = blockIdx.x;
-  const int node = a.items[3 * item];
+  const int node = a.items[4 * item];
   if (node < 0) return;  // padding item (uniform for the work-group)
-  const int hkv = a.items[3 * item + 1];
-  const int row0 = a.items[3 * item + 2];
-  const int blk_off = a.nodes[4 * node + 0];
-  const int nblk = a.nodes[4 * node + 1];
-  const int mem_off = a.nodes[4 * node + 2];
-  const int nmem = a.nodes[4 * node + 3];
+  const int hkv = a.items[4 * item + 1];
+  const int row0 = a.items[4 * item + 2];
+  const int piece = a.items[4 * item + 3];
+  const int blk_off = a.nodes[6 * node + 0];
+  const int node_blocks = a.nodes[6 * node + 1];
+  const int mem_off = a.nodes[6 * node + 2];
+  const int nmem = a.nodes[6 * node + 3];
+  const int piece_blocks = a.nodes[6 * node + 5];
+  const int pb0 = piece * piece_blocks;
+  const int nblk = min(piece_blocks, node_blocks - pb0);
   const int R = nmem * G;
   const int Hkv = a.num_kv_heads;
   const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;
@@ -99,7 +106,7 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
   if (my_row < R) {
     const int member = my_row / G;
     my_b = a.node_members[2 * (mem_off + member)];
-    my_slot = a.node_members[2 * (mem_off + member) + 1];
+    my_slot = a.node_members[2 * (mem_off + member) + 1] + piece;
     my_h = hkv * G + my_row % G;
     const uint16_t* qp = a.q + (static_cast<int64_t>(my_b) * a.num_q_heads + my_h) * D + lgrp * 8;
 #pragma unroll
@@ -114,19 +121,29 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // global -> register staging of one chunk
-  u32x4 kreg[KVEC_PER_THREAD];
-  u32x4 vreg0, vreg1;
   const int vpair = tid & 15;  // tokens 2*vpair, 2*vpair+1
   const int vcol = tid >> 4;   // 8-element column group
   const bool vthread = vcol < D / 8;
 
-  auto block_id = [&](int j) -> int {
+  // the piece's block ids, lane j holding block j (a piece has at most 64 blocks);
+  // read with readlane so the chunk loop issues no scalar memory loads, which would
+  // share a wait counter with the LDS reads
+  const int my_blk = lane < nblk ? a.node_blocks[blk_off + pb0 + lane] : -1;
+  auto block_id = [&](int j) -> int {  // j: block within the piece
     if (j >= nblk) return -1;
-    const int id = a.node_blocks[blk_off + j];
+    const int id = __builtin_amdgcn_readlane(my_blk, j);
     return (id >= 0 && static_cast<int64_t>(id) < a.num_blocks) ? id : -1;
   };
-  auto load_chunk = [&](int ch) {
+
+  struct Stage {
+    u32x4 k[KVEC_PER_THREAD];
+    u32x4 v0, v1;
+  };
+  const int nchunks = (nblk + 1) / 2;
+  // global -> registers (cached loads: the other row tiles of this piece read the
+  // same K/V from L2); past the last chunk the last one is read again (an L2 hit)
+  auto load_chunk = [&](int ch, Stage& st) {
+    ch = min(ch, nchunks - 1);
     const int id0 = block_id(2 * ch), id1 = block_id(2 * ch + 1);
 #pragma unroll
     for (int i = 0; i < KVEC_PER_THREAD; ++i) {
@@ -134,104 +151,119 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
       const int tok = vi / (D / 8);
       const int col = vi % (D / 8);
       const int id = tok < 16 ? id0 : id1;
-      kreg[i] = id >= 0 ? ld16(a.k_pages + (static_cast<int64_t>(id) * 16 + (tok & 15)) * tok_stride +
-                               static_cast<int64_t>(hkv) * D + col * 8)
-                        : u32x4{0, 0, 0, 0};
+      st.k[i] = ld16(a.k_pages + (static_cast<int64_t>(id < 0 ? 0 : id) * 16 + (tok & 15)) * tok_stride +
+                            static_cast<int64_t>(hkv) * D + col * 8);
     }
     if (vthread) {
       const int t0 = 2 * vpair;
       const int id = t0 < 16 ? id0 : id1;
-      if (id >= 0) {
-        const uint16_t* vp = a.v_pages + (static_cast<int64_t>(id) * 16 + (t0 & 15)) * tok_stride +
-                             static_cast<int64_t>(hkv) * D + vcol * 8;
-        vreg0 = ld16(vp);
-        vreg1 = ld16(vp + tok_stride);
-      } else {
-        vreg0 = u32x4{0, 0, 0, 0};
-        vreg1 = u32x4{0, 0, 0, 0};
-      }
+      const uint16_t* vp = a.v_pages + (static_cast<int64_t>(id < 0 ? 0 : id) * 16 + (t0 & 15)) * tok_stride +
+                           static_cast<int64_t>(hkv) * D + vcol * 8;
+      st.v0 = ld16(vp);
+      st.v1 = ld16(vp + tok_stride);
     }
   };
-
-  const int nchunks = (nblk + 1) / 2;
-  if (nchunks > 0) load_chunk(0);
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const bool valid0 = block_id(2 * ch) >= 0;
-    const bool valid1 = block_id(2 * ch + 1) >= 0;
-    __syncthreads();  // every wave is done reading the previous chunk
+  // registers -> LDS buffer: K as is, V transposed to [d][token] pairs
+  auto store_chunk = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int i = 0; i < KVEC_PER_THREAD; ++i) {
       const int vi = tid + 256 * i;
       const int tok = vi / (D / 8);
       const int col = vi % (D / 8);
-      *reinterpret_cast<u32x4*>(&k_lds[tok * KPITCH + col * 8]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&k_lds[buf][tok * KPITCH + col * 8]) = st.k[i];
     }
     if (vthread) {
-      const uint32_t w0[4] = {vreg0.x, vreg0.y, vreg0.z, vreg0.w};
-      const uint32_t w1[4] = {vreg1.x, vreg1.y, vreg1.z, vreg1.w};
+      const uint32_t w0[4] = {st.v0.x, st.v0.y, st.v0.z, st.v0.w};
+      const uint32_t w1[4] = {st.v1.x, st.v1.y, st.v1.z, st.v1.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // element 2e and 2e+1 of the column group, for tokens 2*vpair (low) and 2*vpair+1 (high)
-        vt_lds[(vcol * 8 + 2 * e) * VPITCH + vpair] =
+        // elements 2e and 2e+1 of the column group, for tokens 2*vpair (low) and 2*vpair+1 (high)
+        vt_lds[buf][(vcol * 8 + 2 * e) * VPITCH + vpair] =
             pack2(static_cast<uint16_t>(w0[e] & 0xffff), static_cast<uint16_t>(w1[e] & 0xffff));
-        vt_lds[(vcol * 8 + 2 * e + 1) * VPITCH + vpair] =
+        vt_lds[buf][(vcol * 8 + 2 * e + 1) * VPITCH + vpair] =
             pack2(static_cast<uint16_t>(w0[e] >> 16), static_cast<uint16_t>(w1[e] >> 16));
       }
     }
-    __syncthreads();
-    if (ch + 1 < nchunks) load_chunk(ch + 1);  // in flight while this chunk is evaluated
+  };
+  // evaluate chunk ch from LDS buffer buf for this wave's 16 rows
+  auto compute_chunk = [&](int ch, int buf) {
+    if (!wave_active) return;
+    const bool valid0 = block_id(2 * ch) >= 0;
+    const bool valid1 = block_id(2 * ch + 1) >= 0;
+    // S^T tiles: st[tt][j] = score of token 16*tt + 4*lgrp + j for this lane's row
+    f32x4 st[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(&k_lds[buf][(tt * 16 + lrow) * KPITCH + ks * 32 + lgrp * 8]);
+        c = mfma16x16x32<DT>(kv, qb[ks], c);
+      }
+      st[tt] = c;
+    }
+    float sv[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sv[j] = valid0 ? st[0][j] * a.scale_log2 : kNegInf;
+      sv[4 + j] = valid1 ? st[1][j] * a.scale_log2 : kNegInf;
+    }
+    float cmax = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sv[j]);
+    cmax = fmaxf(cmax, shfl_xor_f32(cmax, 16));
+    cmax = fmaxf(cmax, shfl_xor_f32(cmax, 32));
+    const float mn = fmaxf(m, cmax);
+    if (mn > m) {
+      const float alpha = exp2_diff(m, mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m = mn;
+    }
+    uint16_t ph[8], pl[8];
+    const float mref = fmaxf(m, -3.0e38f);  // m = -inf only while every score is -inf
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = fast_exp2(sv[j] - mref);
+      lsum += p;
+      ph[j] = DT::from_float(p);
+      pl[j] = DT::from_float(p - DT::to_float(ph[j]));
+    }
+    const u32x4 bh = u32x4{pack2(ph[0], ph[1]), pack2(ph[2], ph[3]), pack2(ph[4], ph[5]), pack2(ph[6], ph[7])};
+    const u32x4 bl = u32x4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])};
+    // all V^T operands first, then the MFMAs
+    u32x4 av[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const uint32_t* vrow = &vt_lds[buf][(dt * 16 + lrow) * VPITCH];
+      const uint2 t0 = *reinterpret_cast<const uint2*>(vrow + 2 * lgrp);      // tokens 4*lgrp .. +3
+      const uint2 t1 = *reinterpret_cast<const uint2*>(vrow + 8 + 2 * lgrp);  // tokens 16 + 4*lgrp .. +3
+      av[dt] = u32x4{t0.x, t0.y, t1.x, t1.y};
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma16x16x32<DT>(av[dt], bh, o[dt]);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma16x16x32<DT>(av[dt], bl, o[dt]);
+  };
 
-    if (wave_active) {
-      // S^T tiles: st[tt][j] = score of token 16*tt + 4*lgrp + j for this lane's row
-      f32x4 st[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(&k_lds[(tt * 16 + lrow) * KPITCH + ks * 32 + lgrp * 8]);
-          c = mfma16x16x32<DT>(kv, qb[ks], c);
-        }
-        st[tt] = c;
-      }
-      float sv[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sv[j] = valid0 ? st[0][j] * a.scale_log2 : kNegInf;
-        sv[4 + j] = valid1 ? st[1][j] * a.scale_log2 : kNegInf;
-      }
-      float cmax = sv[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sv[j]);
-      cmax = fmaxf(cmax, shfl_xor_f32(cmax, 16));
-      cmax = fmaxf(cmax, shfl_xor_f32(cmax, 32));
-      const float mn = fmaxf(m, cmax);
-      if (mn > m) {
-        const float alpha = exp2_diff(m, mn);
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-        m = mn;
-      }
-      uint16_t ph[8], pl[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = m == kNegInf ? 0.f : fast_exp2(sv[j] - m);
-        lsum += p;
-        ph[j] = DT::from_float(p);
-        pl[j] = DT::from_float(p - DT::to_float(ph[j]));
-      }
-      const u32x4 bh = u32x4{pack2(ph[0], ph[1]), pack2(ph[2], ph[3]), pack2(ph[4], ph[5]), pack2(ph[6], ph[7])};
-      const u32x4 bl = u32x4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])};
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint32_t* vrow = &vt_lds[(dt * 16 + lrow) * VPITCH];
-        const uint2 t0 = *reinterpret_cast<const uint2*>(vrow + 2 * lgrp);      // tokens 4*lgrp .. +3
-        const uint2 t1 = *reinterpret_cast<const uint2*>(vrow + 8 + 2 * lgrp);  // tokens 16 + 4*lgrp .. +3
-        const u32x4 av = u32x4{t0.x, t0.y, t1.x, t1.y};
-        o[dt] = mfma16x16x32<DT>(av, bh, o[dt]);
-        o[dt] = mfma16x16x32<DT>(av, bl, o[dt]);
-      }
+  if (nchunks > 0) {
+    Stage s0, s1;
+    load_chunk(0, s0);
+    load_chunk(1, s1);
+    store_chunk(s0, 0);
+    load_chunk(2, s0);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ch += 2) {
+      compute_chunk(ch, 0);
+      store_chunk(s1, 1);  // chunk ch+1
+      load_chunk(ch + 3, s1);
+      __syncthreads();
+      if (ch + 1 >= nchunks) break;
+      compute_chunk(ch + 1, 1);
+      store_chunk(s0, 0);  // chunk ch+2
+      load_chunk(ch + 4, s0);
+      __syncthreads();
     }
   }
 

@@ -76,10 +76,11 @@ struct CascadeArgs {
   const uint16_t* q;
   const uint16_t* k_pages;
   const uint16_t* v_pages;
-  const int32_t* items;         // [num_items][3] = (node, kv head, first tile row); node < 0: idle
-  const int32_t* nodes;         // [num_nodes][4] = (block offset, num blocks, member offset, num members)
+  const int32_t* items;         // [num_items][4] = (node, kv head, first tile row, piece); node < 0: idle
+  const int32_t* nodes;         // [num_nodes][6] = (block offset, blocks, member offset, members, pieces,
+                                //                   blocks per piece)
   const int32_t* node_blocks;   // physical block ids
-  const int32_t* node_members;  // [..][2] = (row, partial slot)
+  const int32_t* node_members;  // [..][2] = (row, partial slot of piece 0; piece p uses slot + p)
   float* acc;
   float2* ml;
   int64_t num_blocks;

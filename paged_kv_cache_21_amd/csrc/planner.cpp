@@ -39,6 +39,8 @@ void build_image(pkv_plan* p) {
     im.push_back(n.num_blocks);
     im.push_back(n.member_off);
     im.push_back(n.num_members);
+    im.push_back(n.pieces);
+    im.push_back(n.piece_blocks);
   }
   p->off_blocks = im.size();
   im.insert(im.end(), p->node_blocks.begin(), p->node_blocks.end());
@@ -49,24 +51,69 @@ void build_image(pkv_plan* p) {
   if (im.empty()) im.push_back(0);
 }
 
-// Work items: one per (node, KV head, 64-row tile).  Work-group i runs on XCD
-// i % 8, and each XCD has its own L2, so all tiles of one (node, head) go to the
-// same XCD queue: the tiles after the first find the node's K/V in that L2.
-// Clusters are dealt to the least-loaded queue (load = blocks x tiles); queues
-// are interleaved into launch order and padded with idle items.
+// Token pieces.  A node's work is (64-row tiles) x (KV heads) x (blocks); the
+// chip wants a few work-groups per CU.  Long nodes are cut into pieces of about
+// `target` blocks so the item count lands near kTargetItems, but never below
+// kMinPieceBlocks blocks per piece: every piece costs each member row one more
+// fp32 partial per query head, written and read back once.
+void split_pieces(pkv_plan* p) {
+  constexpr int64_t kTargetItems = 1024;
+  constexpr int32_t kMinPieceBlocks = 32;
+  constexpr int32_t kMaxPieceBlocks = 64;
+  const int rows_per_item = pkv::kCascadeRowsPerItem;
+  int64_t work = 0;
+  for (const auto& n : p->nodes) {
+    const int64_t tiles = (static_cast<int64_t>(n.num_members) * p->group + rows_per_item - 1) / rows_per_item;
+    work += tiles * p->num_kv_heads * n.num_blocks;
+  }
+  const int64_t target = std::max<int64_t>(kMinPieceBlocks, (work + kTargetItems - 1) / kTargetItems);
+  for (auto& n : p->nodes) {
+    // at most kMaxPieceBlocks blocks per piece: the cascade kernel keeps a piece's
+    // block ids in one 64-lane register
+    n.pieces = static_cast<int32_t>(std::max<int64_t>(
+        std::max<int64_t>(1, n.num_blocks / target), (n.num_blocks + kMaxPieceBlocks - 1) / kMaxPieceBlocks));
+    n.piece_blocks = (n.num_blocks + n.pieces - 1) / n.pieces;
+    n.pieces = (n.num_blocks + n.piece_blocks - 1) / n.piece_blocks;
+  }
+}
+
+// Partial slots: along each row's path, node pieces take consecutive slots.
+// path[b] lists (node, member entry) pairs, root first.
+void assign_slots(pkv_plan* p, const std::vector<std::vector<std::pair<int32_t, int32_t>>>& path) {
+  p->max_depth = 0;
+  for (int32_t b = 0; b < p->batch; ++b) {
+    int32_t used = 0;
+    for (const auto& [node, entry] : path[b]) {
+      p->node_members[2 * entry + 1] = used;
+      used += p->nodes[node].pieces;
+    }
+    p->row_info[2 * b + 1] = used;
+    p->max_depth = std::max(p->max_depth, used);
+  }
+}
+
+// Work items: one per (node, KV head, 64-row tile, piece).  Work-group i runs on
+// XCD i % 8, and each XCD has its own L2, so all tiles of one (node, head, piece)
+// go to the same XCD queue: the tiles after the first find the piece's K/V in
+// that L2.  Clusters are dealt to the least-loaded queue (load = blocks x tiles);
+// queues are interleaved into launch order and padded with idle items.
 void build_items(pkv_plan* p) {
   constexpr int kXcds = 8;
   const int rows_per_item = pkv::kCascadeRowsPerItem;
   struct Cluster {
-    int32_t node, head, tiles;
+    int32_t node, head, tiles, piece;
     int64_t load;
   };
   std::vector<Cluster> clusters;
   for (int32_t n = 0; n < static_cast<int32_t>(p->nodes.size()); ++n) {
-    const int32_t rows = p->nodes[n].num_members * p->group;
+    const auto& nd = p->nodes[n];
+    const int32_t rows = nd.num_members * p->group;
     const int32_t tiles = (rows + rows_per_item - 1) / rows_per_item;
-    for (int32_t h = 0; h < p->num_kv_heads; ++h)
-      clusters.push_back({n, h, tiles, static_cast<int64_t>(p->nodes[n].num_blocks) * tiles});
+    for (int32_t pc = 0; pc < nd.pieces; ++pc) {
+      const int32_t blocks = std::min(nd.piece_blocks, nd.num_blocks - pc * nd.piece_blocks);
+      for (int32_t h = 0; h < p->num_kv_heads; ++h)
+        clusters.push_back({n, h, tiles, pc, static_cast<int64_t>(blocks) * tiles});
+    }
   }
   std::stable_sort(clusters.begin(), clusters.end(),
                    [](const Cluster& x, const Cluster& y) { return x.load > y.load; });
@@ -81,20 +128,19 @@ void build_items(pkv_plan* p) {
       queues[q].push_back(c.node);
       queues[q].push_back(c.head);
       queues[q].push_back(t * rows_per_item);
+      queues[q].push_back(c.piece);
     }
   }
   size_t longest = 0;
-  for (const auto& q : queues) longest = std::max(longest, q.size() / 3);
+  for (const auto& q : queues) longest = std::max(longest, q.size() / 4);
   p->items.clear();
   if (clusters.empty()) return;
   for (size_t k = 0; k < longest; ++k)
     for (int q = 0; q < kXcds; ++q) {
-      if (k < queues[q].size() / 3) {
-        p->items.insert(p->items.end(), queues[q].begin() + 3 * k, queues[q].begin() + 3 * k + 3);
+      if (k < queues[q].size() / 4) {
+        p->items.insert(p->items.end(), queues[q].begin() + 4 * k, queues[q].begin() + 4 * k + 4);
       } else {
-        p->items.push_back(-1);
-        p->items.push_back(0);
-        p->items.push_back(0);
+        p->items.insert(p->items.end(), {-1, 0, 0, 0});
       }
     }
 }
@@ -132,6 +178,7 @@ pkv_plan* pkv_plan_build(const int32_t* block_tables, const int32_t* seq_lens, i
   }
   auto id_at = [&](int32_t row, int32_t j) { return block_tables[static_cast<int64_t>(row) * max_blocks_per_seq + j]; };
 
+  std::vector<std::vector<std::pair<int32_t, int32_t>>> path(batch);  // (node, member entry), root first
   std::vector<Group> stack;
   {
     Group g;
@@ -164,12 +211,10 @@ pkv_plan* pkv_plan_build(const int32_t* block_tables, const int32_t* seq_lens, i
       n.num_members = static_cast<int32_t>(g.rows.size());
       for (int32_t j = g.start; j < i; ++j) p->node_blocks.push_back(id_at(g.rows[0], j));
       for (int32_t r : g.rows) {
-        const int32_t depth = p->row_info[2 * r + 1];
+        path[r].emplace_back(static_cast<int32_t>(p->nodes.size()), static_cast<int32_t>(p->node_members.size() / 2));
         p->node_members.push_back(r);
-        p->node_members.push_back(depth);  // partial slot = position on the row's path
+        p->node_members.push_back(0);  // slot, assigned once pieces are known
         p->row_info[2 * r] = i * block_size;
-        p->row_info[2 * r + 1] = depth + 1;
-        p->max_depth = std::max(p->max_depth, depth + 1);
       }
       p->nodes.push_back(n);
     }
@@ -195,6 +240,8 @@ pkv_plan* pkv_plan_build(const int32_t* block_tables, const int32_t* seq_lens, i
     }
     for (auto it = children.rbegin(); it != children.rend(); ++it) stack.push_back(std::move(*it));
   }
+  split_pieces(p);
+  assign_slots(p, path);
   build_items(p);
   build_image(p);
   return p;
@@ -218,6 +265,11 @@ pkv_status pkv_plan_node(const pkv_plan* plan, int32_t node, int32_t* num_blocks
   if (members_out)
     for (int32_t k = 0; k < n.num_members; ++k) members_out[k] = plan->node_members[2 * (n.member_off + k)];
   return PKV_OK;
+}
+
+int32_t pkv_plan_node_pieces(const pkv_plan* plan, int32_t node) {
+  if (!plan || node < 0 || node >= static_cast<int32_t>(plan->nodes.size())) return -1;
+  return plan->nodes[node].pieces;
 }
 
 pkv_status pkv_plan_row(const pkv_plan* plan, int32_t row, int32_t* shared_tokens, int32_t* depth) {

@@ -24,17 +24,15 @@ def check_plan(plan, bt, lens, bs=16, min_members=2):
     B = bt.shape[0]
     full = lens // bs
     nodes = [plan.node(i) for i in range(plan.num_nodes)]
-    path = {b: {} for b in range(B)}
+    pieces = [plan.node_pieces(i) for i in range(plan.num_nodes)]
     for i, (blocks, members) in enumerate(nodes):
         assert len(blocks) >= 1 and len(members) >= min_members
-        for m in members:
-            _, depth = plan.row(m)
-            path[m][i] = None
+        assert 1 <= pieces[i] <= len(blocks)
     # walk each row's path in slot order and check tiling
     for b in range(B):
         shared, depth = plan.row(b)
         mine = [i for i, (_, members) in enumerate(nodes) if b in set(members.tolist())]
-        assert len(mine) == depth
+        assert sum(pieces[i] for i in mine) == depth
         # order nodes by where they sit in the row's table
         pos = 0
         remaining = set(mine)
@@ -75,7 +73,7 @@ def test_tiny_tree_one_prefix_node():
     blocks, members = plan.node(0)
     assert len(blocks) == 16 and sorted(members.tolist()) == [0, 1, 2, 3]
     for b in range(4):
-        assert plan.row(b) == (256, 1)
+        assert plan.row(b) == (256, plan.node_pieces(0))
     check_plan(plan, bt, lens)
 
 
@@ -87,7 +85,8 @@ def test_tree_search_one_node_per_problem():
     for i in range(16):
         blocks, members = plan.node(i)
         assert len(blocks) == 128 and len(members) == 64
-    assert all(plan.row(b) == (2048, 1) for b in range(bt.shape[0]))
+    assert all(plan.row(b) == (2048, plan.node_pieces(b // 64)) for b in range(bt.shape[0]))
+    assert plan.node_pieces(0) == 2  # 16 x 4 tiles x 8 heads x 2 pieces = 1024 work items
 
 
 def test_radix_tree_levels():
@@ -99,7 +98,10 @@ def test_radix_tree_levels():
     assert sizes.count((256, 256)) == 1
     assert sizes.count((16, 64)) == 4 and sizes.count((16, 16)) == 16 and sizes.count((16, 4)) == 64
     assert plan.num_nodes == 85
-    assert all(plan.row(b) == (4096 + 3 * 256, 4) for b in range(256))
+    root = [i for i in range(plan.num_nodes) if len(plan.node(i)[0]) == 256][0]
+    assert plan.node_pieces(root) > 1  # the root is split across work-groups
+    depth = plan.node_pieces(root) + 3
+    assert all(plan.row(b) == (4096 + 3 * 256, depth) for b in range(256))
     check_plan(plan, bt, lens)
 
 
