@@ -109,8 +109,11 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
     my_slot = a.node_members[2 * (mem_off + member) + 1] + piece;
     my_h = hkv * G + my_row % G;
     const uint16_t* qp = a.q + (static_cast<int64_t>(my_b) * a.num_q_heads + my_h) * D + lgrp * 8;
+    // a negative scale is applied as |scale| on -q (flipping sign bits is exact), so the
+    // running max can be taken on the unscaled scores
+    const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qb[ks] = ld16(qp + ks * 32);
+    for (int ks = 0; ks < NKS; ++ks) qb[ks] = ld16(qp + ks * 32) ^ flip;
   } else {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
@@ -140,25 +143,34 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
     u32x4 v0, v1;
   };
   const int nchunks = (nblk + 1) / 2;
+  // Per-thread element offsets inside a block (32-bit: a block is 16 * Hkv * D
+  // elements); per chunk only the two block bases change, and those are uniform.
+  const int64_t blk_stride = 16 * tok_stride;
+  int koff[KVEC_PER_THREAD];
+  bool khi[KVEC_PER_THREAD];  // token in the chunk's second block
+#pragma unroll
+  for (int i = 0; i < KVEC_PER_THREAD; ++i) {
+    const int vi = tid + 256 * i;
+    const int tok = vi / (D / 8);
+    const int col = vi % (D / 8);
+    koff[i] = static_cast<int>((tok & 15) * tok_stride + static_cast<int64_t>(hkv) * D + col * 8);
+    khi[i] = tok >= 16;
+  }
+  const int voff = static_cast<int>(((2 * vpair) & 15) * tok_stride + static_cast<int64_t>(hkv) * D + vcol * 8);
+  const bool vhi = 2 * vpair >= 16;
   // global -> registers (cached loads: the other row tiles of this piece read the
   // same K/V from L2); past the last chunk the last one is read again (an L2 hit)
   auto load_chunk = [&](int ch, Stage& st) {
     ch = min(ch, nchunks - 1);
     const int id0 = block_id(2 * ch), id1 = block_id(2 * ch + 1);
+    const int64_t b0 = static_cast<int64_t>(id0 < 0 ? 0 : id0) * blk_stride;
+    const int64_t b1 = static_cast<int64_t>(id1 < 0 ? 0 : id1) * blk_stride;
+    const uint16_t* k0 = a.k_pages + b0;
+    const uint16_t* k1 = a.k_pages + b1;
 #pragma unroll
-    for (int i = 0; i < KVEC_PER_THREAD; ++i) {
-      const int vi = tid + 256 * i;
-      const int tok = vi / (D / 8);
-      const int col = vi % (D / 8);
-      const int id = tok < 16 ? id0 : id1;
-      st.k[i] = ld16(a.k_pages + (static_cast<int64_t>(id < 0 ? 0 : id) * 16 + (tok & 15)) * tok_stride +
-                            static_cast<int64_t>(hkv) * D + col * 8);
-    }
+    for (int i = 0; i < KVEC_PER_THREAD; ++i) st.k[i] = ld16((khi[i] ? k1 : k0) + koff[i]);
     if (vthread) {
-      const int t0 = 2 * vpair;
-      const int id = t0 < 16 ? id0 : id1;
-      const uint16_t* vp = a.v_pages + (static_cast<int64_t>(id < 0 ? 0 : id) * 16 + (t0 & 15)) * tok_stride +
-                           static_cast<int64_t>(hkv) * D + vcol * 8;
+      const uint16_t* vp = (vhi ? a.v_pages + b1 : a.v_pages + b0) + voff;
       st.v0 = ld16(vp);
       st.v1 = ld16(vp + tok_stride);
     }
@@ -177,11 +189,10 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
       const uint32_t w1[4] = {st.v1.x, st.v1.y, st.v1.z, st.v1.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // elements 2e and 2e+1 of the column group, for tokens 2*vpair (low) and 2*vpair+1 (high)
-        vt_lds[buf][(vcol * 8 + 2 * e) * VPITCH + vpair] =
-            pack2(static_cast<uint16_t>(w0[e] & 0xffff), static_cast<uint16_t>(w1[e] & 0xffff));
-        vt_lds[buf][(vcol * 8 + 2 * e + 1) * VPITCH + vpair] =
-            pack2(static_cast<uint16_t>(w0[e] >> 16), static_cast<uint16_t>(w1[e] >> 16));
+        // elements 2e and 2e+1 of the column group, for tokens 2*vpair (low half) and
+        // 2*vpair+1 (high half): one byte permute each
+        vt_lds[buf][(vcol * 8 + 2 * e) * VPITCH + vpair] = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+        vt_lds[buf][(vcol * 8 + 2 * e + 1) * VPITCH + vpair] = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
       }
     }
   };
@@ -202,19 +213,29 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
       }
       st[tt] = c;
     }
+    // raw scores (scale applied inside the exponent); tokens of missing blocks -> -inf
     float sv[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sv[j] = valid0 ? st[0][j] * a.scale_log2 : kNegInf;
-      sv[4 + j] = valid1 ? st[1][j] * a.scale_log2 : kNegInf;
+      sv[j] = st[0][j];
+      sv[4 + j] = st[1][j];
     }
-    float cmax = sv[0];
+    if (!(valid0 && valid1)) {  // uniform: only at a piece's odd end or for bad ids
 #pragma unroll
-    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, sv[j]);
+      for (int j = 0; j < 4; ++j) {
+        sv[j] = valid0 ? sv[j] : kNegInf;
+        sv[4 + j] = valid1 ? sv[4 + j] : kNegInf;
+      }
+    }
+    float cmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     cmax = fmaxf(cmax, shfl_xor_f32(cmax, 16));
     cmax = fmaxf(cmax, shfl_xor_f32(cmax, 32));
-    const float mn = fmaxf(m, cmax);
-    if (mn > m) {
+    const float c = fabsf(a.scale_log2);
+    const float cm = cmax * c;  // chunk max in log2 units
+    // Rescale only when some row's max grows by more than 2^8: until then the
+    // weights 2^(s - m) stay <= 256, harmless in fp32 and in the 16-bit terms.
+    if (__any(cm > m + 8.f)) {
+      const float mn = fmaxf(m, cm);
       const float alpha = exp2_diff(m, mn);
       lsum *= alpha;
 #pragma unroll
@@ -225,7 +246,7 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
     const float mref = fmaxf(m, -3.0e38f);  // m = -inf only while every score is -inf
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = fast_exp2(sv[j] - mref);
+      const float p = fast_exp2(fmaf(sv[j], c, -mref));
       lsum += p;
       ph[j] = DT::from_float(p);
       pl[j] = DT::from_float(p - DT::to_float(ph[j]));
