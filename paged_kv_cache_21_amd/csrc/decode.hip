@@ -115,6 +115,10 @@ __device__ __forceinline__ int wave_sum(int x) {
 #ifndef PKV_SPLIT_WAVES_PER_EU
 #define PKV_SPLIT_WAVES_PER_EU 1
 #endif
+// Load the next segment's q while the current segment finishes (else at the switch).
+#ifndef PKV_Q_PREFETCH
+#define PKV_Q_PREFETCH 1
+#endif
 
 template <class DT, int D, int G, int LPT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
@@ -168,7 +172,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   Cursor pre = cur;  // position of the next block to load
 
   const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;  // elements between consecutive tokens
-  const int64_t lane_off = static_cast<int64_t>(r) * tok_stride + c * 8;
+  const int64_t blk_stride = 16 * tok_stride;
+  // Byte offsets of this lane's 16-byte pieces inside one (block, KV head): 32-bit and
+  // fixed for the whole kernel, so each load is a uniform base plus one of these.
+  uint32_t voff[TPB][VPL];
+#pragma unroll
+  for (int t = 0; t < TPB; ++t)
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      voff[t][v] = static_cast<uint32_t>(((r + t * ROWS) * tok_stride + (v * LPT + c) * 8) * 2);
 
   auto block_id = [&](const Cursor& p) -> int {
     return a.block_tables[static_cast<int64_t>(p.b) * a.max_blocks + p.blk0 + p.j];
@@ -182,16 +194,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
   };
   auto load_block = [&](const Cursor& p, u32x4(&kk)[TPB][VPL], u32x4(&vv)[TPB][VPL]) -> bool {
-    const int id = block_id(p);
+    // the id and head are the same in every lane; readfirstlane makes that explicit so the
+    // loads use a scalar base with the per-lane 32-bit offsets
+    const int id = __builtin_amdgcn_readfirstlane(block_id(p));
+    const int h = __builtin_amdgcn_readfirstlane(p.h);
     const bool ok = id >= 0 && static_cast<int64_t>(id) < a.num_blocks;
-    const int64_t off = static_cast<int64_t>(ok ? id : 0) * 16 * tok_stride + static_cast<int64_t>(p.h) * D + lane_off;
+    const int64_t base = static_cast<int64_t>(ok ? id : 0) * blk_stride + static_cast<int64_t>(h) * D;
+    const char* kb = reinterpret_cast<const char*>(a.k_pages + base);
+    const char* vb = reinterpret_cast<const char*>(a.v_pages + base);
 #pragma unroll
     for (int t = 0; t < TPB; ++t) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const int64_t o = off + static_cast<int64_t>(t * ROWS) * tok_stride + v * LPT * 8;
-        kk[t][v] = ld16_stream(a.k_pages + o);
-        vv[t][v] = ld16_stream(a.v_pages + o);
+        kk[t][v] = ld16_stream(kb + voff[t][v]);
+        vv[t][v] = ld16_stream(vb + voff[t][v]);
       }
     }
     return ok;
@@ -199,7 +215,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
 
   u32x4 qv[G][VPL], qn[G][VPL];
   load_q(cur, qv);
+  // Reduce-scatter softmax when a token row's TPB*G scores fill its LPT lanes exactly
+  // (16 = 4 tokens x 4 heads for head_dim 128 with GQA group 4): the q.k partial sums
+  // are reduce-scattered so lane c owns the score of token c / G, head c % G; the max,
+  // the exponential and the running (m, l) are then computed once per score instead of
+  // once per lane, and the weights are broadcast back with row_newbcast for the PV update.
+  constexpr bool RS = LPT == 16 && TPB * G == 16;
   float m[G], l[G], acc[G][VPL * 8];
+  float m1 = kNegInf, l1 = 0.f;  // reduce-scatter state: head c % G of this token row
   auto reset_state = [&]() {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -208,8 +231,74 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
 #pragma unroll
       for (int e = 0; e < VPL * 8; ++e) acc[g][e] = 0.f;
     }
+    m1 = kNegInf;
+    l1 = 0.f;
   };
   reset_state();
+
+  // reduce-scatter path (RS): sc[t][g] holds this lane's partial q.k sums
+  auto consume_rs = [&](bool ok, float(&sc)[TPB][G], const u32x4(&vv)[TPB][VPL]) {
+    const bool b3 = c & 8, b2 = c & 4, b1 = c & 2, b0 = c & 1;
+    float y[8], z[4], u[2];
+    // stage bit 3 (partner c^8): keep scores k with bit 3 of k equal to bit 3 of c, k = t*G + g
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float lo = sc[j / G][j % G], hi = sc[(j + 8) / G][(j + 8) % G];
+      y[j] = (b3 ? hi : lo) + dpp_f32<kDppRowRor8>(b3 ? lo : hi);
+    }
+    // stage bit 2 (partner c^7 inside each half row)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = (b2 ? y[j + 4] : y[j]) + dpp_f32<kDppRowHalfMirror>(b2 ? y[j] : y[j + 4]);
+    // stage bit 1 (partner c^2)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) u[j] = (b1 ? z[j + 2] : z[j]) + dpp_f32<kDppQuadXor2>(b1 ? z[j] : z[j + 2]);
+    // stage bit 0 (partner c^1): lane c now holds the full score of k = c
+    float sv = ((b0 ? u[1] : u[0]) + dpp_f32<kDppQuadXor1>(b0 ? u[0] : u[1])) * a.scale_log2;
+    const int tok0 = (cur.blk0 + cur.j) * 16;
+    if (!ok || tok0 + 16 > cur.len) {  // uniform: only a row's last block can be partial
+      const bool valid = ok && tok0 + r + (c / G) * ROWS < cur.len;
+      sv = valid ? sv : kNegInf;
+    }
+    // max over the block's tokens of this lane's head: lanes c, c-4, c-8, c-12 of the row
+    float mx = fmaxf(sv, dpp_f32<kDppRowRor4>(sv));
+    mx = fmaxf(mx, dpp_f32<kDppRowRor8>(mx));
+    const bool grow = mx > m1;
+    if (__any(grow)) {
+      const float mn = fmaxf(m1, mx);
+      const float alpha = exp2_diff(m1, mn);
+      l1 *= alpha;
+      m1 = mn;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float ag = row_bcast_f32(alpha, g);  // lane g of the row holds head g
+#pragma unroll
+        for (int e = 0; e < VPL * 8; ++e) acc[g][e] *= ag;
+      }
+    }
+    const float p = fast_exp2(sv - fmaxf(m1, -3.0e38f));
+    l1 += p;
+#pragma unroll
+    for (int t = 0; t < TPB; ++t) {
+      float vf[VPL * 8];
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        vf[v * 8 + 0] = DT::lo(vv[t][v].x);
+        vf[v * 8 + 1] = DT::hi(vv[t][v].x);
+        vf[v * 8 + 2] = DT::lo(vv[t][v].y);
+        vf[v * 8 + 3] = DT::hi(vv[t][v].y);
+        vf[v * 8 + 4] = DT::lo(vv[t][v].z);
+        vf[v * 8 + 5] = DT::hi(vv[t][v].z);
+        vf[v * 8 + 6] = DT::lo(vv[t][v].w);
+        vf[v * 8 + 7] = DT::hi(vv[t][v].w);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float pk = row_bcast_f32(p, t * G + g);
+#pragma unroll
+        for (int e = 0; e < VPL * 8; ++e) acc[g][e] = fmaf(pk, vf[e], acc[g][e]);
+      }
+    }
+  };
 
   auto consume_block = [&](bool ok, const u32x4(&kk)[TPB][VPL], const u32x4(&vv)[TPB][VPL]) {
     float sc[TPB][G];
@@ -227,6 +316,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
         }
         sc[t][g] = x;
       }
+    }
+    if constexpr (RS) {
+      consume_rs(ok, sc, vv);
+      return;
     }
     // sum over the LPT lanes of each token row, one DPP step at a time across all
     // TPB*G independent sums (keeps the DPP read-after-write hazards hidden)
@@ -315,6 +408,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
 
   // merge the token rows and store this segment piece's partial
   auto finish_segment = [&]() {
+    if constexpr (RS) {
+      // the row's weight sum of head c % G: over the lanes c, c-4, c-8, c-12
+      l1 += dpp_f32<kDppRowRor4>(l1);
+      l1 += dpp_f32<kDppRowRor8>(l1);
+#pragma unroll
+      for (int dist = LPT; dist < 64; dist *= 2) {
+        const float mo = shfl_xor_f32(m1, dist);
+        const float lo_ = shfl_xor_f32(l1, dist);
+        const float mn = fmaxf(m1, mo);
+        const float fa = exp2_diff(m1, mn);
+        const float fb = exp2_diff(mo, mn);
+        l1 = l1 * fa + lo_ * fb;
+        m1 = mn;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float fag = row_bcast_f32(fa, g), fbg = row_bcast_f32(fb, g);
+#pragma unroll
+          for (int e = 0; e < VPL * 8; ++e) {
+            const float ao = shfl_xor_f32(acc[g][e], dist);
+            acc[g][e] = acc[g][e] * fag + ao * fbg;
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        m[g] = row_bcast_f32(m1, g);
+        l[g] = row_bcast_f32(l1, g);
+      }
+    } else {
 #pragma unroll
     for (int dist = LPT; dist < 64; dist *= 2) {
 #pragma unroll
@@ -332,6 +454,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
         }
         m[g] = mn;
       }
+    }
     }
     const int64_t first_wave = cur.seg / chunk;
     const int k = static_cast<int>(w - first_wave);
@@ -366,7 +489,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     if (more) {
       const int old_seg_h = pre.h, old_b = pre.b;
       advance(pre, a);
-      if (pre.h != old_seg_h || pre.b != old_b) {
+      if (PKV_Q_PREFETCH && (pre.h != old_seg_h || pre.b != old_b)) {
         load_q(pre, qn);
         q_pending = true;
       }
@@ -380,7 +503,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
       if (more) {
         advance(cur, a);
         reset_state();
-        if (q_pending) {
+        if (!PKV_Q_PREFETCH) {
+          load_q(cur, qv);
+        } else if (q_pending) {
 #pragma unroll
           for (int g = 0; g < G; ++g)
 #pragma unroll

@@ -71,6 +71,25 @@ constexpr int kDppQuadXor1 = 0xb1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4e;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
 constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within each 16
+constexpr int kDppRowRor4 = 0x124;        // lane i <- lane (i - 4) mod 16 within each 16
+constexpr int kDppRowRor8 = 0x128;        // lane i <- lane i ^ 8 within each 16
+constexpr int kDppRowNewBcast = 0x150;    // + k: every lane of a 16-lane row <- lane k of that row
+
+// Lane k of each 16-lane row, broadcast to the row (k must be a compile-time value
+// after unrolling).
+__device__ __forceinline__ float row_bcast_f32(float x, int k) {
+  switch (k & 15) {
+#define PKV_BCAST_CASE(n) \
+  case n:                 \
+    return dpp_f32<kDppRowNewBcast + n>(x);
+    PKV_BCAST_CASE(0) PKV_BCAST_CASE(1) PKV_BCAST_CASE(2) PKV_BCAST_CASE(3)
+    PKV_BCAST_CASE(4) PKV_BCAST_CASE(5) PKV_BCAST_CASE(6) PKV_BCAST_CASE(7)
+    PKV_BCAST_CASE(8) PKV_BCAST_CASE(9) PKV_BCAST_CASE(10) PKV_BCAST_CASE(11)
+    PKV_BCAST_CASE(12) PKV_BCAST_CASE(13) PKV_BCAST_CASE(14) PKV_BCAST_CASE(15)
+#undef PKV_BCAST_CASE
+  }
+  return x;
+}
 
 // Sum over groups of N consecutive lanes (N in 1, 2, 4, 8, 16); every lane of a
 // group ends with the group's sum.
