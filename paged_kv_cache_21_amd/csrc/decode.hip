@@ -36,7 +36,9 @@ namespace pkv {
 // across token rows with lane shuffles when a segment piece ends.  The K/V
 // loads of the next block are issued before the current one is consumed.
 // Block ids outside [0, num_blocks) are never dereferenced: block 0 is read in
-// their place and the block's scores are masked to -inf.
+// their place and the block's scores are masked to -inf.  The values of masked
+// tokens (rows past a row's length, blocks with bad ids) are zeroed before the
+// PV update, so whatever stale bits such rows hold never reach the output.
 
 namespace {
 
@@ -236,6 +238,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   };
   reset_state();
 
+  // Zero the values of tokens past the row's length (or of a whole block with a bad
+  // id): their weight is 0, and 0 * (stale Inf / NaN) must not reach the sums.
+  auto mask_values = [&](bool ok, u32x4(&vv)[TPB][VPL]) {
+    const int tok0 = (cur.blk0 + cur.j) * 16;
+    if (!ok || tok0 + 16 > cur.len) {  // uniform: only a row's last block can be partial
+#pragma unroll
+      for (int t = 0; t < TPB; ++t) {
+        const bool valid = ok && tok0 + r + t * ROWS < cur.len;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) vv[t][v] = valid ? vv[t][v] : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
   // reduce-scatter path (RS): sc[t][g] holds this lane's partial q.k sums
   auto consume_rs = [&](bool ok, float(&sc)[TPB][G], const u32x4(&vv)[TPB][VPL]) {
     const bool b3 = c & 8, b2 = c & 4, b1 = c & 2, b0 = c & 1;
@@ -300,7 +316,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
   };
 
-  auto consume_block = [&](bool ok, const u32x4(&kk)[TPB][VPL], const u32x4(&vv)[TPB][VPL]) {
+  auto consume_block = [&](bool ok, const u32x4(&kk)[TPB][VPL], u32x4(&vv)[TPB][VPL]) {
+    mask_values(ok, vv);
     float sc[TPB][G];
 #pragma unroll
     for (int t = 0; t < TPB; ++t) {
@@ -483,7 +500,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   u32x4 ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL];
   bool ok_a = load_block(pre, ka, va), ok_b = false;
   bool q_pending = false;
-  auto step = [&](int i, bool ok_cur, const u32x4(&kc)[TPB][VPL], const u32x4(&vc)[TPB][VPL],
+  auto step = [&](int i, bool ok_cur, const u32x4(&kc)[TPB][VPL], u32x4(&vc)[TPB][VPL],
                   u32x4(&kn)[TPB][VPL], u32x4(&vn)[TPB][VPL], bool& ok_next) {
     const bool more = i + 1 < count;
     if (more) {
@@ -526,65 +543,80 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one wave per (row, query head) combines the row's node partials and
-// split partials; rows with no tokens get 0.  Lane p reads partial p's (m, l),
-// the wave reduces the max and the weight sum, then every lane accumulates its
-// D/64 output dims over the partials with independent loads.
+// Merge: combines each (row, query head)'s node partials and split partials,
+//   M = max_i m_i,  o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i,
+// and gives rows with no tokens 0.  A wave covers 64 / (D / 8) query heads of one
+// row, lanes split as (head, 8 output dims).  The row's length, plan entry and
+// partial counts are read together, then the partials in batches of 8 with all
+// their loads in flight at once: two dependent rounds of memory latency in all
+// for up to 8 partials.
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
-  constexpr int DPL = D / 64;
+  constexpr int LPH = D / 8;     // lanes per query head
+  constexpr int HPP = 64 / LPH;  // query heads per wave
+  constexpr int BATCH = 8;       // partials loaded together
   const int lane = threadIdx.x;
-  const int h = blockIdx.x % a.num_q_heads;
-  const int b = blockIdx.x / a.num_q_heads;
+  const int groups = (a.num_q_heads + HPP - 1) / HPP;
+  const int b = blockIdx.x / groups;
+  const int h = (blockIdx.x % groups) * HPP + lane / LPH;
+  const int c = lane % LPH;
+  if (h >= a.num_q_heads) return;
   int len = a.seq_lens[b];
-  len = min(len, a.max_seq_len);
-  len = min(len, a.max_blocks * 16);
   int begin = 0, depth = 0;
   if (a.row_info) {
     begin = a.row_info[2 * b];
     depth = a.row_info[2 * b + 1];
   }
   const int hkv = h / (a.num_q_heads / a.num_kv_heads);
-  const int nsplit = len > begin ? a.counts[static_cast<int64_t>(b) * a.num_kv_heads + hkv] : 0;
+  const int counted = a.counts[static_cast<int64_t>(b) * a.num_kv_heads + hkv];  // valid when the row has own tokens
+  len = min(len, a.max_seq_len);
+  len = min(len, a.max_blocks * 16);
+  const int nsplit = len > begin ? counted : 0;
   const int np = min(depth + nsplit, a.slots);
   const int64_t rec0 = static_cast<int64_t>(b) * a.slots * a.num_q_heads + h;
-  const int64_t rstride = a.num_q_heads;
 
-  float o[DPL];
+  float M = kNegInf, L = 0.f;
+  float o[8];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  float L = 0.f;
-  float M = kNegInf;
-  // running merge over chunks of 64 partials
-  for (int p0 = 0; p0 < np; p0 += 64) {
-    const int p = p0 + lane;
-    float2 ml = make_float2(kNegInf, 0.f);
-    if (p < np) ml = a.ml[rec0 + p * rstride];
-    float cm = ml.x;
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int p0 = 0; p0 < np; p0 += BATCH) {
+    float2 ml[BATCH];
+    float4 x0[BATCH], x1[BATCH];
 #pragma unroll
-    for (int dist = 1; dist < 64; dist *= 2) cm = fmaxf(cm, shfl_xor_f32(cm, dist));
-    const float Mn = fmaxf(M, cm);
-    const float fold = exp2_diff(M, Mn);
-    const float wgt = exp2_diff(ml.x, Mn);
-    float lw = wgt * ml.y;
+    for (int i = 0; i < BATCH; ++i) {
+      ml[i] = make_float2(kNegInf, 0.f);
+      x0[i] = x1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p0 + i < np) {
+        const int64_t rec = rec0 + static_cast<int64_t>(p0 + i) * a.num_q_heads;
+        ml[i] = a.ml[rec];
+        const float4* src = reinterpret_cast<const float4*>(a.acc + rec * D + c * 8);
+        x0[i] = src[0];
+        x1[i] = src[1];
+      }
+    }
 #pragma unroll
-    for (int dist = 1; dist < 64; dist *= 2) lw += shfl_xor_f32(lw, dist);
-    L = L * fold + lw;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] *= fold;
-    M = Mn;
-    const int n = min(64, np - p0);
-    for (int k = 0; k < n; ++k) {
-      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), k));
-      const float* src = a.acc + (rec0 + (p0 + k) * rstride) * D + lane * DPL;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = fmaf(wk, src[e], o[e]);
+    for (int i = 0; i < BATCH; ++i) {
+      if (ml[i].x != kNegInf) {  // an empty partial (or past np) adds nothing
+        const float mn = fmaxf(M, ml[i].x);
+        const float f = exp2_diff(M, mn);
+        const float wgt = fast_exp2(ml[i].x - mn);
+        L = L * f + ml[i].y * wgt;
+        o[0] = o[0] * f + x0[i].x * wgt;
+        o[1] = o[1] * f + x0[i].y * wgt;
+        o[2] = o[2] * f + x0[i].z * wgt;
+        o[3] = o[3] * f + x0[i].w * wgt;
+        o[4] = o[4] * f + x1[i].x * wgt;
+        o[5] = o[5] * f + x1[i].y * wgt;
+        o[6] = o[6] * f + x1[i].z * wgt;
+        o[7] = o[7] * f + x1[i].w * wgt;
+        M = mn;
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  float* dst = a.out + (static_cast<int64_t>(b) * a.num_q_heads + h) * D + lane * DPL;
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) dst[e] = o[e] * inv;
+  float4* dst = reinterpret_cast<float4*>(a.out + (static_cast<int64_t>(b) * a.num_q_heads + h) * D + c * 8);
+  dst[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  dst[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -722,7 +754,8 @@ hipError_t launch_decode_split(int dtype, int head_dim, int group, const SplitAr
 }
 
 hipError_t launch_merge(int head_dim, const MergeArgs& a, hipStream_t stream) {
-  const int64_t grid = static_cast<int64_t>(a.batch) * a.num_q_heads;
+  const int hpp = 64 / (head_dim / 8);  // query heads per wave
+  const int64_t grid = static_cast<int64_t>(a.batch) * ((a.num_q_heads + hpp - 1) / hpp);
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (head_dim == 128)

@@ -76,6 +76,47 @@ def test_random_forest_parity(pkv, shape, seed):
         assert np.all(got[0] == 0)
 
 
+@pytest.mark.parametrize("shape", [("bf16", 32, 8, 128), ("f16", 8, 8, 64)], ids=["bf16-gqa4-d128", "f16-mha-d64"])
+def test_stale_nonfinite_rows_never_reach_output(pkv, shape):
+    """Rows of a block past every referencing row's length hold Inf / NaN bits (as stale or
+    uninitialised pool memory can): they get zero weight and must not reach any output."""
+    dtype, hq, hkv, d = shape
+    w = workloads.random_forest(5, num_rows=12, max_len=600, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                                head_dim=d, share_prob=0.6)
+    pool, k_pages, v_pages, bt, lens, q = setup_workload(w)
+    lens = lens.copy()
+    lens[0] = 0
+    lens[2] = max(int(lens[2]) - 9, 1)
+    bs = w.block_size
+    valid = {}
+    for b in range(len(lens)):
+        n = int(lens[b])
+        for j in range(-(-n // bs)):
+            blk = int(bt[b, j])
+            valid[blk] = max(valid.get(blk, 0), min(bs, n - j * bs))
+    inf_bits, nan_bits = (0x7F80, 0x7FC0) if dtype == "bf16" else (0x7C00, 0x7E00)
+    k_host, v_host = bits_np(k_pages).copy(), bits_np(v_pages).copy()
+    poisoned = 0
+    for blk in range(k_host.shape[0]):
+        rows = valid.get(blk, 0)
+        if rows < bs:
+            k_host[blk, rows:] = nan_bits
+            v_host[blk, rows:] = np.where(np.arange(bs - rows)[:, None, None] % 2 == 0, inf_bits, nan_bits)
+            poisoned += bs - rows
+    assert poisoned > 0
+    torch = __import__("torch")
+    k_pages.copy_(torch.from_numpy(k_host.view(np.int16)).to(k_pages.device))
+    v_pages.copy_(torch.from_numpy(v_host.view(np.int16)).to(v_pages.device))
+    ref = oracle.ref_decode(bits_np(q), k_host, v_host, bt, lens, w.scale, dtype)
+    assert np.all(np.isfinite(ref))
+    for cascade in (False, True):
+        got, plan = run_decode(pkv, w, q, k_pages, v_pages, bt, lens, cascade)
+        err = max_err(got, ref)
+        say(f"stale rows {poisoned}: cascade={cascade} max_err={err:.3e}")
+        assert np.all(np.isfinite(got)) and err <= ATOL
+        assert np.all(got[0] == 0)
+
+
 def test_long_rows_many_splits(pkv):
     """Rows long enough for many split-K chunks plus a ragged last block."""
     w = workloads.random_forest(7, num_rows=6, max_len=5000, dtype="bf16", num_q_heads=32, num_kv_heads=8,
@@ -203,6 +244,24 @@ def test_identical_histories_identical_outputs(pkv):
             assert np.array_equal(got[0], got[2])
         else:
             assert max_err(got[0], got[2]) <= ATOL
+
+
+def test_rows_entirely_inside_shared_nodes(pkv):
+    """Rows whose every token lies in shared full blocks have no own blocks: their output is
+    the merge of the cascade partials alone.  Also a row ending one token into the prefix."""
+    w = workloads.get(1)
+    pool, k_pages, v_pages, bt, lens, q = setup_workload(w)
+    lens = lens.copy()
+    lens[0] = lens[1] = 256  # exactly the 16 shared prefix blocks
+    lens[2] = 255
+    ref = oracle.ref_decode(bits_np(q), bits_np(k_pages), bits_np(v_pages), bt, lens, w.scale, "f16")
+    for cascade in (False, True):
+        got, plan = run_decode(pkv, w, q, k_pages, v_pages, bt, lens, cascade)
+        if cascade:
+            assert plan.row(0)[0] == 256 and plan.row(1)[0] == 256
+        err = max_err(got, ref)
+        say(f"rows inside nodes: cascade={cascade} max_err={err:.3e}")
+        assert err <= ATOL
 
 
 def test_gqa_equals_mha_on_repeated_heads(pkv):
