@@ -62,11 +62,13 @@ __device__ __forceinline__ RowInfo load_row(const SplitArgs& a, int b) {
   int len = a.seq_lens[b];
   len = min(len, a.max_seq_len);
   len = min(len, a.max_blocks * 16);
-  int begin = 0, depth = 0;
-  if (a.row_info) {
-    begin = a.row_info[2 * b];
-    depth = a.row_info[2 * b + 1];
-  }
+  // branch-free: without a plan, read seq_lens[b] in place of the plan entry and drop it
+  const bool plan = a.row_info != nullptr;
+  const int32_t* info = plan ? a.row_info + 2 * b : a.seq_lens + b;
+  const int i0 = info[0];
+  const int i1 = info[plan ? 1 : 0];
+  const int begin = plan ? i0 : 0;
+  const int depth = plan ? i1 : 0;
   RowInfo r;
   r.nb = len > begin ? (len - begin + 15) >> 4 : 0;
   r.blk0 = begin >> 4;
@@ -112,14 +114,85 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
+// This wave's share of the work order and its first position, for batches of at
+// most 64 * KW rows.  Every row's length and plan entry are loaded at once (clamped
+// indices, no branches, so the loads are all in flight together and the wave pays
+// one round of memory latency); the sums and the search then run on registers.
+// Returns false when the wave has no work.
+template <int KW>
+__device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, int64_t& chunk, int& count,
+                                                   Cursor& cur) {
+  const int lane = __lane_id();
+  const int Hkv = a.num_kv_heads;
+  const bool plan = a.row_info != nullptr;
+  int raw_len[KW], raw_beg[KW], raw_dep[KW];
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const int b = min(k * 64 + lane, a.batch - 1);
+    const int32_t* info = plan ? a.row_info + 2 * b : a.seq_lens + b;
+    raw_len[k] = a.seq_lens[b];
+    raw_beg[k] = info[0];
+    raw_dep[k] = info[plan ? 1 : 0];
+  }
+#pragma unroll
+  for (int k = 0; k < KW; ++k) asm volatile("" ::"v"(raw_len[k]), "v"(raw_beg[k]), "v"(raw_dep[k]));
+  int nbk[KW], wsum[KW];
+  int64_t total = 0;
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const bool in = k * 64 + lane < a.batch;
+    int len = min(min(raw_len[k], a.max_seq_len), a.max_blocks * 16);
+    const int begin = plan ? raw_beg[k] : 0;
+    raw_len[k] = len;
+    raw_beg[k] = begin;
+    raw_dep[k] = plan ? raw_dep[k] : 0;
+    nbk[k] = (in && len > begin) ? (len - begin + 15) >> 4 : 0;
+    wsum[k] = wave_sum(nbk[k]);
+    total += wsum[k];
+  }
+  total *= Hkv;
+  chunk = max(static_cast<int64_t>(a.min_chunk), (total + a.num_waves - 1) / a.num_waves);
+  const int64_t start = static_cast<int64_t>(w) * chunk;
+  if (start >= total) return false;
+  count = static_cast<int>(min(chunk, total - start));
+  int64_t run = 0;
+  int kw = -1;
+#pragma unroll
+  for (int k = 0; k < KW; ++k) {
+    const int64_t wk = static_cast<int64_t>(wsum[k]) * Hkv;
+    const bool here = kw < 0 && run + wk > start;
+    kw = here ? k : kw;
+    run += (kw < 0) ? wk : 0;
+  }
+  int s_nb = nbk[0], s_len = raw_len[0], s_beg = raw_beg[0], s_dep = raw_dep[0];
+#pragma unroll
+  for (int k = 1; k < KW; ++k) {
+    s_nb = k == kw ? nbk[k] : s_nb;
+    s_len = k == kw ? raw_len[k] : s_len;
+    s_beg = k == kw ? raw_beg[k] : s_beg;
+    s_dep = k == kw ? raw_dep[k] : s_dep;
+  }
+  const int u = s_nb * Hkv;
+  const int incl = wave_inclusive_scan(u);
+  const uint64_t hit = __ballot(run + incl > start);
+  const int k = __builtin_ctzll(hit);
+  const int64_t row_start = run + __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(u, k);
+  cur.b = kw * 64 + k;
+  cur.nb = __builtin_amdgcn_readlane(s_nb, k);
+  cur.blk0 = __builtin_amdgcn_readlane(s_beg, k) >> 4;
+  cur.depth = __builtin_amdgcn_readlane(s_dep, k);
+  cur.len = __builtin_amdgcn_readlane(s_len, k);
+  const int off = static_cast<int>(start - row_start);
+  cur.h = off / cur.nb;
+  cur.j = off - cur.h * cur.nb;
+  cur.seg = row_start + static_cast<int64_t>(cur.h) * cur.nb;
+  return true;
+}
+
 }  // namespace
 
 #ifndef PKV_SPLIT_WAVES_PER_EU
 #define PKV_SPLIT_WAVES_PER_EU 1
-#endif
-// Load the next segment's q while the current segment finishes (else at the switch).
-#ifndef PKV_Q_PREFETCH
-#define PKV_Q_PREFETCH 1
 #endif
 
 template <class DT, int D, int G, int LPT>
@@ -135,22 +208,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   const int Hkv = a.num_kv_heads;
   const int w = blockIdx.x;
 
-  // ---- this wave's range of the work order
-  int64_t total = 0;
-  for (int base = 0; base < a.batch; base += 64) {
-    const int b = base + lane;
-    const int nb = b < a.batch ? load_row(a, b).nb : 0;
-    total += wave_sum(nb);
-  }
-  total *= Hkv;
-  const int64_t chunk = max(static_cast<int64_t>(a.min_chunk), (total + a.num_waves - 1) / a.num_waves);
-  const int64_t start = static_cast<int64_t>(w) * chunk;
-  if (start >= total) return;
-  const int count = static_cast<int>(min(chunk, total - start));
-
-  // ---- locate the start: first row whose cumulative work passes `start`
+  // ---- this wave's range of the work order, and its first position
+  int64_t chunk = 0;
+  int count = 0;
   Cursor cur;
-  {
+  const int nwin = (a.batch + 63) >> 6;
+  if (nwin <= 16) {
+    const bool any = nwin == 1   ? find_start_windows<1>(a, w, chunk, count, cur)
+                     : nwin <= 4 ? find_start_windows<4>(a, w, chunk, count, cur)
+                                 : find_start_windows<16>(a, w, chunk, count, cur);
+    if (!any) return;
+  } else {
+    int64_t total = 0;
+    for (int base = 0; base < a.batch; base += 64) {
+      const int b = base + lane;
+      const int nb = b < a.batch ? load_row(a, b).nb : 0;
+      total += wave_sum(nb);
+    }
+    total *= Hkv;
+    chunk = max(static_cast<int64_t>(a.min_chunk), (total + a.num_waves - 1) / a.num_waves);
+    const int64_t start = static_cast<int64_t>(w) * chunk;
+    if (start >= total) return;
+    count = static_cast<int>(min(chunk, total - start));
     int64_t run = 0;
     for (int base = 0;; base += 64) {
       const int b = base + lane;
@@ -184,8 +263,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     for (int v = 0; v < VPL; ++v)
       voff[t][v] = static_cast<uint32_t>(((r + t * ROWS) * tok_stride + (v * LPT + c) * 8) * 2);
 
+  // Block ids come from a 64-entry window of the row's table held one per lane, so
+  // the K/V loads of the next block are addressed without a memory round trip
+  // (which, younger than the loads in flight, would make the wave wait for all of
+  // them); the window is reloaded when the cursor leaves it.
+  int tw = -1, tw_b = -1, tw_0 = 0;
   auto block_id = [&](const Cursor& p) -> int {
-    return a.block_tables[static_cast<int64_t>(p.b) * a.max_blocks + p.blk0 + p.j];
+    if (p.b != tw_b || p.j < tw_0 || p.j >= tw_0 + 64) {  // uniform
+      tw_b = p.b;
+      tw_0 = p.j & ~63;
+      const int jj = tw_0 + lane;
+      tw = jj < p.nb ? a.block_tables[static_cast<int64_t>(p.b) * a.max_blocks + p.blk0 + jj] : -1;
+      // consume the window inside the reload branch: the wait for it stays on this
+      // (rare) path instead of being merged into every step
+      asm volatile("" ::"v"(tw));
+    }
+    return __builtin_amdgcn_readlane(tw, p.j - tw_0);
   };
   auto load_q = [&](const Cursor& p, u32x4(&qq)[G][VPL]) {
 #pragma unroll
@@ -423,55 +516,67 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
   };
 
-  // merge the token rows and store this segment piece's partial
+  // merge the token rows and store this segment piece's partial.  Rows are merged
+  // pairwise (distance 8 by DPP, 16 and 32 by the permlane swaps, all on the VALU);
+  // both rows of a pair compute the same combination of (lower, upper), so every
+  // row ends with the same merged state.
   auto finish_segment = [&]() {
     if constexpr (RS) {
       // the row's weight sum of head c % G: over the lanes c, c-4, c-8, c-12
       l1 += dpp_f32<kDppRowRor4>(l1);
       l1 += dpp_f32<kDppRowRor8>(l1);
-#pragma unroll
-      for (int dist = LPT; dist < 64; dist *= 2) {
-        const float mo = shfl_xor_f32(m1, dist);
-        const float lo_ = shfl_xor_f32(l1, dist);
-        const float mn = fmaxf(m1, mo);
-        const float fa = exp2_diff(m1, mn);
-        const float fb = exp2_diff(mo, mn);
-        l1 = l1 * fa + lo_ * fb;
+      auto merge_rows = [&](auto dist_tag) {
+        constexpr int DIST = decltype(dist_tag)::value;
+        float ma, mb, la, lb;
+        pair_values<DIST>(m1, ma, mb);
+        pair_values<DIST>(l1, la, lb);
+        const float mn = fmaxf(ma, mb);
+        const float fa = exp2_diff(ma, mn);
+        const float fb = exp2_diff(mb, mn);
+        l1 = la * fa + lb * fb;
         m1 = mn;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float fag = row_bcast_f32(fa, g), fbg = row_bcast_f32(fb, g);
 #pragma unroll
           for (int e = 0; e < VPL * 8; ++e) {
-            const float ao = shfl_xor_f32(acc[g][e], dist);
-            acc[g][e] = acc[g][e] * fag + ao * fbg;
+            float xa, xb;
+            pair_values<DIST>(acc[g][e], xa, xb);
+            acc[g][e] = xa * fag + xb * fbg;
           }
         }
-      }
+      };
+      merge_rows(std::integral_constant<int, 16>());
+      merge_rows(std::integral_constant<int, 32>());
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         m[g] = row_bcast_f32(m1, g);
         l[g] = row_bcast_f32(l1, g);
       }
     } else {
+      auto merge_rows = [&](auto dist_tag) {
+        constexpr int DIST = decltype(dist_tag)::value;
 #pragma unroll
-    for (int dist = LPT; dist < 64; dist *= 2) {
+        for (int g = 0; g < G; ++g) {
+          float ma, mb, la, lb;
+          pair_values<DIST>(m[g], ma, mb);
+          pair_values<DIST>(l[g], la, lb);
+          const float mn = fmaxf(ma, mb);
+          const float fa = exp2_diff(ma, mn);
+          const float fb = exp2_diff(mb, mn);
+          l[g] = la * fa + lb * fb;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float mo = shfl_xor_f32(m[g], dist);
-        const float lo_ = shfl_xor_f32(l[g], dist);
-        const float mn = fmaxf(m[g], mo);
-        const float fa = exp2_diff(m[g], mn);
-        const float fb = exp2_diff(mo, mn);
-        l[g] = l[g] * fa + lo_ * fb;
-#pragma unroll
-        for (int e = 0; e < VPL * 8; ++e) {
-          const float ao = shfl_xor_f32(acc[g][e], dist);
-          acc[g][e] = acc[g][e] * fa + ao * fb;
+          for (int e = 0; e < VPL * 8; ++e) {
+            float xa, xb;
+            pair_values<DIST>(acc[g][e], xa, xb);
+            acc[g][e] = xa * fa + xb * fb;
+          }
+          m[g] = mn;
         }
-        m[g] = mn;
-      }
-    }
+      };
+      if constexpr (LPT <= 8) merge_rows(std::integral_constant<int, 8>());
+      merge_rows(std::integral_constant<int, 16>());
+      merge_rows(std::integral_constant<int, 32>());
     }
     const int64_t first_wave = cur.seg / chunk;
     const int k = static_cast<int>(w - first_wave);
@@ -496,39 +601,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
   };
 
-  // one step: prefetch block i+1 (when `more`), consume block i, move on
+  // One step: load block i+1 and the q of its segment, consume block i, move on.
+  // Every load is issued on every path (after the last block, block i is read
+  // again: an L2 hit), so the compiler's wait counts never have to assume the
+  // worst of two paths, which would make the wave wait for loads it does not need.
   u32x4 ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL];
   bool ok_a = load_block(pre, ka, va), ok_b = false;
-  bool q_pending = false;
   auto step = [&](int i, bool ok_cur, const u32x4(&kc)[TPB][VPL], u32x4(&vc)[TPB][VPL],
                   u32x4(&kn)[TPB][VPL], u32x4(&vn)[TPB][VPL], bool& ok_next) {
     const bool more = i + 1 < count;
-    if (more) {
-      const int old_seg_h = pre.h, old_b = pre.b;
-      advance(pre, a);
-      if (PKV_Q_PREFETCH && (pre.h != old_seg_h || pre.b != old_b)) {
-        load_q(pre, qn);
-        q_pending = true;
-      }
-    }
-    // unconditional (after the last block it re-reads that block, an L2 hit) so
-    // the wait counts stay the same on every path
+    if (more) advance(pre, a);
+    load_q(pre, qn);
     ok_next = load_block(pre, kn, vn);
     consume_block(ok_cur, kc, vc);
     if (!more || cur.j + 1 == cur.nb) {
       finish_segment();
       if (more) {
-        advance(cur, a);
+        advance(cur, a);  // now at pre's block, whose segment's q is in qn
         reset_state();
-        if (!PKV_Q_PREFETCH) {
-          load_q(cur, qv);
-        } else if (q_pending) {
 #pragma unroll
-          for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int v = 0; v < VPL; ++v) qv[g][v] = qn[g][v];
-          q_pending = false;
-        }
+          for (int v = 0; v < VPL; ++v) qv[g][v] = qn[g][v];
       }
     } else {
       ++cur.j;

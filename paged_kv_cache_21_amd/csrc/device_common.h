@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pkv {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -100,6 +102,26 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 8) x += dpp_f32<kDppRowHalfMirror>(x);
   if constexpr (N >= 16) x += dpp_f32<kDppRowMirror>(x);
   return x;
+}
+
+// The values of lane l and lane l ^ DIST (DIST = 8, 16 or 32) as (lower lane's,
+// upper lane's), in both lanes, without LDS: DPP for 8 (within a 16-lane row),
+// v_permlane16_swap / v_permlane32_swap for 16 / 32.
+template <int DIST>
+__device__ __forceinline__ void pair_values(float x, float& lo, float& hi) {
+  static_assert(DIST == 8 || DIST == 16 || DIST == 32, "pair distance");
+  if constexpr (DIST == 8) {
+    const float other = dpp_f32<kDppRowRor8>(x);
+    const bool upper = __lane_id() & 8;
+    lo = upper ? other : x;
+    hi = upper ? x : other;
+  } else {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = DIST == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                              : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __builtin_bit_cast(float, static_cast<uint32_t>(r[0]));
+    hi = __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+  }
 }
 
 __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {

@@ -117,6 +117,21 @@ def test_stale_nonfinite_rows_never_reach_output(pkv, shape):
         assert np.all(got[0] == 0)
 
 
+@pytest.mark.parametrize("rows", [65, 1100])
+def test_batch_sizes_across_row_windows(pkv, rows):
+    """Batches spanning several 64-row windows, and one above the size whose row lengths the
+    split kernel keeps in registers while it finds its start (the looped search)."""
+    w = workloads.random_forest(11, num_rows=rows, max_len=70, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                                head_dim=64, share_prob=0.3)
+    pool, k_pages, v_pages, bt, lens, q = setup_workload(w)
+    ref = oracle.ref_decode(bits_np(q), bits_np(k_pages), bits_np(v_pages), bt, lens, w.scale, "bf16")
+    for cascade in (False, True):
+        got, _ = run_decode(pkv, w, q, k_pages, v_pages, bt, lens, cascade)
+        err = max_err(got, ref)
+        say(f"batch {rows}: cascade={cascade} max_err={err:.3e}")
+        assert err <= ATOL
+
+
 def test_long_rows_many_splits(pkv):
     """Rows long enough for many split-K chunks plus a ragged last block."""
     w = workloads.random_forest(7, num_rows=6, max_len=5000, dtype="bf16", num_q_heads=32, num_kv_heads=8,
