@@ -13,7 +13,9 @@ Everything here is written from the source pages:
 * "Dismantling the Memory Wall" (blog.bako.co), section "PagedAttention: The
   Virtual Memory Analogy for GPUs" for the 16-token block and the
   token -> logical-block arithmetic; section "Copy-on-Write and Advanced
-  Decoding Strategies" for sharing prompt blocks and allocating on divergence.
+  Decoding Strategies" for sharing prompt blocks and allocating on divergence;
+  section "Chunked Prefill" (with the verification pass of "RKSC", §1) for
+  several new tokens attending causally at once.
 
 Floating point is fp64.  fp16/bf16 inputs arrive as raw 16-bit patterns and
 are decoded here, independently of the GPU code.
@@ -25,6 +27,7 @@ invariants; none of them is "parity unpinned".
 
 from .kvsize import kv_bytes, kv_bytes_per_token
 from .attention import decode_bits, ref_decode, ref_decode_rows, bruteforce_decode
+from .extend import extend_query_positions, ref_extend
 from .pool import RefPool, RefPoolError, apply_append
 
 __all__ = [
@@ -34,6 +37,8 @@ __all__ = [
     "ref_decode",
     "ref_decode_rows",
     "bruteforce_decode",
+    "extend_query_positions",
+    "ref_extend",
     "RefPool",
     "RefPoolError",
     "apply_append",

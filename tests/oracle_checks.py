@@ -381,3 +381,52 @@ def run_pool_pins(RefPool, apply_append):
     check_slot_arithmetic(RefPool)
     check_pool_against_unpaged_model(RefPool, apply_append)
     check_identical_histories_identical_bytes(RefPool, apply_append)
+
+
+# ---------------------------------------------------------------------------
+# multi-token (extend) attention
+
+
+def _extend_case(rng, dtype, lens, q_lens, Hq=4, Hkv=2, d=4, block_size=4):
+    q_rows = int(sum(q_lens))
+    _, k, v, bt, sl = random_paged_case(rng, len(lens), Hq, Hkv, d, block_size, lens, dtype)
+    q = to_bits(rng.standard_normal((q_rows, Hq, d)), dtype)
+    return q, k, v, bt, sl, np.asarray(q_lens, dtype=np.int32)
+
+
+def run_extend_pins(ref_extend, ref_decode, bruteforce_decode):
+    """Pins for the extend oracle: every query token equals an independent token-by-token
+    decode of its row truncated at its own position; one query token per row is plain
+    decode; tokens after a query's position never change its output."""
+    rng = np.random.default_rng(1234)
+    for dtype in ("bf16", "f16"):
+        lens, q_lens = [9, 13, 6, 5], [3, 5, 6, 0]  # a row whose every token is a query; a row with none
+        q, k, v, bt, sl, ql = _extend_case(rng, dtype, lens, q_lens)
+        scale = 0.61
+        got = ref_extend(q, k, v, bt, sl, ql, scale, dtype)
+        assert got.shape == (sum(q_lens), 4, 4)
+        r = 0
+        for b, (n, m) in enumerate(zip(lens, q_lens)):
+            for i in range(m):
+                pos = n - m + i
+                one = bruteforce_decode(q[r:r + 1], k, v, bt[b:b + 1], np.asarray([pos + 1]), scale, dtype)
+                assert np.max(np.abs(np.asarray(one[0]) - got[r])) < 1e-12, (dtype, b, i)
+                r += 1
+        # one query token per row: the decode definition
+        q1 = to_bits(rng.standard_normal((len(lens), 4, 4)), dtype)
+        ones = np.ones(len(lens), dtype=np.int32)
+        assert np.max(np.abs(ref_extend(q1, k, v, bt, sl, ones, scale, dtype) -
+                             ref_decode(q1, k, v, bt, sl, scale, dtype))) < 1e-13
+    # causality: rewrite the tokens after row 1's first query position
+    q, k, v, bt, sl, ql = _extend_case(rng, "bf16", [11, 14], [2, 6])
+    base = ref_extend(q, k, v, bt, sl, ql, 0.5, "bf16")
+    first = 2  # packed index of row 1's first query token
+    pos = 14 - 6
+    k2, v2 = k.copy(), v.copy()
+    for t in range(pos + 1, 14):
+        blk, row = int(bt[1, t // 4]), t % 4
+        k2[blk, row] = to_bits(rng.standard_normal(k.shape[2:]) * 3, "bf16")
+        v2[blk, row] = to_bits(rng.standard_normal(v.shape[2:]) * 3, "bf16")
+    moved = ref_extend(q, k2, v2, bt, sl, ql, 0.5, "bf16")
+    assert np.array_equal(moved[: first + 1], base[: first + 1])
+    assert np.max(np.abs(moved[first + 1:] - base[first + 1:])) > 1e-3
