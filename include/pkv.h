@@ -244,16 +244,69 @@ pkv_status pkv_plan_node(const pkv_plan* plan, int32_t node, int32_t* num_blocks
 /* Token pieces node i is cut into (each piece is a separate work item and a
  * separate partial per member row and query head); -1 for a bad index. */
 int32_t pkv_plan_node_pieces(const pkv_plan* plan, int32_t node);
-/* For row b: tokens covered by its nodes (its remainder starts there) and the
- * number of partial slots its nodes use (the sum of their pieces). */
+/* For query row r (a sequence for a decode plan, a query token for an extend
+ * plan): tokens covered by its shared nodes (a decode row's remainder starts
+ * there) and the number of partial slots its nodes use. */
 pkv_status pkv_plan_row(const pkv_plan* plan, int32_t row, int32_t* shared_tokens, int32_t* depth);
+
+/* ------------------------------------------------------------------------------------------
+ * Device operation 3: multi-token (extend) attention over a paged KV cache.
+ *
+ * Several new tokens per sequence, each attending causally to its sequence's
+ * cache: the verification pass of "RKSC" (gist.science summary, §1: a generated
+ * branch is scored with one forward pass over its tokens, while branches share
+ * their prefix) and "Dismantling the Memory Wall", "Chunked Prefill" (a prompt
+ * is processed in token slices, each slice attending to what is cached before
+ * it).  Row b's q_lens[b] new tokens are the last q_lens[b] of its seq_lens[b]
+ * cached tokens (they were appended first); query token i of row b, at position
+ * p = seq_lens[b] - q_lens[b] + i, gets
+ *
+ *   out[r][h][:] = sum_{t <= p} softmax_t(scale * <q[r][h], K_b[t][h / group]>) V_b[t][h / group]
+ *
+ * with r = q_lens[0] + ... + q_lens[b-1] + i (query rows packed in row order).
+ * All of it runs on the matrix cores: blocks that several rows share are read
+ * once for all of their query tokens (as in the decode cascade), and each row's
+ * remaining blocks once for all of its own query tokens.
+ *
+ * The plan (pkv_plan_build_extend, then pkv_plan_upload) carries the block ids,
+ * so the call takes no tables:
+ *   q            device, [num_query_rows][num_q_heads][head_dim], dtype
+ *   k_pages/v_pages  device, [num_blocks][block_size][num_kv_heads][head_dim], dtype
+ *   workspace    device scratch of at least pkv_extend_workspace_bytes(plan, head_dim)
+ *                bytes; contents on entry are ignored
+ *   out          device, float32 [num_query_rows][num_q_heads][head_dim]
+ * Supported: block_size 16; head_dim 64 or 128; group in {1, 2, 4, 8}.
+ * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ * ---------------------------------------------------------------------------------------- */
+pkv_status pkv_paged_extend_attn(const void* q, int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
+                                 int64_t num_blocks, int32_t block_size, float scale, const pkv_plan* plan,
+                                 void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/* Plan for pkv_paged_extend_attn from host copies of the block tables
+ * ([batch][max_blocks_per_seq]), lengths and query-token counts (0 <= q_lens[b]
+ * <= seq_lens[b]; rows with q_lens[b] == 0 take no part).  Shared nodes are
+ * found as in pkv_plan_build among the rows with query tokens.  Returns NULL on
+ * invalid arguments (see pkv_last_error). */
+pkv_plan* pkv_plan_build_extend(const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_lens,
+                                int32_t batch, int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t min_members);
+
+/* Bytes of device workspace pkv_paged_extend_attn needs with this plan (0 and
+ * an error for a decode plan). */
+size_t pkv_extend_workspace_bytes(const pkv_plan* plan, int32_t head_dim);
+
+/* Query rows of a plan: the batch for a decode plan, the summed q_lens for an
+ * extend plan; -1 for NULL. */
+int32_t pkv_plan_num_query_rows(const pkv_plan* plan);
 
 /* ------------------------------------------------------------------------------------------
  * Kernel timing (for measurement).  When enabled, every kernel launch of the
  * library is bracketed with HIP events on its own stream; pkv_timing_read()
  * synchronizes those events and returns the summed duration and count per
  * kernel since the last reset.  Kernel ids: 0 append, 1 split-K decode,
- * 2 partial merge, 3 cascade.  Costs two event records per launch when on.
+ * 2 partial merge, 3 cascade / extend matrix-core pass.  Costs two event
+ * records per launch when on.
  * ---------------------------------------------------------------------------------------- */
 enum { PKV_KERNEL_APPEND = 0, PKV_KERNEL_DECODE_SPLIT = 1, PKV_KERNEL_MERGE = 2, PKV_KERNEL_CASCADE = 3,
        PKV_NUM_KERNELS = 4 };

@@ -23,6 +23,7 @@ import torch  # noqa: F401
 __all__ = [
     "PkvError", "PkvInvalid", "PkvOOM", "PkvNotFound", "PkvUnsupported", "PkvWorkspaceError", "PkvHipError",
     "kv_append", "paged_decode_attn", "decode_workspace_bytes", "BlockPool", "CascadePlan",
+    "ExtendPlan", "paged_extend_attn", "extend_workspace_bytes",
     "timing_enable", "timing_reset", "timing_read", "KERNELS", "lib", "LIB_PATH", "version",
 ]
 
@@ -98,6 +99,11 @@ _SIGNATURES = {
     "pkv_plan_node": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp]),
     "pkv_plan_row": (_i32, [_vp, _i32, _vp, _vp]),
     "pkv_plan_node_pieces": (_i32, [_vp, _i32]),
+    "pkv_plan_build_extend": (_vp, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pkv_extend_workspace_bytes": (_sz, [_vp, _i32]),
+    "pkv_plan_num_query_rows": (_i32, [_vp]),
+    "pkv_paged_extend_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _f32, _vp, _vp, _sz,
+                                     _vp, _vp]),
     "pkv_timing_enable": (_i32, [_i32]),
     "pkv_timing_reset": (_i32, []),
     "pkv_timing_read": (_i32, [_i32, _vp, _vp]),
@@ -399,6 +405,65 @@ class CascadePlan:
         dp = np.zeros(1, dtype=np.int32)
         _check(_lib.pkv_plan_row(self._handle, int(b), _ptr(st), _ptr(dp)))
         return int(st[0]), int(dp[0])
+
+
+class ExtendPlan(CascadePlan):
+    """Plan for multi-token (extend) attention: block tables, lengths and the number of new query
+    tokens per row (numpy int32); query rows are packed in row order."""
+
+    def __init__(self, block_tables, seq_lens, q_lens, num_q_heads, num_kv_heads, block_size=16, min_members=2):
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        ql = np.ascontiguousarray(q_lens, dtype=np.int32)
+        _require(bt.ndim == 2 and sl.shape == (bt.shape[0],) and ql.shape == sl.shape,
+                 "block_tables [B, max_blocks], seq_lens [B], q_lens [B]")
+        h = _lib.pkv_plan_build_extend(_ptr(bt), _ptr(sl), _ptr(ql), bt.shape[0], bt.shape[1], int(block_size),
+                                       int(num_q_heads), int(num_kv_heads), int(min_members))
+        if not h:
+            raise PkvInvalid(PKV_ERR_INVALID, _lib.pkv_last_error().decode())
+        self._handle = h
+        self.batch = bt.shape[0]
+        self.device_buffer = None
+
+    @property
+    def num_query_rows(self):
+        return int(_lib.pkv_plan_num_query_rows(self._handle))
+
+
+def extend_workspace_bytes(plan, head_dim):
+    n = _lib.pkv_extend_workspace_bytes(plan._handle, int(head_dim))
+    if n == 0:
+        raise PkvInvalid(PKV_ERR_INVALID, _lib.pkv_last_error().decode())
+    return int(n)
+
+
+def paged_extend_attn(q, k_pages, v_pages, plan, scale=None, workspace=None, out=None, dtype=None, stream=None):
+    """Causal multi-token attention: query row r (token i of row b, at position
+    seq_lens[b] - q_lens[b] + i) attends to its row's tokens [0, position] (fp32 output).
+
+    q: [num_query_rows, Hq, d] device tensor; pages [num_blocks, 16, Hkv, d]; ``plan``: an uploaded ExtendPlan.
+    """
+    import torch
+
+    _require(isinstance(plan, ExtendPlan) and plan.device_buffer is not None, "plan must be an uploaded ExtendPlan")
+    _require(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "bad q / page ranks")
+    _require(q.is_contiguous() and k_pages.is_contiguous() and v_pages.is_contiguous(), "inputs must be contiguous")
+    nq, hq, d = q.shape
+    nblk, bs, hkv, dk = k_pages.shape
+    _require(dk == d, "head_dim of q and pages differ")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    need = extend_workspace_bytes(plan, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty((nq, hq, d), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (nq, hq, d), "bad out tensor")
+    _check(_lib.pkv_paged_extend_attn(_ptr(q), nq, hq, hkv, d, _dtype_code(q, dtype), _ptr(k_pages), _ptr(v_pages),
+                                      nblk, bs, float(scale), plan._handle, _ptr(workspace), ws_bytes, _ptr(out),
+                                      _stream(stream, q)))
+    return out
 
 
 # ---------------------------------------------------------------------------

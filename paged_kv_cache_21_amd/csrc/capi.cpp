@@ -172,8 +172,8 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
     fail(PKV_ERR_INVALID, "pkv_decode_workspace_bytes: invalid sizes");
     return 0;
   }
-  if (plan && plan->batch != batch) {
-    fail(PKV_ERR_INVALID, "pkv_decode_workspace_bytes: plan built for batch %d, not %d", plan->batch, batch);
+  if (plan && (plan->kind != pkv_plan::kDecode || plan->batch != batch)) {
+    fail(PKV_ERR_INVALID, "pkv_decode_workspace_bytes: plan not a decode plan for batch %d", batch);
     return 0;
   }
   return pkv::decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan).bytes;
@@ -201,6 +201,8 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
     return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn: GQA group %d (built: 1, 2, 4, 8)", group);
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: scale is not finite");
   if (plan) {
+    if (plan->kind != pkv_plan::kDecode)
+      return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: plan was built by pkv_plan_build_extend");
     if (plan->batch != batch || plan->group != group || plan->num_kv_heads != num_kv_heads ||
         plan->block_size != block_size || plan->max_blocks != max_blocks_per_seq)
       return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: plan was built for different shapes");
@@ -272,6 +274,80 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
   }
   pkv::MergeArgs ma{seq_lens, row_info, counts, acc, ml, out, batch, num_q_heads, num_kv_heads, max_blocks_per_seq,
                     max_seq_len, L.slots};
+  return pkv::launch(PKV_KERNEL_MERGE, "merge", s, [&] { return pkv::launch_merge(head_dim, ma, s); });
+}
+
+size_t pkv_extend_workspace_bytes(const pkv_plan* plan, int32_t head_dim) {
+  pkv::clear_error();
+  if (!plan || plan->kind != pkv_plan::kExtend || head_dim <= 0) {
+    fail(PKV_ERR_INVALID, "pkv_extend_workspace_bytes: needs an extend plan and head_dim > 0");
+    return 0;
+  }
+  const size_t recs = static_cast<size_t>(plan->num_query_rows) * std::max(plan->max_depth, 1) * plan->num_q_heads;
+  const size_t ml_offset = (recs * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255);
+  return ml_offset + recs * sizeof(float2);
+}
+
+pkv_status pkv_paged_extend_attn(const void* q, int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
+                                 int64_t num_blocks, int32_t block_size, float scale, const pkv_plan* plan,
+                                 void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  pkv::clear_error();
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_extend_attn: dtype %d", dtype);
+  if (!plan || plan->kind != pkv_plan::kExtend)
+    return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: needs a plan from pkv_plan_build_extend");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || num_blocks < 0)
+    return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: invalid head counts or pool size");
+  if (plan->num_query_rows != num_query_rows || plan->num_q_heads != num_q_heads ||
+      plan->num_kv_heads != num_kv_heads || plan->block_size != block_size)
+    return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: plan was built for different shapes");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_extend_attn: head_dim %d (built: 64, 128)", head_dim);
+  if (block_size != 16) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_extend_attn: block_size %d (built: 16)", block_size);
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (!pkv::supported_group(group))
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_extend_attn: GQA group %d (built: 1, 2, 4, 8)", group);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: scale is not finite");
+  if (!plan->device) return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: plan not uploaded (pkv_plan_upload)");
+  if (num_query_rows == 0) return PKV_OK;
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: the pool must hold at least one block");
+  if (!q || !k_pages || !v_pages || !out) return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: null pointer");
+  if (!pkv::aligned16(q) || !pkv::aligned16(k_pages) || !pkv::aligned16(v_pages) || !pkv::aligned16(out))
+    return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: q, pages and out must be 16-byte aligned");
+  const size_t need = pkv_extend_workspace_bytes(plan, head_dim);
+  if (workspace_bytes < need || !workspace)
+    return fail(PKV_ERR_WORKSPACE, "pkv_paged_extend_attn: workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (!pkv::aligned16(workspace)) return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: workspace must be 16-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t slots = std::max(plan->max_depth, 1);
+  const size_t recs = static_cast<size_t>(num_query_rows) * slots * num_q_heads;
+  float* acc = static_cast<float*>(workspace);
+  float2* ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
+                                         ((recs * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255)));
+  const float scale_log2 = scale * 1.4426950408889634f;
+  if (plan->num_items() > 0) {
+    pkv::CascadeArgs c{static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k_pages),
+                       static_cast<const uint16_t*>(v_pages),
+                       plan->device + plan->off_items,
+                       plan->device + plan->off_nodes,
+                       plan->device + plan->off_blocks,
+                       plan->device + plan->off_members,
+                       acc,
+                       ml,
+                       num_blocks,
+                       plan->num_items(),
+                       num_q_heads,
+                       num_kv_heads,
+                       slots,
+                       scale_log2};
+    pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
+                                [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
+    if (st != PKV_OK) return st;
+  }
+  pkv::MergeArgs ma{nullptr, plan->device + plan->off_row_info, nullptr, acc, ml, out, num_query_rows, num_q_heads,
+                    num_kv_heads, 0, 0, slots};
   return pkv::launch(PKV_KERNEL_MERGE, "merge", s, [&] { return pkv::launch_merge(head_dim, ma, s); });
 }
 

@@ -18,9 +18,20 @@
 // P is fed to the matrix core as two 16-bit terms, p = p_hi + p_lo, so the
 // product keeps ~16 bits of the fp32 weights rather than 8.
 //
-// Each (row, query head) gets one partial (m, l, acc) per shared node, in the
-// same log2-scaled form as the split-K partials, and the merge kernel combines
-// them with the row's own remainder.
+// Each (query row, query head) gets one partial (m, l, acc) per node piece, in
+// the same log2-scaled form as the split-K partials, and the merge kernel
+// combines them with the row's own remainder.
+//
+// The same kernel runs the multi-token (extend) pass: a query row is then one
+// new token of a sequence, which may attend only to the tokens up to its own
+// position (causal; "Dismantling the Memory Wall", "Chunked Prefill": a prompt
+// is processed in slices, each slice's tokens attending to everything cached
+// before them; the verification pass of "RKSC", §1: a generated branch is
+// scored by one forward pass over its tokens).  Every member entry carries the
+// last token position it may attend to; scores past it are masked, and the
+// values of tokens past a node's valid length are zeroed.
+#include <climits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -81,12 +92,15 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
   const int hkv = a.items[4 * item + 1];
   const int row0 = a.items[4 * item + 2];
   const int piece = a.items[4 * item + 3];
-  const int blk_off = a.nodes[6 * node + 0];
-  const int node_blocks = a.nodes[6 * node + 1];
-  const int mem_off = a.nodes[6 * node + 2];
-  const int nmem = a.nodes[6 * node + 3];
-  const int piece_blocks = a.nodes[6 * node + 5];
+  const int32_t* nrec = a.nodes + kNodeInts * node;
+  const int blk_off = nrec[0];
+  const int node_blocks = nrec[1];
+  const int mem_off = nrec[2];
+  const int nmem = nrec[3];
+  const int piece_blocks = nrec[5];
   const int pb0 = piece * piece_blocks;
+  const int piece_tok0 = nrec[6] + pb0 * 16;  // logical position of the piece's first token
+  const int piece_valid = nrec[7] - pb0 * 16;  // tokens of the piece holding data (may exceed the piece)
   const int nblk = min(piece_blocks, node_blocks - pb0);
   const int R = nmem * G;
   const int Hkv = a.num_kv_heads;
@@ -103,10 +117,13 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
   // queries of this lane's row, as B operands
   u32x4 qb[NKS];
   int my_b = -1, my_slot = 0, my_h = 0;
+  int my_limit = -1;  // last attended position, piece-local (rows past R attend to nothing)
   if (my_row < R) {
-    const int member = my_row / G;
-    my_b = a.node_members[2 * (mem_off + member)];
-    my_slot = a.node_members[2 * (mem_off + member) + 1] + piece;
+    const int32_t* mrec = a.node_members + kMemberInts * (mem_off + my_row / G);
+    my_b = mrec[0];
+    my_slot = mrec[1] + piece;
+    const int limit = mrec[2];
+    my_limit = limit == INT_MAX ? INT_MAX : limit - piece_tok0;
     my_h = hkv * G + my_row % G;
     const uint16_t* qp = a.q + (static_cast<int64_t>(my_b) * a.num_q_heads + my_h) * D + lgrp * 8;
     // a negative scale is applied as |scale| on -q (flipping sign bits is exact), so the
@@ -118,6 +135,16 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
   }
+
+  // the earliest last-attended position over the wave's rows (rows past R count as
+  // unlimited: their results are never stored); chunks entirely at or before it
+  // need no causal mask
+  int wave_min_limit = my_row < R ? my_limit : INT_MAX;
+  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 1));
+  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 2));
+  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 4));
+  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 8));
+  wave_min_limit = __builtin_amdgcn_readfirstlane(wave_min_limit);
 
   float m = kNegInf, lsum = 0.f;
   f32x4 o[NDT];
@@ -175,8 +202,17 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
       st.v1 = ld16(vp + tok_stride);
     }
   };
-  // registers -> LDS buffer: K as is, V transposed to [d][token] pairs
-  auto store_chunk = [&](const Stage& st, int buf) {
+  // registers -> LDS buffer: K as is, V transposed to [d][token] pairs; the values
+  // of tokens without data (past the node's valid length, or in a block with a bad
+  // id) are zeroed, so their zero weights never meet stale Inf / NaN bits
+  auto store_chunk = [&](const Stage& st_in, int ch, int buf) {
+    Stage st = st_in;
+    if (vthread && (ch * 32 + 32 > piece_valid || block_id(2 * ch) < 0 || block_id(2 * ch + 1) < 0)) {  // uniform
+      const int t = ch * 32 + 2 * vpair;
+      const bool blk_ok = block_id(2 * ch + (vhi ? 1 : 0)) >= 0;
+      if (!(blk_ok && t < piece_valid)) st.v0 = u32x4{0, 0, 0, 0};
+      if (!(blk_ok && t + 1 < piece_valid)) st.v1 = u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int i = 0; i < KVEC_PER_THREAD; ++i) {
       const int vi = tid + 256 * i;
@@ -220,11 +256,14 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
       sv[j] = st[0][j];
       sv[4 + j] = st[1][j];
     }
-    if (!(valid0 && valid1)) {  // uniform: only at a piece's odd end or for bad ids
+    // uniform: a piece's odd end, bad ids, the node's partly filled end, or a
+    // chunk past some row's last attended position
+    if (!(valid0 && valid1) || ch * 32 + 31 > wave_min_limit || ch * 32 + 32 > piece_valid) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sv[j] = valid0 ? sv[j] : kNegInf;
-        sv[4 + j] = valid1 ? sv[4 + j] : kNegInf;
+      for (int j = 0; j < 8; ++j) {
+        const int t = ch * 32 + 16 * (j / 4) + 4 * lgrp + (j % 4);  // piece-local token of score j
+        const bool ok = (j < 4 ? valid0 : valid1) && t <= my_limit && t < piece_valid;
+        sv[j] = ok ? sv[j] : kNegInf;
       }
     }
     float cmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
@@ -246,7 +285,7 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
     const float mref = fmaxf(m, -3.0e38f);  // m = -inf only while every score is -inf
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = fast_exp2(fmaf(sv[j], c, -mref));
+      const float p = sv[j] == kNegInf ? 0.f : fast_exp2(fmaf(sv[j], c, -mref));
       lsum += p;
       ph[j] = DT::from_float(p);
       pl[j] = DT::from_float(p - DT::to_float(ph[j]));
@@ -272,17 +311,17 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
     Stage s0, s1;
     load_chunk(0, s0);
     load_chunk(1, s1);
-    store_chunk(s0, 0);
+    store_chunk(s0, 0, 0);
     load_chunk(2, s0);
     __syncthreads();
     for (int ch = 0; ch < nchunks; ch += 2) {
       compute_chunk(ch, 0);
-      store_chunk(s1, 1);  // chunk ch+1
+      store_chunk(s1, ch + 1, 1);
       load_chunk(ch + 3, s1);
       __syncthreads();
       if (ch + 1 >= nchunks) break;
       compute_chunk(ch + 1, 1);
-      store_chunk(s0, 0);  // chunk ch+2
+      store_chunk(s0, ch + 2, 0);
       load_chunk(ch + 4, s0);
       __syncthreads();
     }

@@ -655,17 +655,20 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   const int h = (blockIdx.x % groups) * HPP + lane / LPH;
   const int c = lane % LPH;
   if (h >= a.num_q_heads) return;
-  int len = a.seq_lens[b];
   int begin = 0, depth = 0;
   if (a.row_info) {
     begin = a.row_info[2 * b];
     depth = a.row_info[2 * b + 1];
   }
-  const int hkv = h / (a.num_q_heads / a.num_kv_heads);
-  const int counted = a.counts[static_cast<int64_t>(b) * a.num_kv_heads + hkv];  // valid when the row has own tokens
-  len = min(len, a.max_seq_len);
-  len = min(len, a.max_blocks * 16);
-  const int nsplit = len > begin ? counted : 0;
+  int nsplit = 0;  // no split pieces without lengths (the extend pass)
+  if (a.seq_lens) {
+    int len = a.seq_lens[b];
+    const int hkv = h / (a.num_q_heads / a.num_kv_heads);
+    const int counted = a.counts[static_cast<int64_t>(b) * a.num_kv_heads + hkv];  // valid when the row has own tokens
+    len = min(len, a.max_seq_len);
+    len = min(len, a.max_blocks * 16);
+    nsplit = len > begin ? counted : 0;
+  }
   const int np = min(depth + nsplit, a.slots);
   const int64_t rec0 = static_cast<int64_t>(b) * a.slots * a.num_q_heads + h;
 

@@ -55,10 +55,12 @@ struct SplitArgs {
   float scale_log2;
 };
 
-// Merge of all partials of a row into the normalised output.
+// Merge of all partials of a query row into the normalised output.  Decode:
+// rows are sequences, counts holds each (row, KV head)'s split pieces.  Extend:
+// rows are query tokens, seq_lens and counts are null (node partials only).
 struct MergeArgs {
   const int32_t* seq_lens;
-  const int32_t* row_info;
+  const int32_t* row_info;  // per row: (tokens covered by nodes, node partial slots)
   const int32_t* counts;
   const float* acc;
   const float2* ml;
@@ -77,10 +79,11 @@ struct CascadeArgs {
   const uint16_t* k_pages;
   const uint16_t* v_pages;
   const int32_t* items;         // [num_items][4] = (node, kv head, first tile row, piece); node < 0: idle
-  const int32_t* nodes;         // [num_nodes][6] = (block offset, blocks, member offset, members, pieces,
-                                //                   blocks per piece)
+  const int32_t* nodes;         // [num_nodes][kNodeInts] = (block offset, blocks, member offset, members,
+                                //   pieces, blocks per piece, first token position, tokens holding data)
   const int32_t* node_blocks;   // physical block ids
-  const int32_t* node_members;  // [..][2] = (row, partial slot of piece 0; piece p uses slot + p)
+  const int32_t* node_members;  // [..][kMemberInts] = (query row, partial slot of piece 0 (piece p uses
+                                //   slot + p), last token position it attends to, INT_MAX: all)
   float* acc;
   float2* ml;
   int64_t num_blocks;
@@ -92,6 +95,8 @@ struct CascadeArgs {
 };
 
 constexpr int kCascadeRowsPerItem = 64;  // 4 waves x 16 rows
+constexpr int kNodeInts = 8;             // ints per node record of a plan image
+constexpr int kMemberInts = 3;           // ints per member entry of a plan image
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // dtype: 0 f16, 1 bf16.  Returns hipErrorInvalidValue for shapes not built.

@@ -1,4 +1,4 @@
-// Host representation of a cascade plan and its device image.
+// Host representation of a cascade / extend plan and its device image.
 #pragma once
 
 #include <cstddef>
@@ -6,23 +6,33 @@
 #include <vector>
 
 struct pkv_plan {
+  enum Kind { kDecode = 0, kExtend = 1 };
+  Kind kind = kDecode;
   int32_t batch = 0;
   int32_t max_blocks = 0;
   int32_t block_size = 0;
   int32_t num_q_heads = 0;
   int32_t num_kv_heads = 0;
   int32_t group = 0;
+  // Query rows: decode, one per sequence (row b); extend, one per new token, in
+  // (sequence, token) order.
+  int32_t num_query_rows = 0;
 
   struct Node {
     int32_t block_off, num_blocks, member_off, num_members;
     int32_t pieces = 1, piece_blocks = 0;  // token split of the node across work-groups
+    int32_t start_tok = 0;                 // logical index of the node's first token in its rows
+    int32_t valid_tokens = 0;              // tokens of the node holding data (the rest are masked, values zeroed)
   };
+  static constexpr int kNodeInts = 8;
+  static constexpr int kMemberInts = 3;
   std::vector<Node> nodes;
   std::vector<int32_t> node_blocks;   // physical ids, concatenated per node
-  std::vector<int32_t> node_members;  // (row, partial slot) pairs, concatenated per node
-  std::vector<int32_t> row_info;      // (shared tokens, depth) per row
+  // (query row, partial slot of piece 0, last token the query row may attend to), concatenated per node
+  std::vector<int32_t> node_members;
+  std::vector<int32_t> row_info;  // per query row: (tokens covered by nodes, partial slots used)
   int32_t max_depth = 0;
-  std::vector<int32_t> items;  // (node, kv head, first row, piece) in launch order; node -1 = idle
+  std::vector<int32_t> items;  // (node, kv head, first member row, piece) in launch order; node -1 = idle
 
   // device image: one int32 array holding, in order, row_info, nodes, node_blocks, node_members, items
   std::vector<int32_t> image;

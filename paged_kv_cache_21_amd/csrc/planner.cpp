@@ -12,7 +12,14 @@
 // its last node are its own remainder.  Partly filled blocks are never put in
 // a node (an append may still write them), so a plan stays valid while rows
 // only grow by appends.
+//
+// The extend plan (several new query tokens per row, each attending causally
+// to its row's cache) uses the same nodes, with one member entry per query
+// token instead of per row, plus one private node per row covering the rest of
+// its blocks (the partly filled last block included); every entry carries the
+// last token it may attend to, so one matrix-core kernel serves both.
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <utility>
 #include <vector>
@@ -35,12 +42,8 @@ void build_image(pkv_plan* p) {
   im.insert(im.end(), p->row_info.begin(), p->row_info.end());
   p->off_nodes = im.size();
   for (const auto& n : p->nodes) {
-    im.push_back(n.block_off);
-    im.push_back(n.num_blocks);
-    im.push_back(n.member_off);
-    im.push_back(n.num_members);
-    im.push_back(n.pieces);
-    im.push_back(n.piece_blocks);
+    im.insert(im.end(), {n.block_off, n.num_blocks, n.member_off, n.num_members, n.pieces, n.piece_blocks,
+                         n.start_tok, n.valid_tokens});
   }
   p->off_blocks = im.size();
   im.insert(im.end(), p->node_blocks.begin(), p->node_blocks.end());
@@ -49,6 +52,23 @@ void build_image(pkv_plan* p) {
   p->off_items = im.size();
   im.insert(im.end(), p->items.begin(), p->items.end());
   if (im.empty()) im.push_back(0);
+}
+
+int32_t member_limit(const pkv_plan* p, int32_t entry) { return p->node_members[pkv_plan::kMemberInts * entry + 2]; }
+
+// Pieces of node n that the members of 64-row tile t need: the pieces starting at
+// or before the latest token any of the tile's members may attend to (pieces
+// past it would be fully masked for every member, so no work item runs them).
+int32_t tile_pieces(const pkv_plan* p, int32_t n, int32_t t) {
+  const auto& nd = p->nodes[n];
+  const int32_t per_tile = pkv::kCascadeRowsPerItem / p->group;  // member entries per tile
+  const int32_t e0 = t * per_tile, e1 = std::min(nd.num_members, e0 + per_tile);
+  int32_t lim = INT_MIN;
+  for (int32_t e = e0; e < e1; ++e) lim = std::max(lim, member_limit(p, nd.member_off + e));
+  if (lim == INT_MAX) return nd.pieces;
+  const int64_t span = static_cast<int64_t>(lim) - nd.start_tok;  // latest attended token, node-local
+  if (span < 0) return 0;
+  return static_cast<int32_t>(std::min<int64_t>(nd.pieces, span / (static_cast<int64_t>(nd.piece_blocks) * p->block_size) + 1));
 }
 
 // Token pieces.  A node's work is (64-row tiles) x (KV heads) x (blocks); the
@@ -77,18 +97,23 @@ void split_pieces(pkv_plan* p) {
   }
 }
 
-// Partial slots: along each row's path, node pieces take consecutive slots.
-// path[b] lists (node, member entry) pairs, root first.
-void assign_slots(pkv_plan* p, const std::vector<std::vector<std::pair<int32_t, int32_t>>>& path) {
-  p->max_depth = 0;
-  for (int32_t b = 0; b < p->batch; ++b) {
-    int32_t used = 0;
-    for (const auto& [node, entry] : path[b]) {
-      p->node_members[2 * entry + 1] = used;
-      used += p->nodes[node].pieces;
+// Partial slots: every query row's node pieces take consecutive slots, nodes in
+// creation order (root first along each path).
+void assign_slots(pkv_plan* p) {
+  std::vector<int32_t> used(p->num_query_rows, 0);
+  const int32_t per_tile = pkv::kCascadeRowsPerItem / p->group;
+  for (int32_t n = 0; n < static_cast<int32_t>(p->nodes.size()); ++n) {
+    const auto& nd = p->nodes[n];
+    for (int32_t e = 0; e < nd.num_members; ++e) {
+      int32_t* rec = &p->node_members[pkv_plan::kMemberInts * (nd.member_off + e)];
+      rec[1] = used[rec[0]];
+      used[rec[0]] += tile_pieces(p, n, e / per_tile);
     }
-    p->row_info[2 * b + 1] = used;
-    p->max_depth = std::max(p->max_depth, used);
+  }
+  p->max_depth = 0;
+  for (int32_t r = 0; r < p->num_query_rows; ++r) {
+    p->row_info[2 * r + 1] = used[r];
+    p->max_depth = std::max(p->max_depth, used[r]);
   }
 }
 
@@ -105,14 +130,25 @@ void build_items(pkv_plan* p) {
     int64_t load;
   };
   std::vector<Cluster> clusters;
+  struct Tiles {
+    std::vector<int32_t> first_rows;
+  };
+  std::vector<std::vector<Tiles>> per_piece;  // [node][piece]: tiles that need the piece
   for (int32_t n = 0; n < static_cast<int32_t>(p->nodes.size()); ++n) {
     const auto& nd = p->nodes[n];
     const int32_t rows = nd.num_members * p->group;
     const int32_t tiles = (rows + rows_per_item - 1) / rows_per_item;
+    per_piece.emplace_back(nd.pieces);
+    for (int32_t t = 0; t < tiles; ++t) {
+      const int32_t np = tile_pieces(p, n, t);
+      for (int32_t pc = 0; pc < np; ++pc) per_piece[n][pc].first_rows.push_back(t * rows_per_item);
+    }
     for (int32_t pc = 0; pc < nd.pieces; ++pc) {
       const int32_t blocks = std::min(nd.piece_blocks, nd.num_blocks - pc * nd.piece_blocks);
+      const int32_t nt = static_cast<int32_t>(per_piece[n][pc].first_rows.size());
+      if (nt == 0) continue;
       for (int32_t h = 0; h < p->num_kv_heads; ++h)
-        clusters.push_back({n, h, tiles, pc, static_cast<int64_t>(blocks) * tiles});
+        clusters.push_back({n, h, nt, pc, static_cast<int64_t>(blocks) * nt});
     }
   }
   std::stable_sort(clusters.begin(), clusters.end(),
@@ -124,10 +160,10 @@ void build_items(pkv_plan* p) {
     for (int i = 1; i < kXcds; ++i)
       if (load[i] < load[q]) q = i;
     load[q] += c.load;
-    for (int32_t t = 0; t < c.tiles; ++t) {
+    for (int32_t first_row : per_piece[c.node][c.piece].first_rows) {
       queues[q].push_back(c.node);
       queues[q].push_back(c.head);
-      queues[q].push_back(t * rows_per_item);
+      queues[q].push_back(first_row);
       queues[q].push_back(c.piece);
     }
   }
@@ -145,44 +181,20 @@ void build_items(pkv_plan* p) {
     }
 }
 
-}  // namespace
-
-extern "C" {
-
-pkv_plan* pkv_plan_build(const int32_t* block_tables, const int32_t* seq_lens, int32_t batch,
-                         int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t min_members) {
-  pkv::clear_error();
-  if (batch < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      num_q_heads % num_kv_heads != 0 || min_members < 2 || (batch > 0 && (!block_tables || !seq_lens))) {
-    pkv::fail(PKV_ERR_INVALID, "pkv_plan_build: invalid arguments");
-    return nullptr;
-  }
-  auto* p = new pkv_plan();
-  p->batch = batch;
-  p->max_blocks = max_blocks_per_seq;
-  p->block_size = block_size;
-  p->num_q_heads = num_q_heads;
-  p->num_kv_heads = num_kv_heads;
-  p->group = num_q_heads / num_kv_heads;
-  p->row_info.assign(2 * static_cast<size_t>(batch), 0);
-
-  std::vector<int32_t> full(batch);
-  for (int32_t b = 0; b < batch; ++b) {
-    if (seq_lens[b] < 0 || static_cast<int64_t>(seq_lens[b]) > static_cast<int64_t>(max_blocks_per_seq) * block_size) {
-      delete p;
-      pkv::fail(PKV_ERR_INVALID, "pkv_plan_build: seq_lens[%d] = %d outside [0, max_blocks*block_size]", b, seq_lens[b]);
-      return nullptr;
-    }
-    full[b] = seq_lens[b] / block_size;
-  }
-  auto id_at = [&](int32_t row, int32_t j) { return block_tables[static_cast<int64_t>(row) * max_blocks_per_seq + j]; };
-
-  std::vector<std::vector<std::pair<int32_t, int32_t>>> path(batch);  // (node, member entry), root first
+// The trie walk shared by both plans.  rows_in: rows taking part; full[b]: full
+// blocks of row b; add_members(r): append row r's member entries (query row,
+// slot placeholder, limit) to node_members; covered[r] receives the tokens of row
+// r covered by nodes.
+template <class AddMembers>
+void build_shared_nodes(pkv_plan* p, const int32_t* block_tables, const std::vector<int32_t>& rows_in,
+                        const std::vector<int32_t>& full, int32_t min_members, AddMembers add_members,
+                        std::vector<int32_t>& covered) {
+  const int32_t max_blocks = p->max_blocks, block_size = p->block_size;
+  auto id_at = [&](int32_t row, int32_t j) { return block_tables[static_cast<int64_t>(row) * max_blocks + j]; };
   std::vector<Group> stack;
   {
     Group g;
-    for (int32_t b = 0; b < batch; ++b)
+    for (int32_t b : rows_in)
       if (full[b] > 0) g.rows.push_back(b);
     g.start = 0;
     if (static_cast<int32_t>(g.rows.size()) >= min_members) stack.push_back(std::move(g));
@@ -207,15 +219,15 @@ pkv_plan* pkv_plan_build(const int32_t* block_tables, const int32_t* seq_lens, i
       pkv_plan::Node n;
       n.block_off = static_cast<int32_t>(p->node_blocks.size());
       n.num_blocks = i - g.start;
-      n.member_off = static_cast<int32_t>(p->node_members.size() / 2);
-      n.num_members = static_cast<int32_t>(g.rows.size());
+      n.member_off = static_cast<int32_t>(p->node_members.size() / pkv_plan::kMemberInts);
+      n.start_tok = g.start * block_size;
+      n.valid_tokens = n.num_blocks * block_size;
       for (int32_t j = g.start; j < i; ++j) p->node_blocks.push_back(id_at(g.rows[0], j));
       for (int32_t r : g.rows) {
-        path[r].emplace_back(static_cast<int32_t>(p->nodes.size()), static_cast<int32_t>(p->node_members.size() / 2));
-        p->node_members.push_back(r);
-        p->node_members.push_back(0);  // slot, assigned once pieces are known
-        p->row_info[2 * r] = i * block_size;
+        add_members(r);
+        covered[r] = i * block_size;
       }
+      n.num_members = static_cast<int32_t>(p->node_members.size() / pkv_plan::kMemberInts) - n.member_off;
       p->nodes.push_back(n);
     }
     // split by the id at i; groups keep the rows' order
@@ -240,10 +252,119 @@ pkv_plan* pkv_plan_build(const int32_t* block_tables, const int32_t* seq_lens, i
     }
     for (auto it = children.rbegin(); it != children.rend(); ++it) stack.push_back(std::move(*it));
   }
+}
+
+pkv_plan* new_plan(pkv_plan::Kind kind, int32_t batch, int32_t max_blocks_per_seq, int32_t block_size,
+                   int32_t num_q_heads, int32_t num_kv_heads) {
+  auto* p = new pkv_plan();
+  p->kind = kind;
+  p->batch = batch;
+  p->max_blocks = max_blocks_per_seq;
+  p->block_size = block_size;
+  p->num_q_heads = num_q_heads;
+  p->num_kv_heads = num_kv_heads;
+  p->group = num_q_heads / num_kv_heads;
+  return p;
+}
+
+void finish_plan(pkv_plan* p, const std::vector<int32_t>& covered_per_query_row) {
+  p->row_info.assign(2 * static_cast<size_t>(p->num_query_rows), 0);
+  for (int32_t r = 0; r < p->num_query_rows; ++r) p->row_info[2 * r] = covered_per_query_row[r];
   split_pieces(p);
-  assign_slots(p, path);
+  assign_slots(p);
   build_items(p);
   build_image(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_plan* pkv_plan_build(const int32_t* block_tables, const int32_t* seq_lens, int32_t batch,
+                         int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t min_members) {
+  pkv::clear_error();
+  if (batch < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || min_members < 2 || (batch > 0 && (!block_tables || !seq_lens))) {
+    pkv::fail(PKV_ERR_INVALID, "pkv_plan_build: invalid arguments");
+    return nullptr;
+  }
+  std::vector<int32_t> full(batch), rows(batch);
+  for (int32_t b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 0 || static_cast<int64_t>(seq_lens[b]) > static_cast<int64_t>(max_blocks_per_seq) * block_size) {
+      pkv::fail(PKV_ERR_INVALID, "pkv_plan_build: seq_lens[%d] = %d outside [0, max_blocks*block_size]", b, seq_lens[b]);
+      return nullptr;
+    }
+    full[b] = seq_lens[b] / block_size;
+    rows[b] = b;
+  }
+  pkv_plan* p = new_plan(pkv_plan::kDecode, batch, max_blocks_per_seq, block_size, num_q_heads, num_kv_heads);
+  p->num_query_rows = batch;
+  std::vector<int32_t> covered(batch, 0);
+  build_shared_nodes(
+      p, block_tables, rows, full, min_members,
+      [&](int32_t r) { p->node_members.insert(p->node_members.end(), {r, 0, INT_MAX}); }, covered);
+  finish_plan(p, covered);
+  return p;
+}
+
+pkv_plan* pkv_plan_build_extend(const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_lens,
+                                int32_t batch, int32_t max_blocks_per_seq, int32_t block_size, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t min_members) {
+  pkv::clear_error();
+  if (batch < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || min_members < 2 ||
+      (batch > 0 && (!block_tables || !seq_lens || !q_lens))) {
+    pkv::fail(PKV_ERR_INVALID, "pkv_plan_build_extend: invalid arguments");
+    return nullptr;
+  }
+  std::vector<int32_t> full(batch, 0), q_start(batch + 1, 0), rows;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t len = seq_lens[b], ql = q_lens[b];
+    if (len < 0 || static_cast<int64_t>(len) > static_cast<int64_t>(max_blocks_per_seq) * block_size || ql < 0 ||
+        ql > len) {
+      pkv::fail(PKV_ERR_INVALID, "pkv_plan_build_extend: row %d: need 0 <= q_lens <= seq_lens <= max_blocks*block_size",
+                b);
+      return nullptr;
+    }
+    if (static_cast<int64_t>(q_start[b]) + ql > (1 << 28)) {
+      pkv::fail(PKV_ERR_INVALID, "pkv_plan_build_extend: too many query tokens");
+      return nullptr;
+    }
+    q_start[b + 1] = q_start[b] + ql;
+    if (ql > 0) {
+      rows.push_back(b);
+      full[b] = len / block_size;
+    }
+  }
+  pkv_plan* p = new_plan(pkv_plan::kExtend, batch, max_blocks_per_seq, block_size, num_q_heads, num_kv_heads);
+  p->num_query_rows = q_start[batch];
+  auto add_members = [&](int32_t r) {
+    const int32_t first_pos = seq_lens[r] - q_lens[r];
+    for (int32_t i = 0; i < q_lens[r]; ++i) p->node_members.insert(p->node_members.end(), {q_start[r] + i, 0, first_pos + i});
+  };
+  std::vector<int32_t> covered(batch, 0);
+  build_shared_nodes(p, block_tables, rows, full, min_members, add_members, covered);
+  // one private node per row over the rest of its blocks
+  for (int32_t r : rows) {
+    const int32_t len = seq_lens[r];
+    if (len <= covered[r]) continue;
+    pkv_plan::Node n;
+    n.block_off = static_cast<int32_t>(p->node_blocks.size());
+    const int32_t j0 = covered[r] / block_size, j1 = (len + block_size - 1) / block_size;
+    n.num_blocks = j1 - j0;
+    n.member_off = static_cast<int32_t>(p->node_members.size() / pkv_plan::kMemberInts);
+    n.start_tok = covered[r];
+    n.valid_tokens = len - covered[r];
+    for (int32_t j = j0; j < j1; ++j) p->node_blocks.push_back(block_tables[static_cast<int64_t>(r) * max_blocks_per_seq + j]);
+    add_members(r);
+    n.num_members = q_lens[r];
+    p->nodes.push_back(n);
+  }
+  std::vector<int32_t> covered_q(p->num_query_rows, 0);
+  for (int32_t r : rows)
+    for (int32_t i = 0; i < q_lens[r]; ++i) covered_q[q_start[r] + i] = covered[r];
+  finish_plan(p, covered_q);
   return p;
 }
 
@@ -252,6 +373,8 @@ void pkv_plan_destroy(pkv_plan* plan) { delete plan; }
 size_t pkv_plan_device_bytes(const pkv_plan* plan) { return plan ? plan->image.size() * sizeof(int32_t) : 0; }
 
 int32_t pkv_plan_num_nodes(const pkv_plan* plan) { return plan ? static_cast<int32_t>(plan->nodes.size()) : -1; }
+
+int32_t pkv_plan_num_query_rows(const pkv_plan* plan) { return plan ? plan->num_query_rows : -1; }
 
 pkv_status pkv_plan_node(const pkv_plan* plan, int32_t node, int32_t* num_blocks, int32_t* num_members,
                          int32_t* blocks_out, int32_t* members_out) {
@@ -263,7 +386,8 @@ pkv_status pkv_plan_node(const pkv_plan* plan, int32_t node, int32_t* num_blocks
   if (num_members) *num_members = n.num_members;
   if (blocks_out) std::memcpy(blocks_out, plan->node_blocks.data() + n.block_off, sizeof(int32_t) * n.num_blocks);
   if (members_out)
-    for (int32_t k = 0; k < n.num_members; ++k) members_out[k] = plan->node_members[2 * (n.member_off + k)];
+    for (int32_t k = 0; k < n.num_members; ++k)
+      members_out[k] = plan->node_members[pkv_plan::kMemberInts * (n.member_off + k)];
   return PKV_OK;
 }
 
@@ -274,7 +398,7 @@ int32_t pkv_plan_node_pieces(const pkv_plan* plan, int32_t node) {
 
 pkv_status pkv_plan_row(const pkv_plan* plan, int32_t row, int32_t* shared_tokens, int32_t* depth) {
   pkv::clear_error();
-  if (!plan || row < 0 || row >= plan->batch) return pkv::fail(PKV_ERR_INVALID, "pkv_plan_row: bad plan or row");
+  if (!plan || row < 0 || row >= plan->num_query_rows) return pkv::fail(PKV_ERR_INVALID, "pkv_plan_row: bad plan or row");
   if (shared_tokens) *shared_tokens = plan->row_info[2 * row];
   if (depth) *depth = plan->row_info[2 * row + 1];
   return PKV_OK;

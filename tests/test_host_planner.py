@@ -132,3 +132,28 @@ def test_planner_rejects_bad_lengths():
         pkv.CascadePlan(bt, np.array([10, 40], dtype=np.int32), 4, 2)
     with pytest.raises(ValueError):
         pkv.CascadePlan(bt, np.array([10, 4], dtype=np.int32), 4, 2, min_members=1)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_extend_plan_covers_every_query_row(seed):
+    """Extend plans: every query row's nodes tile its row's blocks from 0 to its last block, and
+    its partial slots count the pieces it needs (pieces wholly after the query are skipped)."""
+    w = workloads.random_forest(seed, num_rows=10, max_len=300, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                                head_dim=64, share_prob=0.6)
+    ref = oracle.RefPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(ref, w.build_ops, allow_cow=True)
+    bt, lens = ref.export_tables(w.steps[0].decode_rows, w.max_blocks)
+    rng = np.random.default_rng(seed)
+    q_lens = np.minimum(lens, rng.integers(0, 40, size=len(lens))).astype(np.int32)
+    plan = pkv.ExtendPlan(bt, lens, q_lens, 8, 2)
+    assert plan.num_query_rows == int(q_lens.sum())
+    where = oracle.extend_query_positions(lens, q_lens)
+    nodes = [plan.node(i) for i in range(plan.num_nodes)]
+    for r, (b, pos) in enumerate(where):
+        mine = [i for i, (_, members) in enumerate(nodes) if r in set(members.tolist())]
+        blocks = np.concatenate([nodes[i][0] for i in mine]) if mine else np.zeros(0, np.int32)
+        nb = -(-int(lens[b]) // 16)
+        assert np.array_equal(blocks, bt[b, :nb]), (r, b)
+        shared, depth = plan.row(r)
+        assert shared % 16 == 0 and shared <= lens[b]
+        assert 1 <= depth <= sum(plan.node_pieces(i) for i in mine)
