@@ -14,6 +14,12 @@ random placement).  ``--config 1..5`` selects the other synthetic workloads.
 Prints one JSON line.  ``value`` = effective unique-KV GB/s of the step: the
 distinct K/V bytes the step must read plus q, output and table bytes, divided
 by the measured step time (inputs resident in HBM, back-to-back steps).
+
+``--extend`` measures the multi-token pass instead (paged_extend_attn): the
+verify pass over the tree-search workload (``--config 3``: the last 8 tokens
+of every branch) or a chunked-prefill slice (``--config 6``: 4,096 tokens over
+28,672 cached), reported as causal attention TFLOP/s against the matrix-core
+peak.
 """
 
 import argparse
@@ -28,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense matrix-core peak per dtype
 
 
 def parse():
@@ -35,7 +42,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--extend", action="store_true",
+                    help="time the multi-token pass (configs 3: verify 8 tokens per branch, 6: chunked prefill)")
     ap.add_argument("--no-cascade", action="store_true", help="decode every row on its own (no shared-prefix pass)")
     ap.add_argument("--cold-iters", type=int, default=10,
                     help="extra steps each preceded by a 1 GiB write that evicts L2 and MALL (0 = skip)")
@@ -75,7 +84,7 @@ def host_rows(q_bits, k_pages, v_pages, bt, lens, rows):
     for i, r in enumerate(rows):
         nb = -(-int(lens[r]) // bs)
         sbt[i, :nb] = [remap[int(x)] for x in bt[r, :nb]]
-    qb = q_bits[list(rows)].cpu().numpy().view(np.uint16)
+    qb = q_bits[list(rows)].cpu().numpy().view(np.uint16) if q_bits is not None else None
     return k, v, sbt, np.asarray([lens[r] for r in rows], dtype=np.int32), qb
 
 
@@ -126,6 +135,128 @@ def measured_traffic(w, kernel_source="paged_kv_cache_21_amd/csrc/decode.hip"):
     return int(round(kib * 1024))
 
 
+def extend_cpu_baseline(w, q_bits, k_pages, v_pages, bt, lens, q_lens, seconds):
+    """Time the fp64 extend oracle (one BLAS thread) over a sample of query rows spread over the
+    workload, until about `seconds` of oracle time; returns causal flop/s."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    where = oracle.extend_query_positions(lens, q_lens)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(where))
+    done, flops, t_total = 0, 0.0, 0.0
+    rows = {}
+    with threadpool_limits(limits=1):
+        for r in order:
+            b, pos = where[int(r)]
+            if b not in rows:
+                rows = {b: host_rows(None, k_pages, v_pages, bt, lens, [b])}
+            k, v, sbt, sl, _ = rows[b]
+            qrow = q_bits[int(r):int(r) + 1].cpu().numpy().view(np.uint16)
+            t0 = time.perf_counter()
+            # the row cut after the query's position, with the query as its one new token
+            oracle.ref_extend(qrow, k, v, sbt, np.asarray([pos + 1], np.int32), np.asarray([1], np.int32), w.scale,
+                              w.dtype)
+            t_total += time.perf_counter() - t0
+            done += 1
+            flops += 4.0 * w.head_dim * (pos + 1) * w.num_q_heads
+            if t_total >= seconds:
+                break
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} query rows drawn at random from the workload's {len(where)} (all {w.num_q_heads} "
+                      f"heads each), {t_total:.1f} s of fp64 numpy oracle time on one host thread"}
+
+
+def run_extend(args, w, dev):
+    """Multi-token pass: one paged_extend_attn call per step over the workload's query tokens."""
+    import torch
+
+    import paged_kv_cache_21_amd as pkv
+    import workloads
+
+    k_pages, v_pages = workloads.make_pages(w, device=dev)
+    pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(pool, w.build_ops)
+    bt, lens = pool.export_tables(w.steps[0].decode_rows, w.max_blocks)
+    q_lens = np.minimum(lens, workloads.EXTEND_QUERY_TOKENS[w.number]).astype(np.int32)
+    t0 = time.perf_counter()
+    plan = pkv.ExtendPlan(bt, lens, q_lens, w.num_q_heads, w.num_kv_heads)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    plan.upload(device=dev)
+    nq = int(q_lens.sum())
+    q = workloads._normal_bits((nq, w.num_q_heads, w.head_dim), w.dtype, 1000 + w.seed, dev)
+    ws = torch.empty(pkv.extend_workspace_bytes(plan, w.head_dim), dtype=torch.uint8, device=dev)
+    out = torch.empty((nq, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step():
+        pkv.paged_extend_attn(q, k_pages, v_pages, plan, scale=w.scale, workspace=ws, out=out, dtype=w.dtype,
+                              stream=stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
+    pkv.timing_reset()
+    pkv.timing_enable(True)
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    pkv.timing_enable(False)
+    kern = {}
+    for name in ("cascade", "merge"):
+        total, count = pkv.timing_read(name)
+        kern[name] = {"avg_us": round(total / count * 1e3, 3) if count else 0.0, "launches": count}
+
+    # causal flops: 2*d per (query, head, attended token) for q.k and again for p.v
+    first = lens - q_lens
+    attended = int(sum(int(q_lens[b]) * int(first[b]) + int(q_lens[b]) * (int(q_lens[b]) + 1) // 2
+                       for b in range(len(lens))))
+    flops = 4.0 * w.head_dim * w.num_q_heads * attended
+    kv_unique = unique_bytes(bt, lens, w)
+    t_mfma = kern["cascade"]["avg_us"] * 1e-6
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    achieved = flops / t_mfma / 1e12 if t_mfma > 0 else 0.0
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = extend_cpu_baseline(w, q, k_pages, v_pages, bt, lens, q_lens, args.cpu_seconds)
+    res = {
+        "metric": "paged extend attn: causal attention TFLOP/s, effective unique-KV GB/s",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}", "query_tokens": nq, "rows": int((q_lens > 0).sum()),
+                   "query_tokens_per_row": int(workloads.EXTEND_QUERY_TOKENS[w.number]),
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "shared_nodes": plan.num_nodes, "accumulate": "f32",
+                   "parallelism": "single GPU"},
+        "effective_kv_gbs": round(kv_unique / (ms * 1e-3) / 1e9, 1),
+        "hbm_peak_frac": round(kv_unique / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "attended_token_pairs": attended,
+        "kernels": kern,
+        "host_us": {"plan_build": round(plan_us, 1)},
+        "roofline": {"bound": "mfma", "kernel": "cascade_kernel", "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "avg_launch_us": kern["cascade"]["avg_us"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -146,6 +277,8 @@ def main():
     torch.cuda.set_device(dev)
     w = workloads.get(args.config)
     print(f"[bench] workload {w.number} {w.name}: {w.description}", file=sys.stderr, flush=True)
+    if args.extend or args.config == 6:
+        return run_extend(args, w, dev)
 
     # ---- set-up (not timed): pages, pool, the step's append plan, tables, cascade plan
     k_pages, v_pages = workloads.make_pages(w, device=dev)

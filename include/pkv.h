@@ -300,6 +300,16 @@ size_t pkv_extend_workspace_bytes(const pkv_plan* plan, int32_t head_dim);
  * extend plan; -1 for NULL. */
 int32_t pkv_plan_num_query_rows(const pkv_plan* plan);
 
+/* The plan's device image (what pkv_plan_upload copies), for inspection on the
+ * host: copies it into out when capacity (int32 entries) suffices, writes the
+ * offsets of its sections (row info, nodes, node blocks, members, items) and the
+ * partial slots per query row into offsets[0..5], and returns the image length
+ * (-1 for NULL).  Node records are 8 ints (block offset, blocks, member offset,
+ * members, pieces, blocks per piece, first token position, tokens holding data),
+ * member entries 3 (query row, slot of piece 0, last attended position or
+ * INT32_MAX), work items 4 (node or -1, KV head, first tile row, piece). */
+int64_t pkv_plan_image(const pkv_plan* plan, int32_t* out, int64_t capacity, int64_t* offsets);
+
 /* ------------------------------------------------------------------------------------------
  * Kernel timing (for measurement).  When enabled, every kernel launch of the
  * library is bracketed with HIP events on its own stream; pkv_timing_read()

@@ -102,6 +102,7 @@ _SIGNATURES = {
     "pkv_plan_build_extend": (_vp, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_extend_workspace_bytes": (_sz, [_vp, _i32]),
     "pkv_plan_num_query_rows": (_i32, [_vp]),
+    "pkv_plan_image": (_i64, [_vp, _vp, _i64, _vp]),
     "pkv_paged_extend_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _f32, _vp, _vp, _sz,
                                      _vp, _vp]),
     "pkv_timing_enable": (_i32, [_i32]),
@@ -274,7 +275,7 @@ class BlockPool:
 
     def __del__(self):
         h = getattr(self, "_handle", None)
-        if h:
+        if h and _lib is not None:  # at interpreter exit the module globals may already be gone
             _lib.pkv_pool_destroy(h)
             self._handle = None
 
@@ -359,7 +360,7 @@ class CascadePlan:
 
     def __del__(self):
         h = getattr(self, "_handle", None)
-        if h:
+        if h and _lib is not None:  # at interpreter exit the module globals may already be gone
             _lib.pkv_plan_destroy(h)
             self._handle = None
 
@@ -398,6 +399,15 @@ class CascadePlan:
         if n < 0:
             raise PkvInvalid(PKV_ERR_INVALID, f"bad node index {i}")
         return n
+
+    def image(self):
+        """(int32 image, {section: offset}, partial slots per query row) as uploaded to the device."""
+        offs = np.zeros(6, dtype=np.int64)
+        n = int(_lib.pkv_plan_image(self._handle, None, 0, _ptr(offs)))
+        img = np.zeros(max(n, 1), dtype=np.int32)
+        _lib.pkv_plan_image(self._handle, _ptr(img), n, _ptr(offs))
+        names = ("row_info", "nodes", "blocks", "members", "items")
+        return img[:n], dict(zip(names, offs[:5].tolist())), int(offs[5])
 
     def row(self, b):
         """(shared tokens, partial slots used by the row's nodes) of row b."""

@@ -241,6 +241,7 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
                        num_q_heads,
                        num_kv_heads,
                        L.slots,
+                       plan->max_piece_blocks(),
                        scale_log2};
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
@@ -341,6 +342,7 @@ pkv_status pkv_paged_extend_attn(const void* q, int32_t num_query_rows, int32_t 
                        num_q_heads,
                        num_kv_heads,
                        slots,
+                       plan->max_piece_blocks(),
                        scale_log2};
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });

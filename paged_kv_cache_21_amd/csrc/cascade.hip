@@ -73,8 +73,10 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
 // is (row 4*(l / 16) + j, column l % 16).  A contraction index may be permuted
 // freely as long as A and B agree; the PV product uses the token order the S^T
 // accumulator leaves in each lane.
-template <class DT, int D, int G>
-__global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
+// NW: 64-block windows of block ids held per lane (1 when every piece of the plan
+// has at most 64 blocks; up to kCascadeMaxPieceBlocks / 64 otherwise).
+template <class DT, int D, int G, int NW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cascade_kernel(CascadeArgs a) {
   constexpr int KPITCH = D + 8;  // K row pitch in LDS (elements); the pad spreads rows over banks
   constexpr int VPITCH = 18;     // V^T row pitch in LDS (32-bit words = 2 tokens each; 16 used)
   constexpr int NKS = D / 32;    // k-steps of the QK product
@@ -155,13 +157,21 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
   const int vcol = tid >> 4;   // 8-element column group
   const bool vthread = vcol < D / 8;
 
-  // the piece's block ids, lane j holding block j (a piece has at most 64 blocks);
-  // read with readlane so the chunk loop issues no scalar memory loads, which would
-  // share a wait counter with the LDS reads
-  const int my_blk = lane < nblk ? a.node_blocks[blk_off + pb0 + lane] : -1;
-  auto block_id = [&](int j) -> int {  // j: block within the piece
+  // the piece's block ids, lane j of register w holding block 64 w + j (a piece has
+  // at most 64 NW blocks); read with readlane so the chunk loop issues no scalar
+  // memory loads, which would share a wait counter with the LDS reads
+  int blk_win[NW];
+#pragma unroll
+  for (int w4 = 0; w4 < NW; ++w4) {
+    const int j = 64 * w4 + lane;
+    blk_win[w4] = j < nblk ? a.node_blocks[blk_off + pb0 + j] : -1;
+  }
+  auto block_id = [&](int j) -> int {  // j: block within the piece (uniform)
     if (j >= nblk) return -1;
-    const int id = __builtin_amdgcn_readlane(my_blk, j);
+    int v = blk_win[0];
+#pragma unroll
+    for (int w4 = 1; w4 < NW; ++w4) v = (j >> 6) == w4 ? blk_win[w4] : v;
+    const int id = __builtin_amdgcn_readlane(v, j & 63);
     return (id >= 0 && static_cast<int64_t>(id) < a.num_blocks) ? id : -1;
   };
 
@@ -207,9 +217,11 @@ __global__ __launch_bounds__(256) void cascade_kernel(CascadeArgs a) {
   // id) are zeroed, so their zero weights never meet stale Inf / NaN bits
   auto store_chunk = [&](const Stage& st_in, int ch, int buf) {
     Stage st = st_in;
-    if (vthread && (ch * 32 + 32 > piece_valid || block_id(2 * ch) < 0 || block_id(2 * ch + 1) < 0)) {  // uniform
+    // block_id reads a lane of a register: its argument must be wave-uniform
+    const bool ok0 = block_id(2 * ch) >= 0, ok1 = block_id(2 * ch + 1) >= 0;
+    if (vthread && (ch * 32 + 32 > piece_valid || !ok0 || !ok1)) {  // uniform
       const int t = ch * 32 + 2 * vpair;
-      const bool blk_ok = block_id(2 * ch + (vhi ? 1 : 0)) >= 0;
+      const bool blk_ok = vhi ? ok1 : ok0;
       if (!(blk_ok && t < piece_valid)) st.v0 = u32x4{0, 0, 0, 0};
       if (!(blk_ok && t + 1 < piece_valid)) st.v1 = u32x4{0, 0, 0, 0};
     }
@@ -345,7 +357,13 @@ namespace {
 template <class DT, int D, int G>
 hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   if (a.num_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL((cascade_kernel<DT, D, G>), dim3(static_cast<unsigned>(a.num_items)), dim3(256), 0, stream, a);
+  if (a.max_piece_blocks > kCascadeMaxPieceBlocks) return hipErrorInvalidValue;
+  if (a.max_piece_blocks <= 64)
+    hipLaunchKernelGGL((cascade_kernel<DT, D, G, 1>), dim3(static_cast<unsigned>(a.num_items)), dim3(256), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL((cascade_kernel<DT, D, G, kCascadeMaxPieceBlocks / 64>),
+                       dim3(static_cast<unsigned>(a.num_items)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

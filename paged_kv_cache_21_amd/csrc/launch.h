@@ -91,10 +91,12 @@ struct CascadeArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t slots;
+  int32_t max_piece_blocks;  // largest piece of the plan (selects the kernel instance)
   float scale_log2;
 };
 
-constexpr int kCascadeRowsPerItem = 64;  // 4 waves x 16 rows
+constexpr int kCascadeRowsPerItem = 64;     // 4 waves x 16 rows
+constexpr int kCascadeMaxPieceBlocks = 256;  // blocks of one work item's token piece
 constexpr int kNodeInts = 8;             // ints per node record of a plan image
 constexpr int kMemberInts = 3;           // ints per member entry of a plan image
 

@@ -40,4 +40,6 @@ struct pkv_plan {
   const int32_t* device = nullptr;  // bound by pkv_plan_upload
 
   int32_t num_items() const { return static_cast<int32_t>(items.size() / 4); }
+  int32_t max_piece_blocks_ = 0;  // largest piece over the nodes, set with the pieces
+  int32_t max_piece_blocks() const { return max_piece_blocks_; }
 };

@@ -79,7 +79,7 @@ int32_t tile_pieces(const pkv_plan* p, int32_t n, int32_t t) {
 void split_pieces(pkv_plan* p) {
   constexpr int64_t kTargetItems = 1024;
   constexpr int32_t kMinPieceBlocks = 32;
-  constexpr int32_t kMaxPieceBlocks = 64;
+  constexpr int32_t kMaxPieceBlocks = pkv::kCascadeMaxPieceBlocks;
   const int rows_per_item = pkv::kCascadeRowsPerItem;
   int64_t work = 0;
   for (const auto& n : p->nodes) {
@@ -89,11 +89,12 @@ void split_pieces(pkv_plan* p) {
   const int64_t target = std::max<int64_t>(kMinPieceBlocks, (work + kTargetItems - 1) / kTargetItems);
   for (auto& n : p->nodes) {
     // at most kMaxPieceBlocks blocks per piece: the cascade kernel keeps a piece's
-    // block ids in one 64-lane register
+    // block ids in four 64-lane registers
     n.pieces = static_cast<int32_t>(std::max<int64_t>(
         std::max<int64_t>(1, n.num_blocks / target), (n.num_blocks + kMaxPieceBlocks - 1) / kMaxPieceBlocks));
     n.piece_blocks = (n.num_blocks + n.pieces - 1) / n.pieces;
     n.pieces = (n.num_blocks + n.piece_blocks - 1) / n.piece_blocks;
+    p->max_piece_blocks_ = std::max(p->max_piece_blocks_, n.piece_blocks);
   }
 }
 
@@ -375,6 +376,21 @@ size_t pkv_plan_device_bytes(const pkv_plan* plan) { return plan ? plan->image.s
 int32_t pkv_plan_num_nodes(const pkv_plan* plan) { return plan ? static_cast<int32_t>(plan->nodes.size()) : -1; }
 
 int32_t pkv_plan_num_query_rows(const pkv_plan* plan) { return plan ? plan->num_query_rows : -1; }
+
+int64_t pkv_plan_image(const pkv_plan* plan, int32_t* out, int64_t capacity, int64_t* offsets) {
+  if (!plan) return -1;
+  const int64_t n = static_cast<int64_t>(plan->image.size());
+  if (out && capacity >= n) std::memcpy(out, plan->image.data(), sizeof(int32_t) * n);
+  if (offsets) {
+    offsets[0] = static_cast<int64_t>(plan->off_row_info);
+    offsets[1] = static_cast<int64_t>(plan->off_nodes);
+    offsets[2] = static_cast<int64_t>(plan->off_blocks);
+    offsets[3] = static_cast<int64_t>(plan->off_members);
+    offsets[4] = static_cast<int64_t>(plan->off_items);
+    offsets[5] = plan->max_depth;
+  }
+  return n;
+}
 
 pkv_status pkv_plan_node(const pkv_plan* plan, int32_t node, int32_t* num_blocks, int32_t* num_members,
                          int32_t* blocks_out, int32_t* members_out) {

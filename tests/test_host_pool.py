@@ -112,7 +112,7 @@ def test_worked_example_refcounts():
     assert lib.refcount(lib.table(1)[1]) == 1 and lib.refcount(lib.table(2)[1]) == 1
 
 
-@pytest.mark.parametrize("number", [1, 2, 3, 5])
+@pytest.mark.parametrize("number", [1, 2, 3, 5, 6])
 def test_workload_build_scripts_identical_tables(number):
     w = workloads.get(number)
     ref = oracle.RefPool(w.num_blocks, w.block_size, w.free_order)

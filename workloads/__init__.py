@@ -310,12 +310,35 @@ def radix_backtrack(seed: int = 5, root_tokens: int = 4096, branching: int = 4, 
                     logical_tokens=len(leaves) * leaf_len, unique_tokens=unique)
 
 
+def chunked_prefill(seed: int = 6, cached: int = 28672, slice_tokens: int = 4096) -> Workload:
+    """One Llama-3-8B-shaped sequence in the middle of a chunked prefill: the last
+    4,096-token slice of a 32,768-token prompt ("Dismantling the Memory Wall",
+    "Chunked Prefill": a 32,000-token prompt processed under a 4,096-token budget)
+    attends causally to the 28,672 tokens cached before it and to itself."""
+    rng = np.random.default_rng(seed)
+    total = cached + slice_tokens
+    nblk = _pool_size(_blocks(total))
+    free_order = rng.permutation(nblk).astype(np.int32)
+    ops = [("alloc", 0, total)]
+    return Workload(6, "chunked_prefill",
+                    f"1 sequence, {slice_tokens}-token slice over {cached} cached tokens, Hq=32, Hkv=8, d=128, bf16",
+                    "bf16", 32, 8, 128, BLOCK_SIZE, nblk, free_order, ops, [Step([], [0], [])],
+                    max_blocks=_blocks(total), seed=seed, logical_tokens=total, unique_tokens=total)
+
+
+# Query tokens per decode row for the multi-token (extend) measurements: the
+# verify pass scores the last 8 tokens of every tree-search branch; the chunked
+# prefill scores its whole slice.
+EXTEND_QUERY_TOKENS = {3: 8, 6: 4096}
+
+
 WORKLOADS = {
     1: tiny_tree,
     2: llama8b_decode,
     3: tree_search,
     4: mha70b_layer,
     5: radix_backtrack,
+    6: chunked_prefill,
 }
 
 
