@@ -157,3 +157,24 @@ def test_extend_plan_covers_every_query_row(seed):
         shared, depth = plan.row(r)
         assert shared % 16 == 0 and shared <= lens[b]
         assert 1 <= depth <= sum(plan.node_pieces(i) for i in mine)
+
+
+@pytest.mark.parametrize("seed", [0, 3])
+@pytest.mark.parametrize("extend", [False, True])
+def test_plan_image_indices_in_bounds(seed, extend):
+    """Every index the matrix-core and merge kernels derive from a plan image is in bounds, and
+    every partial slot a query row merges is written by exactly one work item per head."""
+    from plan_checks import check_plan_image
+
+    w = workloads.random_forest(seed, num_rows=14, max_len=1500, dtype="bf16", num_q_heads=16, num_kv_heads=4,
+                                head_dim=128, share_prob=0.7)
+    ref = oracle.RefPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(ref, w.build_ops, allow_cow=True)
+    bt, lens = ref.export_tables(w.steps[0].decode_rows, w.max_blocks)
+    if extend:
+        q_lens = np.minimum(lens, np.random.default_rng(seed).integers(0, 300, size=len(lens))).astype(np.int32)
+        plan = pkv.ExtendPlan(bt, lens, q_lens, 16, 4)
+    else:
+        plan = pkv.CascadePlan(bt, lens, 16, 4)
+    items, written = check_plan_image(plan, 16, 4, w.num_blocks)
+    assert items > 0 and written > 0
