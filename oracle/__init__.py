@@ -28,6 +28,8 @@ invariants; none of them is "parity unpinned".
 from .kvsize import kv_bytes, kv_bytes_per_token
 from .attention import decode_bits, ref_decode, ref_decode_rows, bruteforce_decode
 from .extend import extend_query_positions, ref_extend
+from .fp8 import (apply_append_fp8, dequantize_heads, dequantize_pages, e4m3_decode, e4m3_encode,
+                  pow2_scale_exponent, quantize_heads, ref_decode_fp8)
 from .pool import RefPool, RefPoolError, apply_append
 
 __all__ = [
@@ -39,6 +41,14 @@ __all__ = [
     "bruteforce_decode",
     "extend_query_positions",
     "ref_extend",
+    "apply_append_fp8",
+    "dequantize_heads",
+    "dequantize_pages",
+    "e4m3_decode",
+    "e4m3_encode",
+    "pow2_scale_exponent",
+    "quantize_heads",
+    "ref_decode_fp8",
     "RefPool",
     "RefPoolError",
     "apply_append",
