@@ -250,6 +250,44 @@ int32_t pkv_plan_node_pieces(const pkv_plan* plan, int32_t node);
 pkv_status pkv_plan_row(const pkv_plan* plan, int32_t row, int32_t* shared_tokens, int32_t* depth);
 
 /* ------------------------------------------------------------------------------------------
+ * FP8 pages.  "The Reasoning Engine Meltdown" names FP8 (and FP4) quantization of
+ * the KV cache among the ways to fit deep search trees in memory (§3, and its
+ * closing outlook); the format and granularity are this library's choice:
+ *   - codes: OCP E4M3 ("fn": largest finite 448, subnormals down to 2^-9), one byte
+ *     per element, k_pages / v_pages [num_blocks][block_size][num_kv_heads][head_dim];
+ *   - scales: float32 [num_blocks][num_kv_heads][block_size], one per token row and
+ *     KV head, a power of two 2^k with k the smallest integer (clamped to
+ *     [-126, 127]) such that max|x| / 2^k <= 448 over the head vector (k = 0 for an
+ *     all-zero vector); a code's value times its scale is the stored element;
+ *   - an appended token's head vector x is stored as round-to-nearest-even(x / 2^k)
+ *     (exact scaling, then the nearest E4M3 value, ties to even), so appending never
+ *     re-quantizes earlier rows.
+ * Halves the KV bytes the decode streams.  The cascade and extend passes take
+ * 16-bit pages only.
+ * ---------------------------------------------------------------------------------------- */
+
+/* As pkv_kv_append, for FP8 pages: copy-on-write copies codes and scales of rows
+ * [0, cow_rows[c]); each new token (k_new / v_new [num_tokens][num_kv_heads][head_dim]
+ * in src_dtype, PKV_F16 or PKV_BF16) is quantized into its slot.  head_dim 64 or
+ * 128.  Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP. */
+pkv_status pkv_kv_append_fp8(void* k_pages, void* v_pages, float* k_scales, float* v_scales, int64_t num_blocks,
+                             int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
+                             const void* k_new, const void* v_new, int32_t num_tokens, const int64_t* slot_mapping,
+                             const int32_t* cow_src, const int32_t* cow_dst, const int32_t* cow_rows, int32_t num_cow,
+                             void* stream);
+
+/* As pkv_paged_decode_attn (no plan), over FP8 pages: K and V elements are code
+ * value x scale; q is q_dtype (PKV_F16 or PKV_BF16) and the arithmetic is that of
+ * the 16-bit path (every E4M3 value is exact in both 16-bit types).  Workspace:
+ * pkv_decode_workspace_bytes(..., NULL).  Errors as pkv_paged_decode_attn. */
+pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t q_dtype, const void* k_pages, const void* v_pages,
+                                     const float* k_scales, const float* v_scales, int64_t num_blocks,
+                                     int32_t block_size, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, int32_t max_seq_len, float scale, void* workspace,
+                                     size_t workspace_bytes, float* out, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Device operation 3: multi-token (extend) attention over a paged KV cache.
  *
  * Several new tokens per sequence, each attending causally to its sequence's

@@ -23,7 +23,7 @@ import torch  # noqa: F401
 __all__ = [
     "PkvError", "PkvInvalid", "PkvOOM", "PkvNotFound", "PkvUnsupported", "PkvWorkspaceError", "PkvHipError",
     "kv_append", "paged_decode_attn", "decode_workspace_bytes", "BlockPool", "CascadePlan",
-    "ExtendPlan", "paged_extend_attn", "extend_workspace_bytes",
+    "ExtendPlan", "paged_extend_attn", "extend_workspace_bytes", "kv_append_fp8", "paged_decode_attn_fp8",
     "timing_enable", "timing_reset", "timing_read", "KERNELS", "lib", "LIB_PATH", "version",
 ]
 
@@ -105,6 +105,10 @@ _SIGNATURES = {
     "pkv_plan_image": (_i64, [_vp, _vp, _i64, _vp]),
     "pkv_paged_extend_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _f32, _vp, _vp, _sz,
                                      _vp, _vp]),
+    "pkv_kv_append_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
+                                 _vp, _i32, _vp]),
+    "pkv_paged_decode_attn_fp8": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _vp,
+                                         _i32, _vp, _i32, _f32, _vp, _sz, _vp, _vp]),
     "pkv_timing_enable": (_i32, [_i32]),
     "pkv_timing_reset": (_i32, []),
     "pkv_timing_read": (_i32, [_i32, _vp, _vp]),
@@ -205,6 +209,66 @@ def kv_append(k_pages, v_pages, k_new, v_new, slot_mapping, cow_src=None, cow_ds
                               _ptr(k_new), _ptr(v_new), n, _ptr(slot_mapping),
                               _ptr(cow_src) if n_cow else None, _ptr(cow_dst) if n_cow else None,
                               _ptr(cow_rows) if n_cow else None, n_cow, _stream(stream, k_pages)))
+
+
+def kv_append_fp8(k_pages, v_pages, k_scales, v_scales, k_new, v_new, slot_mapping, cow_src=None, cow_dst=None,
+                  cow_rows=None, src_dtype=None, stream=None):
+    """FP8 pages: copy-on-write the listed block prefixes (codes and scales), then quantize
+    k_new[i] / v_new[i] into slot slot_mapping[i].
+
+    k_pages, v_pages: uint8 [num_blocks, block_size, Hkv, d]; k_scales, v_scales: float32
+    [num_blocks, Hkv, block_size]; k_new, v_new: [N, Hkv, d] fp16/bf16 (or int16 bits with
+    ``src_dtype``).
+    """
+    import torch
+
+    _require(k_pages.dim() == 4 and v_pages.shape == k_pages.shape and k_pages.dtype == torch.uint8,
+             "k_pages/v_pages must be equal uint8 [num_blocks, block_size, Hkv, d] tensors")
+    nblk, bs, hkv, d = k_pages.shape
+    _require(tuple(k_scales.shape) == (nblk, hkv, bs) and tuple(v_scales.shape) == (nblk, hkv, bs) and
+             k_scales.dtype == v_scales.dtype == torch.float32, "scales must be float32 [num_blocks, Hkv, block_size]")
+    n = int(slot_mapping.numel())
+    _require(tuple(k_new.shape) == (n, hkv, d) and tuple(v_new.shape) == (n, hkv, d), "k_new/v_new must be [N, Hkv, d]")
+    _require(all(t.is_contiguous() for t in (k_pages, v_pages, k_scales, v_scales, k_new, v_new, slot_mapping)),
+             "inputs must be contiguous")
+    _require(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
+    n_cow = 0 if cow_src is None else int(cow_src.numel())
+    _check(_lib.pkv_kv_append_fp8(_ptr(k_pages), _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), nblk, bs, hkv, d,
+                                  _dtype_code(k_new, src_dtype), _ptr(k_new), _ptr(v_new), n, _ptr(slot_mapping),
+                                  _ptr(cow_src) if n_cow else None, _ptr(cow_dst) if n_cow else None,
+                                  _ptr(cow_rows) if n_cow else None, n_cow, _stream(stream, k_pages)))
+
+
+def paged_decode_attn_fp8(q, k_pages, v_pages, k_scales, v_scales, block_tables, seq_lens, max_seq_len, scale=None,
+                          workspace=None, out=None, q_dtype=None, stream=None):
+    """Decode attention over FP8 pages (codes x per-row scales); q [B, Hq, d] fp16/bf16, fp32 output."""
+    import torch
+
+    _require(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape and k_pages.dtype == torch.uint8,
+             "q [B, Hq, d]; uint8 pages [num_blocks, block_size, Hkv, d]")
+    B, hq, d = q.shape
+    nblk, bs, hkv, dk = k_pages.shape
+    _require(dk == d, "head_dim of q and pages differ")
+    _require(tuple(k_scales.shape) == (nblk, hkv, bs) and tuple(v_scales.shape) == (nblk, hkv, bs) and
+             k_scales.dtype == v_scales.dtype == torch.float32, "scales must be float32 [num_blocks, Hkv, block_size]")
+    _require(all(t.is_contiguous() for t in (q, k_pages, v_pages, k_scales, v_scales, block_tables, seq_lens)),
+             "inputs must be contiguous")
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables and lengths must be int32")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == B and seq_lens.numel() == B, "bad table shape")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    need = decode_workspace_bytes(B, hq, hkv, d, int(max_seq_len), None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, hq, d), "bad out tensor")
+    _check(_lib.pkv_paged_decode_attn_fp8(_ptr(q), B, hq, hkv, d, _dtype_code(q, q_dtype), _ptr(k_pages),
+                                          _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), nblk, bs,
+                                          _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens),
+                                          int(max_seq_len), float(scale), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream, q)))
+    return out
 
 
 def decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan=None):

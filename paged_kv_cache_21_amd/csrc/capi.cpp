@@ -157,11 +157,70 @@ pkv_status pkv_kv_append(void* k_pages, void* v_pages, int64_t num_blocks, int32
   if (!pkv::aligned16(k_pages) || !pkv::aligned16(v_pages) || !pkv::aligned16(k_new) || !pkv::aligned16(v_new))
     return fail(PKV_ERR_INVALID, "pkv_kv_append: page and token pointers must be 16-byte aligned");
   if (static_cast<int64_t>(num_tokens) + num_cow > 0x7fffffff) return fail(PKV_ERR_INVALID, "pkv_kv_append: too many work items");
-  pkv::AppendArgs a{static_cast<uint16_t*>(k_pages), static_cast<uint16_t*>(v_pages), num_blocks, block_size,
-                    static_cast<int32_t>(row_elems), static_cast<const uint16_t*>(k_new),
-                    static_cast<const uint16_t*>(v_new), num_tokens, slot_mapping, cow_src, cow_dst, cow_rows, num_cow};
+  pkv::AppendArgs a{static_cast<uint16_t*>(k_pages),
+                    static_cast<uint16_t*>(v_pages),
+                    nullptr,
+                    nullptr,
+                    num_kv_heads,
+                    head_dim,
+                    num_blocks,
+                    block_size,
+                    static_cast<int32_t>(row_elems),
+                    static_cast<const uint16_t*>(k_new),
+                    static_cast<const uint16_t*>(v_new),
+                    num_tokens,
+                    slot_mapping,
+                    cow_src,
+                    cow_dst,
+                    cow_rows,
+                    num_cow};
   hipStream_t s = static_cast<hipStream_t>(stream);
   return pkv::launch(PKV_KERNEL_APPEND, "kv_append", s, [&] { return pkv::launch_kv_append(a, s); });
+}
+
+pkv_status pkv_kv_append_fp8(void* k_pages, void* v_pages, float* k_scales, float* v_scales, int64_t num_blocks,
+                             int32_t block_size, int32_t num_kv_heads, int32_t head_dim, int32_t src_dtype,
+                             const void* k_new, const void* v_new, int32_t num_tokens, const int64_t* slot_mapping,
+                             const int32_t* cow_src, const int32_t* cow_dst, const int32_t* cow_rows, int32_t num_cow,
+                             void* stream) {
+  pkv::clear_error();
+  if (src_dtype != PKV_F16 && src_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_kv_append_fp8: source dtype %d", src_dtype);
+  if (num_blocks < 0 || block_size <= 0 || num_kv_heads <= 0 || num_tokens < 0 || num_cow < 0)
+    return fail(PKV_ERR_INVALID, "pkv_kv_append_fp8: negative or zero size");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_kv_append_fp8: head_dim %d (built: 64, 128)", head_dim);
+  const int64_t row_elems = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (row_elems > (1 << 24)) return fail(PKV_ERR_UNSUPPORTED, "pkv_kv_append_fp8: token row too large");
+  if ((num_tokens > 0 || num_cow > 0) && (!k_pages || !v_pages || !k_scales || !v_scales))
+    return fail(PKV_ERR_INVALID, "pkv_kv_append_fp8: null page or scale pointer");
+  if (num_tokens > 0 && (!k_new || !v_new || !slot_mapping)) return fail(PKV_ERR_INVALID, "pkv_kv_append_fp8: null pointer");
+  if (num_cow > 0 && (!cow_src || !cow_dst || !cow_rows))
+    return fail(PKV_ERR_INVALID, "pkv_kv_append_fp8: null copy-on-write pointer");
+  if (!pkv::aligned16(k_pages) || !pkv::aligned16(v_pages) || !pkv::aligned16(k_new) || !pkv::aligned16(v_new) ||
+      ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & 3u))
+    return fail(PKV_ERR_INVALID, "pkv_kv_append_fp8: pages and tokens must be 16-byte, scales 4-byte aligned");
+  if (static_cast<int64_t>(num_tokens) + num_cow > 0x7fffffff)
+    return fail(PKV_ERR_INVALID, "pkv_kv_append_fp8: too many work items");
+  pkv::AppendArgs a{static_cast<uint16_t*>(k_pages),
+                    static_cast<uint16_t*>(v_pages),
+                    k_scales,
+                    v_scales,
+                    num_kv_heads,
+                    head_dim,
+                    num_blocks,
+                    block_size,
+                    static_cast<int32_t>(row_elems),
+                    static_cast<const uint16_t*>(k_new),
+                    static_cast<const uint16_t*>(v_new),
+                    num_tokens,
+                    slot_mapping,
+                    cow_src,
+                    cow_dst,
+                    cow_rows,
+                    num_cow};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return pkv::launch(PKV_KERNEL_APPEND, "kv_append_fp8", s, [&] { return pkv::launch_kv_append_fp8(src_dtype, a, s); });
 }
 
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -179,14 +238,18 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
   return pkv::decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan).bytes;
 }
 
-pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
-                                 int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
-                                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float scale,
-                                 const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out,
-                                 void* stream) {
-  pkv::clear_error();
-  if (dtype != PKV_F16 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn: dtype %d", dtype);
+}  // extern "C"
+
+namespace {
+
+// Shared body of the 16-bit and FP8 decode calls.  kdtype: kernel type code (0 f16,
+// 1 bf16, 2 FP8 pages with f16 q, 3 FP8 pages with bf16 q).
+pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, const void* k_pages, const void* v_pages, const float* k_scales,
+                       const float* v_scales, int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                       const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  const int dtype = kdtype;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
       max_seq_len < 0)
     return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: negative or zero size");
@@ -256,6 +319,8 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
                       block_tables,
                       seq_lens,
                       row_info,
+                      k_scales,
+                      v_scales,
                       acc,
                       ml,
                       counts,
@@ -276,6 +341,40 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
   pkv::MergeArgs ma{seq_lens, row_info, counts, acc, ml, out, batch, num_q_heads, num_kv_heads, max_blocks_per_seq,
                     max_seq_len, L.slots};
   return pkv::launch(PKV_KERNEL_MERGE, "merge", s, [&] { return pkv::launch_merge(head_dim, ma, s); });
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
+                                 int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                 const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out,
+                                 void* stream) {
+  pkv::clear_error();
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn: dtype %d", dtype);
+  return decode_impl(dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, nullptr, nullptr,
+                     num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
+                     workspace, workspace_bytes, out, stream);
+}
+
+pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t q_dtype, const void* k_pages, const void* v_pages,
+                                     const float* k_scales, const float* v_scales, int64_t num_blocks,
+                                     int32_t block_size, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, int32_t max_seq_len, float scale, void* workspace,
+                                     size_t workspace_bytes, float* out, void* stream) {
+  pkv::clear_error();
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn_fp8: q dtype %d", q_dtype);
+  if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: null scales");
+  if ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & 3u)
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: scales must be 4-byte aligned");
+  return decode_impl(2 + q_dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, k_scales, v_scales,
+                     num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, nullptr,
+                     workspace, workspace_bytes, out, stream);
 }
 
 size_t pkv_extend_workspace_bytes(const pkv_plan* plan, int32_t head_dim) {

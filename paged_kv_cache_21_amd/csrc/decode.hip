@@ -195,10 +195,18 @@ __device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, in
 #define PKV_SPLIT_WAVES_PER_EU 1
 #endif
 
+// DT: BF16 / F16 pages, or FP8<BF16> / FP8<F16> (E4M3 codes with per-(block, head,
+// row) scales; q and the arithmetic in the 16-bit type).  A lane always holds 8
+// consecutive elements of a token row: one 16-byte load for 16-bit pages, one
+// 8-byte load for FP8 pages, widened to 16-bit values before the math.
 template <class DT, int D, int G, int LPT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
+  typedef typename is_fp8<DT>::compute CT;  // type of q and of the dot products
+  constexpr bool Q8 = is_fp8<DT>::value;
+  constexpr int EB = Q8 ? 1 : 2;  // bytes per stored element
+  typedef typename std::conditional<Q8, u32x2, u32x4>::type KV;  // a lane's 8 stored elements
   constexpr int ROWS = 64 / LPT;      // token rows per wave
-  constexpr int VPL = D / (8 * LPT);  // 16-byte vectors per token per lane
+  constexpr int VPL = D / (8 * LPT);  // 8-element vectors per token per lane
   constexpr int TPB = 16 / ROWS;      // tokens per lane per 16-token block
   static_assert(VPL >= 1 && TPB >= 1 && ROWS * TPB == 16, "unsupported lane split");
 
@@ -254,14 +262,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
 
   const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;  // elements between consecutive tokens
   const int64_t blk_stride = 16 * tok_stride;
-  // Byte offsets of this lane's 16-byte pieces inside one (block, KV head): 32-bit and
+  // Byte offsets of this lane's pieces inside one (block, KV head): 32-bit and
   // fixed for the whole kernel, so each load is a uniform base plus one of these.
   uint32_t voff[TPB][VPL];
 #pragma unroll
   for (int t = 0; t < TPB; ++t)
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
-      voff[t][v] = static_cast<uint32_t>(((r + t * ROWS) * tok_stride + (v * LPT + c) * 8) * 2);
+      voff[t][v] = static_cast<uint32_t>(((r + t * ROWS) * tok_stride + (v * LPT + c) * 8) * EB);
 
   // Block ids come from a 64-entry window of the row's table held one per lane, so
   // the K/V loads of the next block are addressed without a memory round trip
@@ -288,21 +296,40 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
       for (int v = 0; v < VPL; ++v) qq[g][v] = ld16(qh + v * LPT * 8);
     }
   };
-  auto load_block = [&](const Cursor& p, u32x4(&kk)[TPB][VPL], u32x4(&vv)[TPB][VPL]) -> bool {
+  // FP8 scales the lane needs per block: the reduce-scatter path owns one token's
+  // scores (token r + (c / G) * ROWS), the other path all TPB of its tokens
+  constexpr bool RS = LPT == 16 && TPB * G == 16;
+  constexpr int NS = RS ? 1 : TPB;
+  auto load_block = [&](const Cursor& p, KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL], float(&ks)[NS],
+                        float(&vs)[NS]) -> bool {
     // the id and head are the same in every lane; readfirstlane makes that explicit so the
     // loads use a scalar base with the per-lane 32-bit offsets
     const int id = __builtin_amdgcn_readfirstlane(block_id(p));
     const int h = __builtin_amdgcn_readfirstlane(p.h);
     const bool ok = id >= 0 && static_cast<int64_t>(id) < a.num_blocks;
-    const int64_t base = static_cast<int64_t>(ok ? id : 0) * blk_stride + static_cast<int64_t>(h) * D;
-    const char* kb = reinterpret_cast<const char*>(a.k_pages + base);
-    const char* vb = reinterpret_cast<const char*>(a.v_pages + base);
+    const int64_t base = (static_cast<int64_t>(ok ? id : 0) * blk_stride + static_cast<int64_t>(h) * D) * EB;
+    const char* kb = reinterpret_cast<const char*>(a.k_pages) + base;
+    const char* vb = reinterpret_cast<const char*>(a.v_pages) + base;
 #pragma unroll
     for (int t = 0; t < TPB; ++t) {
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        kk[t][v] = ld16_stream(kb + voff[t][v]);
-        vv[t][v] = ld16_stream(vb + voff[t][v]);
+        if constexpr (Q8) {
+          kk[t][v] = ld8_stream(kb + voff[t][v]);
+          vv[t][v] = ld8_stream(vb + voff[t][v]);
+        } else {
+          kk[t][v] = ld16_stream(kb + voff[t][v]);
+          vv[t][v] = ld16_stream(vb + voff[t][v]);
+        }
+      }
+    }
+    if constexpr (Q8) {
+      const int64_t sbase = (static_cast<int64_t>(ok ? id : 0) * Hkv + h) * 16;
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        const int row = r + (RS ? c / G : t) * ROWS;
+        ks[t] = a.k_scales[sbase + row];
+        vs[t] = a.v_scales[sbase + row];
       }
     }
     return ok;
@@ -315,7 +342,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   // are reduce-scattered so lane c owns the score of token c / G, head c % G; the max,
   // the exponential and the running (m, l) are then computed once per score instead of
   // once per lane, and the weights are broadcast back with row_newbcast for the PV update.
-  constexpr bool RS = LPT == 16 && TPB * G == 16;
+  // (RS and NS are defined with load_block.)
   float m[G], l[G], acc[G][VPL * 8];
   float m1 = kNegInf, l1 = 0.f;  // reduce-scatter state: head c % G of this token row
   auto reset_state = [&]() {
@@ -333,20 +360,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
 
   // Zero the values of tokens past the row's length (or of a whole block with a bad
   // id): their weight is 0, and 0 * (stale Inf / NaN) must not reach the sums.
-  auto mask_values = [&](bool ok, u32x4(&vv)[TPB][VPL]) {
+  auto mask_values = [&](bool ok, KV(&vv)[TPB][VPL]) {
     const int tok0 = (cur.blk0 + cur.j) * 16;
     if (!ok || tok0 + 16 > cur.len) {  // uniform: only a row's last block can be partial
 #pragma unroll
       for (int t = 0; t < TPB; ++t) {
         const bool valid = ok && tok0 + r + t * ROWS < cur.len;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v) vv[t][v] = valid ? vv[t][v] : u32x4{0, 0, 0, 0};
+        for (int v = 0; v < VPL; ++v) vv[t][v] = valid ? vv[t][v] : KV{};
       }
     }
   };
 
+  // a lane's 8 stored elements as 8 CT values (FP8 codes widened exactly)
+  auto as16 = [&](const KV& x) -> u32x4 {
+    if constexpr (Q8)
+      return widen8<CT>(x);
+    else
+      return x;
+  };
+
   // reduce-scatter path (RS): sc[t][g] holds this lane's partial q.k sums
-  auto consume_rs = [&](bool ok, float(&sc)[TPB][G], const u32x4(&vv)[TPB][VPL]) {
+  auto consume_rs = [&](bool ok, float(&sc)[TPB][G], const KV(&vv)[TPB][VPL], const float(&ks)[NS],
+                        const float(&vs)[NS]) {
     const bool b3 = c & 8, b2 = c & 4, b1 = c & 2, b0 = c & 1;
     float y[8], z[4], u[2];
     // stage bit 3 (partner c^8): keep scores k with bit 3 of k equal to bit 3 of c, k = t*G + g
@@ -362,7 +398,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
 #pragma unroll
     for (int j = 0; j < 2; ++j) u[j] = (b1 ? z[j + 2] : z[j]) + dpp_f32<kDppQuadXor2>(b1 ? z[j] : z[j + 2]);
     // stage bit 0 (partner c^1): lane c now holds the full score of k = c
-    float sv = ((b0 ? u[1] : u[0]) + dpp_f32<kDppQuadXor1>(b0 ? u[0] : u[1])) * a.scale_log2;
+    float sv = ((b0 ? u[1] : u[0]) + dpp_f32<kDppQuadXor1>(b0 ? u[0] : u[1])) *
+               (Q8 ? a.scale_log2 * ks[0] : a.scale_log2);  // FP8: the owned token's K scale
     const int tok0 = (cur.blk0 + cur.j) * 16;
     if (!ok || tok0 + 16 > cur.len) {  // uniform: only a row's last block can be partial
       const bool valid = ok && tok0 + r + (c / G) * ROWS < cur.len;
@@ -386,30 +423,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
     const float p = fast_exp2(sv - fmaxf(m1, -3.0e38f));
     l1 += p;
+    // FP8: the V scale of the owned token folds into its weight (a zero weight stays
+    // zero whatever a masked token's scale holds)
+    const float pv = Q8 ? (p == 0.f ? 0.f : p * vs[0]) : p;
 #pragma unroll
     for (int t = 0; t < TPB; ++t) {
       float vf[VPL * 8];
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        vf[v * 8 + 0] = DT::lo(vv[t][v].x);
-        vf[v * 8 + 1] = DT::hi(vv[t][v].x);
-        vf[v * 8 + 2] = DT::lo(vv[t][v].y);
-        vf[v * 8 + 3] = DT::hi(vv[t][v].y);
-        vf[v * 8 + 4] = DT::lo(vv[t][v].z);
-        vf[v * 8 + 5] = DT::hi(vv[t][v].z);
-        vf[v * 8 + 6] = DT::lo(vv[t][v].w);
-        vf[v * 8 + 7] = DT::hi(vv[t][v].w);
+        const u32x4 w4 = as16(vv[t][v]);
+        vf[v * 8 + 0] = CT::lo(w4.x);
+        vf[v * 8 + 1] = CT::hi(w4.x);
+        vf[v * 8 + 2] = CT::lo(w4.y);
+        vf[v * 8 + 3] = CT::hi(w4.y);
+        vf[v * 8 + 4] = CT::lo(w4.z);
+        vf[v * 8 + 5] = CT::hi(w4.z);
+        vf[v * 8 + 6] = CT::lo(w4.w);
+        vf[v * 8 + 7] = CT::hi(w4.w);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float pk = row_bcast_f32(p, t * G + g);
+        const float pk = row_bcast_f32(pv, t * G + g);
 #pragma unroll
         for (int e = 0; e < VPL * 8; ++e) acc[g][e] = fmaf(pk, vf[e], acc[g][e]);
       }
     }
   };
 
-  auto consume_block = [&](bool ok, const u32x4(&kk)[TPB][VPL], u32x4(&vv)[TPB][VPL]) {
+  auto consume_block = [&](bool ok, const KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL], const float(&ks)[NS],
+                           const float(&vs)[NS]) {
     mask_values(ok, vv);
     float sc[TPB][G];
 #pragma unroll
@@ -419,16 +461,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
         float x = 0.f;
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          x = DT::dot2(kk[t][v].x, qv[g][v].x, x);
-          x = DT::dot2(kk[t][v].y, qv[g][v].y, x);
-          x = DT::dot2(kk[t][v].z, qv[g][v].z, x);
-          x = DT::dot2(kk[t][v].w, qv[g][v].w, x);
+          const u32x4 kw = as16(kk[t][v]);
+          x = CT::dot2(kw.x, qv[g][v].x, x);
+          x = CT::dot2(kw.y, qv[g][v].y, x);
+          x = CT::dot2(kw.z, qv[g][v].z, x);
+          x = CT::dot2(kw.w, qv[g][v].w, x);
         }
         sc[t][g] = x;
       }
     }
     if constexpr (RS) {
-      consume_rs(ok, sc, vv);
+      consume_rs(ok, sc, vv, ks, vs);
       return;
     }
     // sum over the LPT lanes of each token row, one DPP step at a time across all
@@ -458,9 +501,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
         for (int g = 0; g < G; ++g) sc[t][g] += dpp_f32<kDppRowMirror>(sc[t][g]);
     }
 #pragma unroll
-    for (int t = 0; t < TPB; ++t)
+    for (int t = 0; t < TPB; ++t) {
+      const float f = Q8 ? a.scale_log2 * ks[t < NS ? t : 0] : a.scale_log2;  // FP8: the token's K scale
 #pragma unroll
-      for (int g = 0; g < G; ++g) sc[t][g] *= a.scale_log2;
+      for (int g = 0; g < G; ++g) sc[t][g] *= f;
+    }
     const int tok0 = (cur.blk0 + cur.j) * 16;
     if (!ok || tok0 + 16 > cur.len) {  // uniform: only a row's last block can be partial
 #pragma unroll
@@ -495,14 +540,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
       float vf[VPL * 8];
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        vf[v * 8 + 0] = DT::lo(vv[t][v].x);
-        vf[v * 8 + 1] = DT::hi(vv[t][v].x);
-        vf[v * 8 + 2] = DT::lo(vv[t][v].y);
-        vf[v * 8 + 3] = DT::hi(vv[t][v].y);
-        vf[v * 8 + 4] = DT::lo(vv[t][v].z);
-        vf[v * 8 + 5] = DT::hi(vv[t][v].z);
-        vf[v * 8 + 6] = DT::lo(vv[t][v].w);
-        vf[v * 8 + 7] = DT::hi(vv[t][v].w);
+        const u32x4 w4 = as16(vv[t][v]);
+        vf[v * 8 + 0] = CT::lo(w4.x);
+        vf[v * 8 + 1] = CT::hi(w4.x);
+        vf[v * 8 + 2] = CT::lo(w4.y);
+        vf[v * 8 + 3] = CT::hi(w4.y);
+        vf[v * 8 + 4] = CT::lo(w4.z);
+        vf[v * 8 + 5] = CT::hi(w4.z);
+        vf[v * 8 + 6] = CT::lo(w4.w);
+        vf[v * 8 + 7] = CT::hi(w4.w);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -510,8 +556,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
         // 2^(-inf - m) = 0 without a branch
         const float p = fast_exp2(sc[t][g] - fmaxf(m[g], -3.0e38f));
         l[g] += p;
+        const float pw = Q8 ? (p == 0.f ? 0.f : p * vs[t < NS ? t : 0]) : p;  // FP8: the token's V scale
 #pragma unroll
-        for (int e = 0; e < VPL * 8; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+        for (int e = 0; e < VPL * 8; ++e) acc[g][e] = fmaf(pw, vf[e], acc[g][e]);
       }
     }
   };
@@ -605,15 +652,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   // Every load is issued on every path (after the last block, block i is read
   // again: an L2 hit), so the compiler's wait counts never have to assume the
   // worst of two paths, which would make the wave wait for loads it does not need.
-  u32x4 ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL];
-  bool ok_a = load_block(pre, ka, va), ok_b = false;
-  auto step = [&](int i, bool ok_cur, const u32x4(&kc)[TPB][VPL], u32x4(&vc)[TPB][VPL],
-                  u32x4(&kn)[TPB][VPL], u32x4(&vn)[TPB][VPL], bool& ok_next) {
+  KV ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL];
+  float ksa[NS], vsa[NS], ksb[NS], vsb[NS];  // FP8 scales of the two blocks in flight
+  bool ok_a = load_block(pre, ka, va, ksa, vsa), ok_b = false;
+  auto step = [&](int i, bool ok_cur, const KV(&kc)[TPB][VPL], KV(&vc)[TPB][VPL], const float(&ksc)[NS],
+                  const float(&vsc)[NS], KV(&kn)[TPB][VPL], KV(&vn)[TPB][VPL], float(&ksn)[NS], float(&vsn)[NS],
+                  bool& ok_next) {
     const bool more = i + 1 < count;
     if (more) advance(pre, a);
     load_q(pre, qn);
-    ok_next = load_block(pre, kn, vn);
-    consume_block(ok_cur, kc, vc);
+    ok_next = load_block(pre, kn, vn, ksn, vsn);
+    consume_block(ok_cur, kc, vc, ksc, vsc);
     if (!more || cur.j + 1 == cur.nb) {
       finish_segment();
       if (more) {
@@ -630,10 +679,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   };
   int i = 0;
   for (; i + 1 < count; i += 2) {
-    step(i, ok_a, ka, va, kb, vb, ok_b);
-    step(i + 1, ok_b, kb, vb, ka, va, ok_a);
+    step(i, ok_a, ka, va, ksa, vsa, kb, vb, ksb, vsb, ok_b);
+    step(i + 1, ok_b, kb, vb, ksb, vsb, ka, va, ksa, vsa, ok_a);
   }
-  if (i < count) step(i, ok_a, ka, va, kb, vb, ok_b);
+  if (i < count) step(i, ok_a, ka, va, ksa, vsa, kb, vb, ksb, vsb, ok_b);
 }
 
 // ---------------------------------------------------------------------------
@@ -758,7 +807,105 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Append into FP8 pages.  Copy-on-write work-groups copy the codes of rows
+// [0, rows) and their per-head scales; token work-groups quantize each new
+// token's KV-head vectors: amax over the head, scale 2^k with k the smallest
+// exponent (clamped to [-126, 127]) keeping amax / 2^k <= 448, then every
+// element x * 2^-k rounded to the nearest E4M3 code, ties to even (the
+// hardware conversion; |x * 2^-k| <= 448 so nothing saturates).  One thread
+// per 8 elements, the threads of a head contiguous within a wave.
+template <class ST, int D>
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendArgs a) {
+  constexpr int TPH = D / 8;  // threads per head vector
+  const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * D;  // code bytes per token row
+  const int Hkv = a.num_kv_heads;
+  uint8_t* kp = reinterpret_cast<uint8_t*>(a.k_pages);
+  uint8_t* vp = reinterpret_cast<uint8_t*>(a.v_pages);
+  if (static_cast<int>(blockIdx.x) < a.num_cow) {
+    const int cidx = blockIdx.x;
+    const int src = a.cow_src[cidx], dst = a.cow_dst[cidx], rows = a.cow_rows[cidx];
+    if (src < 0 || dst < 0 || static_cast<int64_t>(src) >= a.num_blocks || static_cast<int64_t>(dst) >= a.num_blocks ||
+        rows <= 0 || rows > a.block_size)
+      return;
+    const int64_t n = static_cast<int64_t>(rows) * row_bytes / 16;  // 16-byte vectors (row_bytes % 16 == 0)
+    const u32x4* ks = reinterpret_cast<const u32x4*>(kp + static_cast<int64_t>(src) * a.block_size * row_bytes);
+    const u32x4* vs = reinterpret_cast<const u32x4*>(vp + static_cast<int64_t>(src) * a.block_size * row_bytes);
+    u32x4* kd = reinterpret_cast<u32x4*>(kp + static_cast<int64_t>(dst) * a.block_size * row_bytes);
+    u32x4* vd = reinterpret_cast<u32x4*>(vp + static_cast<int64_t>(dst) * a.block_size * row_bytes);
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+      kd[i] = ks[i];
+      vd[i] = vs[i];
+    }
+    for (int i = threadIdx.x; i < Hkv * rows; i += blockDim.x) {
+      const int h = i / rows, r = i % rows;
+      a.k_scales[(static_cast<int64_t>(dst) * Hkv + h) * a.block_size + r] =
+          a.k_scales[(static_cast<int64_t>(src) * Hkv + h) * a.block_size + r];
+      a.v_scales[(static_cast<int64_t>(dst) * Hkv + h) * a.block_size + r] =
+          a.v_scales[(static_cast<int64_t>(src) * Hkv + h) * a.block_size + r];
+    }
+    return;
+  }
+  const int t = blockIdx.x - a.num_cow;
+  const int64_t slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= a.num_blocks * a.block_size) return;
+  const int64_t blk = slot / a.block_size;
+  const int row = static_cast<int>(slot % a.block_size);
+  auto quantize = [&](const uint16_t* src, uint8_t* pages, float* scales, int i) {
+    // thread i: elements 8 (i % TPH) .. +8 of head i / TPH
+    const int h = i / TPH, part = i % TPH;
+    const u32x4 w = ld16(src + static_cast<int64_t>(t) * row_bytes + h * D + part * 8);
+    float x[8] = {ST::lo(w.x), ST::hi(w.x), ST::lo(w.y), ST::hi(w.y), ST::lo(w.z), ST::hi(w.z), ST::lo(w.w),
+                  ST::hi(w.w)};
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = group_max<TPH>(amax);
+    int k = 0;
+    if (amax > 0.f) {
+      int e2;
+      const float m2 = frexpf(amax, &e2);  // amax = m2 * 2^e2, m2 in [0.5, 1)
+      k = m2 <= 0.875f ? e2 - 9 : e2 - 8;
+      k = min(max(k, -126), 127);
+    }
+    const float inv = ldexpf(1.f, -k);
+    uint32_t c0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, 0, false);
+    c0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * inv, x[3] * inv, c0, true);
+    uint32_t c1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] * inv, x[5] * inv, 0, false);
+    c1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] * inv, x[7] * inv, c1, true);
+    *reinterpret_cast<u32x2*>(pages + slot * row_bytes + h * D + part * 8) = u32x2{c0, c1};
+    if (part == 0) scales[(blk * Hkv + h) * a.block_size + row] = ldexpf(1.f, k);
+  };
+  const uint16_t* kn = a.k_new;
+  const uint16_t* vn = a.v_new;
+  // blockDim.x (256) is a multiple of TPH, so a head's threads stay within one wave
+  for (int i = threadIdx.x; i < Hkv * TPH; i += blockDim.x) {
+    quantize(kn, kp, a.k_scales, i);
+    quantize(vn, vp, a.v_scales, i);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
+
+hipError_t launch_kv_append_fp8(int src_dtype, const AppendArgs& a, hipStream_t stream) {
+  const int64_t grid = static_cast<int64_t>(a.num_cow) + a.num_tokens;
+  if (grid <= 0) return hipSuccess;
+  const dim3 g(static_cast<unsigned>(grid)), b(256);
+  if (a.head_dim == 128) {
+    if (src_dtype == 1)
+      hipLaunchKernelGGL((kv_append_fp8_kernel<BF16, 128>), g, b, 0, stream, a);
+    else
+      hipLaunchKernelGGL((kv_append_fp8_kernel<F16, 128>), g, b, 0, stream, a);
+  } else if (a.head_dim == 64) {
+    if (src_dtype == 1)
+      hipLaunchKernelGGL((kv_append_fp8_kernel<BF16, 64>), g, b, 0, stream, a);
+    else
+      hipLaunchKernelGGL((kv_append_fp8_kernel<F16, 64>), g, b, 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>(a.num_cow) + a.num_tokens;
@@ -843,11 +990,23 @@ int waves_d(int head_dim, int group) {
 }  // namespace
 
 int decode_split_waves(int dtype, int head_dim, int group) {
-  return dtype == 1 ? waves_d<BF16>(head_dim, group) : waves_d<F16>(head_dim, group);
+  switch (dtype) {
+    case 0: return waves_d<F16>(head_dim, group);
+    case 1: return waves_d<BF16>(head_dim, group);
+    case 2: return waves_d<FP8<F16>>(head_dim, group);
+    case 3: return waves_d<FP8<BF16>>(head_dim, group);
+    default: return 0;
+  }
 }
 
 hipError_t launch_decode_split(int dtype, int head_dim, int group, const SplitArgs& a, hipStream_t stream) {
-  return dtype == 1 ? launch_split_d<BF16>(head_dim, group, a, stream) : launch_split_d<F16>(head_dim, group, a, stream);
+  switch (dtype) {
+    case 0: return launch_split_d<F16>(head_dim, group, a, stream);
+    case 1: return launch_split_d<BF16>(head_dim, group, a, stream);
+    case 2: return launch_split_d<FP8<F16>>(head_dim, group, a, stream);
+    case 3: return launch_split_d<FP8<BF16>>(head_dim, group, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_merge(int head_dim, const MergeArgs& a, hipStream_t stream) {

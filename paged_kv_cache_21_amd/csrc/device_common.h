@@ -60,6 +60,64 @@ struct F16 {
   }
 };
 
+// FP8 pages: OCP E4M3 codes, one byte per element, with a power-of-two scale per
+// (block, KV head, token row); q and the arithmetic use the 16-bit type CT.
+// Every E4M3 value is exact in bf16 and in f16, so a code widens to CT exactly
+// (through the hardware's E4M3 -> fp32 conversion).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <class CT>
+struct FP8 {
+  typedef CT compute;
+};
+
+template <class T>
+struct is_fp8 {
+  static constexpr bool value = false;
+  typedef T compute;
+};
+template <class CT>
+struct is_fp8<FP8<CT>> {
+  static constexpr bool value = true;
+  typedef CT compute;
+};
+
+// four E4M3 codes (one word) -> two words of CT pairs (codes 0,1 and 2,3)
+template <class CT>
+__device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi);
+
+template <>
+__device__ __forceinline__ void widen4<BF16>(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  // one conversion per code: combining the two fp32 halves of the packed conversion's
+  // register pair was miscompiled (the second half read as the first)
+  const uint32_t c0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 0));
+  const uint32_t c1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 1));
+  const uint32_t c2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 2));
+  const uint32_t c3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 3));
+  // the values have at most 4 significant bits: the upper half of each fp32 is exact
+  lo = (c0 >> 16) | (c1 & 0xffff0000u);
+  hi = (c2 >> 16) | (c3 & 0xffff0000u);
+}
+
+template <>
+__device__ __forceinline__ void widen4<F16>(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  // every E4M3 value is exact in f16, so the round-toward-zero packing is exact
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_cvt_f32_fp8(w, 0),
+                                                               __builtin_amdgcn_cvt_f32_fp8(w, 1)));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_cvt_f32_fp8(w, 2),
+                                                               __builtin_amdgcn_cvt_f32_fp8(w, 3)));
+}
+
+// eight E4M3 codes -> eight CT values packed as in a 16-bit page vector
+template <class CT>
+__device__ __forceinline__ u32x4 widen8(u32x2 w) {
+  uint32_t a, b, c, d;
+  widen4<CT>(w.x, a, b);
+  widen4<CT>(w.y, c, d);
+  return u32x4{a, b, c, d};
+}
+
 // ---------------------------------------------------------------------------
 // Lane exchanges inside a wave64.
 
@@ -124,6 +182,16 @@ __device__ __forceinline__ void pair_values(float x, float& lo, float& hi) {
   }
 }
 
+// Max over groups of N consecutive lanes (N in 1, 2, 4, 8, 16).
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return x;
+}
+
 __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
   const int lane = __lane_id();
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
@@ -142,6 +210,13 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 #ifndef PKV_NT_LOADS
 #define PKV_NT_LOADS 1
 #endif
+__device__ __forceinline__ u32x2 ld8_stream(const void* p) {
+#if PKV_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+#else
+  return *reinterpret_cast<const u32x2*>(p);
+#endif
+}
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 #if PKV_NT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

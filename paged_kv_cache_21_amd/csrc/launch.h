@@ -9,8 +9,12 @@
 namespace pkv {
 
 struct AppendArgs {
-  uint16_t* k_pages;
+  uint16_t* k_pages;  // 16-bit pages; FP8 pages: byte arrays (cast)
   uint16_t* v_pages;
+  float* k_scales;    // FP8 pages: [num_blocks][num_kv_heads][block_size] (else null)
+  float* v_scales;
+  int32_t num_kv_heads;
+  int32_t head_dim;
   int64_t num_blocks;
   int32_t block_size;
   int32_t row_elems;  // num_kv_heads * head_dim
@@ -40,6 +44,8 @@ struct SplitArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const int32_t* row_info;  // [batch][2] = (shared tokens, depth) from a cascade plan, or null
+  const float* k_scales;    // FP8 pages: [num_blocks][num_kv_heads][16] per-row scales (else null)
+  const float* v_scales;
   float* acc;
   float2* ml;
   int32_t* counts;  // [batch][num_kv_heads] partials per segment (written for non-empty segments)
@@ -101,7 +107,10 @@ constexpr int kNodeInts = 8;             // ints per node record of a plan image
 constexpr int kMemberInts = 3;           // ints per member entry of a plan image
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
-// dtype: 0 f16, 1 bf16.  Returns hipErrorInvalidValue for shapes not built.
+// FP8 pages: quantize each new token's head vectors; src_dtype 0 f16, 1 bf16 for k_new / v_new.
+hipError_t launch_kv_append_fp8(int src_dtype, const AppendArgs& a, hipStream_t stream);
+// dtype: 0 f16, 1 bf16 (q and pages); 2 FP8 pages with f16 q, 3 FP8 pages with bf16 q.
+// Returns hipErrorInvalidValue for shapes not built.
 hipError_t launch_decode_split(int dtype, int head_dim, int group, const SplitArgs& a, hipStream_t stream);
 // Waves the split kernel runs as for these shapes on the current device (all resident at once).
 int decode_split_waves(int dtype, int head_dim, int group);

@@ -163,6 +163,26 @@ def make_pages(w: Workload, device="cpu"):
     return k, v
 
 
+def make_fp8_pages(w: Workload, device="cpu"):
+    """FP8 pages for a workload: random E4M3 codes of magnitude 2^-2 .. 2^5 with random signs,
+    and per-(block, head, row) power-of-two scales 2^-5 or 2^-4 (elements of magnitude about
+    2^-7 .. 2^1, like quantized N(0, 1) data).  Returns (k_codes, v_codes, k_scales, v_scales)
+    as uint8 [num_blocks, block_size, Hkv, d] and float32 [num_blocks, Hkv, block_size]."""
+    torch = _torch()
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(w.seed) * 7 + 3)
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    out = []
+    for _ in range(2):
+        mag = torch.randint(0x28, 0x61, shape, generator=gen, device=device, dtype=torch.int32)
+        sign = torch.randint(0, 2, shape, generator=gen, device=device, dtype=torch.int32) * 0x80
+        out.append((mag | sign).to(torch.uint8))
+    for _ in range(2):
+        e = torch.randint(-5, -3, (w.num_blocks, w.num_kv_heads, w.block_size), generator=gen, device=device)
+        out.append(torch.exp2(e.to(torch.float32)))
+    return tuple(out)
+
+
 def make_q(w: Workload, step: int = 0, device="cpu"):
     """Queries for step ``step`` as an int16 bit tensor [B, Hq, d]."""
     return _normal_bits((len(w.steps[step].decode_rows), w.num_q_heads, w.head_dim), w.dtype,
