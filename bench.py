@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 (E4M3) pages with per-row scales: quantizing append + FP8 decode (configs 2 and 4)")
     ap.add_argument("--extend", action="store_true",
                     help="time the multi-token pass (configs 3: verify 8 tokens per branch, 6: chunked prefill)")
     ap.add_argument("--no-cascade", action="store_true", help="decode every row on its own (no shared-prefix pass)")
@@ -257,6 +259,83 @@ def run_extend(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def run_fp8(args, w, dev):
+    """Append + decode over FP8 pages (no shared-prefix pass): the decode's K/V bytes halve."""
+    import torch
+
+    import paged_kv_cache_21_amd as pkv
+    import workloads
+
+    kc, vc, ks, vs = workloads.make_fp8_pages(w, device=dev)
+    pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(pool, w.build_ops)
+    slots, cows = pool.plan_append(w.steps[0].append_rows)
+    assert len(cows) == 0
+    bt, lens = pool.export_tables(w.steps[0].decode_rows, w.max_blocks)
+    q = workloads.make_q(w, 0, device=dev)
+    k_new, v_new = workloads.make_new_tokens(w, 0, device=dev)
+    slot_d, bt_d, lens_d = (torch.from_numpy(x).to(dev) for x in (slots, bt, lens))
+    max_len = int(lens.max())
+    B = len(lens)
+    ws = torch.empty(max(pkv.decode_workspace_bytes(B, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len), 16),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step():
+        pkv.kv_append_fp8(kc, vc, ks, vs, k_new, v_new, slot_d, src_dtype=w.dtype, stream=stream)
+        pkv.paged_decode_attn_fp8(q, kc, vc, ks, vs, bt_d, lens_d, max_len, scale=w.scale, workspace=ws, out=out,
+                                  q_dtype=w.dtype, stream=stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / max(args.steps, 1)
+    pkv.timing_reset()
+    pkv.timing_enable(True)
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    pkv.timing_enable(False)
+    kern = {}
+    for name in ("append", "decode_split", "merge"):
+        total, count = pkv.timing_read(name)
+        kern[name] = {"avg_us": round(total / count * 1e3, 3) if count else 0.0, "launches": count}
+    # bytes per token of one layer: codes (1 B per element, K and V) + one fp32 scale per head for K and V
+    per_token = w.num_kv_heads * (2 * w.head_dim + 2 * 4)
+    tokens = int(lens.sum())
+    q_bytes = B * w.num_q_heads * w.head_dim * 2
+    split_bytes = tokens * per_token + q_bytes
+    U = split_bytes + B * w.num_q_heads * w.head_dim * 4 + bt.nbytes + lens.nbytes
+    t_split = kern["decode_split"]["avg_us"] * 1e-6
+    achieved = split_bytes / t_split / 1e9 if t_split > 0 else 0.0
+    res = {
+        "metric": "paged decode attn over FP8 pages: effective KV GB/s, decode queries/s",
+        "value": round(U / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.description}; K/V as E4M3 codes with per-row fp32 power-of-two scales",
+                   "batch": B, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "q_dtype": w.dtype, "accumulate": "f32", "parallelism": "single GPU"},
+        "decode_queries_per_s": round(B / (ms * 1e-3), 1),
+        "tokens_per_s_equivalent_16bit_gbs": round(tokens * w.bytes_per_token / (ms * 1e-3) / 1e9, 1),
+        "kernels": kern,
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel<FP8>", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": kern["decode_split"]["avg_us"]},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -279,6 +358,8 @@ def main():
     print(f"[bench] workload {w.number} {w.name}: {w.description}", file=sys.stderr, flush=True)
     if args.extend or args.config == 6:
         return run_extend(args, w, dev)
+    if args.fp8:
+        return run_fp8(args, w, dev)
 
     # ---- set-up (not timed): pages, pool, the step's append plan, tables, cascade plan
     k_pages, v_pages = workloads.make_pages(w, device=dev)

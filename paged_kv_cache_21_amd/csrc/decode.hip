@@ -335,8 +335,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     return ok;
   };
 
-  u32x4 qv[G][VPL], qn[G][VPL];
-  load_q(cur, qv);
   // Reduce-scatter softmax when a token row's TPB*G scores fill its LPT lanes exactly
   // (16 = 4 tokens x 4 heads for head_dim 128 with GQA group 4): the q.k partial sums
   // are reduce-scattered so lane c owns the score of token c / G, head c % G; the max,
@@ -378,6 +376,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
       return widen8<CT>(x);
     else
       return x;
+  };
+
+  // a lane's 8 stored elements as fp32 (FP8 codes converted directly)
+  auto to_f32 = [&](const KV& x, float* out) {
+    if constexpr (Q8) {
+      fp8x8_to_f32(x, out);
+    } else {
+      out[0] = CT::lo(x.x);
+      out[1] = CT::hi(x.x);
+      out[2] = CT::lo(x.y);
+      out[3] = CT::hi(x.y);
+      out[4] = CT::lo(x.z);
+      out[5] = CT::hi(x.z);
+      out[6] = CT::lo(x.w);
+      out[7] = CT::hi(x.w);
+    }
   };
 
   // reduce-scatter path (RS): sc[t][g] holds this lane's partial q.k sums
@@ -430,17 +444,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     for (int t = 0; t < TPB; ++t) {
       float vf[VPL * 8];
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const u32x4 w4 = as16(vv[t][v]);
-        vf[v * 8 + 0] = CT::lo(w4.x);
-        vf[v * 8 + 1] = CT::hi(w4.x);
-        vf[v * 8 + 2] = CT::lo(w4.y);
-        vf[v * 8 + 3] = CT::hi(w4.y);
-        vf[v * 8 + 4] = CT::lo(w4.z);
-        vf[v * 8 + 5] = CT::hi(w4.z);
-        vf[v * 8 + 6] = CT::lo(w4.w);
-        vf[v * 8 + 7] = CT::hi(w4.w);
-      }
+      for (int v = 0; v < VPL; ++v) to_f32(vv[t][v], vf + v * 8);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float pk = row_bcast_f32(pv, t * G + g);
@@ -450,8 +454,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
   };
 
-  auto consume_block = [&](bool ok, const KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL], const float(&ks)[NS],
-                           const float(&vs)[NS]) {
+  auto consume_block = [&](bool ok, const u32x4(&qv)[G][VPL], const KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL],
+                           const float(&ks)[NS], const float(&vs)[NS]) {
     mask_values(ok, vv);
     float sc[TPB][G];
 #pragma unroll
@@ -539,17 +543,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     for (int t = 0; t < TPB; ++t) {
       float vf[VPL * 8];
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const u32x4 w4 = as16(vv[t][v]);
-        vf[v * 8 + 0] = CT::lo(w4.x);
-        vf[v * 8 + 1] = CT::hi(w4.x);
-        vf[v * 8 + 2] = CT::lo(w4.y);
-        vf[v * 8 + 3] = CT::hi(w4.y);
-        vf[v * 8 + 4] = CT::lo(w4.z);
-        vf[v * 8 + 5] = CT::hi(w4.z);
-        vf[v * 8 + 6] = CT::lo(w4.w);
-        vf[v * 8 + 7] = CT::hi(w4.w);
-      }
+      for (int v = 0; v < VPL; ++v) to_f32(vv[t][v], vf + v * 8);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         // m[g] is -inf only while every score so far is -inf; the finite floor keeps
@@ -648,41 +642,59 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
   };
 
-  // One step: load block i+1 and the q of its segment, consume block i, move on.
-  // Every load is issued on every path (after the last block, block i is read
-  // again: an L2 hit), so the compiler's wait counts never have to assume the
-  // worst of two paths, which would make the wave wait for loads it does not need.
-  KV ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL];
-  float ksa[NS], vsa[NS], ksb[NS], vsb[NS];  // FP8 scales of the two blocks in flight
-  bool ok_a = load_block(pre, ka, va, ksa, vsa), ok_b = false;
-  auto step = [&](int i, bool ok_cur, const KV(&kc)[TPB][VPL], KV(&vc)[TPB][VPL], const float(&ksc)[NS],
-                  const float(&vsc)[NS], KV(&kn)[TPB][VPL], KV(&vn)[TPB][VPL], float(&ksn)[NS], float(&vsn)[NS],
-                  bool& ok_next) {
-    const bool more = i + 1 < count;
-    if (more) advance(pre, a);
-    load_q(pre, qn);
-    ok_next = load_block(pre, kn, vn, ksn, vsn);
-    consume_block(ok_cur, kc, vc, ksc, vsc);
-    if (!more || cur.j + 1 == cur.nb) {
+  // The pipeline: NBUF register buffers, each holding one block's K/V (and FP8
+  // scales) plus the q of that block's segment; step i consumes block i and loads
+  // block i + NBUF - 1 (FP8 blocks are half the bytes, so they keep one more block
+  // in flight).  Every load is issued on every path (past the last block, the last
+  // one is read again: an L2 hit), so the compiler's wait counts never have to
+  // assume the worst of two paths, which would make the wave wait for loads it
+  // does not need.  (Separately named buffers, not an indexed array of them: the
+  // compiler keeps those in registers.)
+  constexpr int NBUF = Q8 ? 3 : 2;
+  KV ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL], kx[TPB][VPL], vx[TPB][VPL];
+  float ksa[NS], vsa[NS], ksb[NS], vsb[NS], ksx[NS], vsx[NS];
+  u32x4 qa[G][VPL], qb[G][VPL], qx[G][VPL];
+  bool ok_a, ok_b, ok_x = false;
+  load_q(pre, qa);
+  ok_a = load_block(pre, ka, va, ksa, vsa);
+  if constexpr (NBUF == 3) {
+    if (1 < count) advance(pre, a);
+    load_q(pre, qb);
+    ok_b = load_block(pre, kb, vb, ksb, vsb);
+  }
+  auto step = [&](int i, bool ok_cur, const u32x4(&q_cur)[G][VPL], const KV(&k_cur)[TPB][VPL], KV(&v_cur)[TPB][VPL],
+                  const float(&ks_cur)[NS], const float(&vs_cur)[NS], u32x4(&q_nxt)[G][VPL], KV(&k_nxt)[TPB][VPL],
+                  KV(&v_nxt)[TPB][VPL], float(&ks_nxt)[NS], float(&vs_nxt)[NS], bool& ok_nxt) {
+    if (i + NBUF - 1 < count) advance(pre, a);
+    load_q(pre, q_nxt);
+    ok_nxt = load_block(pre, k_nxt, v_nxt, ks_nxt, vs_nxt);
+    consume_block(ok_cur, q_cur, k_cur, v_cur, ks_cur, vs_cur);
+    if (i + 1 == count || cur.j + 1 == cur.nb) {
       finish_segment();
-      if (more) {
-        advance(cur, a);  // now at pre's block, whose segment's q is in qn
+      if (i + 1 < count) {
+        advance(cur, a);
         reset_state();
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) qv[g][v] = qn[g][v];
       }
     } else {
       ++cur.j;
     }
   };
   int i = 0;
-  for (; i + 1 < count; i += 2) {
-    step(i, ok_a, ka, va, ksa, vsa, kb, vb, ksb, vsb, ok_b);
-    step(i + 1, ok_b, kb, vb, ksb, vsb, ka, va, ksa, vsa, ok_a);
+  if constexpr (NBUF == 2) {
+    for (; i + 1 < count; i += 2) {
+      step(i, ok_a, qa, ka, va, ksa, vsa, qb, kb, vb, ksb, vsb, ok_b);
+      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, qa, ka, va, ksa, vsa, ok_a);
+    }
+    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, qb, kb, vb, ksb, vsb, ok_b);
+  } else {
+    for (; i + 2 < count; i += 3) {
+      step(i, ok_a, qa, ka, va, ksa, vsa, qx, kx, vx, ksx, vsx, ok_x);
+      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, qa, ka, va, ksa, vsa, ok_a);
+      step(i + 2, ok_x, qx, kx, vx, ksx, vsx, qb, kb, vb, ksb, vsb, ok_b);
+    }
+    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, qx, kx, vx, ksx, vsx, ok_x);
+    if (i + 1 < count) step(i + 1, ok_b, qb, kb, vb, ksb, vsb, qa, ka, va, ksa, vsa, ok_a);
   }
-  if (i < count) step(i, ok_a, ka, va, ksa, vsa, kb, vb, ksb, vsb, ok_b);
 }
 
 // ---------------------------------------------------------------------------

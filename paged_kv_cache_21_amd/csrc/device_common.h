@@ -83,30 +83,38 @@ struct is_fp8<FP8<CT>> {
   typedef CT compute;
 };
 
+// Two E4M3 codes (byte pair 0,1 or 2,3 of a word) converted to fp32, as floats and
+// as bit patterns.  Each consumer below uses the one view that hipcc compiles
+// correctly for it: bit-casting one element of the float pair was miscompiled
+// (element 1 read as element 0) in both directions we tried, so the bf16 packing
+// takes the pair through a 2 x u32 view and fp32 consumers take the floats as is.
+template <bool HIGH>
+__device__ __forceinline__ f32x2 fp8_pair_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH);
+}
+template <bool HIGH>
+__device__ __forceinline__ u32x2 fp8_pair_bits(uint32_t w) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH));
+}
+
 // four E4M3 codes (one word) -> two words of CT pairs (codes 0,1 and 2,3)
 template <class CT>
 __device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi);
 
 template <>
 __device__ __forceinline__ void widen4<BF16>(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  // one conversion per code: combining the two fp32 halves of the packed conversion's
-  // register pair was miscompiled (the second half read as the first)
-  const uint32_t c0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 0));
-  const uint32_t c1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 1));
-  const uint32_t c2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 2));
-  const uint32_t c3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_f32_fp8(w, 3));
+  const u32x2 a = fp8_pair_bits<false>(w), b = fp8_pair_bits<true>(w);
   // the values have at most 4 significant bits: the upper half of each fp32 is exact
-  lo = (c0 >> 16) | (c1 & 0xffff0000u);
-  hi = (c2 >> 16) | (c3 & 0xffff0000u);
+  lo = __builtin_amdgcn_perm(a.y, a.x, 0x07060302u);
+  hi = __builtin_amdgcn_perm(b.y, b.x, 0x07060302u);
 }
 
 template <>
 __device__ __forceinline__ void widen4<F16>(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const f32x2 a = fp8_pair_f32<false>(w), b = fp8_pair_f32<true>(w);
   // every E4M3 value is exact in f16, so the round-toward-zero packing is exact
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_cvt_f32_fp8(w, 0),
-                                                               __builtin_amdgcn_cvt_f32_fp8(w, 1)));
-  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_amdgcn_cvt_f32_fp8(w, 2),
-                                                               __builtin_amdgcn_cvt_f32_fp8(w, 3)));
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
 }
 
 // eight E4M3 codes -> eight CT values packed as in a 16-bit page vector
@@ -116,6 +124,20 @@ __device__ __forceinline__ u32x4 widen8(u32x2 w) {
   widen4<CT>(w.x, a, b);
   widen4<CT>(w.y, c, d);
   return u32x4{a, b, c, d};
+}
+
+// eight E4M3 codes -> eight fp32 values
+__device__ __forceinline__ void fp8x8_to_f32(u32x2 w, float* out) {
+  const f32x2 p0 = fp8_pair_f32<false>(w.x), p1 = fp8_pair_f32<true>(w.x);
+  const f32x2 p2 = fp8_pair_f32<false>(w.y), p3 = fp8_pair_f32<true>(w.y);
+  out[0] = p0.x;
+  out[1] = p0.y;
+  out[2] = p1.x;
+  out[3] = p1.y;
+  out[4] = p2.x;
+  out[5] = p2.y;
+  out[6] = p3.x;
+  out[7] = p3.y;
 }
 
 // ---------------------------------------------------------------------------
