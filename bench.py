@@ -51,9 +51,39 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=10,
                     help="extra steps each preceded by a 1 GiB write that evicts L2 and MALL (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline (0 = skip)")
+    ap.add_argument("--read-ceiling-gib", type=int, default=4,
+                    help="also time a plain streaming read of this many GiB (the read-bandwidth yardstick; 0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for scaling HBM counters)")
     return ap.parse_args()
+
+
+def read_ceiling(gib, dev):
+    """Best median GB/s of the library's plain streaming read over `gib` GiB, over a few grid sizes."""
+    import torch
+
+    import paged_kv_cache_21_amd as pkv
+
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = (0.0, 0)
+    for grid in (1024, 2048, 4096, 8192):
+        times = []
+        for it in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pkv.stream_read(buf, sink, grid)
+            e1.record()
+            torch.cuda.synchronize()
+            if it:
+                times.append(e0.elapsed_time(e1))
+        gbs = buf.numel() / (float(np.median(times)) * 1e-3) / 1e9
+        best = max(best, (gbs, grid))
+    del buf
+    torch.cuda.empty_cache()
+    return {"gbs": round(best[0], 1), "grid": best[1], "bytes": gib << 30,
+            "kernel": "stream_read_kernel (16-byte non-temporal loads, 4 in flight per thread)"}
 
 
 def unique_bytes(bt, lens, w):
@@ -477,6 +507,9 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, q, k_pages, v_pages, bt, lens, args.cpu_seconds)
+    ceiling = read_ceiling(args.read_ceiling_gib, dev) if args.read_ceiling_gib > 0 else None
+    if ceiling:
+        roofline["frac_of_measured_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
 
     res = {
         "metric": "paged decode attn: effective KV GB/s, % of HBM peak, decode queries/s",
@@ -504,6 +537,7 @@ def main():
         "cold_ms_per_step_median": round(float(np.median(cold)), 5) if cold else None,
         "host_us": {"plan_append": round(plan_append_us, 1), "plan_build": round(plan_build_us, 1)},
         "roofline": roofline,
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -356,6 +356,13 @@ int64_t pkv_plan_image(const pkv_plan* plan, int32_t* out, int64_t capacity, int
  * 2 partial merge, 3 cascade / extend matrix-core pass.  Costs two event
  * records per launch when on.
  * ---------------------------------------------------------------------------------------- */
+/* Measurement yardstick: read `bytes` (a multiple of 16) of device memory `buf` as
+ * a plain streaming read (16-byte loads, `grid` work-groups of 256 threads; 0 picks
+ * 2048) on `stream`.  `sink` (one device uint32) is written only in a case that
+ * practically never happens.  Time it with events to get the chip's read-stream
+ * ceiling beside the decode kernels' rates. */
+pkv_status pkv_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, void* stream);
+
 enum { PKV_KERNEL_APPEND = 0, PKV_KERNEL_DECODE_SPLIT = 1, PKV_KERNEL_MERGE = 2, PKV_KERNEL_CASCADE = 3,
        PKV_NUM_KERNELS = 4 };
 pkv_status pkv_timing_enable(int32_t on);

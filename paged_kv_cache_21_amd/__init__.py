@@ -24,7 +24,7 @@ __all__ = [
     "PkvError", "PkvInvalid", "PkvOOM", "PkvNotFound", "PkvUnsupported", "PkvWorkspaceError", "PkvHipError",
     "kv_append", "paged_decode_attn", "decode_workspace_bytes", "BlockPool", "CascadePlan",
     "ExtendPlan", "paged_extend_attn", "extend_workspace_bytes", "kv_append_fp8", "paged_decode_attn_fp8",
-    "timing_enable", "timing_reset", "timing_read", "KERNELS", "lib", "LIB_PATH", "version",
+    "timing_enable", "timing_reset", "timing_read", "stream_read", "KERNELS", "lib", "LIB_PATH", "version",
 ]
 
 # PKV_LIBRARY may point at another build of the same library (e.g. a tuning variant).
@@ -109,6 +109,7 @@ _SIGNATURES = {
                                  _vp, _i32, _vp]),
     "pkv_paged_decode_attn_fp8": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _vp,
                                          _i32, _vp, _i32, _f32, _vp, _sz, _vp, _vp]),
+    "pkv_stream_read": (_i32, [_vp, _i64, _vp, _i32, _vp]),
     "pkv_timing_enable": (_i32, [_i32]),
     "pkv_timing_reset": (_i32, []),
     "pkv_timing_read": (_i32, [_i32, _vp, _vp]),
@@ -542,6 +543,12 @@ def paged_extend_attn(q, k_pages, v_pages, plan, scale=None, workspace=None, out
 
 # ---------------------------------------------------------------------------
 # timing
+
+
+def stream_read(buf, sink, grid=0, stream=None):
+    """Plain streaming read of a device tensor (the read-bandwidth yardstick); sink: int32 [1] device."""
+    _check(_lib.pkv_stream_read(_ptr(buf), buf.numel() * buf.element_size() // 16 * 16, _ptr(sink), int(grid),
+                                _stream(stream, buf)))
 
 
 def timing_enable(on=True):

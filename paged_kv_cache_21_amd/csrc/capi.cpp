@@ -464,6 +464,17 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* device_buf, size_t bytes, void*
   return PKV_OK;
 }
 
+pkv_status pkv_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, void* stream) {
+  pkv::clear_error();
+  if (bytes < 0 || grid < 0 || (bytes > 0 && (!buf || !sink)))
+    return fail(PKV_ERR_INVALID, "pkv_stream_read: invalid arguments");
+  if (!pkv::aligned16(buf)) return fail(PKV_ERR_INVALID, "pkv_stream_read: buffer must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = pkv::launch_stream_read(buf, bytes, sink, grid > 0 ? grid : 2048, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_stream_read: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 pkv_status pkv_timing_enable(int32_t on) {
   pkv::clear_error();
   auto& t = pkv::timing();

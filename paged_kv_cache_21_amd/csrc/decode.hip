@@ -897,6 +897,30 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Read-stream ceiling: the bandwidth a plain streaming read of a large buffer
+// reaches on this chip (16-byte non-temporal loads, four in flight per thread),
+// the yardstick the decode kernels' HBM rates are compared with.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, int64_t n, uint32_t* sink) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride), d = __builtin_nontemporal_load(p + i + 3 * stride);
+    x ^= a.x ^ b.y ^ c.z ^ d.w;
+  }
+  for (; i < n; i += stride) x ^= __builtin_nontemporal_load(p + i).x;
+  if (x == 0x9e3779b9u) sink[0] = x;  // keeps the loads; practically never taken
+}
+
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int grid, hipStream_t stream) {
+  if (bytes < 16 || grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 
 hipError_t launch_kv_append_fp8(int src_dtype, const AppendArgs& a, hipStream_t stream) {

@@ -115,6 +115,7 @@ hipError_t launch_decode_split(int dtype, int head_dim, int group, const SplitAr
 // Waves the split kernel runs as for these shapes on the current device (all resident at once).
 int decode_split_waves(int dtype, int head_dim, int group);
 hipError_t launch_merge(int head_dim, const MergeArgs& a, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int grid, hipStream_t stream);
 hipError_t launch_cascade(int dtype, int head_dim, int group, const CascadeArgs& a, hipStream_t stream);
 
 }  // namespace pkv
