@@ -15,7 +15,9 @@ Everything here is written from the source pages:
   token -> logical-block arithmetic; section "Copy-on-Write and Advanced
   Decoding Strategies" for sharing prompt blocks and allocating on divergence;
   section "Chunked Prefill" (with the verification pass of "RKSC", §1) for
-  several new tokens attending causally at once.
+  several new tokens attending causally at once; section "RadixAttention" for
+  the prefix cache (with "RKSC", §2 C "RSBCM" for its score/depth eviction
+  order).
 
 Floating point is fp64.  fp16/bf16 inputs arrive as raw 16-bit patterns and
 are decoded here, independently of the GPU code.
@@ -31,6 +33,7 @@ from .extend import extend_query_positions, ref_extend
 from .fp8 import (apply_append_fp8, dequantize_heads, dequantize_pages, e4m3_decode, e4m3_encode,
                   pow2_scale_exponent, quantize_heads, ref_decode_fp8)
 from .pool import RefPool, RefPoolError, apply_append
+from .radix import RadixCache, RadixError
 
 __all__ = [
     "kv_bytes",
@@ -52,4 +55,6 @@ __all__ = [
     "RefPool",
     "RefPoolError",
     "apply_append",
+    "RadixCache",
+    "RadixError",
 ]

@@ -42,6 +42,13 @@ capacity overflow, which contradicts the prose; the prose wins):
       nothing changed.
 * R5  ``free(seq)`` lowers the counts in table order; a block reaching 0 goes to
       the back of the free pool.  An unknown sequence is a no-op.
+* R6  Holders other than sequences (a prefix cache) take and drop references
+      with ``retain`` / ``release``; ``alloc_with_prefix(seq, prefix, n)`` starts a
+      sequence on cached blocks ("Dismantling the Memory Wall", "RadixAttention":
+      a request that shares a cached prefix points at the existing memory and
+      only computes the new tokens): its table is ``prefix`` (one more reference
+      each) followed by fresh blocks for the rest of the n tokens, or MemoryError
+      with nothing changed.
 """
 
 from collections import deque
@@ -129,6 +136,45 @@ class RefPool:
                 self._free.append(b)
         del self._tables[seq]
         del self._lens[seq]
+
+    # -- R6 ----------------------------------------------------------------
+    def retain(self, block: int):
+        if not (0 <= block < self.num_blocks) or self._ref[block] == 0:
+            raise RefPoolError(f"block {block} is not allocated")
+        self._ref[block] += 1
+
+    def release(self, block: int) -> bool:
+        """Drop one reference; True when the block went back to the free pool."""
+        if not (0 <= block < self.num_blocks) or self._ref[block] == 0:
+            raise RefPoolError(f"block {block} is not allocated")
+        self._ref[block] -= 1
+        if self._ref[block] == 0:
+            self._free.append(block)
+            return True
+        return False
+
+    def alloc_with_prefix(self, seq, prefix_blocks, num_tokens: int):
+        prefix_blocks = [int(b) for b in prefix_blocks]
+        if seq in self._tables:
+            raise RefPoolError(f"sequence {seq!r} already exists")
+        if num_tokens < len(prefix_blocks) * self.block_size:
+            raise RefPoolError("num_tokens must cover the prefix blocks")
+        for b in prefix_blocks:
+            if not (0 <= b < self.num_blocks) or self._ref[b] == 0:
+                raise RefPoolError(f"prefix block {b} is not allocated")
+        need = -(-int(num_tokens) // self.block_size) - len(prefix_blocks)
+        if need > len(self._free):
+            raise MemoryError(f"OOM: requested {need} blocks, only {len(self._free)} free")
+        for b in prefix_blocks:
+            self._ref[b] += 1
+        blocks = list(prefix_blocks)
+        for _ in range(need):
+            b = self._free.popleft()
+            self._ref[b] = 1
+            blocks.append(b)
+        self._tables[seq] = blocks
+        self._lens[seq] = int(num_tokens)
+        return list(blocks)
 
     # -- R4 ----------------------------------------------------------------
     def plan_append(self, seqs):
