@@ -15,6 +15,9 @@
  *                          planning (slots + copy-on-write list) and free.
  *   pkv_plan_*             host cascade planner: finds the blocks that several block
  *                          tables share and lays out the shared-prefix work.
+ *   pkv_radix_*            host prefix cache: a radix tree of cached token runs and
+ *                          their blocks, longest-prefix match, locks, LRU or
+ *                          score/depth leaf eviction.
  *
  * Sources.  "The Reasoning Engine Meltdown" (atozofsoftwareengineering.blog):
  * §2.1 defines attention, softmax(Q K^T / sqrt(d_k)) V, the decode step (the new
@@ -66,6 +69,13 @@ typedef enum { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
 
 typedef struct pkv_pool pkv_pool;
 typedef struct pkv_plan pkv_plan;
+typedef struct pkv_radix pkv_radix;
+
+/* Leaf eviction order of the prefix cache (pkv_radix_create). */
+typedef enum {
+  PKV_EVICT_LRU = 0,  /* least recently used first */
+  PKV_EVICT_RSBCM = 1 /* lowest score / (depth + 1) first, then least recently used */
+} pkv_evict_policy;
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* pkv_last_error(void);
@@ -173,6 +183,14 @@ void pkv_pool_destroy(pkv_pool* pool);
  * PKV_ERR_INVALID if seq exists or num_tokens < 0. */
 pkv_status pkv_seq_alloc(pkv_pool* pool, int64_t seq, int32_t num_tokens);
 
+/* New sequence starting on cached blocks (a prefix-cache hit): its table is
+ * prefix_blocks[0..num_prefix_blocks) (each count + 1; each must be allocated)
+ * followed by fresh blocks up to ceil(num_tokens/block_size).  num_tokens must be
+ * at least num_prefix_blocks*block_size.  PKV_ERR_OOM (nothing changed) if too few
+ * blocks are free; PKV_ERR_INVALID for an existing seq or a bad prefix. */
+pkv_status pkv_seq_alloc_prefix(pkv_pool* pool, int64_t seq, const int32_t* prefix_blocks,
+                                int32_t num_prefix_blocks, int32_t num_tokens);
+
 /* child gets a copy of parent's block table (a partly filled last block included)
  * and the same length; every block's count goes up by one; no KV data moves.
  * PKV_ERR_NOT_FOUND for an unknown parent, PKV_ERR_INVALID if child exists. */
@@ -205,6 +223,81 @@ int32_t pkv_free_count(const pkv_pool* pool);
 int32_t pkv_num_seqs(const pkv_pool* pool);
 /* Copy up to cap free-list entries, front first; returns the free count. */
 int32_t pkv_free_list(const pkv_pool* pool, int32_t* out, int32_t cap);
+
+/* ------------------------------------------------------------------------------------------
+ * Prefix cache ("Dismantling the Memory Wall", "RadixAttention: The Tree of Life
+ * for Agentic Swarms": a radix tree keeps the KV of finished requests, a new
+ * request reuses its longest cached prefix, a request in flight locks its node and
+ * the node's ancestors, and eviction takes least recently used unlocked leaves;
+ * "RKSC - Reasoning-Aware KV Cache Sharing en Confident Early Exit", §2 C "RSBCM":
+ * evict the lowest branch_score / (depth + 1) first).
+ *
+ * The tree caches whole blocks of a pool: keys are token ids compared in runs of
+ * block_size, so a partly filled last block is never cached, and each cached
+ * block holds one reference in the pool (it survives the sequences that wrote
+ * it).  Node ids are int64 handles; the root is 0; ids are never reused.  Time is
+ * a logical clock (one tick per match or insert).  Not thread-safe; destroy the
+ * cache before its pool.
+ * ---------------------------------------------------------------------------------------- */
+
+/* NULL on a null pool or an unknown policy (pkv_evict_policy). */
+pkv_radix* pkv_radix_create(pkv_pool* pool, int32_t policy);
+/* Drops every cached block's reference (nodes in increasing id order), then frees. */
+void pkv_radix_destroy(pkv_radix* cache);
+/* Same release as destroy; the cache stays usable and empty. */
+pkv_status pkv_radix_clear(pkv_radix* cache);
+
+/* Longest cached prefix of tokens[0..num_tokens), in whole blocks.  Where the match
+ * ends inside a node, the node is split there (the new upper node gets a new id),
+ * so *node_out ends exactly at the match (0 if nothing matched).  Every node on the
+ * path gets the current time.  *matched_tokens = matched blocks * block_size;
+ * blocks_out (optional; room for num_tokens/block_size ids) gets their block ids.
+ * A caller that must compute at least one token passes num_tokens - 1. */
+pkv_status pkv_radix_match(pkv_radix* cache, const int32_t* tokens, int32_t num_tokens, int32_t* matched_tokens,
+                           int32_t* blocks_out, int32_t blocks_cap, int64_t* node_out);
+
+/* Cache the full blocks of a sequence: tokens[0..num_tokens) with its block table
+ * blocks[0..num_blocks) (num_blocks >= num_tokens/block_size; each of those blocks
+ * allocated in the pool).  Where the path is cached the tree keeps its own blocks
+ * (the caller's duplicates stay the caller's); the rest becomes one new leaf under
+ * the last matched node and the tree takes one pool reference per adopted block.
+ * Path nodes take the current time and max(score, their score); the new leaf takes
+ * (score, depth).  *node_out: the node that ends at the last full block;
+ * *adopted_out: blocks adopted.  score must be finite, depth >= 0. */
+pkv_status pkv_radix_insert(pkv_radix* cache, const int32_t* tokens, int32_t num_tokens, const int32_t* blocks,
+                            int32_t num_blocks, double score, int32_t depth, int64_t* node_out,
+                            int32_t* adopted_out);
+
+/* lock_ref + 1 / - 1 on the node and every ancestor below the root (a locked node is
+ * never evicted).  Unlock of an unlocked node is PKV_ERR_INVALID with nothing
+ * changed; an unknown id is PKV_ERR_NOT_FOUND. */
+pkv_status pkv_radix_lock(pkv_radix* cache, int64_t node);
+pkv_status pkv_radix_unlock(pkv_radix* cache, int64_t node);
+
+/* Branch score for the RSBCM order: the node's score becomes `score` and every
+ * ancestor's is raised to at least `score`. */
+pkv_status pkv_radix_set_score(pkv_radix* cache, int64_t node, double score);
+
+/* Remove unlocked leaves one at a time, in the cache's policy order (ties: smaller
+ * id), until num_blocks blocks went back to the pool's free list or no unlocked
+ * leaf is left.  Removing a leaf drops the tree's reference on each of its blocks
+ * in key order (blocks still used by sequences stay allocated) and may make its
+ * parent a leaf.  *released_out: blocks that reached the free list; the first
+ * evicted_cap evicted ids go to evicted_out, *num_evicted_out counts all. */
+pkv_status pkv_radix_evict(pkv_radix* cache, int32_t num_blocks, int32_t* released_out, int64_t* evicted_out,
+                           int32_t evicted_cap, int32_t* num_evicted_out);
+
+int32_t pkv_radix_num_nodes(const pkv_radix* cache);       /* the root included */
+int32_t pkv_radix_cached_blocks(const pkv_radix* cache);   /* blocks the tree references */
+int32_t pkv_radix_evictable_blocks(const pkv_radix* cache); /* blocks in nodes with lock_ref 0 */
+/* Copy up to cap node ids in increasing order; returns the node count. */
+int32_t pkv_radix_node_ids(const pkv_radix* cache, int64_t* out, int32_t cap);
+/* A node's parent (-1 for the root), lock_ref, last access time, score, depth,
+ * number of blocks, block ids and tokens (outputs optional; blocks_out needs room
+ * for the block count, tokens_out for block count * block_size). */
+pkv_status pkv_radix_node_info(const pkv_radix* cache, int64_t node, int64_t* parent, int32_t* lock_ref,
+                               int64_t* last_access, double* score, int32_t* depth, int32_t* num_blocks,
+                               int32_t* blocks_out, int32_t blocks_cap, int32_t* tokens_out, int32_t tokens_cap);
 
 /* ------------------------------------------------------------------------------------------
  * Cascade planner ("Dismantling the Memory Wall", "RadixAttention": a prefix tree

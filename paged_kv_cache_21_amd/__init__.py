@@ -33,6 +33,7 @@ LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_NOT_FOUND, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP, PKV_ERR_WORKSPACE = (
     0, -1, -2, -3, -4, -5, -6)
 PKV_F16, PKV_BF16 = 0, 1
+PKV_EVICT_LRU, PKV_EVICT_RSBCM = 0, 1
 KERNELS = {"append": 0, "decode_split": 1, "merge": 2, "cascade": 3}
 
 
@@ -70,7 +71,7 @@ _ERRORS = {PKV_ERR_INVALID: PkvInvalid, PKV_ERR_OOM: PkvOOM, PKV_ERR_NOT_FOUND: 
            PKV_ERR_UNSUPPORTED: PkvUnsupported, PKV_ERR_HIP: PkvHipError, PKV_ERR_WORKSPACE: PkvWorkspaceError}
 
 _c = ctypes
-_vp, _i32, _i64, _sz, _f32 = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_size_t, _c.c_float
+_vp, _i32, _i64, _sz, _f32, _f64 = _c.c_void_p, _c.c_int32, _c.c_int64, _c.c_size_t, _c.c_float, _c.c_double
 
 _SIGNATURES = {
     "pkv_last_error": (_c.c_char_p, []),
@@ -82,6 +83,7 @@ _SIGNATURES = {
     "pkv_pool_create": (_vp, [_i32, _i32, _vp]),
     "pkv_pool_destroy": (None, [_vp]),
     "pkv_seq_alloc": (_i32, [_vp, _i64, _i32]),
+    "pkv_seq_alloc_prefix": (_i32, [_vp, _i64, _vp, _i32, _i32]),
     "pkv_seq_fork": (_i32, [_vp, _i64, _i64]),
     "pkv_seq_free": (_i32, [_vp, _i64]),
     "pkv_plan_append": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -91,6 +93,20 @@ _SIGNATURES = {
     "pkv_free_count": (_i32, [_vp]),
     "pkv_num_seqs": (_i32, [_vp]),
     "pkv_free_list": (_i32, [_vp, _vp, _i32]),
+    "pkv_radix_create": (_vp, [_vp, _i32]),
+    "pkv_radix_destroy": (None, [_vp]),
+    "pkv_radix_clear": (_i32, [_vp]),
+    "pkv_radix_match": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp]),
+    "pkv_radix_insert": (_i32, [_vp, _vp, _i32, _vp, _i32, _f64, _i32, _vp, _vp]),
+    "pkv_radix_lock": (_i32, [_vp, _i64]),
+    "pkv_radix_unlock": (_i32, [_vp, _i64]),
+    "pkv_radix_set_score": (_i32, [_vp, _i64, _f64]),
+    "pkv_radix_evict": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp]),
+    "pkv_radix_num_nodes": (_i32, [_vp]),
+    "pkv_radix_cached_blocks": (_i32, [_vp]),
+    "pkv_radix_evictable_blocks": (_i32, [_vp]),
+    "pkv_radix_node_ids": (_i32, [_vp, _vp, _i32]),
+    "pkv_radix_node_info": (_i32, [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32]),
     "pkv_plan_build": (_vp, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_plan_destroy": (None, [_vp]),
     "pkv_plan_device_bytes": (_sz, [_vp]),
@@ -335,17 +351,27 @@ class BlockPool:
         if not h:
             raise PkvInvalid(PKV_ERR_INVALID, _lib.pkv_last_error().decode())
         self._handle = h
+        self._radix_handles = set()  # prefix caches holding references in this pool
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
 
     def __del__(self):
         h = getattr(self, "_handle", None)
         if h and _lib is not None:  # at interpreter exit the module globals may already be gone
+            # a cache must go before its pool; garbage cycles finalize in any order
+            for r in list(self._radix_handles):
+                _lib.pkv_radix_destroy(r)
+            self._radix_handles.clear()
             _lib.pkv_pool_destroy(h)
             self._handle = None
 
     def alloc(self, seq, num_tokens):
         _check(_lib.pkv_seq_alloc(self._handle, int(seq), int(num_tokens)))
+
+    def alloc_with_prefix(self, seq, prefix_blocks, num_tokens):
+        """New sequence whose table starts with the cached ``prefix_blocks``."""
+        pb = np.ascontiguousarray(prefix_blocks, dtype=np.int32)
+        _check(_lib.pkv_seq_alloc_prefix(self._handle, int(seq), _ptr(pb), pb.shape[0], int(num_tokens)))
 
     def fork(self, parent, child):
         _check(_lib.pkv_seq_fork(self._handle, int(parent), int(child)))
@@ -402,6 +428,125 @@ class BlockPool:
 
     def __contains__(self, seq):
         return self.length(seq) >= 0
+
+
+# ---------------------------------------------------------------------------
+# prefix cache
+
+
+class RadixCache:
+    """Radix tree of cached token blocks over a BlockPool (runs in libpkv).
+
+    ``policy`` is "lru" (least recently used unlocked leaf first) or "rsbcm"
+    (lowest score / (depth + 1) first).  Keep the pool alive while the cache is.
+    """
+
+    POLICIES = {"lru": PKV_EVICT_LRU, "rsbcm": PKV_EVICT_RSBCM}
+
+    def __init__(self, pool, policy="lru"):
+        _require(policy in self.POLICIES, f"unknown policy {policy!r}")
+        h = _lib.pkv_radix_create(pool._handle, self.POLICIES[policy])
+        if not h:
+            raise PkvInvalid(PKV_ERR_INVALID, _lib.pkv_last_error().decode())
+        self._handle = h
+        self._pool = pool  # the cache holds references in this pool
+        pool._radix_handles.add(h)
+        self.policy = policy
+        self.block_size = pool.block_size
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        pool = getattr(self, "_pool", None)
+        if h and _lib is not None and pool is not None and h in pool._radix_handles:
+            pool._radix_handles.discard(h)
+            _lib.pkv_radix_destroy(h)
+        self._handle = None
+
+    @staticmethod
+    def _tokens(tokens):
+        return np.ascontiguousarray(tokens, dtype=np.int32)
+
+    def match_prefix(self, tokens):
+        """(matched tokens, their block ids, node id)."""
+        t = self._tokens(tokens)
+        nb = t.shape[0] // self.block_size
+        blocks = np.empty(max(nb, 1), dtype=np.int32)
+        matched = np.zeros(1, dtype=np.int32)
+        node = np.zeros(1, dtype=np.int64)
+        _check(_lib.pkv_radix_match(self._handle, _ptr(t), t.shape[0], _ptr(matched), _ptr(blocks), nb,
+                                    _ptr(node)))
+        m = int(matched[0])
+        return m, [int(x) for x in blocks[:m // self.block_size]], int(node[0])
+
+    def insert(self, tokens, blocks, score=0.0, depth=0):
+        """(node id ending at the last full block, blocks adopted)."""
+        t = self._tokens(tokens)
+        b = np.ascontiguousarray(blocks, dtype=np.int32)
+        node = np.zeros(1, dtype=np.int64)
+        adopted = np.zeros(1, dtype=np.int32)
+        _check(_lib.pkv_radix_insert(self._handle, _ptr(t), t.shape[0], _ptr(b), b.shape[0], float(score),
+                                     int(depth), _ptr(node), _ptr(adopted)))
+        return int(node[0]), int(adopted[0])
+
+    def lock(self, node):
+        _check(_lib.pkv_radix_lock(self._handle, int(node)))
+
+    def unlock(self, node):
+        _check(_lib.pkv_radix_unlock(self._handle, int(node)))
+
+    def set_score(self, node, score):
+        _check(_lib.pkv_radix_set_score(self._handle, int(node), float(score)))
+
+    def evict(self, num_blocks):
+        """(blocks released to the pool's free list, evicted node ids in order)."""
+        released = np.zeros(1, dtype=np.int32)
+        count = np.zeros(1, dtype=np.int32)
+        cap = max(self.num_nodes(), 1)
+        ids = np.empty(cap, dtype=np.int64)
+        _check(_lib.pkv_radix_evict(self._handle, int(num_blocks), _ptr(released), _ptr(ids), cap, _ptr(count)))
+        return int(released[0]), [int(x) for x in ids[:int(count[0])]]
+
+    def clear(self):
+        _check(_lib.pkv_radix_clear(self._handle))
+
+    def num_nodes(self):
+        return int(_lib.pkv_radix_num_nodes(self._handle))
+
+    def cached_blocks(self):
+        return int(_lib.pkv_radix_cached_blocks(self._handle))
+
+    def evictable_blocks(self):
+        return int(_lib.pkv_radix_evictable_blocks(self._handle))
+
+    def node_ids(self):
+        n = self.num_nodes()
+        out = np.empty(n, dtype=np.int64)
+        _lib.pkv_radix_node_ids(self._handle, _ptr(out), n)
+        return [int(x) for x in out]
+
+    def _info(self, node):
+        parent = np.zeros(1, dtype=np.int64)
+        lock = np.zeros(1, dtype=np.int32)
+        last = np.zeros(1, dtype=np.int64)
+        score = np.zeros(1, dtype=np.float64)
+        depth = np.zeros(1, dtype=np.int32)
+        nb = np.zeros(1, dtype=np.int32)
+        _check(_lib.pkv_radix_node_info(self._handle, int(node), _ptr(parent), _ptr(lock), _ptr(last), _ptr(score),
+                                        _ptr(depth), _ptr(nb), None, 0, None, 0))
+        n = int(nb[0])
+        blocks = np.empty(max(n, 1), dtype=np.int32)
+        tokens = np.empty(max(n * self.block_size, 1), dtype=np.int32)
+        _check(_lib.pkv_radix_node_info(self._handle, int(node), None, None, None, None, None, None, _ptr(blocks), n,
+                                        _ptr(tokens), n * self.block_size))
+        return (int(parent[0]), [int(x) for x in blocks[:n]], int(lock[0]), int(last[0]), float(score[0]),
+                int(depth[0])), [int(x) for x in tokens[:n * self.block_size]]
+
+    def node_info(self, node):
+        """(parent id, block ids, lock_ref, last access time, score, depth); parent -1 for the root."""
+        return self._info(node)[0]
+
+    def node_tokens(self, node):
+        return self._info(node)[1]
 
 
 # ---------------------------------------------------------------------------

@@ -17,24 +17,10 @@
 // Order is deterministic: a FIFO free list seeded by the caller, batches
 // processed in the order given.
 #include <algorithm>
-#include <deque>
-#include <unordered_map>
 #include <unordered_set>
-#include <vector>
 
 #include "host_common.h"
-
-struct pkv_pool {
-  struct Seq {
-    std::vector<int32_t> table;
-    int32_t len = 0;
-  };
-  int32_t num_blocks = 0;
-  int32_t block_size = 0;
-  std::vector<int32_t> ref;
-  std::deque<int32_t> free_list;
-  std::unordered_map<int64_t, Seq> seqs;
-};
+#include "pool.h"
 
 namespace {
 
@@ -88,6 +74,42 @@ pkv_status pkv_seq_alloc(pkv_pool* pool, int64_t seq, int32_t num_tokens) {
   s.table.reserve(need);
   for (int32_t i = 0; i < need; ++i) {
     int32_t b = pool->free_list.front();
+    pool->free_list.pop_front();
+    pool->ref[b] = 1;
+    s.table.push_back(b);
+  }
+  s.len = num_tokens;
+  pool->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_alloc_prefix(pkv_pool* pool, int64_t seq, const int32_t* prefix_blocks, int32_t num_prefix_blocks,
+                                int32_t num_tokens) {
+  pkv::clear_error();
+  if (!pool) return pkv::fail(PKV_ERR_INVALID, "pkv_seq_alloc_prefix: null pool");
+  if (num_prefix_blocks < 0 || (num_prefix_blocks > 0 && !prefix_blocks))
+    return pkv::fail(PKV_ERR_INVALID, "pkv_seq_alloc_prefix: bad prefix");
+  if (num_tokens < 0 || static_cast<int64_t>(num_prefix_blocks) * pool->block_size > num_tokens)
+    return pkv::fail(PKV_ERR_INVALID, "pkv_seq_alloc_prefix: num_tokens must cover the prefix blocks");
+  if (pool->seqs.count(seq))
+    return pkv::fail(PKV_ERR_INVALID, "pkv_seq_alloc_prefix: sequence %lld exists", (long long)seq);
+  for (int32_t i = 0; i < num_prefix_blocks; ++i) {
+    const int32_t b = prefix_blocks[i];
+    if (b < 0 || b >= pool->num_blocks || pool->ref[b] == 0)
+      return pkv::fail(PKV_ERR_INVALID, "pkv_seq_alloc_prefix: prefix block %d is not allocated", b);
+  }
+  const int32_t need = blocks_for(num_tokens, pool->block_size) - num_prefix_blocks;
+  if (need > static_cast<int64_t>(pool->free_list.size()))
+    return pkv::fail(PKV_ERR_OOM, "pkv_seq_alloc_prefix: requested %d blocks, only %zu free", need,
+                     pool->free_list.size());
+  pkv_pool::Seq s;
+  s.table.reserve(num_prefix_blocks + need);
+  for (int32_t i = 0; i < num_prefix_blocks; ++i) {
+    pool->ref[prefix_blocks[i]] += 1;
+    s.table.push_back(prefix_blocks[i]);
+  }
+  for (int32_t i = 0; i < need; ++i) {
+    const int32_t b = pool->free_list.front();
     pool->free_list.pop_front();
     pool->ref[b] = 1;
     s.table.push_back(b);
