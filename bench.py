@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 (E4M3) pages with per-row scales: quantizing append + FP8 decode (configs 2 and 4)")
+    ap.add_argument("--radix", action="store_true",
+                    help="host prefix cache: request throughput and hit rate on request traces (no GPU work)")
     ap.add_argument("--extend", action="store_true",
                     help="time the multi-token pass (configs 3: verify 8 tokens per branch, 6: chunked prefill)")
     ap.add_argument("--no-cascade", action="store_true", help="decode every row on its own (no shared-prefix pass)")
@@ -366,6 +368,87 @@ def run_fp8(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def radix_replay(Pool, Cache, reqs, num_blocks, policy, block_size=16, batch=32, seconds=None, meta=None):
+    """Serve ``reqs`` in order through a prefix cache, ``batch`` at a time: one batched
+    admission (each request matches all but its last token, locks it, evicts when
+    the pool is short, starts on the matched blocks), then one batched completion
+    (cache the full blocks with their (score, depth) from ``meta``, unlock,
+    release).  Requests that did not fit go first
+    in the next batch.  Returns (requests done, seconds, matched tokens, total
+    tokens, admission calls)."""
+    pool = Pool(num_blocks, block_size)
+    cache = Cache(pool, policy)
+    hits = total = done = calls = 0
+    queue = list(range(len(reqs)))
+    t0 = time.perf_counter()
+    while queue:
+        ids = queue[:batch]
+        got = cache.admit([reqs[i] for i in ids], ids)
+        calls += 1
+        if not got:
+            raise RuntimeError(f"request {ids[0]} does not fit in a pool of {num_blocks} blocks")
+        adm = ids[:len(got)]
+        cache.finish([reqs[i] for i in adm], adm, [n for _, n in got],
+                     None if meta is None else [meta[i][0] for i in adm],
+                     None if meta is None else [meta[i][1] for i in adm])
+        queue = ids[len(got):] + queue[batch:]
+        for (m, _), i in zip(got, adm):
+            hits += m
+            total += len(reqs[i])
+        done += len(got)
+        if seconds is not None and time.perf_counter() - t0 > seconds:
+            break
+    return done, time.perf_counter() - t0, hits, total, calls
+
+
+def run_radix(args):
+    """Host prefix cache on two request traces: the RadixAttention section's 1,000
+    users behind one 2,000-token system prompt, and a multi-turn, branching agent
+    stream over 8 system prompts in a pool of 4,096 blocks, far fewer than its
+    distinct blocks (so leaves are evicted), under both eviction orders.  Requests
+    go through batched admission and completion, 32 per call.  The library is
+    timed; the oracle serves a bounded prefix of the same traces the same way."""
+    import oracle
+    import paged_kv_cache_21_amd as pkv
+    import workloads
+
+    agent, agent_meta = workloads.agent_sessions(seed=8, requests=4000, meta=True)
+    traces = [
+        ("system_prompt_1000x2000", workloads.system_prompt_requests(seed=7), None, 1 << 16, "lru"),
+        ("agent_sessions_4000_lru", agent, agent_meta, 4096, "lru"),
+        ("agent_sessions_4000_rsbcm", agent, agent_meta, 4096, "rsbcm"),
+    ]
+    per = {}
+    total_req = total_s = 0.0
+    for name, reqs, meta, nblk, policy in traces:
+        radix_replay(pkv.BlockPool, pkv.RadixCache, reqs[:50], nblk, policy, meta=meta)  # warm-up
+        done, sec, hits, tok, calls = radix_replay(pkv.BlockPool, pkv.RadixCache, reqs, nblk, policy, meta=meta)
+        per[name] = {"requests": done, "us_per_request": round(sec / done * 1e6, 2),
+                     "hit_rate": round(hits / tok, 4), "admission_calls": calls, "pool_blocks": nblk,
+                     "tokens_per_request": round(tok / done, 1)}
+        total_req += done
+        total_s += sec
+        print(f"[bench] radix {name}: {done} requests, {sec / done * 1e6:.1f} us/request, "
+              f"hit rate {hits / tok:.3f}, {calls} admission calls", file=sys.stderr, flush=True)
+    value = total_req / total_s
+    cpu = None
+    if args.cpu_seconds > 0:
+        c_req = c_s = 0.0
+        for name, reqs, meta, nblk, policy in traces:
+            done, sec, _, _, _ = radix_replay(oracle.RefPool, oracle.RadixCache, reqs, nblk, policy,
+                                              seconds=args.cpu_seconds / len(traces), meta=meta)
+            c_req += done
+            c_s += sec
+        cpu = {"value": round(c_req / c_s, 2), "unit": "requests/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {int(c_req)} requests over the three traces, about {args.cpu_seconds:.0f} s"}
+    line = {"metric": "prefix_cache_requests_per_s", "value": round(value, 1), "unit": "requests/s",
+            "n_gpus": 0, "steps": int(total_req), "warmup": 150, "ms_per_step": round(total_s / total_req * 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+            "data": "synthetic", "config": {"workload": "prefix cache request traces", "traces": per},
+            "roofline": None, "cpu_baseline": cpu}
+    print(json.dumps(line))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -373,6 +456,9 @@ def main():
               "(the path shards by rows / heads with no exchange, but nothing here launches more than one GPU).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.radix:
+        return run_radix(args)
 
     import torch
 

@@ -218,6 +218,8 @@ pkv_status pkv_export_tables(const pkv_pool* pool, const int64_t* seqs, int32_t 
                              int32_t* tables_out, int32_t* lens_out);
 
 int32_t pkv_seq_len(const pkv_pool* pool, int64_t seq);     /* -1 if unknown */
+/* Copy up to cap entries of seq's block table; returns its block count (-1 if unknown). */
+int32_t pkv_seq_table(const pkv_pool* pool, int64_t seq, int32_t* out, int32_t cap);
 int32_t pkv_refcount(const pkv_pool* pool, int32_t block);  /* -1 if out of range */
 int32_t pkv_free_count(const pkv_pool* pool);
 int32_t pkv_num_seqs(const pkv_pool* pool);
@@ -286,6 +288,25 @@ pkv_status pkv_radix_set_score(pkv_radix* cache, int64_t node, double score);
  * evicted_cap evicted ids go to evicted_out, *num_evicted_out counts all. */
 pkv_status pkv_radix_evict(pkv_radix* cache, int32_t num_blocks, int32_t* released_out, int64_t* evicted_out,
                            int32_t evicted_cap, int32_t* num_evicted_out);
+
+/* Batched admission for a scheduler, one call per batch.  Request i is the token run
+ * tokens[offsets[i] .. offsets[i+1]) (at least one token) and becomes sequence
+ * seqs[i] (new ids, no repeats).  In order, each request matches all but its last
+ * token, locks the match, evicts (blocks needed - free blocks) when the pool is short,
+ * and starts its sequence on the matched blocks plus fresh ones; the first request
+ * that still does not fit is unlocked and ends the batch.  matched_out / node_out get
+ * the matched tokens and the locked node of each admitted request; *num_admitted
+ * counts them (a short count is not an error).  The caller writes K/V for positions
+ * from matched_out[i] on (pkv_seq_table gives the slots). */
+pkv_status pkv_radix_admit(pkv_radix* cache, const int32_t* tokens, const int64_t* offsets, int32_t n,
+                           const int64_t* seqs, int32_t* matched_out, int64_t* node_out, int32_t* num_admitted);
+
+/* Batched completion: for each i, cache sequence seqs[i]'s full blocks under the token
+ * run tokens[offsets[i] .. offsets[i+1]) (at most the sequence's length) with
+ * scores[i] / depths[i] (NULL: 0), unlock nodes[i] (its admission node) and free the
+ * sequence.  Every entry is checked first; on an error nothing changes. */
+pkv_status pkv_radix_finish(pkv_radix* cache, const int32_t* tokens, const int64_t* offsets, int32_t n,
+                            const int64_t* seqs, const int64_t* nodes, const double* scores, const int32_t* depths);
 
 int32_t pkv_radix_num_nodes(const pkv_radix* cache);       /* the root included */
 int32_t pkv_radix_cached_blocks(const pkv_radix* cache);   /* blocks the tree references */

@@ -50,6 +50,13 @@ Readings (the pages fix the structure and the policies, not every detail):
       ancestor's to at least s (a prefix is worth its best branch).
 * K8  A split copies lock_ref, last_access_time, score and depth to the new
       upper node.
+* K9  Batched admission, in order: a request matches all but its last token
+      (at least one token is computed), locks the match, evicts
+      (blocks needed - free blocks) when the pool is short, and starts its
+      sequence on the matched blocks; the first request that still does not fit
+      is unlocked and stops the batch.  ``finish`` caches each sequence's
+      tokens (insert with its score and depth), unlocks its admission node and
+      frees the sequence, after checking every entry.
 """
 
 import math
@@ -225,6 +232,51 @@ class RadixCache:
             del self.nodes[victim.id]
             evicted.append(victim.id)
         return released, evicted
+
+    # -- K9 ------------------------------------------------------------------
+    def admit(self, requests, seqs):
+        """requests: token lists; returns [(matched tokens, node)] of the admitted prefix."""
+        seqs = list(seqs)
+        if len(set(seqs)) != len(seqs) or any(s in self.pool for s in seqs) or any(len(t) < 1 for t in requests):
+            raise RadixError("admit: repeated or existing sequence id, or an empty request")
+        out = []
+        for toks, seq in zip(requests, seqs):
+            m, blocks, node = self.match_prefix(list(toks)[:-1])
+            self.lock(node)
+            need = -(-len(toks) // self.block_size) - len(blocks)
+            if need > self.pool.free_count():
+                self.evict(need - self.pool.free_count())
+            try:
+                self.pool.alloc_with_prefix(seq, blocks, len(toks))
+            except MemoryError:
+                self.unlock(node)
+                break
+            out.append((m, node))
+        return out
+
+    def finish(self, requests, seqs, nodes, scores=None, depths=None):
+        seqs = list(seqs)
+        if len(set(seqs)) != len(seqs):
+            raise RadixError("finish: repeated sequence id")
+        pending = {}
+        for i, (toks, seq, node) in enumerate(zip(requests, seqs, nodes)):
+            if seq not in self.pool:
+                raise KeyError(f"sequence {seq} does not exist")
+            if len(toks) > self.pool.length(seq):
+                raise RadixError("finish: more tokens than the sequence holds")
+            for n in self._path(self._node(node)):
+                pending[n.id] = pending.get(n.id, 0) + 1
+                if pending[n.id] > n.lock_ref:
+                    raise RadixError(f"node {node} is not locked")
+            if scores is not None and not math.isfinite(scores[i]):
+                raise RadixError("score must be finite")
+            if depths is not None and depths[i] < 0:
+                raise RadixError("depth must be >= 0")
+        for i, (toks, seq, node) in enumerate(zip(requests, seqs, nodes)):
+            self.insert(toks, self.pool.table(seq), 0.0 if scores is None else scores[i],
+                        0 if depths is None else depths[i])
+            self.unlock(node)
+            self.pool.free(seq)
 
     def clear(self):
         """Drop every cached node (ids in increasing order, blocks in key order)."""

@@ -89,6 +89,7 @@ _SIGNATURES = {
     "pkv_plan_append": (_i32, [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "pkv_export_tables": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "pkv_seq_len": (_i32, [_vp, _i64]),
+    "pkv_seq_table": (_i32, [_vp, _i64, _vp, _i32]),
     "pkv_refcount": (_i32, [_vp, _i32]),
     "pkv_free_count": (_i32, [_vp]),
     "pkv_num_seqs": (_i32, [_vp]),
@@ -102,6 +103,8 @@ _SIGNATURES = {
     "pkv_radix_unlock": (_i32, [_vp, _i64]),
     "pkv_radix_set_score": (_i32, [_vp, _i64, _f64]),
     "pkv_radix_evict": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp]),
+    "pkv_radix_admit": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "pkv_radix_finish": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
     "pkv_radix_num_nodes": (_i32, [_vp]),
     "pkv_radix_cached_blocks": (_i32, [_vp]),
     "pkv_radix_evictable_blocks": (_i32, [_vp]),
@@ -352,6 +355,7 @@ class BlockPool:
             raise PkvInvalid(PKV_ERR_INVALID, _lib.pkv_last_error().decode())
         self._handle = h
         self._radix_handles = set()  # prefix caches holding references in this pool
+        self._table_buf = np.empty(1024, dtype=np.int32)
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
 
@@ -370,7 +374,7 @@ class BlockPool:
 
     def alloc_with_prefix(self, seq, prefix_blocks, num_tokens):
         """New sequence whose table starts with the cached ``prefix_blocks``."""
-        pb = np.ascontiguousarray(prefix_blocks, dtype=np.int32)
+        pb = np.asarray(prefix_blocks, dtype=np.int32)
         _check(_lib.pkv_seq_alloc_prefix(self._handle, int(seq), _ptr(pb), pb.shape[0], int(num_tokens)))
 
     def fork(self, parent, child):
@@ -401,12 +405,14 @@ class BlockPool:
         return bt, lens
 
     def table(self, seq):
-        n = self.length(seq)
+        buf = self._table_buf
+        n = _lib.pkv_seq_table(self._handle, int(seq), buf.ctypes.data, buf.shape[0])
         if n < 0:
             raise PkvNotFound(PKV_ERR_NOT_FOUND, f"sequence {seq} does not exist")
-        nb = -(-n // self.block_size)
-        bt, _ = self.export_tables([seq], max(nb, 1))
-        return [int(x) for x in bt[0, :nb]]
+        if n > buf.shape[0]:
+            self._table_buf = buf = np.empty(2 * n, dtype=np.int32)
+            _lib.pkv_seq_table(self._handle, int(seq), buf.ctypes.data, buf.shape[0])
+        return buf[:n].tolist()
 
     def length(self, seq):
         return int(_lib.pkv_seq_len(self._handle, int(seq)))
@@ -453,6 +459,9 @@ class RadixCache:
         pool._radix_handles.add(h)
         self.policy = policy
         self.block_size = pool.block_size
+        self._i32 = np.zeros(2, dtype=np.int32)   # scratch outputs (one call at a time)
+        self._i64 = np.zeros(1, dtype=np.int64)
+        self._blocks = np.empty(1024, dtype=np.int32)
 
     def __del__(self):
         h = getattr(self, "_handle", None)
@@ -470,23 +479,57 @@ class RadixCache:
         """(matched tokens, their block ids, node id)."""
         t = self._tokens(tokens)
         nb = t.shape[0] // self.block_size
-        blocks = np.empty(max(nb, 1), dtype=np.int32)
-        matched = np.zeros(1, dtype=np.int32)
-        node = np.zeros(1, dtype=np.int64)
-        _check(_lib.pkv_radix_match(self._handle, _ptr(t), t.shape[0], _ptr(matched), _ptr(blocks), nb,
-                                    _ptr(node)))
-        m = int(matched[0])
-        return m, [int(x) for x in blocks[:m // self.block_size]], int(node[0])
+        if nb > self._blocks.shape[0]:
+            self._blocks = np.empty(2 * nb, dtype=np.int32)
+        i32, i64, blocks = self._i32, self._i64, self._blocks
+        _check(_lib.pkv_radix_match(self._handle, t.ctypes.data, t.shape[0], i32.ctypes.data, blocks.ctypes.data,
+                                    blocks.shape[0], i64.ctypes.data))
+        m = int(i32[0])
+        return m, blocks[:m // self.block_size].tolist(), int(i64[0])
 
     def insert(self, tokens, blocks, score=0.0, depth=0):
         """(node id ending at the last full block, blocks adopted)."""
         t = self._tokens(tokens)
-        b = np.ascontiguousarray(blocks, dtype=np.int32)
-        node = np.zeros(1, dtype=np.int64)
-        adopted = np.zeros(1, dtype=np.int32)
-        _check(_lib.pkv_radix_insert(self._handle, _ptr(t), t.shape[0], _ptr(b), b.shape[0], float(score),
-                                     int(depth), _ptr(node), _ptr(adopted)))
-        return int(node[0]), int(adopted[0])
+        b = np.asarray(blocks, dtype=np.int32)
+        i32, i64 = self._i32, self._i64
+        _check(_lib.pkv_radix_insert(self._handle, t.ctypes.data, t.shape[0], b.ctypes.data, b.shape[0],
+                                     float(score), int(depth), i64.ctypes.data, i32.ctypes.data))
+        return int(i64[0]), int(i32[0])
+
+    @staticmethod
+    def _pack(requests):
+        if isinstance(requests, tuple) and len(requests) == 2 and isinstance(requests[1], np.ndarray):
+            return np.ascontiguousarray(requests[0], dtype=np.int32), np.ascontiguousarray(requests[1], dtype=np.int64)
+        lens = np.fromiter((len(t) for t in requests), dtype=np.int64, count=len(requests))
+        offsets = np.zeros(len(requests) + 1, dtype=np.int64)
+        np.cumsum(lens, out=offsets[1:])
+        flat = np.concatenate([np.asarray(t, dtype=np.int32) for t in requests]) if len(requests) else \
+            np.zeros(1, dtype=np.int32)
+        return np.ascontiguousarray(flat, dtype=np.int32), offsets
+
+    def admit(self, requests, seqs):
+        """Admit token runs (a list of token lists, or (flat tokens, offsets)) as sequences
+        ``seqs``; returns [(matched tokens, locked node)] for the admitted prefix."""
+        flat, offsets = self._pack(requests)
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = s.shape[0]
+        matched = np.empty(max(n, 1), dtype=np.int32)
+        nodes = np.empty(max(n, 1), dtype=np.int64)
+        count = np.zeros(1, dtype=np.int32)
+        _check(_lib.pkv_radix_admit(self._handle, flat.ctypes.data, offsets.ctypes.data, n, s.ctypes.data,
+                                    matched.ctypes.data, nodes.ctypes.data, count.ctypes.data))
+        k = int(count[0])
+        return list(zip(matched[:k].tolist(), nodes[:k].tolist()))
+
+    def finish(self, requests, seqs, nodes, scores=None, depths=None):
+        """Cache, unlock and free finished sequences (see pkv_radix_finish)."""
+        flat, offsets = self._pack(requests)
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        nd = np.ascontiguousarray(nodes, dtype=np.int64)
+        sc = None if scores is None else np.ascontiguousarray(scores, dtype=np.float64)
+        dp = None if depths is None else np.ascontiguousarray(depths, dtype=np.int32)
+        _check(_lib.pkv_radix_finish(self._handle, flat.ctypes.data, offsets.ctypes.data, s.shape[0], s.ctypes.data,
+                                     nd.ctypes.data, _ptr(sc), _ptr(dp)))
 
     def lock(self, node):
         _check(_lib.pkv_radix_lock(self._handle, int(node)))
@@ -504,7 +547,7 @@ class RadixCache:
         cap = max(self.num_nodes(), 1)
         ids = np.empty(cap, dtype=np.int64)
         _check(_lib.pkv_radix_evict(self._handle, int(num_blocks), _ptr(released), _ptr(ids), cap, _ptr(count)))
-        return int(released[0]), [int(x) for x in ids[:int(count[0])]]
+        return int(released[0]), ids[:int(count[0])].tolist()
 
     def clear(self):
         _check(_lib.pkv_radix_clear(self._handle))
@@ -522,7 +565,7 @@ class RadixCache:
         n = self.num_nodes()
         out = np.empty(n, dtype=np.int64)
         _lib.pkv_radix_node_ids(self._handle, _ptr(out), n)
-        return [int(x) for x in out]
+        return out.tolist()
 
     def _info(self, node):
         parent = np.zeros(1, dtype=np.int64)
@@ -538,8 +581,8 @@ class RadixCache:
         tokens = np.empty(max(n * self.block_size, 1), dtype=np.int32)
         _check(_lib.pkv_radix_node_info(self._handle, int(node), None, None, None, None, None, None, _ptr(blocks), n,
                                         _ptr(tokens), n * self.block_size))
-        return (int(parent[0]), [int(x) for x in blocks[:n]], int(lock[0]), int(last[0]), float(score[0]),
-                int(depth[0])), [int(x) for x in tokens[:n * self.block_size]]
+        return (int(parent[0]), blocks[:n].tolist(), int(lock[0]), int(last[0]), float(score[0]),
+                int(depth[0])), tokens[:n * self.block_size].tolist()
 
     def node_info(self, node):
         """(parent id, block ids, lock_ref, last access time, score, depth); parent -1 for the root."""

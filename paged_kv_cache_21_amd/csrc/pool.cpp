@@ -235,6 +235,16 @@ pkv_status pkv_export_tables(const pkv_pool* pool, const int64_t* seqs, int32_t 
   return PKV_OK;
 }
 
+int32_t pkv_seq_table(const pkv_pool* pool, int64_t seq, int32_t* out, int32_t cap) {
+  if (!pool) return -1;
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return -1;
+  const auto& t = it->second.table;
+  if (out)
+    for (int32_t i = 0; i < cap && i < static_cast<int32_t>(t.size()); ++i) out[i] = t[i];
+  return static_cast<int32_t>(t.size());
+}
+
 int32_t pkv_seq_len(const pkv_pool* pool, int64_t seq) {
   if (!pool) return -1;
   auto it = pool->seqs.find(seq);

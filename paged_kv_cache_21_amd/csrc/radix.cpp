@@ -32,8 +32,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
 #include <memory>
-#include <queue>
 #include <tuple>
 #include <unordered_map>
 #include <unordered_set>
@@ -43,6 +43,16 @@
 #include "pool.h"
 
 namespace {
+
+// Eviction order: smallest key first (omega is 0 under the LRU policy).
+struct EvictKey {
+  double omega;
+  int64_t last_access;
+  int64_t id;
+  bool operator<(const EvictKey& o) const {
+    return std::tie(omega, last_access, id) < std::tie(o.omega, o.last_access, o.id);
+  }
+};
 
 struct Node {
   int64_t id = 0;
@@ -54,6 +64,8 @@ struct Node {
   double score = 0.0;
   int32_t depth = 0;
   std::unordered_multimap<uint64_t, Node*> children;  // by hash of the child's first key block
+  bool queued = false;  // in the eviction order (an unlocked leaf), under `key`
+  EvictKey key{};
 };
 
 uint64_t hash_block(const int32_t* t, int32_t n) {
@@ -76,8 +88,32 @@ struct pkv_radix {
   int64_t next_id = 1;
   std::unordered_map<int64_t, std::unique_ptr<Node>> nodes;
   Node* root = nullptr;
-  std::unordered_set<Node*> leaves;  // non-root nodes without children
-  int64_t cached = 0;                // blocks held by the tree
+  std::map<EvictKey, Node*> order;  // unlocked leaves, next victim first
+  int64_t cached = 0;               // blocks held by the tree
+
+  bool evictable(const Node* n) const { return n != root && n->children.empty() && n->lock_ref == 0; }
+
+  EvictKey key_of(const Node* n) const {
+    const double omega = policy == PKV_EVICT_RSBCM ? n->score / static_cast<double>(n->depth + 1) : 0.0;
+    return {omega, n->last_access, n->id};
+  }
+
+  void dequeue(Node* n) {
+    if (n->queued) {
+      order.erase(n->key);
+      n->queued = false;
+    }
+  }
+
+  // Call after a change to a node's time, score, lock or children.
+  void requeue(Node* n) {
+    dequeue(n);
+    if (evictable(n)) {
+      n->key = key_of(n);
+      order.emplace(n->key, n);
+      n->queued = true;
+    }
+  }
 
   size_t block_bytes() const { return static_cast<size_t>(bs) * sizeof(int32_t); }
 
@@ -154,30 +190,10 @@ struct pkv_radix {
       for (int32_t b : nodes[id]->blocks) pool->release(b);
     for (int64_t id : ids) nodes.erase(id);
     root->children.clear();
-    leaves.clear();
+    order.clear();
     cached = 0;
   }
 };
-
-namespace {
-
-// Eviction order: smallest key first.
-struct Candidate {
-  double omega;
-  int64_t last_access;
-  int64_t id;
-  Node* node;
-  bool operator>(const Candidate& o) const {
-    return std::tie(omega, last_access, id) > std::tie(o.omega, o.last_access, o.id);
-  }
-};
-
-Candidate candidate(const pkv_radix* r, Node* n) {
-  const double omega = r->policy == PKV_EVICT_RSBCM ? n->score / static_cast<double>(n->depth + 1) : 0.0;
-  return {omega, n->last_access, n->id, n};
-}
-
-}  // namespace
 
 extern "C" {
 
@@ -232,6 +248,7 @@ pkv_status pkv_radix_match(pkv_radix* r, const int32_t* tokens, int32_t num_toke
     const int32_t m = r->common(c, q, nb - i);
     if (m < static_cast<int32_t>(c->blocks.size())) c = r->split(c, m);
     c->last_access = r->clock;
+    r->requeue(c);
     if (blocks_out) std::memcpy(blocks_out + i, c->blocks.data(), sizeof(int32_t) * m);
     i += m;
     node = c;
@@ -266,6 +283,7 @@ pkv_status pkv_radix_insert(pkv_radix* r, const int32_t* tokens, int32_t num_tok
       if (m < static_cast<int32_t>(c->blocks.size())) c = r->split(c, m);
       c->last_access = r->clock;
       c->score = std::max(c->score, score);
+      r->requeue(c);
       node = c;
       i += m;
       continue;
@@ -281,9 +299,9 @@ pkv_status pkv_radix_insert(pkv_radix* r, const int32_t* tokens, int32_t num_tok
     l->depth = depth;
     for (int32_t b : l->blocks) r->pool->retain(b);
     node->children.emplace(hash_block(q, r->bs), l);
-    if (node != r->root) r->leaves.erase(node);
-    r->leaves.insert(l);
     r->nodes.emplace(l->id, std::move(leaf));
+    r->requeue(node);
+    r->requeue(l);
     adopted = nb - i;
     r->cached += adopted;
     node = l;
@@ -299,7 +317,10 @@ pkv_status pkv_radix_lock(pkv_radix* r, int64_t node) {
   if (!r) return pkv::fail(PKV_ERR_INVALID, "pkv_radix_lock: null cache");
   Node* n = r->get(node);
   if (!n) return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_radix_lock: node %lld does not exist", (long long)node);
-  for (; n != r->root; n = n->parent) n->lock_ref += 1;
+  for (; n != r->root; n = n->parent) {
+    n->lock_ref += 1;
+    r->requeue(n);
+  }
   return PKV_OK;
 }
 
@@ -310,7 +331,10 @@ pkv_status pkv_radix_unlock(pkv_radix* r, int64_t node) {
   if (!n) return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_radix_unlock: node %lld does not exist", (long long)node);
   for (Node* p = n; p != r->root; p = p->parent)
     if (p->lock_ref == 0) return pkv::fail(PKV_ERR_INVALID, "pkv_radix_unlock: node %lld is not locked", (long long)node);
-  for (; n != r->root; n = n->parent) n->lock_ref -= 1;
+  for (; n != r->root; n = n->parent) {
+    n->lock_ref -= 1;
+    r->requeue(n);
+  }
   return PKV_OK;
 }
 
@@ -322,7 +346,11 @@ pkv_status pkv_radix_set_score(pkv_radix* r, int64_t node, double score) {
   if (!n) return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_radix_set_score: node %lld does not exist", (long long)node);
   if (n == r->root) return pkv::fail(PKV_ERR_INVALID, "pkv_radix_set_score: the root has no score");
   n->score = score;
-  for (Node* p = n->parent; p != r->root; p = p->parent) p->score = std::max(p->score, score);
+  r->requeue(n);
+  for (Node* p = n->parent; p != r->root; p = p->parent) {
+    p->score = std::max(p->score, score);
+    r->requeue(p);
+  }
   return PKV_OK;
 }
 
@@ -331,27 +359,19 @@ pkv_status pkv_radix_evict(pkv_radix* r, int32_t num_blocks, int32_t* released_o
   pkv::clear_error();
   if (!r || num_blocks < 0 || evicted_cap < 0 || (evicted_cap > 0 && !evicted_out))
     return pkv::fail(PKV_ERR_INVALID, "pkv_radix_evict: null argument or negative size");
-  std::priority_queue<Candidate, std::vector<Candidate>, std::greater<Candidate>> heap;
-  if (num_blocks > 0)
-    for (Node* l : r->leaves)
-      if (l->lock_ref == 0) heap.push(candidate(r, l));
   int32_t released = 0, evicted = 0;
-  while (released < num_blocks && !heap.empty()) {
-    Node* v = heap.top().node;
-    heap.pop();
+  while (released < num_blocks && !r->order.empty()) {
+    Node* v = r->order.begin()->second;
+    r->dequeue(v);
     for (int32_t b : v->blocks)
       if (r->pool->release(b)) ++released;
     Node* parent = v->parent;
     r->unlink_child(parent, v);
-    r->leaves.erase(v);
     r->cached -= static_cast<int64_t>(v->blocks.size());
     if (evicted < evicted_cap) evicted_out[evicted] = v->id;
     ++evicted;
     r->nodes.erase(v->id);
-    if (parent != r->root && parent->children.empty()) {
-      r->leaves.insert(parent);
-      if (parent->lock_ref == 0) heap.push(candidate(r, parent));
-    }
+    r->requeue(parent);
   }
   if (released_out) *released_out = released;
   if (num_evicted_out) *num_evicted_out = evicted;
@@ -399,6 +419,87 @@ pkv_status pkv_radix_node_info(const pkv_radix* r, int64_t node, int64_t* parent
   if (num_blocks) *num_blocks = nb;
   if (blocks_out && nb) std::memcpy(blocks_out, n->blocks.data(), sizeof(int32_t) * nb);
   if (tokens_out && nb) std::memcpy(tokens_out, n->tokens.data(), sizeof(int32_t) * n->tokens.size());
+  return PKV_OK;
+}
+
+pkv_status pkv_radix_admit(pkv_radix* r, const int32_t* tokens, const int64_t* offsets, int32_t n,
+                           const int64_t* seqs, int32_t* matched_out, int64_t* node_out, int32_t* num_admitted) {
+  pkv::clear_error();
+  if (!r || n < 0 || (n > 0 && (!tokens || !offsets || !seqs || !matched_out || !node_out)) || !num_admitted)
+    return pkv::fail(PKV_ERR_INVALID, "pkv_radix_admit: null argument or n < 0");
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t len = offsets[i + 1] - offsets[i];
+    if (offsets[i] < 0 || len < 1 || len > INT32_MAX)
+      return pkv::fail(PKV_ERR_INVALID, "pkv_radix_admit: request %d has %lld tokens", i, (long long)len);
+    if (r->pool->seqs.count(seqs[i]))
+      return pkv::fail(PKV_ERR_INVALID, "pkv_radix_admit: sequence %lld exists", (long long)seqs[i]);
+  }
+  {
+    std::unordered_set<int64_t> seen(seqs, seqs + n);
+    if (static_cast<int32_t>(seen.size()) != n) return pkv::fail(PKV_ERR_INVALID, "pkv_radix_admit: repeated sequence id");
+  }
+  thread_local std::vector<int32_t> blocks;
+  int32_t done = 0;
+  for (; done < n; ++done) {
+    const int32_t* t = tokens + offsets[done];
+    const int32_t len = static_cast<int32_t>(offsets[done + 1] - offsets[done]);
+    blocks.resize(static_cast<size_t>(len / r->bs) + 1);
+    int32_t m = 0;
+    int64_t node = 0;
+    pkv_radix_match(r, t, len - 1, &m, blocks.data(), static_cast<int32_t>(blocks.size()), &node);
+    pkv_radix_lock(r, node);
+    const int32_t cached = m / r->bs;
+    const int32_t need = (len + r->bs - 1) / r->bs - cached;
+    const int32_t free_now = static_cast<int32_t>(r->pool->free_list.size());
+    if (need > free_now) pkv_radix_evict(r, need - free_now, nullptr, nullptr, 0, nullptr);
+    if (pkv_seq_alloc_prefix(r->pool, seqs[done], blocks.data(), cached, len) != PKV_OK) {
+      pkv_radix_unlock(r, node);
+      break;
+    }
+    matched_out[done] = m;
+    node_out[done] = node;
+  }
+  pkv::clear_error();
+  *num_admitted = done;
+  return PKV_OK;
+}
+
+pkv_status pkv_radix_finish(pkv_radix* r, const int32_t* tokens, const int64_t* offsets, int32_t n,
+                            const int64_t* seqs, const int64_t* nodes, const double* scores, const int32_t* depths) {
+  pkv::clear_error();
+  if (!r || n < 0 || (n > 0 && (!tokens || !offsets || !seqs || !nodes)))
+    return pkv::fail(PKV_ERR_INVALID, "pkv_radix_finish: null argument or n < 0");
+  // Check everything first, so that a bad entry changes nothing.
+  std::unordered_map<int64_t, int32_t> unlocks;
+  {
+    std::unordered_set<int64_t> seen(seqs, seqs + n);
+    if (static_cast<int32_t>(seen.size()) != n) return pkv::fail(PKV_ERR_INVALID, "pkv_radix_finish: repeated sequence id");
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = r->pool->seqs.find(seqs[i]);
+    if (it == r->pool->seqs.end())
+      return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_radix_finish: sequence %lld does not exist", (long long)seqs[i]);
+    const int64_t len = offsets[i + 1] - offsets[i];
+    if (offsets[i] < 0 || len < 0 || len > it->second.len)
+      return pkv::fail(PKV_ERR_INVALID, "pkv_radix_finish: request %d: %lld tokens for a %d-token sequence", i,
+                       (long long)len, it->second.len);
+    if (scores && !std::isfinite(scores[i])) return pkv::fail(PKV_ERR_INVALID, "pkv_radix_finish: score not finite");
+    if (depths && depths[i] < 0) return pkv::fail(PKV_ERR_INVALID, "pkv_radix_finish: depth < 0");
+    Node* nd = r->get(nodes[i]);
+    if (!nd) return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_radix_finish: node %lld does not exist", (long long)nodes[i]);
+    for (Node* p = nd; p != r->root; p = p->parent)
+      if (p->lock_ref < ++unlocks[p->id])
+        return pkv::fail(PKV_ERR_INVALID, "pkv_radix_finish: node %lld is not locked", (long long)nodes[i]);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& seq = r->pool->seqs.find(seqs[i])->second;
+    const std::vector<int32_t> table = seq.table;
+    pkv_radix_insert(r, tokens + offsets[i], static_cast<int32_t>(offsets[i + 1] - offsets[i]), table.data(),
+                     static_cast<int32_t>(table.size()), scores ? scores[i] : 0.0, depths ? depths[i] : 0, nullptr,
+                     nullptr);
+    pkv_radix_unlock(r, nodes[i]);
+    pkv_seq_free(r->pool, seqs[i]);
+  }
   return PKV_OK;
 }
 

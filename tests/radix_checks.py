@@ -225,6 +225,29 @@ class PinnedCache:
     def node_info(self, node):
         return self.cache.node_info(node)
 
+    # batched calls, taken step by step through the checked calls above
+    def admit(self, requests, seqs):
+        out = []
+        for toks, seq in zip(requests, seqs):
+            m, blocks, node = self.match_prefix(list(toks)[:-1])
+            self.lock(node)
+            need = -(-len(toks) // self.bs) - len(blocks)
+            if need > self.pool.free_count():
+                self.evict(need - self.pool.free_count())
+            try:
+                self.alloc_with_prefix(seq, blocks, len(toks))
+            except MemoryError:
+                self.unlock(node)
+                break
+            out.append((m, node))
+        return out
+
+    def finish(self, requests, seqs, nodes, scores, depths):
+        for toks, seq, node, sc, dp in zip(requests, seqs, nodes, scores, depths):
+            self.insert(toks, self.pool.table(seq), sc, dp)
+            self.unlock(node)
+            self.free(seq)
+
     # pool calls the driver makes
     def alloc_with_prefix(self, seq, blocks, n):
         self.pool.alloc_with_prefix(seq, blocks, n)
@@ -256,6 +279,7 @@ class TraceDriver:
         self.history = []
         self.next_seq = 0
         self.log = []
+        self.batched = hasattr(sys, "admit")
 
     def _tokens(self):
         rng = self.rng
@@ -331,9 +355,34 @@ class TraceDriver:
         self.history.append(list(toks))
         self.log.append(("turn", seq, new_node))
 
+    def batch(self):
+        """Admit a few requests in one call, then finish a few active ones in one call."""
+        reqs = [self._tokens() for _ in range(int(self.rng.integers(1, 5)))]
+        seqs = list(range(self.next_seq, self.next_seq + len(reqs)))
+        self.next_seq += len(reqs)
+        got = self.sys.admit(reqs, seqs)
+        for (m, node), toks, seq in zip(got, reqs, seqs):
+            self.active[seq] = [toks, node]
+            self.history.append(toks)
+        self.log.append(("admit", len(reqs), len(got)) + tuple(m for m, _ in got))
+        done = [s for s in sorted(self.active) if self.active[s][1] is not None]
+        if done:
+            k = int(self.rng.integers(1, min(4, len(done)) + 1))
+            pick = [done[i] for i in sorted(self.rng.choice(len(done), size=k, replace=False))]
+            toks = [self.active[s][0] for s in pick]
+            nodes = [self.active[s][1] for s in pick]
+            scores = [float(self.rng.integers(0, 8)) / 4.0 for _ in pick]
+            depths = [int(self.rng.integers(0, 4)) for _ in pick]
+            self.sys.finish(toks, pick, nodes, scores, depths)
+            for s in pick:
+                del self.active[s]
+            self.log.append(("finish_batch",) + tuple(pick))
+
     def step(self):
         r = self.rng.random()
-        if r < 0.35 or not self.active:
+        if self.batched and r < 0.15:
+            self.batch()
+        elif r < 0.35 or not self.active:
             self.arrive()
         elif r < 0.6:
             self.finish()
@@ -499,6 +548,51 @@ def scenario_evict_blocks_in_use(Cache, Pool, bs=4):
     assert pool.free_list()[-3:] == t0
 
 
+def scenario_batched_admission(Cache, Pool, bs=16):
+    """Batched admission (reading K9).  100 users behind a 2,000-token prompt in
+    batches of 10: nothing is cached until the first batch finishes, so its 10
+    requests match nothing; every later request matches the whole prompt.  A pool
+    with room for the cached prompt plus a few tails admits requests while free
+    blocks and evictable leaves last, and releases the lock of the first request
+    that does not fit."""
+    import workloads
+
+    reqs = [[int(t) for t in r] for r in workloads.system_prompt_requests(
+        seed=5, users=100, prompt_tokens=2000, user_lo=16, user_hi=16)]   # 2,016 tokens: 126 blocks each
+    pool = Pool(126 * 10 + 8, bs)
+    cache = Cache(pool, "lru")
+    for b in range(10):
+        ids = list(range(10 * b, 10 * b + 10))
+        got = cache.admit([reqs[i] for i in ids], ids)
+        assert len(got) == 10
+        assert [m for m, _ in got] == ([0] * 10 if b == 0 else [2000] * 10), (b, got)
+        cache.finish([reqs[i] for i in ids], ids, [n for _, n in got])
+    # the prompt (125 blocks) and one 16-token tail block per user, all unlocked again
+    assert cache.cached_blocks() == 125 + 100 == cache.evictable_blocks()
+    # a repeated request leaves its last block to compute: 2,000 of its 2,016 tokens match
+    again = cache.admit([reqs[0]], [500])
+    assert again[0][0] == 2000
+    cache.finish([reqs[0]], [500], [again[0][1]])
+    pool2 = Pool(125 + 1 + 4, bs)
+    cache2 = Cache(pool2, "lru")
+    first = cache2.admit([reqs[0]], [1000])
+    cache2.finish([reqs[0]], [1000], [first[0][1]])       # prompt + 1 tail cached: 126 blocks, 4 free
+    prompt_node = cache2.match_prefix(reqs[1][:2000])[2]
+    got = cache2.admit([reqs[i] for i in range(1, 9)], list(range(2001, 2009)))
+    # each request needs 1 fresh block: 4 free ones, then the first tail's leaf is evicted -> 5 admitted
+    assert len(got) == 5 and all(m == 2000 for m, _ in got), got
+    assert cache2.node_info(prompt_node)[2] == 5          # the 6th request's lock was released
+    for bad in (([reqs[1]], [2001], [10 ** 9]),            # no such node
+                ([reqs[1], reqs[1]], [2001, 2001], [got[0][1]] * 2)):   # repeated sequence
+        try:
+            cache2.finish(*bad)
+        except (ValueError, KeyError):
+            pass
+        else:
+            raise AssertionError(f"finish accepted {bad[1]}")
+    assert cache2.node_info(prompt_node)[2] == 5 and pool2.free_count() == 0
+
+
 def scenario_rsbcm_order(Cache, Pool, bs=2):
     """RSBCM ("RKSC", §2 C): blocks go in order of branch_score / (depth + 1),
     lowest first.  Three leaves with (score, depth) = (0.9, 1), (0.3, 0),
@@ -553,4 +647,5 @@ def run_radix_pins(Cache, Pool):
     scenario_leaf_only_eviction(Cache, Pool)
     scenario_evict_blocks_in_use(Cache, Pool)
     scenario_rsbcm_order(Cache, Pool)
+    scenario_batched_admission(Cache, Pool)
     run_traces(Cache, Pool, seeds=(0, 1), steps=200)

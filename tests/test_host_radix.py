@@ -79,6 +79,12 @@ class Twin:
     def evict(self, n):
         return self._both("evict", n)
 
+    def admit(self, requests, seqs):
+        return self._both("admit", requests, seqs)
+
+    def finish(self, requests, seqs, nodes, scores, depths):
+        return self._both("finish", requests, seqs, nodes, scores, depths)
+
     def node_ids(self):
         return self.oc.node_ids()
 
@@ -128,6 +134,7 @@ def test_scenarios_on_the_library():
     rc.scenario_leaf_only_eviction(pk.RadixCache, pk.BlockPool)
     rc.scenario_evict_blocks_in_use(pk.RadixCache, pk.BlockPool)
     rc.scenario_rsbcm_order(pk.RadixCache, pk.BlockPool)
+    rc.scenario_batched_admission(pk.RadixCache, pk.BlockPool)
 
 
 def test_errors_leave_state_unchanged():

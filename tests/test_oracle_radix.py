@@ -30,6 +30,10 @@ def test_evicting_blocks_still_in_use():
     rc.scenario_evict_blocks_in_use(RadixCache, RefPool)
 
 
+def test_batched_admission():
+    rc.scenario_batched_admission(RadixCache, RefPool)
+
+
 def test_rsbcm_order():
     rc.scenario_rsbcm_order(RadixCache, RefPool)
 
@@ -104,6 +108,14 @@ RADIX_MUTANTS = [
     ("eviction stops one block early", "while released < num_blocks:", "while released < num_blocks - 1:"),
     ("score not raised on ancestors", "for n in self._path(node.parent):\n            n.score = max(n.score, float(score))",
      "for n in self._path(node.parent):\n            pass"),
+    ("admission evicts nothing", "                self.evict(need - self.pool.free_count())",
+     "                pass"),
+    ("admission keeps the lock of a request that does not fit", "                self.unlock(node)\n                break",
+     "                break"),
+    ("admission matches every token", "m, blocks, node = self.match_prefix(list(toks)[:-1])",
+     "m, blocks, node = self.match_prefix(list(toks))"),
+    ("finish forgets to unlock", "            self.unlock(node)\n            self.pool.free(seq)",
+     "            self.pool.free(seq)"),
     ("partial blocks cached", "for i in range(len(tokens) // bs)]", "for i in range(-(-len(tokens) // bs))]"),
 ]
 

@@ -30,6 +30,15 @@ new tokens from seeded torch generators on the target device):
    are pruned and 64 survivors are forked into their places, so the next
    append hits shared, partly filled tail blocks; GQA 32/8, d = 128, bf16.
 
+Request traces for the prefix cache (token ids only):
+
+* ``system_prompt_requests``: many users whose requests all begin with one
+  long system prompt (1,000 users and a 2,000-token prompt in the RadixAttention
+  section's example), each followed by the user's own tokens.
+* ``agent_sessions``: multi-turn sessions over a few shared system prompts;
+  each turn resends the session's whole history plus new tokens, and sessions
+  fork (two continuations of one history, as an agent exploring branches).
+
 Values are N(0, 1) in fp32, rounded to nearest-even fp16/bf16.  Physical
 placement is a seeded permutation of the pool (the pool's initial free list).
 The pool is the blocks a workload needs plus 25 %.
@@ -404,3 +413,54 @@ def random_forest(seed: int, num_rows: int, max_len: int, dtype: str, num_q_head
     return Workload(0, f"random_forest_{seed}", "random small forest", dtype, num_q_heads, num_kv_heads,
                     head_dim, BLOCK_SIZE, nblk, free_order, ops, [Step([], rows, [])],
                     max_blocks=_blocks(max_len) + 1, seed=seed, logical_tokens=logical, unique_tokens=0)
+
+
+# ---------------------------------------------------------------------------
+# request traces for the prefix cache
+
+
+def system_prompt_requests(seed: int = 7, users: int = 1000, prompt_tokens: int = 2000, user_lo: int = 1,
+                           user_hi: int = 256, vocab: int = 32000) -> List[np.ndarray]:
+    """Token lists (int32) of ``users`` requests: one shared ``prompt_tokens``-token
+    system prompt, then the user's own tokens (length uniform in [user_lo, user_hi])."""
+    rng = np.random.default_rng(seed)
+    prompt = rng.integers(0, vocab, size=prompt_tokens)
+    lens = rng.integers(user_lo, user_hi + 1, size=users)
+    return [np.concatenate([prompt, rng.integers(0, vocab, size=int(n))]).astype(np.int32) for n in lens]
+
+
+def agent_sessions(seed: int = 8, requests: int = 2000, prompts: int = 8, prompt_lo: int = 512,
+                   prompt_hi: int = 2048, msg_lo: int = 16, msg_hi: int = 256, open_max: int = 64,
+                   fork_p: float = 0.2, vocab: int = 32000, meta: bool = False):
+    """Token lists of a multi-turn, branching request stream.  Each request is, with
+    equal odds while fewer than ``open_max`` sessions are open, a new session (one of
+    ``prompts`` system prompts plus a message) or the next turn of a random open
+    session (its history plus a reply and a message, uniform in [msg_lo, msg_hi]
+    tokens each); a turn forks its session with probability ``fork_p`` (the old
+    history stays open as a second branch).  With ``meta``, also returns per
+    request (branch score, depth): the depth is the turn number within the
+    session's branch, the score a uniform [0, 1) draw per branch."""
+    rng = np.random.default_rng(seed)
+    sys_prompts = [rng.integers(0, vocab, size=int(rng.integers(prompt_lo, prompt_hi + 1))) for _ in range(prompts)]
+    sessions: List[list] = []   # [tokens, depth, score]
+    out, info = [], []
+    for _ in range(requests):
+        if not sessions or (len(sessions) < open_max and rng.random() < 0.5):
+            toks = np.concatenate([sys_prompts[int(rng.integers(prompts))],
+                                   rng.integers(0, vocab, size=int(rng.integers(msg_lo, msg_hi + 1)))])
+            sessions.append([toks, 0, float(rng.random())])
+            depth, score = 0, sessions[-1][2]
+        else:
+            i = int(rng.integers(len(sessions)))
+            toks = np.concatenate([sessions[i][0],
+                                   rng.integers(0, vocab, size=int(rng.integers(2 * msg_lo, 2 * msg_hi + 1)))])
+            depth = sessions[i][1] + 1
+            if rng.random() < fork_p:
+                sessions.append([toks, depth, float(rng.random())])
+                score = sessions[-1][2]
+            else:
+                sessions[i][0], sessions[i][1] = toks, depth
+                score = sessions[i][2]
+        out.append(toks.astype(np.int32))
+        info.append((score, depth))
+    return (out, info) if meta else out
