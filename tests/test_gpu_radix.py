@@ -88,6 +88,8 @@ class Harness:
         q = _bits(self.gen, (len(seqs), HQ, D))
         scale = 1.0 / np.sqrt(D)
         cplan = self.pk.CascadePlan(bt, lens, HQ, HKV, BS) if plan else None
+        if cplan is not None:
+            cplan.upload(device="cuda")
         out = self.pk.paged_decode_attn(q.cuda(), self.k, self.v, torch.from_numpy(bt).cuda(),
                                         torch.from_numpy(lens).cuda(), int(lens.max()), scale=scale, plan=cplan,
                                         dtype="bf16")
