@@ -17,7 +17,8 @@ Everything here is written from the source pages:
   section "Chunked Prefill" (with the verification pass of "RKSC", §1) for
   several new tokens attending causally at once; section "RadixAttention" for
   the prefix cache (with "RKSC", §2 C "RSBCM" for its score/depth eviction
-  order).
+  order); section "Cross-Tier Memory Offloading" for moving blocks to host
+  memory and back.
 
 Floating point is fp64.  fp16/bf16 inputs arrive as raw 16-bit patterns and
 are decoded here, independently of the GPU code.
@@ -32,7 +33,7 @@ from .attention import decode_bits, ref_decode, ref_decode_rows, bruteforce_deco
 from .extend import extend_query_positions, ref_extend
 from .fp8 import (apply_append_fp8, dequantize_heads, dequantize_pages, e4m3_decode, e4m3_encode,
                   pow2_scale_exponent, quantize_heads, ref_decode_fp8)
-from .pool import RefPool, RefPoolError, apply_append
+from .pool import RefPool, RefPoolError, apply_append, apply_swap
 from .radix import RadixCache, RadixError
 
 __all__ = [
@@ -55,6 +56,7 @@ __all__ = [
     "RefPool",
     "RefPoolError",
     "apply_append",
+    "apply_swap",
     "RadixCache",
     "RadixError",
 ]

@@ -49,6 +49,22 @@ capacity overflow, which contradicts the prose; the prose wins):
       only computes the new tokens): its table is ``prefix`` (one more reference
       each) followed by fresh blocks for the rest of the n tokens, or MemoryError
       with nothing changed.
+* R7  Swap space ("Dismantling the Memory Wall", "Cross-Tier Memory Offloading":
+      when the KV cache overflows the GPU, blocks move down to CPU memory and
+      are brought back before attention needs them).  The pool also keeps
+      ``num_host_slots`` host slots with their own FIFO free list (seeded by
+      ``host_order``).  ``swap_out(seq)`` moves, in table order, every block that
+      the sequence holds alone (count 1) to a host slot taken from the front of
+      the host list, and returns that device block to the back of the device
+      list; blocks shared with other holders stay on the device and keep the
+      sequence's reference.  ``swap_in(seq)`` takes a device block from the
+      front of the device list for each host-resident entry, in table order,
+      and returns the host slot to the back of the host list.  Both are
+      all-or-nothing (MemoryError with nothing changed) and return the copies to
+      perform: (device block, host slot) pairs out, (host slot, device block)
+      pairs in.  A swapped-out sequence cannot be appended to, forked or
+      exported; freeing it releases its host slots (table order) and its
+      remaining device references.
 """
 
 from collections import deque
@@ -61,7 +77,8 @@ class RefPoolError(ValueError):
 
 
 class RefPool:
-    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+    def __init__(self, num_blocks: int, block_size: int, free_order=None, num_host_slots: int = 0,
+                 host_order=None):
         if num_blocks < 0 or block_size <= 0:
             raise RefPoolError("num_blocks must be >= 0 and block_size > 0")
         self.num_blocks = int(num_blocks)
@@ -73,9 +90,17 @@ class RefPool:
         self._ref = [0] * self.num_blocks
         self._tables = {}
         self._lens = {}
+        self.num_host_slots = int(num_host_slots)
+        horder = list(range(self.num_host_slots)) if host_order is None else [int(x) for x in host_order]
+        if sorted(horder) != list(range(self.num_host_slots)):
+            raise RefPoolError("host_order must be a permutation of range(num_host_slots)")
+        self._host_free = deque(horder)
+        self._swapped = {}   # seq -> [("host", slot) | ("device", block)] in table order
 
     # -- queries -----------------------------------------------------------
     def table(self, seq):
+        if seq in self._swapped:
+            raise RefPoolError(f"sequence {seq!r} is swapped out")
         return list(self._tables[seq])
 
     def length(self, seq):
@@ -94,11 +119,26 @@ class RefPool:
         return list(self._tables.keys())
 
     def __contains__(self, seq):
-        return seq in self._tables
+        return seq in self._tables or seq in self._swapped
+
+    def is_swapped(self, seq):
+        return seq in self._swapped
+
+    def host_free_count(self) -> int:
+        return len(self._host_free)
+
+    def host_free_list(self):
+        return list(self._host_free)
+
+    def placement(self, seq):
+        """Table entries of a sequence as ("device", block) / ("host", slot)."""
+        if seq in self._swapped:
+            return list(self._swapped[seq])
+        return [("device", b) for b in self._tables[seq]]
 
     # -- R2 ----------------------------------------------------------------
     def alloc(self, seq, num_tokens: int):
-        if seq in self._tables:
+        if seq in self:
             raise RefPoolError(f"sequence {seq!r} already exists")
         if num_tokens < 0:
             raise RefPoolError("num_tokens must be >= 0")
@@ -116,9 +156,11 @@ class RefPool:
 
     # -- R3 ----------------------------------------------------------------
     def fork(self, parent, child):
+        if parent in self._swapped:
+            raise RefPoolError(f"parent {parent!r} is swapped out")
         if parent not in self._tables:
             raise KeyError(f"parent {parent!r} does not exist")
-        if child in self._tables:
+        if child in self:
             raise RefPoolError(f"sequence {child!r} already exists")
         for b in self._tables[parent]:
             self._ref[b] += 1
@@ -128,6 +170,16 @@ class RefPool:
 
     # -- R5 ----------------------------------------------------------------
     def free(self, seq):
+        if seq in self._swapped:
+            for kind, x in self._swapped.pop(seq):
+                if kind == "host":
+                    self._host_free.append(x)
+                else:
+                    self._ref[x] -= 1
+                    if self._ref[x] == 0:
+                        self._free.append(x)
+            del self._lens[seq]
+            return
         if seq not in self._tables:
             return
         for b in self._tables[seq]:
@@ -155,7 +207,7 @@ class RefPool:
 
     def alloc_with_prefix(self, seq, prefix_blocks, num_tokens: int):
         prefix_blocks = [int(b) for b in prefix_blocks]
-        if seq in self._tables:
+        if seq in self:
             raise RefPoolError(f"sequence {seq!r} already exists")
         if num_tokens < len(prefix_blocks) * self.block_size:
             raise RefPoolError("num_tokens must cover the prefix blocks")
@@ -176,6 +228,53 @@ class RefPool:
         self._lens[seq] = int(num_tokens)
         return list(blocks)
 
+    # -- R7 ----------------------------------------------------------------
+    def swap_out(self, seq):
+        if seq in self._swapped:
+            raise RefPoolError(f"sequence {seq!r} is already swapped out")
+        if seq not in self._tables:
+            raise KeyError(f"sequence {seq!r} does not exist")
+        table = self._tables[seq]
+        alone = [b for b in table if self._ref[b] == 1]
+        if len(alone) > len(self._host_free):
+            raise MemoryError(f"OOM: {len(alone)} host slots needed, {len(self._host_free)} free")
+        entries, copies = [], []
+        for b in table:
+            if self._ref[b] == 1:
+                h = self._host_free.popleft()
+                copies.append((b, h))
+                entries.append(("host", h))
+                self._ref[b] = 0
+                self._free.append(b)
+            else:
+                entries.append(("device", b))
+        del self._tables[seq]
+        self._swapped[seq] = entries
+        return copies
+
+    def swap_in(self, seq):
+        if seq not in self._swapped:
+            if seq in self._tables:
+                raise RefPoolError(f"sequence {seq!r} is not swapped out")
+            raise KeyError(f"sequence {seq!r} does not exist")
+        entries = self._swapped[seq]
+        need = sum(1 for kind, _ in entries if kind == "host")
+        if need > len(self._free):
+            raise MemoryError(f"OOM: {need} device blocks needed, {len(self._free)} free")
+        table, copies = [], []
+        for kind, x in entries:
+            if kind == "host":
+                y = self._free.popleft()
+                self._ref[y] = 1
+                copies.append((x, y))
+                self._host_free.append(x)
+                table.append(y)
+            else:
+                table.append(x)
+        del self._swapped[seq]
+        self._tables[seq] = table
+        return copies
+
     # -- R4 ----------------------------------------------------------------
     def plan_append(self, seqs):
         """Append one token to each sequence in ``seqs`` (batch order).
@@ -187,6 +286,8 @@ class RefPool:
         if len(set(seqs)) != len(seqs):
             raise RefPoolError("a sequence may appear at most once per append batch")
         for s in seqs:
+            if s in self._swapped:
+                raise RefPoolError(f"sequence {s!r} is swapped out")
             if s not in self._tables:
                 raise KeyError(f"sequence {s!r} does not exist")
         # capacity for the whole batch first (all-or-nothing)
@@ -233,6 +334,8 @@ class RefPool:
         bt = np.full((len(seqs), max_blocks), pad, dtype=np.int32)
         lens = np.zeros(len(seqs), dtype=np.int32)
         for i, s in enumerate(seqs):
+            if s in self._swapped:
+                raise RefPoolError(f"sequence {s!r} is swapped out")
             t = self._tables[s]
             if len(t) > max_blocks:
                 raise RefPoolError(f"sequence {s!r} has {len(t)} blocks > max_blocks {max_blocks}")
@@ -264,3 +367,13 @@ def apply_append(k_pages, v_pages, slots, cows, k_new, v_new):
         k[blk, row] = k_new[i]
         v[blk, row] = v_new[i]
     return k, v
+
+
+def apply_swap(dst_pages, src_pages, copies):
+    """Copy whole blocks: dst_pages[d] = src_pages[s] for each (s, d) in ``copies``
+    (device -> host for ``swap_out``'s (block, slot) pairs, host -> device for
+    ``swap_in``'s (slot, block) pairs).  Returns a new array."""
+    out = np.array(dst_pages, copy=True)
+    for s, d in copies:
+        out[d] = src_pages[s]
+    return out
