@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 (E4M3) pages with per-row scales: quantizing append + FP8 decode (configs 2 and 4)")
+    ap.add_argument("--swap", action="store_true",
+                    help="block swap between HBM and pinned host memory: GB/s each way, overlap with decode")
+    ap.add_argument("--swap-blocks", type=int, default=16384, help="blocks per swap batch (32 KiB of K and of V each)")
     ap.add_argument("--radix", action="store_true",
                     help="host prefix cache: request throughput and hit rate on request traces (no GPU work)")
     ap.add_argument("--extend", action="store_true",
@@ -449,6 +452,155 @@ def run_radix(args):
     print(json.dumps(line))
 
 
+def run_swap(args, dev):
+    """Swap traffic of the 8B-shaped layer (Hkv 8, d 128, bf16: 32 KiB of K and 32 KiB
+    of V per block): ``--swap-blocks`` scattered blocks out to scattered pinned host
+    slots and back, one pkv_copy_blocks launch per direction (K and V together).
+    Beside it: the same copies as runtime copies (per block, and in runs of 16
+    blocks), the rate of one contiguous copy of the same size (hipMemcpyAsync
+    through torch), and 40 decode steps of the 8B workload run alone, back to back
+    with a swap-in of a quarter of the blocks, and concurrently with it on a second
+    stream."""
+    import torch
+
+    import paged_kv_cache_21_amd as pkv
+    import workloads
+
+    n = int(args.swap_blocks)
+    hkv, d = 8, 128
+    per_block = 2 * 16 * hkv * d * 2
+    rng = np.random.default_rng(21)
+    k = torch.randint(-2 ** 15, 2 ** 15 - 1, (n, 16, hkv, d), dtype=torch.int16, device=dev)
+    v = torch.randint(-2 ** 15, 2 ** 15 - 1, (n, 16, hkv, d), dtype=torch.int16, device=dev)
+    hk = torch.empty((n, 16, hkv, d), dtype=torch.int16, pin_memory=True)
+    hv = torch.empty((n, 16, hkv, d), dtype=torch.int16, pin_memory=True)
+    dev_ids = torch.from_numpy(rng.permutation(n).astype(np.int32)).to(dev)
+    host_ids = torch.from_numpy(rng.permutation(n).astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = max(args.steps // 10, 3)
+    out_ms = timed(lambda: pkv.copy_blocks([hk, hv], [k, v], host_ids, dev_ids, stream=stream), reps)
+    in_ms = timed(lambda: pkv.copy_blocks([k, v], [hk, hv], dev_ids, host_ids, stream=stream), reps)
+    dev_np, host_np = dev_ids.cpu().numpy(), host_ids.cpu().numpy()
+    mc_out_ms = timed(lambda: pkv.copy_blocks_memcpy([hk, hv], [k, v], host_np, dev_np, stream=stream), reps)
+    mc_in_ms = timed(lambda: pkv.copy_blocks_memcpy([k, v], [hk, hv], dev_np, host_np, stream=stream), reps)
+    # runs of 16 consecutive blocks on both sides (256-token pieces of sequences), in shuffled order
+    run = 16
+    perm_d, perm_h = rng.permutation(n // run), rng.permutation(n // run)
+    run_dev = (perm_d[:, None] * run + np.arange(run)[None, :]).reshape(-1).astype(np.int32)
+    run_host = (perm_h[:, None] * run + np.arange(run)[None, :]).reshape(-1).astype(np.int32)
+    mc_run_in_ms = timed(lambda: pkv.copy_blocks_memcpy([k, v], [hk, hv], run_dev, run_host, stream=stream), reps)
+    capped = {}
+    for g in (16, 32, 64, 128, 256):
+        capped[g] = timed(lambda: pkv.copy_blocks([k, v], [hk, hv], dev_ids, host_ids, stream=stream,
+                                                  max_workgroups=g), reps)
+    # the last swap-out and swap-in moved the same bytes: sampled blocks agree
+    chk = torch.from_numpy(rng.integers(0, n, size=64)).to(dev)
+    assert torch.equal(k[dev_ids[chk].long()].cpu(), hk[host_ids[chk].long().cpu()])
+    # the link's own rate: one contiguous copy of the same bytes each way
+    kf, hkf = k.view(-1), hk.view(-1)
+    d2h_ms = timed(lambda: hkf.copy_(kf, non_blocking=True), reps) * 2   # K only: scale to K+V
+    h2d_ms = timed(lambda: kf.copy_(hkf, non_blocking=True), reps) * 2
+    gb = n * per_block / 1e9
+    out_gbs, in_gbs, d2h_gbs, h2d_gbs = gb / (out_ms / 1e3), gb / (in_ms / 1e3), gb / (d2h_ms / 1e3), gb / (h2d_ms / 1e3)
+    mc_out_gbs, mc_in_gbs = gb / (mc_out_ms / 1e3), gb / (mc_in_ms / 1e3)
+    mc_run_in_gbs = gb / (mc_run_in_ms / 1e3)
+    print(f"[bench] swap {n} blocks ({gb:.2f} GB): kernel out {out_ms:.2f} ms = {out_gbs:.1f} GB/s, "
+          f"in {in_ms:.2f} ms = {in_gbs:.1f} GB/s; runtime copies per block out {mc_out_gbs:.1f}, "
+          f"in {mc_in_gbs:.1f} GB/s, in runs of {run} {mc_run_in_gbs:.1f} GB/s; "
+          f"contiguous copy d2h {d2h_gbs:.1f}, h2d {h2d_gbs:.1f} GB/s", file=sys.stderr, flush=True)
+
+    # overlap: decode steps of the 8B workload with a concurrent swap-in of a quarter of the blocks
+    w = workloads.get(2)
+    kp, vp = workloads.make_pages(w, device=dev)
+    pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(pool, w.build_ops)
+    bt, lens = pool.export_tables(w.steps[0].decode_rows, w.max_blocks)
+    q = workloads.make_q(w, 0, device=dev)
+    bt_d, lens_d = torch.from_numpy(bt).to(dev), torch.from_numpy(lens).to(dev)
+    max_len = int(lens.max())
+    ws = torch.empty(pkv.decode_workspace_bytes(len(lens), w.num_q_heads, w.num_kv_heads, w.head_dim, max_len),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((len(lens), w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream(dev)
+    m = n // 4
+    sub_dev, sub_host = dev_ids[:m].contiguous(), host_ids[:m].contiguous()
+    sub_dev_np, sub_host_np = run_dev[:m].copy(), run_host[:m].copy()
+    steps = 40
+
+    def decode_steps(st):
+        for _ in range(steps):
+            pkv.paged_decode_attn(q, kp, vp, bt_d, lens_d, max_len, scale=w.scale, workspace=ws, out=o,
+                                  dtype=w.dtype, stream=st)
+
+    cap = [0]
+
+    def swap_in(st):
+        if cap[0] < 0:
+            pkv.copy_blocks_memcpy([k, v], [hk, hv], sub_dev_np, sub_host_np, stream=st)
+        else:
+            pkv.copy_blocks([k, v], [hk, hv], sub_dev, sub_host, stream=st, max_workgroups=cap[0])
+
+    def wall(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3
+
+    def both():
+        side.wait_stream(stream)
+        swap_in(side)
+        decode_steps(stream)
+        stream.wait_stream(side)
+
+    t_dec = wall(lambda: decode_steps(stream))
+    overlap = {}
+    for g in (0, 32, -1):
+        cap[0] = g
+        t_swp = wall(lambda: swap_in(stream))
+        t_serial = wall(lambda: (decode_steps(stream), swap_in(stream)))
+        t_both = wall(both)
+        hidden = (t_serial - t_both) / min(t_dec, t_swp) if min(t_dec, t_swp) > 0 else 0.0
+        overlap[g] = {"swap_in_ms": round(t_swp, 3), "back_to_back_ms": round(t_serial, 3),
+                      "concurrent_ms": round(t_both, 3), "hidden_fraction": round(hidden, 3)}
+        how = "runtime copies, runs of 16" if g < 0 else f"copy kernel, {g or 'one work-group per block'}"
+        print(f"[bench] overlap ({how}): {steps} decode steps {t_dec:.2f} ms, "
+              f"swap-in of {m} blocks {t_swp:.2f} ms, back to back {t_serial:.2f} ms, concurrent {t_both:.2f} ms "
+              f"({hidden:.0%} of the shorter hidden)", file=sys.stderr, flush=True)
+    line = {"metric": "swap_in_gb_per_s", "value": round(in_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": reps,
+            "warmup": 2, "ms_per_step": round(in_ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"swap of {n} scattered blocks, Hkv 8, d 128, bf16 (K and V, {per_block} B per block)",
+                       "swap_out_gb_per_s": round(out_gbs, 2), "contiguous_copy_d2h_gb_per_s": round(d2h_gbs, 2),
+                       "contiguous_copy_h2d_gb_per_s": round(h2d_gbs, 2),
+                       "swap_in_gb_per_s_by_workgroups": {str(g): round(gb / (t / 1e3), 2) for g, t in capped.items()},
+                       "overlap": {"decode_steps": steps, "decode_ms": round(t_dec, 3), "swap_in_blocks": m,
+                                   "by_path": {("runtime_copies" if g < 0 else f"kernel_{g}"): v for g, v in overlap.items()}},
+                       "runtime_copies_per_block_out_gb_per_s": round(mc_out_gbs, 2),
+                       "runtime_copies_per_block_in_gb_per_s": round(mc_in_gbs, 2),
+                       "runtime_copies_runs_of_16_in_gb_per_s": round(mc_run_in_gbs, 2)},
+            "roofline": {"bound": "host link", "achieved": round(in_gbs, 2), "peak": 64.0, "unit": "GB/s",
+                         "frac": round(in_gbs / 64.0, 4), "traffic": None,
+                         "frac_of_contiguous_copy": round(in_gbs / h2d_gbs, 4)},
+            "cpu_baseline": None}
+    print(json.dumps(line))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -470,6 +622,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.swap:
+        return run_swap(args, dev)
     w = workloads.get(args.config)
     print(f"[bench] workload {w.number} {w.name}: {w.description}", file=sys.stderr, flush=True)
     if args.extend or args.config == 6:

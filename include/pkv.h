@@ -218,13 +218,80 @@ pkv_status pkv_export_tables(const pkv_pool* pool, const int64_t* seqs, int32_t 
                              int32_t* tables_out, int32_t* lens_out);
 
 int32_t pkv_seq_len(const pkv_pool* pool, int64_t seq);     /* -1 if unknown */
-/* Copy up to cap entries of seq's block table; returns its block count (-1 if unknown). */
+/* Copy up to cap entries of seq's block table; returns its block count (-1 if unknown,
+ * -2 if swapped out). */
 int32_t pkv_seq_table(const pkv_pool* pool, int64_t seq, int32_t* out, int32_t cap);
 int32_t pkv_refcount(const pkv_pool* pool, int32_t block);  /* -1 if out of range */
 int32_t pkv_free_count(const pkv_pool* pool);
 int32_t pkv_num_seqs(const pkv_pool* pool);
 /* Copy up to cap free-list entries, front first; returns the free count. */
 int32_t pkv_free_list(const pkv_pool* pool, int32_t* out, int32_t cap);
+
+/* ------------------------------------------------------------------------------------------
+ * Swap space ("Dismantling the Memory Wall", "Cross-Tier Memory Offloading": KV blocks
+ * that overflow the GPU move down to CPU memory and are brought back before attention
+ * needs them).
+ *
+ * The pool keeps host slots (one block each, in caller-owned pinned host buffers) with
+ * their own FIFO free list.  A swap-out moves the blocks a sequence holds alone
+ * (count 1), in table order, to host slots from the front of the host list and returns
+ * those device blocks to the back of the device free list; blocks it shares stay on the
+ * device with its reference.  A swap-in takes a device block from the front of the
+ * device list for each host-resident entry and returns the slot to the back of the host
+ * list.  Both are all-or-nothing (PKV_ERR_OOM with nothing changed) and return the
+ * copies that pkv_copy_blocks must perform, on the stream that later reads or reuses
+ * the blocks.  A swapped-out sequence cannot be appended to, forked, exported or cached
+ * (PKV_ERR_INVALID); freeing it returns its host slots in table order and drops its
+ * remaining device references.
+ * ---------------------------------------------------------------------------------------- */
+
+/* Once per pool: num_host_slots host slots, free list seeded by host_order (a
+ * permutation, NULL for 0, 1, 2, ...).  PKV_ERR_INVALID if already set. */
+pkv_status pkv_pool_set_host_slots(pkv_pool* pool, int32_t num_host_slots, const int32_t* host_order);
+
+/* Copies (device_blocks_out[i] -> host_slots_out[i]), *num_copies of them; capacity
+ * must cover the sequence's unshared blocks. */
+pkv_status pkv_seq_swap_out(pkv_pool* pool, int64_t seq, int32_t* device_blocks_out, int32_t* host_slots_out,
+                            int32_t capacity, int32_t* num_copies);
+/* Copies (host_slots_out[i] -> device_blocks_out[i]). */
+pkv_status pkv_seq_swap_in(pkv_pool* pool, int64_t seq, int32_t* host_slots_out, int32_t* device_blocks_out,
+                           int32_t capacity, int32_t* num_copies);
+int32_t pkv_seq_is_swapped(const pkv_pool* pool, int64_t seq);  /* 1, 0, or -1 if unknown */
+/* Up to cap table entries (block ids, or host slots where on_host_out[i] = 1); returns
+ * the entry count, -1 if unknown. */
+int32_t pkv_seq_placement(const pkv_pool* pool, int64_t seq, int32_t* ids_out, int8_t* on_host_out, int32_t cap);
+int32_t pkv_host_free_count(const pkv_pool* pool);
+/* Copy up to cap host free-list entries, front first; returns the count. */
+int32_t pkv_host_free_list(const pkv_pool* pool, int32_t* out, int32_t cap);
+
+/* Device op: whole-block copies between two block arrays, each in device memory or in
+ * pinned host memory (hipHostMalloc, torch pin_memory), e.g. K and V pages (and FP8
+ * scale arrays) to and from host slot buffers.  For i < n and each array k <
+ * num_arrays (1..4): block dst_ids[i] of dst[k] = block src_ids[i] of src[k],
+ * block_bytes[k] bytes each (a positive multiple of 16; arrays 16-byte aligned;
+ * dst[k] holds dst_blocks blocks, src[k] src_blocks).  dst, src and block_bytes are
+ * host arrays of num_arrays entries; dst_ids and src_ids are int32 arrays of n
+ * entries in device or pinned host memory.  Ids outside [0, dst_blocks) /
+ * [0, src_blocks) are skipped; repeated destinations race.  Memory that HIP does not
+ * know as device memory or as device-mapped host memory is refused
+ * (PKV_ERR_INVALID).  max_workgroups > 0 caps the launch (the work-groups loop over
+ * the blocks), leaving the rest of the chip to kernels that run beside the copy, e.g.
+ * a prefetch on a second stream under decode; 0 launches one work-group per block
+ * and array.  One launch on `stream`; no synchronization. */
+pkv_status pkv_copy_blocks(int32_t num_arrays, void* const* dst, const void* const* src, const int64_t* block_bytes,
+                           int64_t dst_blocks, int64_t src_blocks, const int32_t* dst_ids, const int32_t* src_ids,
+                           int32_t n, int32_t max_workgroups, void* stream);
+
+/* The same copies as runtime copies: one hipMemcpyAsync per run of consecutive ids on
+ * both sides (the runtime picks the engine; ROCm 7 runs them as short blit kernels).
+ * Many short copies interleave with a long kernel on another stream, where one
+ * pkv_copy_blocks launch holding compute units would delay it: the prefetch path
+ * under decode.  dst_ids / src_ids are HOST int32 arrays here; an id out of range is
+ * PKV_ERR_INVALID (nothing enqueued).  Each run costs a host enqueue (about 10 us), so
+ * scattered single blocks are slow to issue; host block arrays must be pinned. */
+pkv_status pkv_copy_blocks_memcpy(int32_t num_arrays, void* const* dst, const void* const* src,
+                               const int64_t* block_bytes, int64_t dst_blocks, int64_t src_blocks,
+                               const int32_t* dst_ids, const int32_t* src_ids, int32_t n, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Prefix cache ("Dismantling the Memory Wall", "RadixAttention: The Tree of Life
@@ -467,8 +534,8 @@ int64_t pkv_plan_image(const pkv_plan* plan, int32_t* out, int64_t capacity, int
  * library is bracketed with HIP events on its own stream; pkv_timing_read()
  * synchronizes those events and returns the summed duration and count per
  * kernel since the last reset.  Kernel ids: 0 append, 1 split-K decode,
- * 2 partial merge, 3 cascade / extend matrix-core pass.  Costs two event
- * records per launch when on.
+ * 2 partial merge, 3 cascade / extend matrix-core pass, 4 block copy.  Costs two
+ * event records per launch when on.
  * ---------------------------------------------------------------------------------------- */
 /* Measurement yardstick: read `bytes` (a multiple of 16) of device memory `buf` as
  * a plain streaming read (16-byte loads, `grid` work-groups of 256 threads; 0 picks
@@ -478,7 +545,7 @@ int64_t pkv_plan_image(const pkv_plan* plan, int32_t* out, int64_t capacity, int
 pkv_status pkv_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, void* stream);
 
 enum { PKV_KERNEL_APPEND = 0, PKV_KERNEL_DECODE_SPLIT = 1, PKV_KERNEL_MERGE = 2, PKV_KERNEL_CASCADE = 3,
-       PKV_NUM_KERNELS = 4 };
+       PKV_KERNEL_COPY = 4, PKV_NUM_KERNELS = 5 };
 pkv_status pkv_timing_enable(int32_t on);
 pkv_status pkv_timing_reset(void);
 pkv_status pkv_timing_read(int32_t kernel, double* total_ms, int64_t* launches);

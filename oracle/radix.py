@@ -262,6 +262,8 @@ class RadixCache:
         for i, (toks, seq, node) in enumerate(zip(requests, seqs, nodes)):
             if seq not in self.pool:
                 raise KeyError(f"sequence {seq} does not exist")
+            if self.pool.is_swapped(seq):
+                raise RadixError(f"sequence {seq} is swapped out")
             if len(toks) > self.pool.length(seq):
                 raise RadixError("finish: more tokens than the sequence holds")
             for n in self._path(self._node(node)):

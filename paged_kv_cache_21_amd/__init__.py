@@ -129,6 +129,15 @@ _SIGNATURES = {
     "pkv_paged_decode_attn_fp8": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _vp,
                                          _i32, _vp, _i32, _f32, _vp, _sz, _vp, _vp]),
     "pkv_stream_read": (_i32, [_vp, _i64, _vp, _i32, _vp]),
+    "pkv_pool_set_host_slots": (_i32, [_vp, _i32, _vp]),
+    "pkv_seq_swap_out": (_i32, [_vp, _i64, _vp, _vp, _i32, _vp]),
+    "pkv_seq_swap_in": (_i32, [_vp, _i64, _vp, _vp, _i32, _vp]),
+    "pkv_seq_is_swapped": (_i32, [_vp, _i64]),
+    "pkv_seq_placement": (_i32, [_vp, _i64, _vp, _vp, _i32]),
+    "pkv_host_free_count": (_i32, [_vp]),
+    "pkv_host_free_list": (_i32, [_vp, _vp, _i32]),
+    "pkv_copy_blocks": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _vp]),
+    "pkv_copy_blocks_memcpy": (_i32, [_i32, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _vp]),
     "pkv_timing_enable": (_i32, [_i32]),
     "pkv_timing_reset": (_i32, []),
     "pkv_timing_read": (_i32, [_i32, _vp, _vp]),
@@ -344,7 +353,7 @@ def paged_decode_attn(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len, 
 class BlockPool:
     """Reference-counted block pool with fork / copy-on-write append / free (runs in libpkv)."""
 
-    def __init__(self, num_blocks, block_size=16, free_order=None):
+    def __init__(self, num_blocks, block_size=16, free_order=None, num_host_slots=0, host_order=None):
         order = None
         if free_order is not None:
             order = np.ascontiguousarray(free_order, dtype=np.int32)
@@ -358,6 +367,11 @@ class BlockPool:
         self._table_buf = np.empty(1024, dtype=np.int32)
         self.num_blocks = int(num_blocks)
         self.block_size = int(block_size)
+        self.num_host_slots = int(num_host_slots)
+        if num_host_slots:
+            ho = None if host_order is None else np.ascontiguousarray(host_order, dtype=np.int32)
+            _require(ho is None or ho.shape == (num_host_slots,), "host_order must have num_host_slots entries")
+            _check(_lib.pkv_pool_set_host_slots(h, int(num_host_slots), _ptr(ho)))
 
     def __del__(self):
         h = getattr(self, "_handle", None)
@@ -407,6 +421,8 @@ class BlockPool:
     def table(self, seq):
         buf = self._table_buf
         n = _lib.pkv_seq_table(self._handle, int(seq), buf.ctypes.data, buf.shape[0])
+        if n == -2:
+            raise PkvInvalid(PKV_ERR_INVALID, f"sequence {seq} is swapped out")
         if n < 0:
             raise PkvNotFound(PKV_ERR_NOT_FOUND, f"sequence {seq} does not exist")
         if n > buf.shape[0]:
@@ -434,6 +450,47 @@ class BlockPool:
 
     def __contains__(self, seq):
         return self.length(seq) >= 0
+
+    # swap space
+    def _swap(self, fn, seq):
+        n = max(self.length(seq), 0)
+        cap = max(-(-n // self.block_size), 1)
+        a = np.empty(cap, dtype=np.int32)
+        b = np.empty(cap, dtype=np.int32)
+        cnt = np.zeros(1, dtype=np.int32)
+        _check(fn(self._handle, int(seq), a.ctypes.data, b.ctypes.data, cap, cnt.ctypes.data))
+        k = int(cnt[0])
+        return list(zip(a[:k].tolist(), b[:k].tolist()))
+
+    def swap_out(self, seq):
+        """Plan a swap-out; returns the (device block, host slot) copies to perform."""
+        return self._swap(_lib.pkv_seq_swap_out, seq)
+
+    def swap_in(self, seq):
+        """Plan a swap-in; returns the (host slot, device block) copies to perform."""
+        return self._swap(_lib.pkv_seq_swap_in, seq)
+
+    def is_swapped(self, seq):
+        return _lib.pkv_seq_is_swapped(self._handle, int(seq)) == 1
+
+    def placement(self, seq):
+        n = max(self.length(seq), 0)
+        cap = max(-(-n // self.block_size), 1)
+        ids = np.empty(cap, dtype=np.int32)
+        host = np.empty(cap, dtype=np.int8)
+        k = _lib.pkv_seq_placement(self._handle, int(seq), ids.ctypes.data, host.ctypes.data, cap)
+        if k < 0:
+            raise PkvNotFound(PKV_ERR_NOT_FOUND, f"sequence {seq} does not exist")
+        return [("host" if h else "device", int(i)) for i, h in zip(ids[:k], host[:k])]
+
+    def host_free_count(self):
+        return int(_lib.pkv_host_free_count(self._handle))
+
+    def host_free_list(self):
+        n = self.host_free_count()
+        out = np.empty(max(n, 1), dtype=np.int32)
+        _lib.pkv_host_free_list(self._handle, out.ctypes.data, n)
+        return out[:n].tolist()
 
 
 # ---------------------------------------------------------------------------
@@ -731,6 +788,55 @@ def paged_extend_attn(q, k_pages, v_pages, plan, scale=None, workspace=None, out
 
 # ---------------------------------------------------------------------------
 # timing
+
+
+def copy_blocks(dst, src, dst_ids, src_ids, stream=None, max_workgroups=0):
+    """Block copies between block arrays (device tensors or pinned host tensors):
+    block dst_ids[i] of each dst[k] = block src_ids[i] of src[k].  dst and src are
+    equal-length lists of tensors whose first dimension counts blocks; the id
+    tensors are int32 on the device (or pinned host memory).  ``max_workgroups``
+    caps the launch (0: one work-group per block and array)."""
+    _require(len(dst) == len(src) and 1 <= len(dst) <= 4, "1..4 destination / source arrays")
+    n = int(dst_ids.numel())
+    _require(int(src_ids.numel()) == n, "dst_ids and src_ids differ in length")
+    for t in (dst_ids, src_ids):
+        _require(str(t.dtype) == "torch.int32" and t.is_contiguous(), "ids must be contiguous int32 tensors")
+    nd, ns = int(dst[0].shape[0]), int(src[0].shape[0])
+    bb = []
+    for d, s in zip(dst, src):
+        _require(d.is_contiguous() and s.is_contiguous(), "block arrays must be contiguous")
+        _require(d.shape[0] == nd and s.shape[0] == ns, "every array of one side must hold the same block count")
+        b = d[0].numel() * d.element_size() if nd else s[0].numel() * s.element_size()
+        _require(s[0].numel() * s.element_size() == b if ns else True, "block sizes differ between dst and src")
+        bb.append(b)
+    dp = (_vp * len(dst))(*[t.data_ptr() for t in dst])
+    sp = (_vp * len(src))(*[t.data_ptr() for t in src])
+    bytes_ = (_i64 * len(dst))(*bb)
+    dev = dst_ids if dst_ids.is_cuda else (dst[0] if dst[0].is_cuda else src[0])
+    _check(_lib.pkv_copy_blocks(len(dst), dp, sp, bytes_, nd, ns, _ptr(dst_ids), _ptr(src_ids), n,
+                                int(max_workgroups), _stream(stream, dev)))
+
+
+def copy_blocks_memcpy(dst, src, dst_ids, src_ids, stream=None):
+    """``copy_blocks`` as one runtime copy per run of consecutive ids; ids are host sequences of ints."""
+    _require(len(dst) == len(src) and 1 <= len(dst) <= 4, "1..4 destination / source arrays")
+    di = np.ascontiguousarray(dst_ids, dtype=np.int32)
+    si = np.ascontiguousarray(src_ids, dtype=np.int32)
+    _require(di.shape == si.shape and di.ndim == 1, "dst_ids and src_ids differ in shape")
+    nd, ns = int(dst[0].shape[0]), int(src[0].shape[0])
+    bb = []
+    for d, s in zip(dst, src):
+        _require(d.is_contiguous() and s.is_contiguous(), "block arrays must be contiguous")
+        _require(d.shape[0] == nd and s.shape[0] == ns, "every array of one side must hold the same block count")
+        b = d[0].numel() * d.element_size() if nd else s[0].numel() * s.element_size()
+        _require(s[0].numel() * s.element_size() == b if ns else True, "block sizes differ between dst and src")
+        bb.append(b)
+    dp = (_vp * len(dst))(*[t.data_ptr() for t in dst])
+    sp = (_vp * len(src))(*[t.data_ptr() for t in src])
+    bytes_ = (_i64 * len(dst))(*bb)
+    dev = dst[0] if dst[0].is_cuda else src[0]
+    _check(_lib.pkv_copy_blocks_memcpy(len(dst), dp, sp, bytes_, nd, ns, di.ctypes.data, si.ctypes.data, di.shape[0],
+                                    _stream(stream, dev)))
 
 
 def stream_read(buf, sink, grid=0, stream=None):

@@ -475,6 +475,114 @@ pkv_status pkv_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32
   return PKV_OK;
 }
 
+namespace {
+
+// Device address of a block array: device memory as is, pinned host memory through
+// its device mapping; anything else (pageable host memory) is refused.
+bool device_address(const void* p, const char** where, char** out) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    *where = "memory unknown to HIP (pageable host memory?)";
+    return false;
+  }
+  if (attr.type == hipMemoryTypeDevice) {
+    *out = static_cast<char*>(const_cast<void*>(p));
+    return true;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer) {
+    // the mapping of the allocation's base; keep p's offset inside it
+    const char* host_base = static_cast<const char*>(attr.hostPointer ? attr.hostPointer : p);
+    *out = static_cast<char*>(attr.devicePointer) + (static_cast<const char*>(p) - host_base);
+    return true;
+  }
+  *where = "host memory without a device mapping";
+  return false;
+}
+
+}  // namespace
+
+pkv_status pkv_copy_blocks(int32_t num_arrays, void* const* dst, const void* const* src, const int64_t* block_bytes,
+                           int64_t dst_blocks, int64_t src_blocks, const int32_t* dst_ids, const int32_t* src_ids,
+                           int32_t n, int32_t max_workgroups, void* stream) {
+  pkv::clear_error();
+  if (num_arrays < 1 || num_arrays > 4 || !dst || !src || !block_bytes || n < 0 || dst_blocks < 0 || src_blocks < 0 ||
+      max_workgroups < 0)
+    return fail(PKV_ERR_INVALID, "pkv_copy_blocks: invalid arguments (1..4 arrays, n >= 0)");
+  if (n > 0 && (!dst_ids || !src_ids)) return fail(PKV_ERR_INVALID, "pkv_copy_blocks: null id arrays");
+  if (n == 0) return PKV_OK;
+  pkv::CopyArgs a{};
+  a.num_arrays = num_arrays;
+  for (int32_t k = 0; k < num_arrays; ++k) {
+    if (!dst[k] || !src[k] || block_bytes[k] <= 0 || block_bytes[k] % 16 != 0)
+      return fail(PKV_ERR_INVALID, "pkv_copy_blocks: array %d: null pointer or block_bytes not a positive multiple of 16", k);
+    if (!pkv::aligned16(dst[k]) || !pkv::aligned16(src[k]))
+      return fail(PKV_ERR_INVALID, "pkv_copy_blocks: array %d is not 16-byte aligned", k);
+    const char* why = nullptr;
+    char* p = nullptr;
+    if (!device_address(dst[k], &why, &p)) return fail(PKV_ERR_INVALID, "pkv_copy_blocks: destination %d: %s", k, why);
+    a.dst[k] = p;
+    if (!device_address(src[k], &why, &p)) return fail(PKV_ERR_INVALID, "pkv_copy_blocks: source %d: %s", k, why);
+    a.src[k] = p;
+    a.block_bytes[k] = block_bytes[k];
+  }
+  for (int32_t k = 0; k < 2; ++k) {  // id arrays are read by the kernel: device memory or pinned host memory
+    const char* why = nullptr;
+    char* p = nullptr;
+    if (!device_address(k == 0 ? static_cast<const void*>(dst_ids) : static_cast<const void*>(src_ids), &why, &p))
+      return fail(PKV_ERR_INVALID, "pkv_copy_blocks: %s ids: %s", k == 0 ? "destination" : "source", why);
+    (k == 0 ? a.dst_ids : a.src_ids) = reinterpret_cast<const int32_t*>(p);
+  }
+  a.dst_blocks = dst_blocks;
+  a.src_blocks = src_blocks;
+  a.n = n;
+  a.max_workgroups = max_workgroups;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return pkv::launch(PKV_KERNEL_COPY, "pkv_copy_blocks", s, [&] { return pkv::launch_copy_blocks(a, s); });
+}
+
+pkv_status pkv_copy_blocks_memcpy(int32_t num_arrays, void* const* dst, const void* const* src,
+                               const int64_t* block_bytes, int64_t dst_blocks, int64_t src_blocks,
+                               const int32_t* dst_ids, const int32_t* src_ids, int32_t n, void* stream) {
+  pkv::clear_error();
+  if (num_arrays < 1 || num_arrays > 4 || !dst || !src || !block_bytes || n < 0 || dst_blocks < 0 || src_blocks < 0)
+    return fail(PKV_ERR_INVALID, "pkv_copy_blocks_memcpy: invalid arguments (1..4 arrays, n >= 0)");
+  if (n > 0 && (!dst_ids || !src_ids)) return fail(PKV_ERR_INVALID, "pkv_copy_blocks_memcpy: null id arrays");
+  for (int32_t i = 0; i < n; ++i)
+    if (dst_ids[i] < 0 || dst_ids[i] >= dst_blocks || src_ids[i] < 0 || src_ids[i] >= src_blocks)
+      return fail(PKV_ERR_INVALID, "pkv_copy_blocks_memcpy: entry %d (%d <- %d) out of range", i, dst_ids[i], src_ids[i]);
+  for (int32_t k = 0; k < num_arrays; ++k) {
+    if (!dst[k] || !src[k] || block_bytes[k] <= 0)
+      return fail(PKV_ERR_INVALID, "pkv_copy_blocks_memcpy: array %d: null pointer or block_bytes <= 0", k);
+    const char* why = nullptr;
+    char* p = nullptr;
+    if (!device_address(dst[k], &why, &p)) return fail(PKV_ERR_INVALID, "pkv_copy_blocks_memcpy: destination %d: %s", k, why);
+    if (!device_address(src[k], &why, &p)) return fail(PKV_ERR_INVALID, "pkv_copy_blocks_memcpy: source %d: %s", k, why);
+  }
+  if (n == 0) return PKV_OK;
+  // runs of consecutive (dst, src) ids become one copy each
+  std::vector<void*> dsts, srcs;
+  std::vector<size_t> sizes;
+  for (int32_t i = 0; i < n;) {
+    int32_t r = 1;
+    while (i + r < n && dst_ids[i + r] == dst_ids[i] + r && src_ids[i + r] == src_ids[i] + r) ++r;
+    for (int32_t k = 0; k < num_arrays; ++k) {
+      dsts.push_back(static_cast<char*>(dst[k]) + static_cast<int64_t>(dst_ids[i]) * block_bytes[k]);
+      srcs.push_back(static_cast<char*>(const_cast<void*>(src[k])) + static_cast<int64_t>(src_ids[i]) * block_bytes[k]);
+      sizes.push_back(static_cast<size_t>(r) * static_cast<size_t>(block_bytes[k]));
+    }
+    i += r;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return pkv::launch(PKV_KERNEL_COPY, "pkv_copy_blocks_memcpy", s, [&] {
+    for (size_t c = 0; c < sizes.size(); ++c) {
+      const hipError_t e = hipMemcpyAsync(dsts[c], srcs[c], sizes[c], hipMemcpyDefault, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  });
+}
+
 pkv_status pkv_timing_enable(int32_t on) {
   pkv::clear_error();
   auto& t = pkv::timing();

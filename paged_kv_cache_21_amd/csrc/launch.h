@@ -8,6 +8,24 @@
 
 namespace pkv {
 
+// Block copies: for i < n and array k < num_arrays, block dst_ids[i] of dst[k]
+// gets block src_ids[i] of src[k] (block_bytes[k] bytes, a multiple of 16).
+// Pointers are device addresses (for pinned host memory, its device mapping).
+struct CopyArgs {
+  char* dst[4];
+  const char* src[4];
+  int64_t block_bytes[4];
+  int32_t num_arrays;
+  int64_t dst_blocks;
+  int64_t src_blocks;
+  const int32_t* dst_ids;
+  const int32_t* src_ids;
+  int32_t n;
+  int32_t max_workgroups;  // 0: one work-group per (block, array) item
+};
+
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+
 struct AppendArgs {
   uint16_t* k_pages;  // 16-bit pages; FP8 pages: byte arrays (cast)
   uint16_t* v_pages;

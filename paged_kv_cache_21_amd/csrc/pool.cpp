@@ -16,6 +16,14 @@
 // shared and partly filled gets a fresh block holding a copy of the valid rows.
 // Order is deterministic: a FIFO free list seeded by the caller, batches
 // processed in the order given.
+//
+// Swap space ("Dismantling the Memory Wall", "Cross-Tier Memory Offloading":
+// KV blocks that overflow the GPU move to CPU memory and come back before
+// attention): host slots with their own FIFO list.  A swap-out moves the blocks
+// a sequence holds alone to host slots and frees them on the device; blocks it
+// shares stay on the device with its reference.  A swap-in takes device blocks
+// for the host-resident entries.  Both are all-or-nothing and return the block
+// copies that pkv_copy_blocks performs.
 #include <algorithm>
 #include <unordered_set>
 
@@ -124,6 +132,7 @@ pkv_status pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t child) {
   if (!pool) return pkv::fail(PKV_ERR_INVALID, "pkv_seq_fork: null pool");
   auto it = pool->seqs.find(parent);
   if (it == pool->seqs.end()) return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_seq_fork: parent %lld does not exist", (long long)parent);
+  if (it->second.swapped) return pkv::fail(PKV_ERR_INVALID, "pkv_seq_fork: parent %lld is swapped out", (long long)parent);
   if (pool->seqs.count(child)) return pkv::fail(PKV_ERR_INVALID, "pkv_seq_fork: sequence %lld exists", (long long)child);
   pkv_pool::Seq s = it->second;  // copy of the table, partly filled tail included
   for (int32_t b : s.table) pool->ref[b] += 1;
@@ -136,8 +145,13 @@ pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq) {
   if (!pool) return pkv::fail(PKV_ERR_INVALID, "pkv_seq_free: null pool");
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return PKV_OK;  // unknown id: nothing to do
-  for (int32_t b : it->second.table) {
-    if (--pool->ref[b] == 0) pool->free_list.push_back(b);
+  const auto& s = it->second;
+  for (size_t i = 0; i < s.table.size(); ++i) {
+    const int32_t b = s.table[i];
+    if (s.swapped && s.on_host[i])
+      pool->host_free.push_back(b);
+    else if (--pool->ref[b] == 0)
+      pool->free_list.push_back(b);
   }
   pool->seqs.erase(it);
   return PKV_OK;
@@ -159,6 +173,8 @@ pkv_status pkv_plan_append(pkv_pool* pool, const int64_t* seqs, int32_t n, int64
         return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_plan_append: sequence %lld does not exist", (long long)seqs[i]);
       if (!seen.insert(seqs[i]).second)
         return pkv::fail(PKV_ERR_INVALID, "pkv_plan_append: sequence %lld appears twice", (long long)seqs[i]);
+      if (it->second.swapped)
+        return pkv::fail(PKV_ERR_INVALID, "pkv_plan_append: sequence %lld is swapped out", (long long)seqs[i]);
       if (it->second.len == INT32_MAX) return pkv::fail(PKV_ERR_INVALID, "pkv_plan_append: sequence too long");
       ss[i] = &it->second;
     }
@@ -221,6 +237,8 @@ pkv_status pkv_export_tables(const pkv_pool* pool, const int64_t* seqs, int32_t 
     auto it = pool->seqs.find(seqs[i]);
     if (it == pool->seqs.end())
       return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_export_tables: sequence %lld does not exist", (long long)seqs[i]);
+    if (it->second.swapped)
+      return pkv::fail(PKV_ERR_INVALID, "pkv_export_tables: sequence %lld is swapped out", (long long)seqs[i]);
     if (static_cast<int64_t>(it->second.table.size()) > max_blocks)
       return pkv::fail(PKV_ERR_INVALID, "pkv_export_tables: sequence %lld has %zu blocks > max_blocks %d",
                        (long long)seqs[i], it->second.table.size(), max_blocks);
@@ -239,6 +257,7 @@ int32_t pkv_seq_table(const pkv_pool* pool, int64_t seq, int32_t* out, int32_t c
   if (!pool) return -1;
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return -1;
+  if (it->second.swapped) return -2;
   const auto& t = it->second.table;
   if (out)
     for (int32_t i = 0; i < cap && i < static_cast<int32_t>(t.size()); ++i) out[i] = t[i];
@@ -266,6 +285,124 @@ int32_t pkv_free_list(const pkv_pool* pool, int32_t* out, int32_t cap) {
   if (out)
     for (auto it = pool->free_list.begin(); it != pool->free_list.end() && i < cap; ++it) out[i++] = *it;
   return static_cast<int32_t>(pool->free_list.size());
+}
+
+pkv_status pkv_pool_set_host_slots(pkv_pool* pool, int32_t num_host_slots, const int32_t* host_order) {
+  pkv::clear_error();
+  if (!pool || num_host_slots < 0) return pkv::fail(PKV_ERR_INVALID, "pkv_pool_set_host_slots: bad arguments");
+  if (pool->num_host_slots != 0) return pkv::fail(PKV_ERR_INVALID, "pkv_pool_set_host_slots: already set");
+  std::deque<int32_t> order;
+  if (host_order) {
+    std::vector<char> seen(num_host_slots, 0);
+    for (int32_t i = 0; i < num_host_slots; ++i) {
+      const int32_t h = host_order[i];
+      if (h < 0 || h >= num_host_slots || seen[h])
+        return pkv::fail(PKV_ERR_INVALID, "pkv_pool_set_host_slots: host_order is not a permutation");
+      seen[h] = 1;
+      order.push_back(h);
+    }
+  } else {
+    for (int32_t i = 0; i < num_host_slots; ++i) order.push_back(i);
+  }
+  pool->num_host_slots = num_host_slots;
+  pool->host_free = std::move(order);
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_swap_out(pkv_pool* pool, int64_t seq, int32_t* device_blocks_out, int32_t* host_slots_out,
+                            int32_t capacity, int32_t* num_copies) {
+  pkv::clear_error();
+  if (!pool || !num_copies || capacity < 0 || (capacity > 0 && (!device_blocks_out || !host_slots_out)))
+    return pkv::fail(PKV_ERR_INVALID, "pkv_seq_swap_out: null argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_seq_swap_out: sequence %lld does not exist", (long long)seq);
+  auto& s = it->second;
+  if (s.swapped) return pkv::fail(PKV_ERR_INVALID, "pkv_seq_swap_out: sequence %lld is swapped out", (long long)seq);
+  int32_t alone = 0;
+  for (int32_t b : s.table) alone += pool->ref[b] == 1;
+  if (alone > capacity) return pkv::fail(PKV_ERR_INVALID, "pkv_seq_swap_out: capacity %d < %d copies", capacity, alone);
+  if (alone > static_cast<int64_t>(pool->host_free.size()))
+    return pkv::fail(PKV_ERR_OOM, "pkv_seq_swap_out: %d host slots needed, %zu free", alone, pool->host_free.size());
+  s.on_host.assign(s.table.size(), 0);
+  int32_t n = 0;
+  for (size_t i = 0; i < s.table.size(); ++i) {
+    const int32_t b = s.table[i];
+    if (pool->ref[b] != 1) continue;
+    const int32_t h = pool->host_free.front();
+    pool->host_free.pop_front();
+    device_blocks_out[n] = b;
+    host_slots_out[n] = h;
+    ++n;
+    pool->ref[b] = 0;
+    pool->free_list.push_back(b);
+    s.table[i] = h;
+    s.on_host[i] = 1;
+  }
+  s.swapped = true;
+  *num_copies = n;
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_swap_in(pkv_pool* pool, int64_t seq, int32_t* host_slots_out, int32_t* device_blocks_out,
+                           int32_t capacity, int32_t* num_copies) {
+  pkv::clear_error();
+  if (!pool || !num_copies || capacity < 0 || (capacity > 0 && (!device_blocks_out || !host_slots_out)))
+    return pkv::fail(PKV_ERR_INVALID, "pkv_seq_swap_in: null argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_seq_swap_in: sequence %lld does not exist", (long long)seq);
+  auto& s = it->second;
+  if (!s.swapped) return pkv::fail(PKV_ERR_INVALID, "pkv_seq_swap_in: sequence %lld is not swapped out", (long long)seq);
+  int32_t need = 0;
+  for (uint8_t h : s.on_host) need += h;
+  if (need > capacity) return pkv::fail(PKV_ERR_INVALID, "pkv_seq_swap_in: capacity %d < %d copies", capacity, need);
+  if (need > static_cast<int64_t>(pool->free_list.size()))
+    return pkv::fail(PKV_ERR_OOM, "pkv_seq_swap_in: %d device blocks needed, %zu free", need, pool->free_list.size());
+  int32_t n = 0;
+  for (size_t i = 0; i < s.table.size(); ++i) {
+    if (!s.on_host[i]) continue;
+    const int32_t y = pool->free_list.front();
+    pool->free_list.pop_front();
+    pool->ref[y] = 1;
+    host_slots_out[n] = s.table[i];
+    device_blocks_out[n] = y;
+    ++n;
+    pool->host_free.push_back(s.table[i]);
+    s.table[i] = y;
+  }
+  s.on_host.clear();
+  s.swapped = false;
+  *num_copies = n;
+  return PKV_OK;
+}
+
+int32_t pkv_seq_is_swapped(const pkv_pool* pool, int64_t seq) {
+  if (!pool) return -1;
+  auto it = pool->seqs.find(seq);
+  return it == pool->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
+}
+
+int32_t pkv_seq_placement(const pkv_pool* pool, int64_t seq, int32_t* ids_out, int8_t* on_host_out, int32_t cap) {
+  if (!pool) return -1;
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return -1;
+  const auto& s = it->second;
+  for (int32_t i = 0; i < cap && i < static_cast<int32_t>(s.table.size()); ++i) {
+    if (ids_out) ids_out[i] = s.table[i];
+    if (on_host_out) on_host_out[i] = s.swapped ? static_cast<int8_t>(s.on_host[i]) : 0;
+  }
+  return static_cast<int32_t>(s.table.size());
+}
+
+int32_t pkv_host_free_count(const pkv_pool* pool) { return pool ? static_cast<int32_t>(pool->host_free.size()) : -1; }
+
+int32_t pkv_host_free_list(const pkv_pool* pool, int32_t* out, int32_t cap) {
+  if (!pool) return -1;
+  int32_t i = 0;
+  if (out)
+    for (auto it = pool->host_free.begin(); it != pool->host_free.end() && i < cap; ++it) out[i++] = *it;
+  return static_cast<int32_t>(pool->host_free.size());
 }
 
 }  // extern "C"

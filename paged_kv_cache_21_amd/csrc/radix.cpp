@@ -479,6 +479,8 @@ pkv_status pkv_radix_finish(pkv_radix* r, const int32_t* tokens, const int64_t* 
     auto it = r->pool->seqs.find(seqs[i]);
     if (it == r->pool->seqs.end())
       return pkv::fail(PKV_ERR_NOT_FOUND, "pkv_radix_finish: sequence %lld does not exist", (long long)seqs[i]);
+    if (it->second.swapped)
+      return pkv::fail(PKV_ERR_INVALID, "pkv_radix_finish: sequence %lld is swapped out", (long long)seqs[i]);
     const int64_t len = offsets[i + 1] - offsets[i];
     if (offsets[i] < 0 || len < 0 || len > it->second.len)
       return pkv::fail(PKV_ERR_INVALID, "pkv_radix_finish: request %d: %lld tokens for a %d-token sequence", i,

@@ -35,9 +35,10 @@ def check_swap_against_unpaged_model(RefPool, apply_append, apply_swap, seed=0, 
         if r < 0.15 or not seqs:
             n = int(rng.integers(0, 9))
             try:
-                table = pool.alloc(nxt_seq, n)
+                pool.alloc(nxt_seq, n)
             except MemoryError:
                 continue
+            table = pool.table(nxt_seq)
             for t in range(n):
                 pages[table[t // bs], t % bs, 0, 0] = nxt_tok + t
             model[nxt_seq] = list(range(nxt_tok, nxt_tok + n))
@@ -110,20 +111,20 @@ def check_swap_closed_forms(RefPool):
     blocks from the front and returns the slots; both fail whole on shortage."""
     bs = 4
     pool = RefPool(20, bs, list(range(20)), 8, list(range(8)))
-    pool.alloc("root", 3 * bs)                      # blocks 0, 1, 2
-    pool.fork("root", "a")
-    pool.plan_append(["a"])                         # block 3
+    pool.alloc(100, 3 * bs)                      # blocks 0, 1, 2
+    pool.fork(100, 101)
+    pool.plan_append([101])                         # block 3
     for _ in range(5 * bs - 1):
-        pool.plan_append(["a"])                     # blocks 4..7
-    assert pool.table("a") == [0, 1, 2, 3, 4, 5, 6, 7]
-    copies = pool.swap_out("a")
+        pool.plan_append([101])                     # blocks 4..7
+    assert pool.table(101) == [0, 1, 2, 3, 4, 5, 6, 7]
+    copies = pool.swap_out(101)
     assert copies == [(3, 0), (4, 1), (5, 2), (6, 3), (7, 4)]
-    assert pool.placement("a") == [("device", 0), ("device", 1), ("device", 2)] + [("host", h) for h in range(5)]
+    assert pool.placement(101) == [("device", 0), ("device", 1), ("device", 2)] + [("host", h) for h in range(5)]
     assert pool.free_list() == list(range(8, 20)) + [3, 4, 5, 6, 7]
     assert pool.host_free_list() == [5, 6, 7]
     assert [pool.refcount(b) for b in range(3)] == [2, 2, 2]
-    for bad in (lambda: pool.plan_append(["a"]), lambda: pool.fork("a", "b"), lambda: pool.table("a"),
-                lambda: pool.export_tables(["a"], 8), lambda: pool.swap_out("a")):
+    for bad in (lambda: pool.plan_append([101]), lambda: pool.fork(101, 102), lambda: pool.table(101),
+                lambda: pool.export_tables([101], 8), lambda: pool.swap_out(101)):
         try:
             bad()
         except (ValueError, KeyError):
@@ -131,37 +132,37 @@ def check_swap_closed_forms(RefPool):
         else:
             raise AssertionError("an operation on a swapped-out sequence was accepted")
     try:
-        pool.swap_in("root")
+        pool.swap_in(100)
     except (ValueError, KeyError):
         pass
     else:
         raise AssertionError("swap_in of a resident sequence was accepted")
-    pool.alloc("filler", 14 * bs)                   # leaves 3 device blocks: too few to swap "a" in
+    pool.alloc(103, 14 * bs)                   # leaves 3 device blocks: too few to swap 101 in
     snap = (pool.free_list(), pool.host_free_list())
     try:
-        pool.swap_in("a")
+        pool.swap_in(101)
     except MemoryError:
         assert snap == (pool.free_list(), pool.host_free_list())
     else:
         raise AssertionError("swap_in without room was accepted")
-    pool.free("filler")
+    pool.free(103)
     assert pool.free_list() == [5, 6, 7] + list(range(8, 20)) + [3, 4]
-    copies = pool.swap_in("a")
+    copies = pool.swap_in(101)
     assert copies == [(0, 5), (1, 6), (2, 7), (3, 8), (4, 9)]
-    assert pool.table("a") == [0, 1, 2, 5, 6, 7, 8, 9]
+    assert pool.table(101) == [0, 1, 2, 5, 6, 7, 8, 9]
     assert pool.host_free_list() == [5, 6, 7, 0, 1, 2, 3, 4]
     # host shortage: a 9-block private sequence needs 9 of 8 slots
-    pool.alloc("big", 9 * bs)
+    pool.alloc(104, 9 * bs)
     snap = (pool.free_list(), pool.host_free_list())
     try:
-        pool.swap_out("big")
+        pool.swap_out(104)
     except MemoryError:
         assert snap == (pool.free_list(), pool.host_free_list())
     else:
         raise AssertionError("swap_out without host room was accepted")
     # freeing a swapped-out sequence returns its slots and drops its shared references
-    pool.swap_out("a")
-    pool.free("a")
+    pool.swap_out(101)
+    pool.free(101)
     assert pool.host_free_count() == 8 and [pool.refcount(b) for b in range(3)] == [1, 1, 1]
 
 

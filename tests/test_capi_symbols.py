@@ -74,3 +74,14 @@ def test_workspace_bytes_formula_is_consistent():
     b = pkv.decode_workspace_bytes(64, 32, 8, 128, 4097)
     assert 0 < a <= b
     assert pkv.decode_workspace_bytes(0, 32, 8, 128, 4096) >= 0
+
+
+def test_library_loads_beside_torch_hip_runtime():
+    """torch ships its own HIP runtime; the library must need no symbol that only a
+    newer runtime has (it is loaded after torch in every GPU process)."""
+    import subprocess
+    import sys
+
+    code = "import torch, paged_kv_cache_21_amd as m; print(m.version())"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]

@@ -1,0 +1,158 @@
+"""Swap-out / swap-in of KV blocks through pinned host memory on the device:
+copies bit-exact against the oracle's apply_swap, decode after a round trip
+bitwise equal to decode before it (the blocks come back at other places),
+FP8 codes and scales moved together, out-of-range ids skipped, pageable host
+memory refused before any launch."""
+
+import numpy as np
+import pytest
+
+from gpu_util import say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+BS = 16
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_21_amd as m
+
+    return m
+
+
+def _bits(gen, shape):
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+
+
+def _ids(pairs, k):
+    return torch.tensor([p[k] for p in pairs], dtype=torch.int32).cuda()
+
+
+@pytest.mark.parametrize("hkv,d", [(8, 128), (2, 64)])
+def test_round_trip_bit_exact_and_decode_unchanged(pkv, hkv, d):
+    import oracle
+    from oracle.pool import apply_swap
+
+    say(f"swap: round trip hkv={hkv} d={d}")
+    gen = torch.Generator().manual_seed(hkv * 100 + d)
+    nblk, nhost = 96, 64
+    pool = pkv.BlockPool(nblk, BS, np.random.default_rng(1).permutation(nblk), nhost,
+                         np.random.default_rng(2).permutation(nhost))
+    k = _bits(gen, (nblk, BS, hkv, d)).cuda()
+    v = _bits(gen, (nblk, BS, hkv, d)).cuda()
+    hk = torch.zeros((nhost, BS, hkv, d), dtype=torch.int16, pin_memory=True)
+    hv = torch.zeros((nhost, BS, hkv, d), dtype=torch.int16, pin_memory=True)
+    pool.alloc(0, 40 * BS + 5)          # a prefix that a fork shares
+    pool.fork(0, 1)
+    for _ in range(9 * BS + 3):
+        pool.plan_append([1])           # sequence 1's own blocks (its last shared block is copied on write)
+    bt, lens = pool.export_tables([1], 64)
+    hq = hkv * 4 if hkv == 8 else hkv
+    q = _bits(gen, (1, hq, d)).cuda()
+    dec = lambda bt, lens: pkv.paged_decode_attn(q, k, v, torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(),
+                                                 int(lens.max()), dtype="bf16")
+    before = dec(bt, lens).cpu()
+    k_host0, v_host0 = k.cpu().numpy(), v.cpu().numpy()
+    out = pool.swap_out(1)
+    assert len(out) == 10
+    pkv.copy_blocks([hk, hv], [k, v], _ids(out, 1), _ids(out, 0))
+    torch.cuda.synchronize()
+    exp_k = apply_swap(np.zeros_like(hk.numpy()), k_host0, out)
+    exp_v = apply_swap(np.zeros_like(hv.numpy()), v_host0, out)
+    assert np.array_equal(hk.numpy(), exp_k) and np.array_equal(hv.numpy(), exp_v)
+    # every free block, the ten just freed included, is overwritten (bf16 +Inf) before the swap-in
+    free = torch.tensor(pool.free_list(), dtype=torch.int64).cuda()
+    k[free] = 0x7F80
+    v[free] = 0x7F80
+    back = pool.swap_in(1)
+    pkv.copy_blocks([k, v], [hk, hv], _ids(back, 1), _ids(back, 0))
+    torch.cuda.synchronize()
+    k_now, v_now = k.cpu().numpy(), v.cpu().numpy()
+    assert np.array_equal(k_now[[b for _, b in back]], exp_k[[h for h, _ in back]])
+    assert np.array_equal(v_now[[b for _, b in back]], exp_v[[h for h, _ in back]])
+    bt2, lens2 = pool.export_tables([1], 64)
+    assert not np.array_equal(bt, bt2)
+    after = dec(bt2, lens2).cpu()
+    assert torch.equal(before, after)
+    ref = oracle.ref_decode(q.cpu().numpy().view(np.uint16), k_now.view(np.uint16), v_now.view(np.uint16), bt2, lens2,
+                            1.0 / np.sqrt(d), "bf16")
+    assert float(np.max(np.abs(after.numpy() - ref))) <= 2e-3
+
+
+@pytest.mark.parametrize("max_wg", [0, 3])
+def test_fp8_codes_and_scales_move_together(pkv, max_wg):
+    say(f"swap: fp8 pages, 4 arrays, max_workgroups={max_wg}")
+    gen = torch.Generator().manual_seed(7)
+    nblk, nhost, hkv, d = 48, 32, 8, 128
+    codes_k = torch.randint(0, 255, (nblk, BS, hkv, d), generator=gen, dtype=torch.uint8).cuda()
+    codes_v = torch.randint(0, 255, (nblk, BS, hkv, d), generator=gen, dtype=torch.uint8).cuda()
+    sk = torch.rand((nblk, hkv, BS), generator=gen).cuda()
+    sv = torch.rand((nblk, hkv, BS), generator=gen).cuda()
+    host = [torch.zeros((nhost,) + tuple(t.shape[1:]), dtype=t.dtype, pin_memory=True)
+            for t in (codes_k, codes_v, sk, sv)]
+    src_ids = [3, 17, 40, 5, 22]
+    dst_ids = [0, 31, 7, 12, 2]
+    pkv.copy_blocks(host, [codes_k, codes_v, sk, sv], torch.tensor(dst_ids, dtype=torch.int32).cuda(),
+                    torch.tensor(src_ids, dtype=torch.int32).cuda(), max_workgroups=max_wg)
+    torch.cuda.synchronize()
+    for h, t in zip(host, (codes_k, codes_v, sk, sv)):
+        assert torch.equal(h[dst_ids], t.cpu()[src_ids])
+        untouched = [i for i in range(nhost) if i not in dst_ids]
+        assert not h[untouched].any()
+
+
+def test_out_of_range_ids_are_skipped(pkv):
+    say("swap: out-of-range ids")
+    a = torch.arange(8 * 64, dtype=torch.int32).view(8, 64).cuda()
+    b = torch.full((4, 64), -1, dtype=torch.int32).cuda()
+    pkv.copy_blocks([b], [a], torch.tensor([0, 1, -1, 9, 3], dtype=torch.int32).cuda(),
+                    torch.tensor([2, 99, 4, 5, -7], dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    got = b.cpu()
+    assert torch.equal(got[0], a.cpu()[2])
+    assert (got[1:] == -1).all()
+
+
+def test_pageable_host_memory_is_refused(pkv):
+    say("swap: pageable host memory refused")
+    a = torch.zeros((4, 64), dtype=torch.int32).cuda()
+    pageable = torch.zeros((4, 64), dtype=torch.int32)
+    ids = torch.tensor([0], dtype=torch.int32).cuda()
+    with pytest.raises(pkv.PkvInvalid):
+        pkv.copy_blocks([pageable], [a], ids, ids)
+    with pytest.raises(pkv.PkvInvalid):
+        pkv.copy_blocks([a], [pageable], ids, ids)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("hkv,d", [(8, 128)])
+def test_memcpy_path_round_trip(pkv, hkv, d):
+    """The runtime-copy path moves the same bytes as the kernel path: scattered and
+    consecutive ids (runs are merged into one copy), both directions, K and V."""
+    say("swap: runtime-copy path round trip")
+    gen = torch.Generator().manual_seed(11)
+    nblk, nhost = 64, 40
+    k = _bits(gen, (nblk, BS, hkv, d)).cuda()
+    v = _bits(gen, (nblk, BS, hkv, d)).cuda()
+    hk = torch.zeros((nhost, BS, hkv, d), dtype=torch.int16, pin_memory=True)
+    hv = torch.zeros((nhost, BS, hkv, d), dtype=torch.int16, pin_memory=True)
+    src = [5, 6, 7, 8, 30, 2, 3, 63, 0]
+    dst = [10, 11, 12, 13, 0, 39, 38, 20, 21]
+    pkv.copy_blocks_memcpy([hk, hv], [k, v], dst, src)
+    torch.cuda.synchronize()
+    kc, vc = k.cpu(), v.cpu()
+    assert torch.equal(hk[dst], kc[src]) and torch.equal(hv[dst], vc[src])
+    assert not hk[[i for i in range(nhost) if i not in dst]].any()
+    back = [50, 51, 52, 53, 54, 1, 9, 60, 61]
+    pkv.copy_blocks_memcpy([k, v], [hk, hv], back, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(k.cpu()[back], kc[src]) and torch.equal(v.cpu()[back], vc[src])
+    with pytest.raises(pkv.PkvInvalid):
+        pkv.copy_blocks_memcpy([hk], [k], [nhost], [0])          # destination out of range: nothing enqueued
+    with pytest.raises(pkv.PkvInvalid):
+        pkv.copy_blocks_memcpy([torch.zeros_like(hk)], [k], [0], [0])   # pageable host memory
+    torch.cuda.synchronize()
