@@ -249,17 +249,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     if (!wave_active) return;
     const bool valid0 = block_id(2 * ch) >= 0;
     const bool valid1 = block_id(2 * ch + 1) >= 0;
-    // S^T tiles: st[tt][j] = score of token 16*tt + 4*lgrp + j for this lane's row
-    f32x4 st[2];
+    // S^T tiles: st[tt][j] = score of token 16*tt + 4*lgrp + j for this lane's row;
+    // the two tiles' accumulation chains interleave
+    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int tt = 0; tt < 2; ++tt) {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(&k_lds[buf][(tt * 16 + lrow) * KPITCH + ks * 32 + lgrp * 8]);
-        c = mfma16x16x32<DT>(kv, qb[ks], c);
+        st[tt] = mfma16x16x32<DT>(kv, qb[ks], st[tt]);
       }
-      st[tt] = c;
     }
     // raw scores (scale applied inside the exponent); tokens of missing blocks -> -inf
     float sv[8];
@@ -279,9 +278,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
       }
     }
     float cmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    cmax = fmaxf(cmax, shfl_xor_f32(cmax, 16));
-    cmax = fmaxf(cmax, shfl_xor_f32(cmax, 32));
-    const float c = fabsf(a.scale_log2);
+    cmax = xor_max<16>(cmax);
+    cmax = xor_max<32>(cmax);
+    // c > 0, so a masked (-inf) score gives exp2(-inf) = 0 with no test per score
+    const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
     const float cm = cmax * c;  // chunk max in log2 units
     // Rescale only when some row's max grows by more than 2^8: until then the
     // weights 2^(s - m) stay <= 256, harmless in fp32 and in the 16-bit terms.
@@ -293,17 +293,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
       for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
       m = mn;
     }
-    uint16_t ph[8], pl[8];
     const float mref = fmaxf(m, -3.0e38f);  // m = -inf only while every score is -inf
+    u32x4 bh, bl;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = sv[j] == kNegInf ? 0.f : fast_exp2(fmaf(sv[j], c, -mref));
-      lsum += p;
-      ph[j] = DT::from_float(p);
-      pl[j] = DT::from_float(p - DT::to_float(ph[j]));
+    for (int j2 = 0; j2 < 4; ++j2) {
+      const float p0 = fast_exp2(fmaf(sv[2 * j2], c, -mref));
+      const float p1 = fast_exp2(fmaf(sv[2 * j2 + 1], c, -mref));
+      lsum += p0 + p1;
+      const uint32_t h = DT::pack2(p0, p1);  // the 16-bit terms, then what they leave
+      bh[j2] = h;
+      bl[j2] = DT::pack2(p0 - DT::lo(h), p1 - DT::hi(h));
     }
-    const u32x4 bh = u32x4{pack2(ph[0], ph[1]), pack2(ph[2], ph[3]), pack2(ph[4], ph[5]), pack2(ph[6], ph[7])};
-    const u32x4 bl = u32x4{pack2(pl[0], pl[1]), pack2(pl[2], pl[3]), pack2(pl[4], pl[5]), pack2(pl[6], pl[7])};
     // all V^T operands first, then the MFMAs
     u32x4 av[NDT];
 #pragma unroll
@@ -340,8 +340,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
   }
 
   // every lane group holds part of the row's weight sum
-  lsum += shfl_xor_f32(lsum, 16);
-  lsum += shfl_xor_f32(lsum, 32);
+  {
+    float lo, hi;
+    pair_values<16>(lsum, lo, hi);
+    lsum = lo + hi;
+    pair_values<32>(lsum, lo, hi);
+    lsum = lo + hi;
+  }
   if (my_row < R) {
     const int64_t rec = (static_cast<int64_t>(my_b) * a.slots + my_slot) * a.num_q_heads + my_h;
     float* dst = a.acc + rec * D + lgrp * 4;

@@ -15,6 +15,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -39,6 +40,10 @@ struct BF16 {
   static __device__ __forceinline__ float to_float(uint16_t h) {
     return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
   }
+  // two fp32 values -> one packed pair (a low), round-to-nearest-even
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  }
 };
 
 struct F16 {
@@ -58,6 +63,9 @@ struct F16 {
   static __device__ __forceinline__ float to_float(uint16_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, h));
   }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+  }
 };
 
 // FP8 pages: OCP E4M3 codes, one byte per element, with a power-of-two scale per
@@ -65,7 +73,6 @@ struct F16 {
 // Every E4M3 value is exact in bf16 and in f16, so a code widens to CT exactly
 // (through the hardware's E4M3 -> fp32 conversion).
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <class CT>
 struct FP8 {
@@ -202,6 +209,14 @@ __device__ __forceinline__ void pair_values(float x, float& lo, float& hi) {
     lo = __builtin_bit_cast(float, static_cast<uint32_t>(r[0]));
     hi = __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
   }
+}
+
+// max(x of lane l, x of lane l ^ DIST), in both lanes (DIST = 8, 16 or 32).
+template <int DIST>
+__device__ __forceinline__ float xor_max(float x) {
+  float lo, hi;
+  pair_values<DIST>(x, lo, hi);
+  return fmaxf(lo, hi);
 }
 
 // Max over groups of N consecutive lanes (N in 1, 2, 4, 8, 16).
