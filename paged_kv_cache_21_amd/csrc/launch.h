@@ -121,9 +121,6 @@ struct CascadeArgs {
 
 constexpr int kCascadeRowsPerItem = 64;     // 4 waves x 16 rows
 constexpr int kCascadeMaxPieceBlocks = 256;  // blocks of one work item's token piece
-// Cascade work-groups resident at once on an MI355X: 256 compute units x 3 (the
-// kernel's occupancy, 256 threads at up to 168 VGPRs); the planner sizes rounds of it.
-constexpr int kCascadeConcurrentItems = 768;
 constexpr int kNodeInts = 8;             // ints per node record of a plan image
 constexpr int kMemberInts = 3;           // ints per member entry of a plan image
 

@@ -71,56 +71,29 @@ int32_t tile_pieces(const pkv_plan* p, int32_t n, int32_t t) {
   return static_cast<int32_t>(std::min<int64_t>(nd.pieces, span / (static_cast<int64_t>(nd.piece_blocks) * p->block_size) + 1));
 }
 
-// Token pieces.  A node's work is (64-row tiles) x (KV heads) x (blocks), and the
-// work items run in waves of kCascadeConcurrentItems work-groups.  A work item's
-// time grows with its piece, so the pass takes about
-//   ceil(items / concurrent) x (largest piece)
-// and a last round that is only partly full wastes the rest of the chip.  Long
-// nodes are cut into pieces for the item target (1..8 full rounds) that
-// minimizes that estimate, never below kMinPieceBlocks blocks per piece (every
-// piece costs each member row one more fp32 partial per query head, written and
-// read back once) nor above kCascadeMaxPieceBlocks (the kernel keeps a piece's
-// block ids in four 64-lane registers).
+// Token pieces.  A node's work is (64-row tiles) x (KV heads) x (blocks); the
+// chip wants a few work-groups per CU.  Long nodes are cut into pieces of about
+// `target` blocks so the item count lands near kTargetItems, but never below
+// kMinPieceBlocks blocks per piece: every piece costs each member row one more
+// fp32 partial per query head, written and read back once.
 void split_pieces(pkv_plan* p) {
-  constexpr int64_t kConcurrent = pkv::kCascadeConcurrentItems;
+  constexpr int64_t kTargetItems = 1024;
   constexpr int32_t kMinPieceBlocks = 32;
   constexpr int32_t kMaxPieceBlocks = pkv::kCascadeMaxPieceBlocks;
   const int rows_per_item = pkv::kCascadeRowsPerItem;
   int64_t work = 0;
-  std::vector<int64_t> units(p->nodes.size());  // tiles x heads per node
-  for (size_t i = 0; i < p->nodes.size(); ++i) {
-    const auto& n = p->nodes[i];
+  for (const auto& n : p->nodes) {
     const int64_t tiles = (static_cast<int64_t>(n.num_members) * p->group + rows_per_item - 1) / rows_per_item;
-    units[i] = tiles * p->num_kv_heads;
-    work += units[i] * n.num_blocks;
+    work += tiles * p->num_kv_heads * n.num_blocks;
   }
-  auto pieces_for = [&](const pkv_plan::Node& n, int64_t target) {
-    int64_t np = std::max<int64_t>(1, (n.num_blocks + target - 1) / target);
-    np = std::min<int64_t>(np, std::max<int64_t>(1, n.num_blocks / kMinPieceBlocks));
-    np = std::max<int64_t>(np, (n.num_blocks + kMaxPieceBlocks - 1) / kMaxPieceBlocks);
-    const int64_t pb = (n.num_blocks + np - 1) / np;
-    return std::make_pair((n.num_blocks + pb - 1) / pb, pb);  // (pieces, blocks per piece)
-  };
-  int64_t best_target = std::max<int64_t>(1, work), best_cost = INT64_MAX, best_items = INT64_MAX;
-  for (int64_t rounds = 1; rounds <= 8; ++rounds) {
-    const int64_t target = std::max<int64_t>(1, (work + rounds * kConcurrent - 1) / (rounds * kConcurrent));
-    int64_t items = 0, largest = 0;
-    for (size_t i = 0; i < p->nodes.size(); ++i) {
-      const auto pp = pieces_for(p->nodes[i], target);
-      items += units[i] * pp.first;
-      largest = std::max(largest, pp.second);
-    }
-    const int64_t cost = (items + kConcurrent - 1) / kConcurrent * largest;
-    if (cost < best_cost || (cost == best_cost && items < best_items)) {
-      best_cost = cost;
-      best_items = items;
-      best_target = target;
-    }
-  }
+  const int64_t target = std::max<int64_t>(kMinPieceBlocks, (work + kTargetItems - 1) / kTargetItems);
   for (auto& n : p->nodes) {
-    const auto pp = pieces_for(n, best_target);
-    n.pieces = static_cast<int32_t>(pp.first);
-    n.piece_blocks = static_cast<int32_t>(pp.second);
+    // at most kMaxPieceBlocks blocks per piece: the cascade kernel keeps a piece's
+    // block ids in four 64-lane registers
+    n.pieces = static_cast<int32_t>(std::max<int64_t>(
+        std::max<int64_t>(1, n.num_blocks / target), (n.num_blocks + kMaxPieceBlocks - 1) / kMaxPieceBlocks));
+    n.piece_blocks = (n.num_blocks + n.pieces - 1) / n.pieces;
+    n.pieces = (n.num_blocks + n.piece_blocks - 1) / n.piece_blocks;
     p->max_piece_blocks_ = std::max(p->max_piece_blocks_, n.piece_blocks);
   }
 }

