@@ -744,6 +744,13 @@ def main():
                 "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                 "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": kern["decode_split"]["avg_us"]}
 
+    # the paged_decode_attn call alone (cascade + split + merge kernels, no append): the
+    # same unique bytes over the sum of its kernels' event-timed averages
+    t_attn = sum(kern[k]["avg_us"] for k in ("cascade", "decode_split", "merge")) * 1e-6
+    attn_gbs = U / t_attn / 1e9 if t_attn > 0 else 0.0
+    attn_only = {"us": round(t_attn * 1e6, 3), "gb_per_s": round(attn_gbs, 1),
+                 "hbm_peak_frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, q, k_pages, v_pages, bt, lens, args.cpu_seconds)
@@ -770,6 +777,7 @@ def main():
                    "cascade": plan is not None, "shared_nodes": n_nodes, "parallelism": "single GPU"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "decode_queries_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "decode_attn_only": attn_only,
         "bytes": {"kv_unique": kv_unique, "kv_logical": kv_logical, "q": q_bytes, "out": o_bytes,
                   "tables": tbl_bytes, "step_total_U": U},
         "kernels": kern,

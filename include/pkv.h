@@ -529,6 +529,10 @@ int32_t pkv_plan_num_query_rows(const pkv_plan* plan);
  * INT32_MAX), work items 4 (node or -1, KV head, first tile row, piece). */
 int64_t pkv_plan_image(const pkv_plan* plan, int32_t* out, int64_t capacity, int64_t* offsets);
 
+/* Query rows of one work item of the plan's matrix-core pass (a work item's first
+ * row is a multiple of it): 64 for decode plans, 128 for extend plans. -1 for NULL. */
+int32_t pkv_plan_rows_per_item(const pkv_plan* plan);
+
 /* ------------------------------------------------------------------------------------------
  * Kernel timing (for measurement).  When enabled, every kernel launch of the
  * library is bracketed with HIP events on its own stream; pkv_timing_read()

@@ -121,6 +121,7 @@ _SIGNATURES = {
     "pkv_plan_build_extend": (_vp, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pkv_extend_workspace_bytes": (_sz, [_vp, _i32]),
     "pkv_plan_num_query_rows": (_i32, [_vp]),
+    "pkv_plan_rows_per_item": (_i32, [_vp]),
     "pkv_plan_image": (_i64, [_vp, _vp, _i64, _vp]),
     "pkv_paged_extend_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _f32, _vp, _vp, _sz,
                                      _vp, _vp]),
@@ -709,6 +710,11 @@ class CascadePlan:
         if n < 0:
             raise PkvInvalid(PKV_ERR_INVALID, f"bad node index {i}")
         return n
+
+    @property
+    def rows_per_item(self):
+        """Query rows per work item of the matrix-core pass (64 decode, 128 extend)."""
+        return int(_lib.pkv_plan_rows_per_item(self._handle))
 
     def image(self):
         """(int32 image, {section: offset}, partial slots per query row) as uploaded to the device."""

@@ -305,7 +305,8 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
                        num_kv_heads,
                        L.slots,
                        plan->max_piece_blocks(),
-                       scale_log2};
+                       scale_log2,
+                       plan->rows_per_item};
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
     if (st != PKV_OK) return st;
@@ -442,7 +443,8 @@ pkv_status pkv_paged_extend_attn(const void* q, int32_t num_query_rows, int32_t 
                        num_kv_heads,
                        slots,
                        plan->max_piece_blocks(),
-                       scale_log2};
+                       scale_log2,
+                       plan->rows_per_item};
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
     if (st != PKV_OK) return st;

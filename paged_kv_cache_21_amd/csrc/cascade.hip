@@ -60,8 +60,8 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
 
 }  // namespace
 
-// Work-group: 4 waves, 64 query rows (16 per wave), one token piece of one
-// node for one KV head.  Row rho of a node is (member rho / G, query head
+// Work-group: 4 waves, 64 x RB query rows (16 x RB per wave), one token piece of
+// one node for one KV head.  Row rho of a node is (member rho / G, query head
 // hkv*G + rho % G).  Tokens are processed in chunks of 32 (two blocks): the
 // work-group stages K [32 x D] and V^T [D x 32] in LDS, each wave evaluates its
 // 16 rows.  Pipeline: two LDS buffers and a two-chunk register ring, so chunk
@@ -75,8 +75,12 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
 // accumulator leaves in each lane.
 // NW: 64-block windows of block ids held per lane (1 when every piece of the plan
 // has at most 64 blocks; up to kCascadeMaxPieceBlocks / 64 otherwise).
-template <class DT, int D, int G, int NW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void cascade_kernel(CascadeArgs a) {
+// RB: 16-row blocks per wave (64 * RB rows per work item).  Each K / V^T operand
+// read from LDS then feeds RB products; the registers it costs lower the
+// occupancy (3 waves per SIMD at RB = 1, 2 at RB = 2).
+template <class DT, int D, int G, int NW, int RB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3 : 2))) void cascade_kernel(
+    CascadeArgs a) {
   constexpr int KPITCH = D + 8;  // K row pitch in LDS (elements); the pad spreads rows over banks
   constexpr int VPITCH = 18;     // V^T row pitch in LDS (32-bit words = 2 tokens each; 16 used)
   constexpr int NKS = D / 32;    // k-steps of the QK product
@@ -113,45 +117,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
   const int lane = tid & 63;
   const int lrow = lane & 15;  // MFMA row / column index
   const int lgrp = lane >> 4;  // MFMA k group
-  const int my_row = row0 + wave * 16 + lrow;
-  const bool wave_active = row0 + wave * 16 < R;
+  const bool wave_active = row0 + wave * 16 * RB < R;
 
-  // queries of this lane's row, as B operands
-  u32x4 qb[NKS];
-  int my_b = -1, my_slot = 0, my_h = 0;
-  int my_limit = -1;  // last attended position, piece-local (rows past R attend to nothing)
-  if (my_row < R) {
-    const int32_t* mrec = a.node_members + kMemberInts * (mem_off + my_row / G);
-    my_b = mrec[0];
-    my_slot = mrec[1] + piece;
-    const int limit = mrec[2];
-    my_limit = limit == INT_MAX ? INT_MAX : limit - piece_tok0;
-    my_h = hkv * G + my_row % G;
-    const uint16_t* qp = a.q + (static_cast<int64_t>(my_b) * a.num_q_heads + my_h) * D + lgrp * 8;
-    // a negative scale is applied as |scale| on -q (flipping sign bits is exact), so the
-    // running max can be taken on the unscaled scores
-    const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  // queries of this lane's rows (one per row block), as B operands
+  u32x4 qb[RB][NKS];
+  int my_row[RB], my_b[RB], my_slot[RB], my_h[RB];
+  int my_limit[RB];  // last attended position, piece-local (rows past R attend to nothing)
+  int wave_min_limit = INT_MAX;
+  // a negative scale is applied as |scale| on -q (flipping sign bits is exact), so the
+  // running max can be taken on the unscaled scores
+  const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qb[ks] = ld16(qp + ks * 32) ^ flip;
-  } else {
+  for (int rb = 0; rb < RB; ++rb) {
+    my_row[rb] = row0 + wave * 16 * RB + rb * 16 + lrow;
+    my_b[rb] = -1;
+    my_slot[rb] = 0;
+    my_h[rb] = 0;
+    my_limit[rb] = -1;
+    if (my_row[rb] < R) {
+      const int32_t* mrec = a.node_members + kMemberInts * (mem_off + my_row[rb] / G);
+      my_b[rb] = mrec[0];
+      my_slot[rb] = mrec[1] + piece;
+      const int limit = mrec[2];
+      my_limit[rb] = limit == INT_MAX ? INT_MAX : limit - piece_tok0;
+      my_h[rb] = hkv * G + my_row[rb] % G;
+      const uint16_t* qp = a.q + (static_cast<int64_t>(my_b[rb]) * a.num_q_heads + my_h[rb]) * D + lgrp * 8;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < NKS; ++ks) qb[rb][ks] = ld16(qp + ks * 32) ^ flip;
+      wave_min_limit = min(wave_min_limit, my_limit[rb]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qb[rb][ks] = u32x4{0, 0, 0, 0};
+    }
   }
-
   // the earliest last-attended position over the wave's rows (rows past R count as
   // unlimited: their results are never stored); chunks entirely at or before it
   // need no causal mask
-  int wave_min_limit = my_row < R ? my_limit : INT_MAX;
   wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 1));
   wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 2));
   wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 4));
   wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 8));
   wave_min_limit = __builtin_amdgcn_readfirstlane(wave_min_limit);
 
-  float m = kNegInf, lsum = 0.f;
-  f32x4 o[NDT];
+  float m[RB], lsum[RB];
+  f32x4 o[RB][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegInf;
+    lsum[rb] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int vpair = tid & 15;  // tokens 2*vpair, 2*vpair+1
   const int vcol = tid >> 4;   // 8-element column group
@@ -244,79 +260,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
       }
     }
   };
-  // evaluate chunk ch from LDS buffer buf for this wave's 16 rows
+  // evaluate chunk ch from LDS buffer buf for this wave's RB x 16 rows
   auto compute_chunk = [&](int ch, int buf) {
     if (!wave_active) return;
     const bool valid0 = block_id(2 * ch) >= 0;
     const bool valid1 = block_id(2 * ch + 1) >= 0;
-    // S^T tiles: st[tt][j] = score of token 16*tt + 4*lgrp + j for this lane's row;
-    // the two tiles' accumulation chains interleave
-    f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // S^T tiles: st[rb][tt][j] = score of token 16*tt + 4*lgrp + j for this lane's row of
+    // block rb; each K operand read from LDS feeds RB products
+    f32x4 st[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) st[rb][0] = st[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(&k_lds[buf][(tt * 16 + lrow) * KPITCH + ks * 32 + lgrp * 8]);
-        st[tt] = mfma16x16x32<DT>(kv, qb[ks], st[tt]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) st[rb][tt] = mfma16x16x32<DT>(kv, qb[rb][ks], st[rb][tt]);
       }
     }
-    // raw scores (scale applied inside the exponent); tokens of missing blocks -> -inf
-    float sv[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sv[j] = st[0][j];
-      sv[4 + j] = st[1][j];
-    }
-    // uniform: a piece's odd end, bad ids, the node's partly filled end, or a
-    // chunk past some row's last attended position
-    if (!(valid0 && valid1) || ch * 32 + 31 > wave_min_limit || ch * 32 + 32 > piece_valid) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = ch * 32 + 16 * (j / 4) + 4 * lgrp + (j % 4);  // piece-local token of score j
-        const bool ok = (j < 4 ? valid0 : valid1) && t <= my_limit && t < piece_valid;
-        sv[j] = ok ? sv[j] : kNegInf;
-      }
-    }
-    float cmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    cmax = xor_max<16>(cmax);
-    cmax = xor_max<32>(cmax);
     // c > 0, so a masked (-inf) score gives exp2(-inf) = 0 with no test per score
     const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
-    const float cm = cmax * c;  // chunk max in log2 units
-    // Rescale only when some row's max grows by more than 2^8: until then the
-    // weights 2^(s - m) stay <= 256, harmless in fp32 and in the 16-bit terms.
-    if (__any(cm > m + 8.f)) {
-      const float mn = fmaxf(m, cm);
-      const float alpha = exp2_diff(m, mn);
-      lsum *= alpha;
+    // uniform: a piece's odd end, bad ids, the node's partly filled end, or a
+    // chunk past some row's last attended position
+    const bool mask_chunk = !(valid0 && valid1) || ch * 32 + 31 > wave_min_limit || ch * 32 + 32 > piece_valid;
+    u32x4 bh[RB], bl[RB];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-      m = mn;
-    }
-    const float mref = fmaxf(m, -3.0e38f);  // m = -inf only while every score is -inf
-    u32x4 bh, bl;
+    for (int rb = 0; rb < RB; ++rb) {
+      float sv[8];
 #pragma unroll
-    for (int j2 = 0; j2 < 4; ++j2) {
-      const float p0 = fast_exp2(fmaf(sv[2 * j2], c, -mref));
-      const float p1 = fast_exp2(fmaf(sv[2 * j2 + 1], c, -mref));
-      lsum += p0 + p1;
-      const uint32_t h = DT::pack2(p0, p1);  // the 16-bit terms, then what they leave
-      bh[j2] = h;
-      bl[j2] = DT::pack2(p0 - DT::lo(h), p1 - DT::hi(h));
+      for (int j = 0; j < 4; ++j) {
+        sv[j] = st[rb][0][j];
+        sv[4 + j] = st[rb][1][j];
+      }
+      if (mask_chunk) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = ch * 32 + 16 * (j / 4) + 4 * lgrp + (j % 4);  // piece-local token of score j
+          const bool ok = (j < 4 ? valid0 : valid1) && t <= my_limit[rb] && t < piece_valid;
+          sv[j] = ok ? sv[j] : kNegInf;
+        }
+      }
+      float cmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      cmax = xor_max<16>(cmax);
+      cmax = xor_max<32>(cmax);
+      const float cm = cmax * c;  // chunk max in log2 units
+      // Rescale only when some row's max grows by more than 2^8: until then the
+      // weights 2^(s - m) stay <= 256, harmless in fp32 and in the 16-bit terms.
+      if (__any(cm > m[rb] + 8.f)) {
+        const float mn = fmaxf(m[rb], cm);
+        const float alpha = exp2_diff(m[rb], mn);
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[rb][dt] *= alpha;
+        m[rb] = mn;
+      }
+      const float mref = fmaxf(m[rb], -3.0e38f);  // m = -inf only while every score is -inf
+#pragma unroll
+      for (int j2 = 0; j2 < 4; ++j2) {
+        const float p0 = fast_exp2(fmaf(sv[2 * j2], c, -mref));
+        const float p1 = fast_exp2(fmaf(sv[2 * j2 + 1], c, -mref));
+        lsum[rb] += p0 + p1;
+        const uint32_t h = DT::pack2(p0, p1);  // the 16-bit terms, then what they leave
+        bh[rb][j2] = h;
+        bl[rb][j2] = DT::pack2(p0 - DT::lo(h), p1 - DT::hi(h));
+      }
     }
-    // all V^T operands first, then the MFMAs
-    u32x4 av[NDT];
+    // each V^T operand read from LDS feeds 2 x RB products
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       const uint32_t* vrow = &vt_lds[buf][(dt * 16 + lrow) * VPITCH];
       const uint2 t0 = *reinterpret_cast<const uint2*>(vrow + 2 * lgrp);      // tokens 4*lgrp .. +3
       const uint2 t1 = *reinterpret_cast<const uint2*>(vrow + 8 + 2 * lgrp);  // tokens 16 + 4*lgrp .. +3
-      av[dt] = u32x4{t0.x, t0.y, t1.x, t1.y};
+      const u32x4 av = u32x4{t0.x, t0.y, t1.x, t1.y};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        o[rb][dt] = mfma16x16x32<DT>(av, bh[rb], o[rb][dt]);
+        o[rb][dt] = mfma16x16x32<DT>(av, bl[rb], o[rb][dt]);
+      }
     }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma16x16x32<DT>(av[dt], bh, o[dt]);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma16x16x32<DT>(av[dt], bl, o[dt]);
   };
 
   if (nchunks > 0) {
@@ -339,37 +361,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void c
     }
   }
 
-  // every lane group holds part of the row's weight sum
-  {
-    float lo, hi;
-    pair_values<16>(lsum, lo, hi);
-    lsum = lo + hi;
-    pair_values<32>(lsum, lo, hi);
-    lsum = lo + hi;
-  }
-  if (my_row < R) {
-    const int64_t rec = (static_cast<int64_t>(my_b) * a.slots + my_slot) * a.num_q_heads + my_h;
-    float* dst = a.acc + rec * D + lgrp * 4;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<float4*>(dst + dt * 16) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (lgrp == 0) a.ml[rec] = make_float2(m, lsum);
+  for (int rb = 0; rb < RB; ++rb) {
+    // every lane group holds part of the row's weight sum
+    float lo, hi;
+    pair_values<16>(lsum[rb], lo, hi);
+    float ls = lo + hi;
+    pair_values<32>(ls, lo, hi);
+    ls = lo + hi;
+    if (my_row[rb] < R) {
+      const int64_t rec = (static_cast<int64_t>(my_b[rb]) * a.slots + my_slot[rb]) * a.num_q_heads + my_h[rb];
+      float* dst = a.acc + rec * D + lgrp * 4;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<float4*>(dst + dt * 16) = make_float4(o[rb][dt][0], o[rb][dt][1], o[rb][dt][2], o[rb][dt][3]);
+      if (lgrp == 0) a.ml[rec] = make_float2(m[rb], ls);
+    }
   }
 }
 
 namespace {
 
+template <class DT, int D, int G, int RB>
+hipError_t launch_cascade_rb(const CascadeArgs& a, hipStream_t stream) {
+  if (a.max_piece_blocks <= 64)
+    hipLaunchKernelGGL((cascade_kernel<DT, D, G, 1, RB>), dim3(static_cast<unsigned>(a.num_items)), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((cascade_kernel<DT, D, G, kCascadeMaxPieceBlocks / 64, RB>),
+                       dim3(static_cast<unsigned>(a.num_items)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <class DT, int D, int G>
 hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   if (a.num_items <= 0) return hipSuccess;
   if (a.max_piece_blocks > kCascadeMaxPieceBlocks) return hipErrorInvalidValue;
-  if (a.max_piece_blocks <= 64)
-    hipLaunchKernelGGL((cascade_kernel<DT, D, G, 1>), dim3(static_cast<unsigned>(a.num_items)), dim3(256), 0, stream,
-                       a);
-  else
-    hipLaunchKernelGGL((cascade_kernel<DT, D, G, kCascadeMaxPieceBlocks / 64>),
-                       dim3(static_cast<unsigned>(a.num_items)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if (a.rows_per_item == kCascadeRowsPerItem) return launch_cascade_rb<DT, D, G, 1>(a, stream);
+  if (a.rows_per_item == 2 * kCascadeRowsPerItem) return launch_cascade_rb<DT, D, G, 2>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 template <class DT, int D>

@@ -117,9 +117,11 @@ struct CascadeArgs {
   int32_t slots;
   int32_t max_piece_blocks;  // largest piece of the plan (selects the kernel instance)
   float scale_log2;
+  int32_t rows_per_item;     // query rows per work item: kCascadeRowsPerItem or kExtendRowsPerItem
 };
 
-constexpr int kCascadeRowsPerItem = 64;     // 4 waves x 16 rows
+constexpr int kCascadeRowsPerItem = 64;     // decode plans: 4 waves x 16 rows
+constexpr int kExtendRowsPerItem = 128;     // extend plans: 4 waves x 2 x 16 rows
 constexpr int kCascadeMaxPieceBlocks = 256;  // blocks of one work item's token piece
 constexpr int kNodeInts = 8;             // ints per node record of a plan image
 constexpr int kMemberInts = 3;           // ints per member entry of a plan image

@@ -17,6 +17,7 @@ struct pkv_plan {
   // Query rows: decode, one per sequence (row b); extend, one per new token, in
   // (sequence, token) order.
   int32_t num_query_rows = 0;
+  int32_t rows_per_item = 64;  // query rows of a cascade work item (tile), set by the plan's kind
 
   struct Node {
     int32_t block_off, num_blocks, member_off, num_members;

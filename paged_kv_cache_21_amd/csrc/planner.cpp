@@ -61,7 +61,7 @@ int32_t member_limit(const pkv_plan* p, int32_t entry) { return p->node_members[
 // past it would be fully masked for every member, so no work item runs them).
 int32_t tile_pieces(const pkv_plan* p, int32_t n, int32_t t) {
   const auto& nd = p->nodes[n];
-  const int32_t per_tile = pkv::kCascadeRowsPerItem / p->group;  // member entries per tile
+  const int32_t per_tile = p->rows_per_item / p->group;  // member entries per tile
   const int32_t e0 = t * per_tile, e1 = std::min(nd.num_members, e0 + per_tile);
   int32_t lim = INT_MIN;
   for (int32_t e = e0; e < e1; ++e) lim = std::max(lim, member_limit(p, nd.member_off + e));
@@ -80,7 +80,7 @@ void split_pieces(pkv_plan* p) {
   constexpr int64_t kTargetItems = 1024;
   constexpr int32_t kMinPieceBlocks = 32;
   constexpr int32_t kMaxPieceBlocks = pkv::kCascadeMaxPieceBlocks;
-  const int rows_per_item = pkv::kCascadeRowsPerItem;
+  const int rows_per_item = p->rows_per_item;
   int64_t work = 0;
   for (const auto& n : p->nodes) {
     const int64_t tiles = (static_cast<int64_t>(n.num_members) * p->group + rows_per_item - 1) / rows_per_item;
@@ -102,7 +102,7 @@ void split_pieces(pkv_plan* p) {
 // creation order (root first along each path).
 void assign_slots(pkv_plan* p) {
   std::vector<int32_t> used(p->num_query_rows, 0);
-  const int32_t per_tile = pkv::kCascadeRowsPerItem / p->group;
+  const int32_t per_tile = p->rows_per_item / p->group;
   for (int32_t n = 0; n < static_cast<int32_t>(p->nodes.size()); ++n) {
     const auto& nd = p->nodes[n];
     for (int32_t e = 0; e < nd.num_members; ++e) {
@@ -125,7 +125,7 @@ void assign_slots(pkv_plan* p) {
 // queues are interleaved into launch order and padded with idle items.
 void build_items(pkv_plan* p) {
   constexpr int kXcds = 8;
-  const int rows_per_item = pkv::kCascadeRowsPerItem;
+  const int rows_per_item = p->rows_per_item;
   struct Cluster {
     int32_t node, head, tiles, piece;
     int64_t load;
@@ -265,6 +265,9 @@ pkv_plan* new_plan(pkv_plan::Kind kind, int32_t batch, int32_t max_blocks_per_se
   p->num_q_heads = num_q_heads;
   p->num_kv_heads = num_kv_heads;
   p->group = num_q_heads / num_kv_heads;
+  // the extend pass is compute-bound: register blocking two 16-row blocks per wave
+  // pays there; a decode cascade keeps more resident waves with one
+  p->rows_per_item = kind == pkv_plan::kExtend ? pkv::kExtendRowsPerItem : pkv::kCascadeRowsPerItem;
   return p;
 }
 
@@ -376,6 +379,8 @@ size_t pkv_plan_device_bytes(const pkv_plan* plan) { return plan ? plan->image.s
 int32_t pkv_plan_num_nodes(const pkv_plan* plan) { return plan ? static_cast<int32_t>(plan->nodes.size()) : -1; }
 
 int32_t pkv_plan_num_query_rows(const pkv_plan* plan) { return plan ? plan->num_query_rows : -1; }
+
+int32_t pkv_plan_rows_per_item(const pkv_plan* plan) { return plan ? plan->rows_per_item : -1; }
 
 int64_t pkv_plan_image(const pkv_plan* plan, int32_t* out, int64_t capacity, int64_t* offsets) {
   if (!plan) return -1;

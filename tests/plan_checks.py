@@ -4,13 +4,14 @@ row's merge reads written by exactly one work item per query head."""
 
 import numpy as np
 
-ROWS_PER_ITEM = 64
 NODE_INTS, MEMBER_INTS = 8, 3
 INT32_MAX = 2**31 - 1
 
 
 def check_plan_image(plan, num_q_heads, num_kv_heads, num_blocks):
     img, off, slots_max = plan.image()
+    ROWS_PER_ITEM = plan.rows_per_item
+    assert ROWS_PER_ITEM == (128 if hasattr(plan, "num_query_rows") else 64)
     group = num_q_heads // num_kv_heads
     nq = plan.num_query_rows if hasattr(plan, "num_query_rows") else plan.batch
     slots = max(slots_max, 1)
