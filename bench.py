@@ -295,7 +295,8 @@ def run_extend(args, w, dev):
 
 
 def run_fp8(args, w, dev):
-    """Append + decode over FP8 pages (no shared-prefix pass): the decode's K/V bytes halve."""
+    """Append + decode over FP8 pages (with the shared-prefix pass when the workload shares
+    blocks): the decode's K/V bytes halve."""
     import torch
 
     import paged_kv_cache_21_amd as pkv
@@ -305,22 +306,29 @@ def run_fp8(args, w, dev):
     pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
     workloads.replay(pool, w.build_ops)
     slots, cows = pool.plan_append(w.steps[0].append_rows)
-    assert len(cows) == 0
+    cow = np.asarray(cows, dtype=np.int32).reshape(-1, 3)
+    cow_d = [torch.from_numpy(np.ascontiguousarray(cow[:, i])).to(dev) for i in range(3)] if len(cow) else [None] * 3
     bt, lens = pool.export_tables(w.steps[0].decode_rows, w.max_blocks)
+    plan = None if args.no_cascade else pkv.CascadePlan(bt, lens, w.num_q_heads, w.num_kv_heads)
+    if plan is not None and plan.num_nodes == 0:
+        plan = None
+    if plan is not None:
+        plan.upload(device=dev)
     q = workloads.make_q(w, 0, device=dev)
     k_new, v_new = workloads.make_new_tokens(w, 0, device=dev)
     slot_d, bt_d, lens_d = (torch.from_numpy(x).to(dev) for x in (slots, bt, lens))
     max_len = int(lens.max())
     B = len(lens)
-    ws = torch.empty(max(pkv.decode_workspace_bytes(B, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len), 16),
+    ws = torch.empty(max(pkv.decode_workspace_bytes(B, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, plan), 16),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def one_step():
-        pkv.kv_append_fp8(kc, vc, ks, vs, k_new, v_new, slot_d, src_dtype=w.dtype, stream=stream)
-        pkv.paged_decode_attn_fp8(q, kc, vc, ks, vs, bt_d, lens_d, max_len, scale=w.scale, workspace=ws, out=out,
-                                  q_dtype=w.dtype, stream=stream)
+        pkv.kv_append_fp8(kc, vc, ks, vs, k_new, v_new, slot_d, cow_d[0], cow_d[1], cow_d[2], src_dtype=w.dtype,
+                          stream=stream)
+        pkv.paged_decode_attn_fp8(q, kc, vc, ks, vs, bt_d, lens_d, max_len, scale=w.scale, plan=plan, workspace=ws,
+                                  out=out, q_dtype=w.dtype, stream=stream)
 
     for _ in range(args.warmup):
         one_step()
@@ -339,15 +347,17 @@ def run_fp8(args, w, dev):
     torch.cuda.synchronize()
     pkv.timing_enable(False)
     kern = {}
-    for name in ("append", "decode_split", "merge"):
+    for name in ("append", "decode_split", "merge", "cascade"):
         total, count = pkv.timing_read(name)
         kern[name] = {"avg_us": round(total / count * 1e3, 3) if count else 0.0, "launches": count}
     # bytes per token of one layer: codes (1 B per element, K and V) + one fp32 scale per head for K and V
     per_token = w.num_kv_heads * (2 * w.head_dim + 2 * 4)
     tokens = int(lens.sum())
+    unique_tokens = unique_bytes(bt, lens, w) // w.bytes_per_token  # distinct cached tokens referenced
+    own_tokens = sum(int(lens[b]) - plan.row(b)[0] for b in range(B)) if plan is not None else tokens
     q_bytes = B * w.num_q_heads * w.head_dim * 2
-    split_bytes = tokens * per_token + q_bytes
-    U = split_bytes + B * w.num_q_heads * w.head_dim * 4 + bt.nbytes + lens.nbytes
+    split_bytes = own_tokens * per_token + q_bytes
+    U = unique_tokens * per_token + q_bytes + B * w.num_q_heads * w.head_dim * 4 + bt.nbytes + lens.nbytes
     t_split = kern["decode_split"]["avg_us"] * 1e-6
     achieved = split_bytes / t_split / 1e9 if t_split > 0 else 0.0
     res = {
@@ -359,7 +369,8 @@ def run_fp8(args, w, dev):
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}; K/V as E4M3 codes with per-row fp32 power-of-two scales",
                    "batch": B, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "block_size": w.block_size, "q_dtype": w.dtype, "accumulate": "f32", "parallelism": "single GPU"},
+                   "block_size": w.block_size, "q_dtype": w.dtype, "accumulate": "f32", "cascade": plan is not None,
+                   "parallelism": "single GPU"},
         "decode_queries_per_s": round(B / (ms * 1e-3), 1),
         "tokens_per_s_equivalent_16bit_gbs": round(tokens * w.bytes_per_token / (ms * 1e-3) / 1e9, 1),
         "kernels": kern,
@@ -744,9 +755,21 @@ def main():
                 "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                 "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": kern["decode_split"]["avg_us"]}
 
-    # the paged_decode_attn call alone (cascade + split + merge kernels, no append): the
-    # same unique bytes over the sum of its kernels' event-timed averages
-    t_attn = sum(kern[k]["avg_us"] for k in ("cascade", "decode_split", "merge")) * 1e-6
+    # the paged_decode_attn call alone (no append): K back-to-back calls on the same
+    # inputs, bracketed by events; the same unique bytes over the time per call
+    def attn_call():
+        pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, max_len, scale=w.scale, plan=plan, workspace=ws,
+                              out=out, dtype=w.dtype, stream=stream)
+
+    for _ in range(args.warmup):
+        attn_call()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        attn_call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_attn = ev0.elapsed_time(ev1) / max(args.steps, 1) * 1e-3
     attn_gbs = U / t_attn / 1e9 if t_attn > 0 else 0.0
     attn_only = {"us": round(t_attn * 1e6, 3), "gb_per_s": round(attn_gbs, 1),
                  "hbm_peak_frac": round(attn_gbs / HBM_PEAK_GBS, 4)}

@@ -457,16 +457,18 @@ pkv_status pkv_kv_append_fp8(void* k_pages, void* v_pages, float* k_scales, floa
                              const int32_t* cow_src, const int32_t* cow_dst, const int32_t* cow_rows, int32_t num_cow,
                              void* stream);
 
-/* As pkv_paged_decode_attn (no plan), over FP8 pages: K and V elements are code
- * value x scale; q is q_dtype (PKV_F16 or PKV_BF16) and the arithmetic is that of
- * the 16-bit path (every E4M3 value is exact in both 16-bit types).  Workspace:
- * pkv_decode_workspace_bytes(..., NULL).  Errors as pkv_paged_decode_attn. */
+/* As pkv_paged_decode_attn, over FP8 pages: K and V elements are code value x scale;
+ * q is q_dtype (PKV_F16 or PKV_BF16) and the arithmetic is that of the 16-bit path
+ * (every E4M3 value is exact in both 16-bit types).  With a cascade plan the shared
+ * blocks go through the matrix-core pass, their codes widened to q's type in LDS, the
+ * K scale applied to each score and the V scale folded into each weight.  Workspace:
+ * pkv_decode_workspace_bytes(..., plan).  Errors as pkv_paged_decode_attn. */
 pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t q_dtype, const void* k_pages, const void* v_pages,
                                      const float* k_scales, const float* v_scales, int64_t num_blocks,
                                      int32_t block_size, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                     const int32_t* seq_lens, int32_t max_seq_len, float scale, void* workspace,
-                                     size_t workspace_bytes, float* out, void* stream);
+                                     const int32_t* seq_lens, int32_t max_seq_len, float scale, const pkv_plan* plan,
+                                     void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Device operation 3: multi-token (extend) attention over a paged KV cache.

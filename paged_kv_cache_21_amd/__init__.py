@@ -128,7 +128,7 @@ _SIGNATURES = {
     "pkv_kv_append_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                  _vp, _i32, _vp]),
     "pkv_paged_decode_attn_fp8": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _vp,
-                                         _i32, _vp, _i32, _f32, _vp, _sz, _vp, _vp]),
+                                         _i32, _vp, _i32, _f32, _vp, _vp, _sz, _vp, _vp]),
     "pkv_stream_read": (_i32, [_vp, _i64, _vp, _i32, _vp]),
     "pkv_pool_set_host_slots": (_i32, [_vp, _i32, _vp]),
     "pkv_seq_swap_out": (_i32, [_vp, _i64, _vp, _vp, _i32, _vp]),
@@ -270,8 +270,9 @@ def kv_append_fp8(k_pages, v_pages, k_scales, v_scales, k_new, v_new, slot_mappi
 
 
 def paged_decode_attn_fp8(q, k_pages, v_pages, k_scales, v_scales, block_tables, seq_lens, max_seq_len, scale=None,
-                          workspace=None, out=None, q_dtype=None, stream=None):
-    """Decode attention over FP8 pages (codes x per-row scales); q [B, Hq, d] fp16/bf16, fp32 output."""
+                          plan=None, workspace=None, out=None, q_dtype=None, stream=None):
+    """Decode attention over FP8 pages (codes x per-row scales); q [B, Hq, d] fp16/bf16, fp32 output.
+    ``plan``: an uploaded CascadePlan of the same tables (shared blocks through the matrix-core pass)."""
     import torch
 
     _require(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape and k_pages.dtype == torch.uint8,
@@ -287,7 +288,7 @@ def paged_decode_attn_fp8(q, k_pages, v_pages, k_scales, v_scales, block_tables,
     _require(block_tables.dim() == 2 and block_tables.shape[0] == B and seq_lens.numel() == B, "bad table shape")
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
-    need = decode_workspace_bytes(B, hq, hkv, d, int(max_seq_len), None)
+    need = decode_workspace_bytes(B, hq, hkv, d, int(max_seq_len), plan)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if out is None:
@@ -296,7 +297,8 @@ def paged_decode_attn_fp8(q, k_pages, v_pages, k_scales, v_scales, block_tables,
     _check(_lib.pkv_paged_decode_attn_fp8(_ptr(q), B, hq, hkv, d, _dtype_code(q, q_dtype), _ptr(k_pages),
                                           _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), nblk, bs,
                                           _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens),
-                                          int(max_seq_len), float(scale), _ptr(workspace),
+                                          int(max_seq_len), float(scale), plan._handle if plan is not None else None,
+                                          _ptr(workspace),
                                           workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream, q)))
     return out
 

@@ -306,7 +306,9 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
                        L.slots,
                        plan->max_piece_blocks(),
                        scale_log2,
-                       plan->rows_per_item};
+                       plan->rows_per_item,
+                       k_scales,
+                       v_scales};
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
     if (st != PKV_OK) return st;
@@ -365,8 +367,8 @@ pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q
                                      int32_t head_dim, int32_t q_dtype, const void* k_pages, const void* v_pages,
                                      const float* k_scales, const float* v_scales, int64_t num_blocks,
                                      int32_t block_size, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                     const int32_t* seq_lens, int32_t max_seq_len, float scale, void* workspace,
-                                     size_t workspace_bytes, float* out, void* stream) {
+                                     const int32_t* seq_lens, int32_t max_seq_len, float scale, const pkv_plan* plan,
+                                     void* workspace, size_t workspace_bytes, float* out, void* stream) {
   pkv::clear_error();
   if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn_fp8: q dtype %d", q_dtype);
@@ -374,7 +376,7 @@ pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q
   if ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & 3u)
     return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: scales must be 4-byte aligned");
   return decode_impl(2 + q_dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, k_scales, v_scales,
-                     num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, nullptr,
+                     num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
                      workspace, workspace_bytes, out, stream);
 }
 

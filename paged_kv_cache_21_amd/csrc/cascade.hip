@@ -81,6 +81,13 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
 template <class DT, int D, int G, int NW, int RB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3 : 2))) void cascade_kernel(
     CascadeArgs a) {
+  // FP8 pages: E4M3 codes widened to the 16-bit type of q on their way into LDS
+  // (exact), the per-token K scale applied to each score and the V scale folded
+  // into each weight
+  using CT = typename is_fp8<DT>::compute;
+  constexpr bool Q8 = is_fp8<DT>::value;
+  constexpr int EB = Q8 ? 1 : 2;  // bytes per page element
+  typedef typename std::conditional<Q8, u32x2, u32x4>::type KV;  // 8 page elements
   constexpr int KPITCH = D + 8;  // K row pitch in LDS (elements); the pad spreads rows over banks
   constexpr int VPITCH = 18;     // V^T row pitch in LDS (32-bit words = 2 tokens each; 16 used)
   constexpr int NKS = D / 32;    // k-steps of the QK product
@@ -91,6 +98,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][32 * KPITCH];
   __shared__ __attribute__((aligned(16))) uint32_t vt_lds[2][D * VPITCH];
+  // FP8: the chunk's 32 K scales, then its 32 V scales (zero for tokens without data)
+  __shared__ __attribute__((aligned(16))) float sc_lds[2][Q8 ? 64 : 1];
 
   const int item = blockIdx.x;
   const int node = a.items[4 * item];
@@ -192,8 +201,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
   };
 
   struct Stage {
-    u32x4 k[KVEC_PER_THREAD];
-    u32x4 v0, v1;
+    KV k[KVEC_PER_THREAD];
+    KV v0, v1;
+    f32x4 sc;  // FP8, threads 0..15: four scales of the chunk
   };
   const int nchunks = (nblk + 1) / 2;
   // Per-thread element offsets inside a block (32-bit: a block is 16 * Hkv * D
@@ -216,16 +226,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
   auto load_chunk = [&](int ch, Stage& st) {
     ch = min(ch, nchunks - 1);
     const int id0 = block_id(2 * ch), id1 = block_id(2 * ch + 1);
-    const int64_t b0 = static_cast<int64_t>(id0 < 0 ? 0 : id0) * blk_stride;
-    const int64_t b1 = static_cast<int64_t>(id1 < 0 ? 0 : id1) * blk_stride;
-    const uint16_t* k0 = a.k_pages + b0;
-    const uint16_t* k1 = a.k_pages + b1;
+    const int64_t b0 = static_cast<int64_t>(id0 < 0 ? 0 : id0) * blk_stride * EB;  // bytes
+    const int64_t b1 = static_cast<int64_t>(id1 < 0 ? 0 : id1) * blk_stride * EB;
+    const char* kbase = reinterpret_cast<const char*>(a.k_pages);
+    const char* vbase = reinterpret_cast<const char*>(a.v_pages);
 #pragma unroll
-    for (int i = 0; i < KVEC_PER_THREAD; ++i) st.k[i] = ld16((khi[i] ? k1 : k0) + koff[i]);
+    for (int i = 0; i < KVEC_PER_THREAD; ++i)
+      st.k[i] = *reinterpret_cast<const KV*>(kbase + (khi[i] ? b1 : b0) + static_cast<int64_t>(koff[i]) * EB);
     if (vthread) {
-      const uint16_t* vp = (vhi ? a.v_pages + b1 : a.v_pages + b0) + voff;
-      st.v0 = ld16(vp);
-      st.v1 = ld16(vp + tok_stride);
+      const char* vp = vbase + (vhi ? b1 : b0) + static_cast<int64_t>(voff) * EB;
+      st.v0 = *reinterpret_cast<const KV*>(vp);
+      st.v1 = *reinterpret_cast<const KV*>(vp + tok_stride * EB);
+    }
+    if constexpr (Q8) {
+      if (tid < 16) {  // (K | V) x (block 0 | 1) x rows 4 p .. 4 p + 3
+        const int which = tid >> 2, part = tid & 3;
+        const int id = (which & 1) ? id1 : id0;
+        const float* sb = which < 2 ? a.k_scales : a.v_scales;
+        st.sc = *reinterpret_cast<const f32x4*>(sb + (static_cast<int64_t>(id < 0 ? 0 : id) * Hkv + hkv) * 16 + 4 * part);
+      }
     }
   };
   // registers -> LDS buffer: K as is, V transposed to [d][token] pairs; the values
@@ -238,19 +257,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     if (vthread && (ch * 32 + 32 > piece_valid || !ok0 || !ok1)) {  // uniform
       const int t = ch * 32 + 2 * vpair;
       const bool blk_ok = vhi ? ok1 : ok0;
-      if (!(blk_ok && t < piece_valid)) st.v0 = u32x4{0, 0, 0, 0};
-      if (!(blk_ok && t + 1 < piece_valid)) st.v1 = u32x4{0, 0, 0, 0};
+      if (!(blk_ok && t < piece_valid)) st.v0 = KV{};
+      if (!(blk_ok && t + 1 < piece_valid)) st.v1 = KV{};
+    }
+    if constexpr (Q8) {
+      if (tid < 16) {
+        const int which = tid >> 2, part = tid & 3;
+        const bool blk_ok = (which & 1) ? ok1 : ok0;
+        const int t0 = ch * 32 + (which & 1) * 16 + 4 * part;
+        f32x4 v = st.sc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (blk_ok && t0 + e < piece_valid) ? v[e] : 0.f;
+        *reinterpret_cast<f32x4*>(&sc_lds[buf][(which >> 1) * 32 + (which & 1) * 16 + 4 * part]) = v;
+      }
     }
 #pragma unroll
     for (int i = 0; i < KVEC_PER_THREAD; ++i) {
       const int vi = tid + 256 * i;
       const int tok = vi / (D / 8);
       const int col = vi % (D / 8);
-      *reinterpret_cast<u32x4*>(&k_lds[buf][tok * KPITCH + col * 8]) = st.k[i];
+      u32x4 kw;
+      if constexpr (Q8)
+        kw = widen8<CT>(st.k[i]);
+      else
+        kw = st.k[i];
+      *reinterpret_cast<u32x4*>(&k_lds[buf][tok * KPITCH + col * 8]) = kw;
     }
     if (vthread) {
-      const uint32_t w0[4] = {st.v0.x, st.v0.y, st.v0.z, st.v0.w};
-      const uint32_t w1[4] = {st.v1.x, st.v1.y, st.v1.z, st.v1.w};
+      u32x4 v0w, v1w;
+      if constexpr (Q8) {
+        v0w = widen8<CT>(st.v0);
+        v1w = widen8<CT>(st.v1);
+      } else {
+        v0w = st.v0;
+        v1w = st.v1;
+      }
+      const uint32_t w0[4] = {v0w.x, v0w.y, v0w.z, v0w.w};
+      const uint32_t w1[4] = {v1w.x, v1w.y, v1w.z, v1w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // elements 2e and 2e+1 of the column group, for tokens 2*vpair (low half) and
@@ -276,7 +319,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
       for (int tt = 0; tt < 2; ++tt) {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(&k_lds[buf][(tt * 16 + lrow) * KPITCH + ks * 32 + lgrp * 8]);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) st[rb][tt] = mfma16x16x32<DT>(kv, qb[rb][ks], st[rb][tt]);
+        for (int rb = 0; rb < RB; ++rb) st[rb][tt] = mfma16x16x32<CT>(kv, qb[rb][ks], st[rb][tt]);
       }
     }
     // c > 0, so a masked (-inf) score gives exp2(-inf) = 0 with no test per score
@@ -285,6 +328,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     // chunk past some row's last attended position
     const bool mask_chunk = !(valid0 && valid1) || ch * 32 + 31 > wave_min_limit || ch * 32 + 32 > piece_valid;
     u32x4 bh[RB], bl[RB];
+    float ksc[8], vsc[8];  // FP8: this lane's tokens' scales
+    if constexpr (Q8) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 kq = *reinterpret_cast<const f32x4*>(&sc_lds[buf][16 * tt + 4 * lgrp]);
+        const f32x4 vq = *reinterpret_cast<const f32x4*>(&sc_lds[buf][32 + 16 * tt + 4 * lgrp]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ksc[4 * tt + j] = kq[j];
+          vsc[4 * tt + j] = vq[j];
+        }
+      }
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float sv[8];
@@ -292,6 +348,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
       for (int j = 0; j < 4; ++j) {
         sv[j] = st[rb][0][j];
         sv[4 + j] = st[rb][1][j];
+      }
+      if constexpr (Q8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] *= ksc[j];
       }
       if (mask_chunk) {
 #pragma unroll
@@ -318,12 +378,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
       const float mref = fmaxf(m[rb], -3.0e38f);  // m = -inf only while every score is -inf
 #pragma unroll
       for (int j2 = 0; j2 < 4; ++j2) {
-        const float p0 = fast_exp2(fmaf(sv[2 * j2], c, -mref));
-        const float p1 = fast_exp2(fmaf(sv[2 * j2 + 1], c, -mref));
+        float p0 = fast_exp2(fmaf(sv[2 * j2], c, -mref));
+        float p1 = fast_exp2(fmaf(sv[2 * j2 + 1], c, -mref));
         lsum[rb] += p0 + p1;
-        const uint32_t h = DT::pack2(p0, p1);  // the 16-bit terms, then what they leave
+        if constexpr (Q8) {  // the V scale rides on the weight
+          p0 *= vsc[2 * j2];
+          p1 *= vsc[2 * j2 + 1];
+        }
+        const uint32_t h = CT::pack2(p0, p1);  // the 16-bit terms, then what they leave
         bh[rb][j2] = h;
-        bl[rb][j2] = DT::pack2(p0 - DT::lo(h), p1 - DT::hi(h));
+        bl[rb][j2] = CT::pack2(p0 - CT::lo(h), p1 - CT::hi(h));
       }
     }
     // each V^T operand read from LDS feeds 2 x RB products
@@ -335,8 +399,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
       const u32x4 av = u32x4{t0.x, t0.y, t1.x, t1.y};
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        o[rb][dt] = mfma16x16x32<DT>(av, bh[rb], o[rb][dt]);
-        o[rb][dt] = mfma16x16x32<DT>(av, bl[rb], o[rb][dt]);
+        o[rb][dt] = mfma16x16x32<CT>(av, bh[rb], o[rb][dt]);
+        o[rb][dt] = mfma16x16x32<CT>(av, bl[rb], o[rb][dt]);
       }
     }
   };
@@ -425,8 +489,13 @@ hipError_t launch_cascade_d(int head_dim, int group, const CascadeArgs& a, hipSt
 }  // namespace
 
 hipError_t launch_cascade(int dtype, int head_dim, int group, const CascadeArgs& a, hipStream_t stream) {
-  return dtype == 1 ? launch_cascade_d<BF16>(head_dim, group, a, stream)
-                    : launch_cascade_d<F16>(head_dim, group, a, stream);
+  switch (dtype) {
+    case 0: return launch_cascade_d<F16>(head_dim, group, a, stream);
+    case 1: return launch_cascade_d<BF16>(head_dim, group, a, stream);
+    case 2: return launch_cascade_d<FP8<F16>>(head_dim, group, a, stream);
+    case 3: return launch_cascade_d<FP8<BF16>>(head_dim, group, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pkv

@@ -118,6 +118,8 @@ struct CascadeArgs {
   int32_t max_piece_blocks;  // largest piece of the plan (selects the kernel instance)
   float scale_log2;
   int32_t rows_per_item;     // query rows per work item: kCascadeRowsPerItem or kExtendRowsPerItem
+  const float* k_scales;     // FP8 pages: [num_blocks][num_kv_heads][16] per-row scales (else null)
+  const float* v_scales;
 };
 
 constexpr int kCascadeRowsPerItem = 64;     // decode plans: 4 waves x 16 rows

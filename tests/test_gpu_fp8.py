@@ -103,8 +103,9 @@ def test_append_random_walk_bit_exact(pkv, seed, shape):
 SHAPES = [("bf16", 32, 8, 128), ("f16", 8, 8, 64), ("bf16", 16, 2, 128), ("f16", 64, 8, 128)]
 
 
+@pytest.mark.parametrize("use_plan", [False, True], ids=["split", "cascade"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}-hq{s[1]}-hkv{s[2]}-d{s[3]}" for s in SHAPES])
-def test_decode_parity_random_forest(pkv, shape):
+def test_decode_parity_random_forest(pkv, shape, use_plan):
     torch = __import__("torch")
     dtype, hq, hkv, d = shape
     w = workloads.random_forest(3, num_rows=12, max_len=900, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
@@ -132,11 +133,17 @@ def test_decode_parity_random_forest(pkv, shape):
         vs[blk, :, rows:] = np.inf
     q = workloads._normal_bits((len(lens), hq, d), dtype, 13, "cuda")
     k_d, v_d, ks_d, vs_d, bt_d, l_d = to_dev(kc, vc, ks.astype(np.float32), vs.astype(np.float32), bt, lens)
-    got = pkv.paged_decode_attn_fp8(q, k_d, v_d, ks_d, vs_d, bt_d, l_d, int(lens.max()), scale=w.scale, q_dtype=dtype)
+    plan = None
+    if use_plan:
+        plan = pkv.CascadePlan(bt, lens, hq, hkv)
+        assert plan.num_nodes > 0
+        plan.upload(device="cuda")
+    got = pkv.paged_decode_attn_fp8(q, k_d, v_d, ks_d, vs_d, bt_d, l_d, int(lens.max()), scale=w.scale, plan=plan,
+                                    q_dtype=dtype)
     torch.cuda.synchronize()
     ref = oracle.ref_decode_fp8(bits_np(q), kc, vc, ks, vs, bt, lens, w.scale, dtype)
     err = max_err(got.cpu().numpy(), ref)
-    say(f"fp8 decode {shape}: max_err {err:.3e}")
+    say(f"fp8 decode {shape} plan={use_plan}: max_err {err:.3e}")
     assert np.all(np.isfinite(got.cpu().numpy())) and err <= ATOL
     assert np.all(got.cpu().numpy()[0] == 0)
 
@@ -168,6 +175,41 @@ def test_decode_llama8b_shape_sampled_rows(pkv):
     assert err <= ATOL
 
 
+@pytest.mark.parametrize("cfg,rows", [(3, [0, 63, 64, 500, 1023]), (5, [0, 1, 100, 255])], ids=["tree-search", "radix"])
+def test_tree_workloads_fp8_with_cascade_sampled_rows(pkv, cfg, rows):
+    """The tree workloads at full size over FP8 pages, shared prefixes through the
+    matrix-core pass: sampled rows against the oracle on the same codes and scales."""
+    torch = __import__("torch")
+    w = workloads.get(cfg)
+    pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(pool, w.build_ops)
+    bt, lens = pool.export_tables(w.steps[0].decode_rows, w.max_blocks)
+    kc, vc, ks, vs = workloads.make_fp8_pages(w, device="cuda")
+    q = workloads.make_q(w, 0, device="cuda")
+    bt_d, l_d = to_dev(bt, lens)
+    plan = pkv.CascadePlan(bt, lens, w.num_q_heads, w.num_kv_heads)
+    assert plan.num_nodes > 0
+    plan.upload(device="cuda")
+    got = pkv.paged_decode_attn_fp8(q, kc, vc, ks, vs, bt_d, l_d, int(lens.max()), scale=w.scale, plan=plan,
+                                    q_dtype=w.dtype)
+    plain = pkv.paged_decode_attn_fp8(q, kc, vc, ks, vs, bt_d, l_d, int(lens.max()), scale=w.scale, q_dtype=w.dtype)
+    torch.cuda.synchronize()
+    ids = sorted({int(x) for r in rows for x in bt[r, : -(-int(lens[r]) // 16)]})
+    remap = {b: i for i, b in enumerate(ids)}
+    idx = torch.tensor(ids, dtype=torch.int64, device="cuda")
+    sub_bt = np.full((len(rows), bt.shape[1]), -1, np.int32)
+    for i, r in enumerate(rows):
+        nb = -(-int(lens[r]) // 16)
+        sub_bt[i, :nb] = [remap[int(x)] for x in bt[r, :nb]]
+    ref = oracle.ref_decode_fp8(bits_np(q)[rows], kc[idx].cpu().numpy(), vc[idx].cpu().numpy(),
+                                ks[idx].cpu().numpy(), vs[idx].cpu().numpy(), sub_bt, lens[rows], w.scale, w.dtype)
+    err = max_err(got.cpu().numpy()[rows], ref)
+    err_plain = max_err(plain.cpu().numpy()[rows], ref)
+    say(f"fp8 config {cfg} cascade: max_err {err:.3e} (split only {err_plain:.3e})")
+    assert err <= ATOL and err_plain <= ATOL
+    assert float((got - plain).abs().max()) <= 2 * ATOL
+
+
 def test_errors(pkv):
     torch = __import__("torch")
     k = torch.zeros((4, 16, 2, 64), dtype=torch.uint8, device="cuda")
@@ -179,4 +221,4 @@ def test_errors(pkv):
         pkv.paged_decode_attn_fp8(q.float(), k, k, s, s, bt, ln, 1)  # fp32 q
     lib = pkv.lib()
     assert lib.pkv_paged_decode_attn_fp8(q.data_ptr(), 1, 2, 2, 64, 1, k.data_ptr(), k.data_ptr(), None, None, 4, 16,
-                                         bt.data_ptr(), 1, ln.data_ptr(), 1, 0.1, None, 0, None, None) == -1
+                                         bt.data_ptr(), 1, ln.data_ptr(), 1, 0.1, None, None, 0, None, None) == -1
