@@ -211,7 +211,10 @@ def run_extend(args, w, dev):
     import paged_kv_cache_21_amd as pkv
     import workloads
 
-    k_pages, v_pages = workloads.make_pages(w, device=dev)
+    if args.fp8:
+        k_pages, v_pages, k_scales, v_scales = workloads.make_fp8_pages(w, device=dev)
+    else:
+        k_pages, v_pages = workloads.make_pages(w, device=dev)
     pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
     workloads.replay(pool, w.build_ops)
     bt, lens = pool.export_tables(w.steps[0].decode_rows, w.max_blocks)
@@ -227,8 +230,12 @@ def run_extend(args, w, dev):
     stream = torch.cuda.current_stream(dev)
 
     def one_step():
-        pkv.paged_extend_attn(q, k_pages, v_pages, plan, scale=w.scale, workspace=ws, out=out, dtype=w.dtype,
-                              stream=stream)
+        if args.fp8:
+            pkv.paged_extend_attn_fp8(q, k_pages, v_pages, k_scales, v_scales, plan, scale=w.scale, workspace=ws,
+                                      out=out, q_dtype=w.dtype, stream=stream)
+        else:
+            pkv.paged_extend_attn(q, k_pages, v_pages, plan, scale=w.scale, workspace=ws, out=out, dtype=w.dtype,
+                                  stream=stream)
 
     for _ in range(args.warmup):
         one_step()
@@ -261,7 +268,7 @@ def run_extend(args, w, dev):
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     achieved = flops / t_mfma / 1e12 if t_mfma > 0 else 0.0
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.fp8:
         cpu = extend_cpu_baseline(w, q, k_pages, v_pages, bt, lens, q_lens, args.cpu_seconds)
     res = {
         "metric": "paged extend attn: causal attention TFLOP/s, effective unique-KV GB/s",
@@ -274,9 +281,9 @@ def run_extend(args, w, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "fp8e4m3 pages, " + w.dtype + " q" if args.fp8 else w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.description}", "query_tokens": nq, "rows": int((q_lens > 0).sum()),
+        "config": {"workload": f"{w.name}: {w.description}" + ("; FP8 pages" if args.fp8 else ""), "query_tokens": nq, "rows": int((q_lens > 0).sum()),
                    "query_tokens_per_row": int(workloads.EXTEND_QUERY_TOKENS[w.number]),
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "shared_nodes": plan.num_nodes, "accumulate": "f32",

@@ -461,8 +461,9 @@ pkv_status pkv_kv_append_fp8(void* k_pages, void* v_pages, float* k_scales, floa
  * q is q_dtype (PKV_F16 or PKV_BF16) and the arithmetic is that of the 16-bit path
  * (every E4M3 value is exact in both 16-bit types).  With a cascade plan the shared
  * blocks go through the matrix-core pass, their codes widened to q's type in LDS, the
- * K scale applied to each score and the V scale folded into each weight.  Workspace:
- * pkv_decode_workspace_bytes(..., plan).  Errors as pkv_paged_decode_attn. */
+ * K scale applied to each score and the V scale folded into each weight; the scales
+ * must then be 16-byte aligned (else 4).  Workspace: pkv_decode_workspace_bytes(...,
+ * plan).  Errors as pkv_paged_decode_attn. */
 pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t q_dtype, const void* k_pages, const void* v_pages,
                                      const float* k_scales, const float* v_scales, int64_t num_blocks,
@@ -503,6 +504,16 @@ pkv_status pkv_paged_extend_attn(const void* q, int32_t num_query_rows, int32_t 
                                  int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
                                  int64_t num_blocks, int32_t block_size, float scale, const pkv_plan* plan,
                                  void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/* As pkv_paged_extend_attn, over FP8 pages (codes as for pkv_paged_decode_attn_fp8,
+ * scales float32 [num_blocks][num_kv_heads][block_size], 16-byte aligned); q is
+ * q_dtype (PKV_F16 or PKV_BF16).  Codes are widened to q's type in LDS (exact), the K
+ * scale multiplies each score, the V scale each weight. */
+pkv_status pkv_paged_extend_attn_fp8(const void* q, int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t q_dtype, const void* k_pages, const void* v_pages,
+                                     const float* k_scales, const float* v_scales, int64_t num_blocks,
+                                     int32_t block_size, float scale, const pkv_plan* plan, void* workspace,
+                                     size_t workspace_bytes, float* out, void* stream);
 
 /* Plan for pkv_paged_extend_attn from host copies of the block tables
  * ([batch][max_blocks_per_seq]), lengths and query-token counts (0 <= q_lens[b]

@@ -32,7 +32,7 @@ from .kvsize import kv_bytes, kv_bytes_per_token
 from .attention import decode_bits, ref_decode, ref_decode_rows, bruteforce_decode
 from .extend import extend_query_positions, ref_extend
 from .fp8 import (apply_append_fp8, dequantize_heads, dequantize_pages, e4m3_decode, e4m3_encode,
-                  pow2_scale_exponent, quantize_heads, ref_decode_fp8)
+                  pow2_scale_exponent, quantize_heads, ref_decode_fp8, ref_extend_fp8)
 from .pool import RefPool, RefPoolError, apply_append, apply_swap
 from .radix import RadixCache, RadixError
 
@@ -53,6 +53,7 @@ __all__ = [
     "pow2_scale_exponent",
     "quantize_heads",
     "ref_decode_fp8",
+    "ref_extend_fp8",
     "RefPool",
     "RefPoolError",
     "apply_append",

@@ -118,3 +118,14 @@ def ref_decode_fp8(q, k_codes, v_codes, k_scales, v_scales, block_tables, seq_le
 
     return ref_decode(decode_bits(q, q_dtype), dequantize_pages(k_codes, k_scales),
                       dequantize_pages(v_codes, v_scales), block_tables, seq_lens, scale, "f64")
+
+
+def ref_extend_fp8(q, k_codes, v_codes, k_scales, v_scales, block_tables, seq_lens, q_lens, scale, q_dtype,
+                   query_rows=None):
+    """Multi-token (extend) attention over FP8 pages: the extend oracle on the
+    dequantized values (q given as 16-bit bit patterns of ``q_dtype``)."""
+    from .attention import decode_bits
+    from .extend import ref_extend
+
+    return ref_extend(decode_bits(q, q_dtype), dequantize_pages(k_codes, k_scales), dequantize_pages(v_codes, v_scales),
+                      block_tables, seq_lens, q_lens, scale, "f64", query_rows)

@@ -125,6 +125,8 @@ _SIGNATURES = {
     "pkv_plan_image": (_i64, [_vp, _vp, _i64, _vp]),
     "pkv_paged_extend_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _f32, _vp, _vp, _sz,
                                      _vp, _vp]),
+    "pkv_paged_extend_attn_fp8": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _f32,
+                                         _vp, _vp, _sz, _vp, _vp]),
     "pkv_kv_append_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                  _vp, _i32, _vp]),
     "pkv_paged_decode_attn_fp8": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _vp,
@@ -791,6 +793,35 @@ def paged_extend_attn(q, k_pages, v_pages, plan, scale=None, workspace=None, out
     _check(_lib.pkv_paged_extend_attn(_ptr(q), nq, hq, hkv, d, _dtype_code(q, dtype), _ptr(k_pages), _ptr(v_pages),
                                       nblk, bs, float(scale), plan._handle, _ptr(workspace), ws_bytes, _ptr(out),
                                       _stream(stream, q)))
+    return out
+
+
+def paged_extend_attn_fp8(q, k_pages, v_pages, k_scales, v_scales, plan, scale=None, workspace=None, out=None,
+                          q_dtype=None, stream=None):
+    """``paged_extend_attn`` over FP8 pages (uint8 codes, float32 scales [num_blocks, Hkv, 16])."""
+    import torch
+
+    _require(isinstance(plan, ExtendPlan) and plan.device_buffer is not None, "plan must be an uploaded ExtendPlan")
+    _require(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape and k_pages.dtype == torch.uint8,
+             "q [NQ, Hq, d]; uint8 pages [num_blocks, block_size, Hkv, d]")
+    nq, hq, d = q.shape
+    nblk, bs, hkv, dk = k_pages.shape
+    _require(dk == d, "head_dim of q and pages differ")
+    _require(tuple(k_scales.shape) == (nblk, hkv, bs) and tuple(v_scales.shape) == (nblk, hkv, bs) and
+             k_scales.dtype == v_scales.dtype == torch.float32, "scales must be float32 [num_blocks, Hkv, block_size]")
+    _require(all(t.is_contiguous() for t in (q, k_pages, v_pages, k_scales, v_scales)), "inputs must be contiguous")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    need = extend_workspace_bytes(plan, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((nq, hq, d), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (nq, hq, d), "bad out tensor")
+    _check(_lib.pkv_paged_extend_attn_fp8(_ptr(q), nq, hq, hkv, d, _dtype_code(q, q_dtype), _ptr(k_pages),
+                                          _ptr(v_pages), _ptr(k_scales), _ptr(v_scales), nblk, bs, float(scale),
+                                          plan._handle, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _ptr(out), _stream(stream, q)))
     return out
 
 

@@ -373,8 +373,8 @@ pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q
   if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn_fp8: q dtype %d", q_dtype);
   if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: null scales");
-  if ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & 3u)
-    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: scales must be 4-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & (plan ? 15u : 3u))
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: scales must be 4-byte aligned (16 with a plan)");
   return decode_impl(2 + q_dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, k_scales, v_scales,
                      num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
                      workspace, workspace_bytes, out, stream);
@@ -391,12 +391,14 @@ size_t pkv_extend_workspace_bytes(const pkv_plan* plan, int32_t head_dim) {
   return ml_offset + recs * sizeof(float2);
 }
 
-pkv_status pkv_paged_extend_attn(const void* q, int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
-                                 int64_t num_blocks, int32_t block_size, float scale, const pkv_plan* plan,
-                                 void* workspace, size_t workspace_bytes, float* out, void* stream) {
-  pkv::clear_error();
-  if (dtype != PKV_F16 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_extend_attn: dtype %d", dtype);
+namespace {
+
+// kdtype: 0 f16, 1 bf16 pages; 2 / 3 FP8 pages with f16 / bf16 queries (scales given)
+pkv_status extend_impl(int kdtype, const void* q, int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, const void* k_pages, const void* v_pages, const float* k_scales,
+                       const float* v_scales, int64_t num_blocks, int32_t block_size, float scale,
+                       const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  const int dtype = kdtype;
   if (!plan || plan->kind != pkv_plan::kExtend)
     return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn: needs a plan from pkv_plan_build_extend");
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || num_blocks < 0)
@@ -446,7 +448,9 @@ pkv_status pkv_paged_extend_attn(const void* q, int32_t num_query_rows, int32_t 
                        slots,
                        plan->max_piece_blocks(),
                        scale_log2,
-                       plan->rows_per_item};
+                       plan->rows_per_item,
+                       k_scales,
+                       v_scales};
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
     if (st != PKV_OK) return st;
@@ -454,6 +458,34 @@ pkv_status pkv_paged_extend_attn(const void* q, int32_t num_query_rows, int32_t 
   pkv::MergeArgs ma{nullptr, plan->device + plan->off_row_info, nullptr, acc, ml, out, num_query_rows, num_q_heads,
                     num_kv_heads, 0, 0, slots};
   return pkv::launch(PKV_KERNEL_MERGE, "merge", s, [&] { return pkv::launch_merge(head_dim, ma, s); });
+}
+
+}  // namespace
+
+pkv_status pkv_paged_extend_attn(const void* q, int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
+                                 int64_t num_blocks, int32_t block_size, float scale, const pkv_plan* plan,
+                                 void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  pkv::clear_error();
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_extend_attn: dtype %d", dtype);
+  return extend_impl(dtype, q, num_query_rows, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, nullptr,
+                     nullptr, num_blocks, block_size, scale, plan, workspace, workspace_bytes, out, stream);
+}
+
+pkv_status pkv_paged_extend_attn_fp8(const void* q, int32_t num_query_rows, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t q_dtype, const void* k_pages, const void* v_pages,
+                                     const float* k_scales, const float* v_scales, int64_t num_blocks,
+                                     int32_t block_size, float scale, const pkv_plan* plan, void* workspace,
+                                     size_t workspace_bytes, float* out, void* stream) {
+  pkv::clear_error();
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_extend_attn_fp8: q dtype %d", q_dtype);
+  if (num_query_rows > 0 && (!k_scales || !v_scales))
+    return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn_fp8: null scales");
+  if ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & 15u)
+    return fail(PKV_ERR_INVALID, "pkv_paged_extend_attn_fp8: scales must be 16-byte aligned");
+  return extend_impl(2 + q_dtype, q, num_query_rows, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, k_scales,
+                     v_scales, num_blocks, block_size, scale, plan, workspace, workspace_bytes, out, stream);
 }
 
 pkv_status pkv_plan_upload(pkv_plan* plan, void* device_buf, size_t bytes, void* stream) {

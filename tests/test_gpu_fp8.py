@@ -222,3 +222,30 @@ def test_errors(pkv):
     lib = pkv.lib()
     assert lib.pkv_paged_decode_attn_fp8(q.data_ptr(), 1, 2, 2, 64, 1, k.data_ptr(), k.data_ptr(), None, None, 4, 16,
                                          bt.data_ptr(), 1, ln.data_ptr(), 1, 0.1, None, None, 0, None, None) == -1
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}-hq{s[1]}-hkv{s[2]}-d{s[3]}" for s in SHAPES])
+def test_extend_parity_random_forest(pkv, shape):
+    """Multi-token causal attention over FP8 pages (shared prefixes, ragged tails, a row
+    without query tokens, a row whose every token is a query) against the FP8 extend oracle."""
+    torch = __import__("torch")
+    dtype, hq, hkv, d = shape
+    w = workloads.random_forest(4, num_rows=10, max_len=500, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                                head_dim=d, share_prob=0.6)
+    ref_pool = oracle.RefPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(ref_pool, w.build_ops, allow_cow=True)
+    bt, lens = ref_pool.export_tables(w.steps[0].decode_rows, w.max_blocks)
+    rng = np.random.default_rng(55)
+    q_lens = np.minimum(lens, rng.integers(0, 40, size=len(lens))).astype(np.int32)
+    q_lens[0] = 0
+    q_lens[1] = lens[1]
+    kc, vc, ks, vs = quantized_pages(rng, w.num_blocks, w.block_size, hkv, d, dtype)
+    q = workloads._normal_bits((int(q_lens.sum()), hq, d), dtype, 21, "cuda")
+    k_d, v_d, ks_d, vs_d = to_dev(kc, vc, ks.astype(np.float32), vs.astype(np.float32))
+    plan = pkv.ExtendPlan(bt, lens, q_lens, hq, hkv).upload()
+    got = pkv.paged_extend_attn_fp8(q, k_d, v_d, ks_d, vs_d, plan, scale=w.scale, q_dtype=dtype)
+    torch.cuda.synchronize()
+    ref = oracle.ref_extend_fp8(bits_np(q), kc, vc, ks, vs, bt, lens, q_lens, w.scale, dtype)
+    err = max_err(got.cpu().numpy(), ref)
+    say(f"fp8 extend {shape}: rows {int(q_lens.sum())} nodes {plan.num_nodes} max_err {err:.3e}")
+    assert np.all(np.isfinite(got.cpu().numpy())) and err <= ATOL

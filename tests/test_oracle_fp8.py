@@ -80,6 +80,32 @@ def run_fp8_decode_pin(fp8):
     assert np.array_equal(a, b)
 
 
+def run_fp8_extend_pin(fp8):
+    """FP8 extend over bf16-exact values equals the extend oracle on those bf16 pages bit
+    for bit, and one query token per row equals the FP8 decode oracle."""
+    rng = np.random.default_rng(9)
+    lens = [9, 14, 5]
+    q_lens = [3, 1, 5]
+    _, _, _, bt, sl = oc.random_paged_case(rng, 3, 4, 2, 8, 4, lens, "bf16")
+    nblk = int(bt.max()) + 2
+    kc = rng.integers(0, 0x7F, (nblk, 4, 2, 8)).astype(np.uint8) | (rng.integers(0, 2, (nblk, 4, 2, 8)) << 7).astype(np.uint8)
+    vc = rng.integers(0, 0x7F, (nblk, 4, 2, 8)).astype(np.uint8)
+    ks = 2.0 ** rng.integers(-4, 3, (nblk, 2, 4)).astype(np.float32)
+    vs = 2.0 ** rng.integers(-4, 3, (nblk, 2, 4)).astype(np.float32)
+    kb, vb = oc.bf16_bits(fp8.dequantize_pages(kc, ks)), oc.bf16_bits(fp8.dequantize_pages(vc, vs))
+    q = oc.bf16_bits(rng.standard_normal((sum(q_lens), 4, 8)))
+    a = fp8.ref_extend_fp8(q, kc, vc, ks, vs, bt, sl, q_lens, 0.6, "bf16")
+    b = oracle.ref_extend(q, kb, vb, bt, sl, q_lens, 0.6, "bf16")
+    assert np.array_equal(a, b)
+    last = np.cumsum(q_lens) - 1  # each row's last query token sits at its last position
+    d = fp8.ref_decode_fp8(q[last], kc, vc, ks, vs, bt, sl, 0.6, "bf16")
+    assert np.allclose(a[last], d, rtol=0, atol=1e-12)
+
+
+def test_fp8_extend_pin():
+    run_fp8_extend_pin(oracle.fp8)
+
+
 def test_fp8_format_pins():
     run_fp8_pins(oracle.fp8)
 
@@ -111,6 +137,7 @@ def _load_fp8(old, new):
     src = open(os.path.join(ORACLE_DIR, "fp8.py")).read()
     assert src.count(old) >= 1, f"mutation site not found: {old!r}"
     src = src.replace(old, new, 1).replace("from .attention import", "from oracle.attention import")
+    src = src.replace("from .extend import", "from oracle.extend import")
     mod = types.ModuleType("oracle_mutant_fp8")
     exec(compile(src, "fp8.py", "exec"), mod.__dict__)
     return mod
