@@ -156,3 +156,25 @@ def test_memcpy_path_round_trip(pkv, hkv, d):
     with pytest.raises(pkv.PkvInvalid):
         pkv.copy_blocks_memcpy([torch.zeros_like(hk)], [k], [0], [0])   # pageable host memory
     torch.cuda.synchronize()
+
+
+def test_views_into_pinned_and_device_buffers(pkv):
+    """Block arrays that start inside an allocation (a slice of a pinned host buffer, a
+    slice of the device pages): the copies land relative to the views' first blocks."""
+    say("swap: views into larger allocations")
+    gen = torch.Generator().manual_seed(3)
+    pages = _bits(gen, (40, BS, 2, 64)).cuda()
+    host = torch.zeros((30, BS, 2, 64), dtype=torch.int16, pin_memory=True)
+    hview, dview = host[7:], pages[9:]
+    src, dst = [0, 5, 30], [2, 0, 22]
+    pkv.copy_blocks([hview], [dview], torch.tensor(dst, dtype=torch.int32).cuda(),
+                    torch.tensor(src, dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    pc = pages.cpu()
+    for s_, d_ in zip(src, dst):
+        assert torch.equal(host[7 + d_], pc[9 + s_])
+    assert not host[:7].any() and not host[[7 + i for i in range(23) if i not in dst]].any()
+    back = torch.zeros((10, BS, 2, 64), dtype=torch.int16).cuda()
+    pkv.copy_blocks_memcpy([back[3:]], [hview], [1, 4], [22, 2])
+    torch.cuda.synchronize()
+    assert torch.equal(back[4].cpu(), pc[9 + 30]) and torch.equal(back[7].cpu(), pc[9 + 0])
