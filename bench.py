@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 (E4M3) pages with per-row scales: quantizing append + FP8 decode (configs 2 and 4)")
+    ap.add_argument("--protocol", action="store_true",
+                    help="run every step of a multi-step workload (the radix tree's 16 append + decode steps "
+                         "with backtracking), timing host planning and device work per step")
     ap.add_argument("--swap", action="store_true",
                     help="block swap between HBM and pinned host memory: GB/s each way, overlap with decode")
     ap.add_argument("--swap-blocks", type=int, default=16384, help="blocks per swap batch (32 KiB of K and of V each)")
@@ -470,6 +473,84 @@ def run_radix(args):
     print(json.dumps(line))
 
 
+def run_protocol(args, w, dev):
+    """All steps of a multi-step workload as a serving loop would run them: per step the
+    host plans the append (slots, copy-on-write list) and exports the tables, replans
+    the shared-prefix pass when the tree changed (after a backtrack), then the device
+    appends and decodes.  Device time per step from events around its kernels; host
+    time per step from the host clock; effective GB/s over each step's unique bytes."""
+    import torch
+
+    import paged_kv_cache_21_amd as pkv
+    import workloads
+
+    k_pages, v_pages = workloads.make_pages(w, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run_once(record):
+        pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
+        workloads.replay(pool, w.build_ops)
+        plan = None
+        ws = None
+        for s, st in enumerate(w.steps):
+            t0 = time.perf_counter()
+            slots, cows = pool.plan_append(st.append_rows)
+            t1 = time.perf_counter()
+            bt, lens = pool.export_tables(st.decode_rows, w.max_blocks)
+            replanned = plan is None
+            if replanned:
+                plan = pkv.CascadePlan(bt, lens, w.num_q_heads, w.num_kv_heads)
+            t2 = time.perf_counter()
+            max_len = int(lens.max())
+            need = pkv.decode_workspace_bytes(len(lens), w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, plan)
+            if ws is None or ws.numel() < need:
+                ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+            if replanned:
+                plan.upload(device=dev)
+            kn, vn = workloads.make_new_tokens(w, s, device=dev)
+            q = workloads.make_q(w, s, device=dev)
+            slot_d = torch.from_numpy(slots).to(dev)
+            cow = np.asarray(cows, dtype=np.int32).reshape(-1, 3)
+            cow_d = ([torch.from_numpy(np.ascontiguousarray(cow[:, i])).to(dev) for i in range(3)] if len(cow)
+                     else [None] * 3)
+            bt_d, lens_d = torch.from_numpy(bt).to(dev), torch.from_numpy(lens).to(dev)
+            out = torch.empty((len(lens), w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pkv.kv_append(k_pages, v_pages, kn, vn, slot_d, cow_d[0], cow_d[1], cow_d[2], dtype=w.dtype,
+                          stream=stream)
+            pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, max_len, scale=w.scale, plan=plan,
+                                  workspace=ws, out=out, dtype=w.dtype, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if record is not None:
+                U = (unique_bytes(bt, lens, w) + len(lens) * w.num_q_heads * w.head_dim * 6 + bt.nbytes +
+                     lens.nbytes)
+                record.append({"step": s + 1, "device_us": round(e0.elapsed_time(e1) * 1e3, 2),
+                               "plan_append_us": round((t1 - t0) * 1e6, 1),
+                               "export_and_plan_us": round((t2 - t1) * 1e6, 1), "replanned": replanned,
+                               "copy_on_write": len(cow), "gb_per_s": round(U / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)})
+            if st.after_ops:
+                workloads.replay(pool, st.after_ops)
+                plan = None
+
+    run_once(None)  # warm-up pass
+    steps = []
+    run_once(steps)
+    dev_us = [x["device_us"] for x in steps]
+    host_us = [x["plan_append_us"] + x["export_and_plan_us"] for x in steps]
+    line = {"metric": "multi-step decode protocol: device time per step, effective KV GB/s", "value":
+            round(float(np.mean([x["gb_per_s"] for x in steps])), 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": len(steps), "warmup": len(steps), "ms_per_step": round(float(np.mean(dev_us)) / 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+            "config": {"workload": f"{w.name}: {w.description}", "per_step": steps},
+            "host_us_per_step_mean": round(float(np.mean(host_us)), 1),
+            "copy_on_write_total": int(sum(x["copy_on_write"] for x in steps)),
+            "roofline": None, "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
 def run_swap(args, dev):
     """Swap traffic of the 8B-shaped layer (Hkv 8, d 128, bf16: 32 KiB of K and 32 KiB
     of V per block): ``--swap-blocks`` scattered blocks out to scattered pinned host
@@ -644,6 +725,8 @@ def main():
         return run_swap(args, dev)
     w = workloads.get(args.config)
     print(f"[bench] workload {w.number} {w.name}: {w.description}", file=sys.stderr, flush=True)
+    if args.protocol:
+        return run_protocol(args, w, dev)
     if args.extend or args.config == 6:
         return run_extend(args, w, dev)
     if args.fp8:
