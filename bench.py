@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--extend", action="store_true",
                     help="time the multi-token pass (configs 3: verify 8 tokens per branch, 6: chunked prefill)")
     ap.add_argument("--no-cascade", action="store_true", help="decode every row on its own (no shared-prefix pass)")
+    ap.add_argument("--fused", action="store_true",
+                    help="step = the one-launch paged_decode_attn_append (default: kv_append then paged_decode_attn)")
     ap.add_argument("--cold-iters", type=int, default=10,
                     help="extra steps each preceded by a 1 GiB write that evicts L2 and MALL (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline (0 = skip)")
@@ -760,8 +762,18 @@ def main():
                                                     plan), 16), dtype=torch.uint8, device=dev)
     out = torch.empty((len(lens), w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    fused = args.fused
+    if fused and list(step.append_rows) != list(step.decode_rows):
+        print("--fused needs the step to append one token to every decoded row", file=sys.stderr)
+        sys.exit(2)
+    cow_src_d = torch.from_numpy(pkv.row_cow_sources(slots, cows, w.block_size)).to(dev)
 
     def one_step():
+        if fused:  # append + decode in one launch
+            pkv.paged_decode_attn_append(q, k_pages, v_pages, bt_d, lens_d, max_len, k_new, v_new, cow_src_d,
+                                         scale=w.scale, plan=plan, workspace=ws, out=out, dtype=w.dtype,
+                                         stream=stream)
+            return
         pkv.kv_append(k_pages, v_pages, k_new, v_new, slot_d, cow_d[0], cow_d[1], cow_d[2], dtype=w.dtype,
                       stream=stream)
         pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, max_len, scale=w.scale, plan=plan, workspace=ws,
@@ -837,6 +849,8 @@ def main():
     else:
         own_tokens = int(lens.sum())
     split_bytes = own_tokens * w.bytes_per_token + q_bytes
+    if fused:  # the split kernel also reads the new tokens and writes them and the copied-on-write rows
+        split_bytes += (2 * B + sum(int(c[2]) for c in cows)) * w.bytes_per_token
     t_split = kern["decode_split"]["avg_us"] * 1e-6
     achieved = split_bytes / t_split / 1e9 if t_split > 0 else 0.0
     traffic = measured_traffic(w) if plan is None or plan.num_nodes == 0 else None
@@ -887,7 +901,9 @@ def main():
         "config": {"workload": f"{w.name}: {w.description}", "batch": B, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
                    "mean_seq_len": round(float(lens.mean()), 1), "max_seq_len": max_len, "accumulate": "f32",
-                   "cascade": plan is not None, "shared_nodes": n_nodes, "parallelism": "single GPU"},
+                   "cascade": plan is not None, "shared_nodes": n_nodes,
+                   "step": "paged_decode_attn_append (one launch)" if fused else "kv_append + paged_decode_attn",
+                   "parallelism": "single GPU"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "decode_queries_per_s": round(B / (ms_per_step * 1e-3), 1),
         "decode_attn_only": attn_only,

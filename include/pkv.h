@@ -160,6 +160,33 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
                                  const pkv_plan* plan, void* workspace, size_t workspace_bytes,
                                  float* out, void* stream);
 
+/* Append and decode in one launch: pkv_kv_append of one new token per row (with the
+ * copy-on-write of a partly filled shared last block) followed by pkv_paged_decode_attn,
+ * as in "The Reasoning Engine Meltdown", §5 (a write lands only in a block its row
+ * owns) and §2.1 (the decode query attends to every cached token, the new one included).
+ *
+ * block_tables and seq_lens are the tables AFTER the append (as pkv_plan_append and
+ * pkv_export_tables leave them): row b's new token is its token seq_lens[b] - 1, in
+ * row (seq_lens[b] - 1) % 16 of its last block D = block_tables[b][(seq_lens[b]-1)/16].
+ *   k_new/v_new  device, [batch][num_kv_heads][head_dim], dtype, 16-byte aligned: the
+ *                new token's K and V, written into that row of D.
+ *   cow_src      device, int32 [batch]: the block D was copied from on write (rows
+ *                [0, (seq_lens[b]-1) % 16) of cow_src[b] are copied into D), or -1.
+ * Everything else as for pkv_paged_decode_attn (16-bit pages only); out equals
+ * pkv_kv_append followed by pkv_paged_decode_attn up to float rounding order, and the
+ * pages afterwards are bit-identical.  Rows with seq_lens[b] == 0, above max_seq_len or
+ * above max_blocks_per_seq * 16 append nothing; copy-on-write sources outside
+ * [0, num_blocks) are ignored.  A plan must come from the post-append tables: one that
+ * puts a row's last token in a shared node is rejected with PKV_ERR_INVALID.  Workspace:
+ * pkv_decode_workspace_bytes.  Errors: as pkv_paged_decode_attn. */
+pkv_status pkv_paged_decode_attn_append(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t dtype, void* k_pages, void* v_pages,
+                                        int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                        const void* k_new, const void* v_new, const int32_t* cow_src, float scale,
+                                        const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out,
+                                        void* stream);
+
 /* Bytes of device workspace pkv_paged_decode_attn needs for these sizes (and plan,
  * which may be NULL).  Returns 0 for invalid arguments (see pkv_last_error). */
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -24,6 +24,7 @@ __all__ = [
     "PkvError", "PkvInvalid", "PkvOOM", "PkvNotFound", "PkvUnsupported", "PkvWorkspaceError", "PkvHipError",
     "kv_append", "paged_decode_attn", "decode_workspace_bytes", "BlockPool", "CascadePlan",
     "ExtendPlan", "paged_extend_attn", "extend_workspace_bytes", "kv_append_fp8", "paged_decode_attn_fp8",
+    "paged_decode_attn_append", "row_cow_sources",
     "timing_enable", "timing_reset", "timing_read", "stream_read", "KERNELS", "lib", "LIB_PATH", "version",
 ]
 
@@ -79,6 +80,8 @@ _SIGNATURES = {
     "pkv_kv_append": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pkv_paged_decode_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32,
                                      _f32, _vp, _vp, _sz, _vp, _vp]),
+    "pkv_paged_decode_attn_append": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp,
+                                            _i32, _vp, _vp, _vp, _f32, _vp, _vp, _sz, _vp, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_pool_create": (_vp, [_i32, _i32, _vp]),
     "pkv_pool_destroy": (None, [_vp]),
@@ -349,6 +352,55 @@ def paged_decode_attn(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len, 
                                       float(scale), hplan, _ptr(workspace), ws_bytes, _ptr(out),
                                       _stream(stream, q)))
     return out
+
+
+def paged_decode_attn_append(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len, k_new, v_new, cow_src,
+                             scale=None, plan=None, workspace=None, out=None, dtype=None, stream=None):
+    """kv_append of one new token per row followed by paged_decode_attn, in one launch.
+
+    The tables are those after the append; row b's new token (k_new/v_new [B, Hkv, d]) is
+    its token seq_lens[b] - 1, and cow_src (int32 [B], -1 for none) names the block its
+    last block was copied from on write (see row_cow_sources).  Returns out [B, Hq, d] fp32.
+    """
+    import torch
+
+    _require(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "bad q / page ranks")
+    _require(q.is_contiguous() and k_pages.is_contiguous() and v_pages.is_contiguous(), "inputs must be contiguous")
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables and lengths must be int32")
+    _require(block_tables.is_contiguous() and seq_lens.is_contiguous(), "tables and lengths must be contiguous")
+    B, hq, d = q.shape
+    nblk, bs, hkv, dk = k_pages.shape
+    _require(dk == d, "head_dim of q and pages differ")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == B and seq_lens.numel() == B, "bad table shape")
+    _require(tuple(k_new.shape) == (B, hkv, d) and tuple(v_new.shape) == (B, hkv, d), "k_new / v_new must be [B, Hkv, d]")
+    _require(k_new.dtype == k_pages.dtype and v_new.dtype == k_pages.dtype, "new tokens must have the pages' dtype")
+    _require(k_new.is_contiguous() and v_new.is_contiguous(), "new tokens must be contiguous")
+    _require(cow_src.dtype == torch.int32 and cow_src.numel() == B and cow_src.is_contiguous(), "cow_src: int32 [B]")
+    max_blocks = int(block_tables.shape[1])
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    hplan = plan._handle if plan is not None else None
+    need = decode_workspace_bytes(B, hq, hkv, d, int(max_seq_len), plan)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, hq, d), "bad out tensor")
+    _check(_lib.pkv_paged_decode_attn_append(_ptr(q), B, hq, hkv, d, _dtype_code(q, dtype), _ptr(k_pages),
+                                             _ptr(v_pages), nblk, bs, _ptr(block_tables), max_blocks, _ptr(seq_lens),
+                                             int(max_seq_len), _ptr(k_new), _ptr(v_new), _ptr(cow_src), float(scale),
+                                             hplan, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream, q)))
+    return out
+
+
+def row_cow_sources(slots, cows, block_size=16):
+    """Per-row copy-on-write sources for paged_decode_attn_append from an append plan
+    (BlockPool.plan_append's slots [n] and (src, dst, rows) triples): row i's entry is the
+    source of the copy whose destination holds slots[i], else -1."""
+    slots = np.asarray(slots, dtype=np.int64)
+    src_of = {int(d): int(s_) for s_, d, _ in np.asarray(cows, dtype=np.int64).reshape(-1, 3)}
+    return np.asarray([src_of.get(int(x) // block_size, -1) for x in slots], dtype=np.int32)
 
 
 # ---------------------------------------------------------------------------

@@ -248,8 +248,10 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
                        int32_t head_dim, const void* k_pages, const void* v_pages, const float* k_scales,
                        const float* v_scales, int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float scale,
-                       const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out, void* stream) {
+                       const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out, void* stream,
+                       const void* k_new = nullptr, const void* v_new = nullptr, const int32_t* cow_src = nullptr) {
   const int dtype = kdtype;
+  const bool fused = k_new != nullptr;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
       max_seq_len < 0)
     return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: negative or zero size");
@@ -315,7 +317,7 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
   }
   int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.counts_offset);
   if (L.slots > (plan ? plan->max_depth : 0)) {
-    const int waves = pkv::decode_split_waves(dtype, head_dim, group);
+    const int waves = pkv::decode_split_waves(dtype, head_dim, group, fused);
     pkv::SplitArgs sa{static_cast<const uint16_t*>(q),
                       static_cast<const uint16_t*>(k_pages),
                       static_cast<const uint16_t*>(v_pages),
@@ -327,6 +329,9 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
                       acc,
                       ml,
                       counts,
+                      static_cast<const uint16_t*>(k_new),
+                      static_cast<const uint16_t*>(v_new),
+                      cow_src,
                       num_blocks,
                       batch,
                       num_q_heads,
@@ -361,6 +366,30 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
   return decode_impl(dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, nullptr, nullptr,
                      num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
                      workspace, workspace_bytes, out, stream);
+}
+
+pkv_status pkv_paged_decode_attn_append(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t dtype, void* k_pages, void* v_pages,
+                                        int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                        const void* k_new, const void* v_new, const int32_t* cow_src, float scale,
+                                        const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out,
+                                        void* stream) {
+  pkv::clear_error();
+  if (dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn_append: dtype %d", dtype);
+  if (batch > 0 && (!k_new || !v_new || !cow_src))
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_append: null new-token or copy-on-write pointer");
+  if (!pkv::aligned16(k_new) || !pkv::aligned16(v_new))
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_append: k_new and v_new must be 16-byte aligned");
+  if (plan && !plan->last_tokens_own)
+    return fail(PKV_ERR_INVALID,
+                "pkv_paged_decode_attn_append: the plan puts some row's last token in a shared node "
+                "(build it from the tables after the append)");
+  if (batch == 0) return PKV_OK;
+  return decode_impl(dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, nullptr, nullptr,
+                     num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
+                     workspace, workspace_bytes, out, stream, k_new, v_new, cow_src);
 }
 
 pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

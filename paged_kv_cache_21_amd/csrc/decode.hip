@@ -199,7 +199,15 @@ __device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, in
 // row) scales; q and the arithmetic in the 16-bit type).  A lane always holds 8
 // consecutive elements of a token row: one 16-byte load for 16-bit pages, one
 // 8-byte load for FP8 pages, widened to 16-bit values before the math.
-template <class DT, int D, int G, int LPT>
+//
+// FUSED (16-bit pages): each row's new token is appended in the same launch.  The
+// wave that reads the last block of segment (b, h) takes the new token's K/V row
+// of head h from k_new / v_new instead of the page, and, when the row's last block
+// was just copied on write, rows [0, new row) from the copy's source block; it
+// then writes those rows and the new token into the row's own block.  Reads never
+// depend on this launch's writes (no other segment reads a row's last block: it is
+// private to the row), so no wave waits for another.
+template <class DT, int D, int G, int LPT, bool FUSED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
   typedef typename is_fp8<DT>::compute CT;  // type of q and of the dot products
   constexpr bool Q8 = is_fp8<DT>::value;
@@ -276,15 +284,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   // (which, younger than the loads in flight, would make the wave wait for all of
   // them); the window is reloaded when the cursor leaves it.
   int tw = -1, tw_b = -1, tw_0 = 0;
+  // FUSED: the window's row's copy-on-write source and whether its new token lies in
+  // the attended range (its length not clamped), loaded with the window
+  int tw_cow = -1;
+  bool tw_app = false;
   auto block_id = [&](const Cursor& p) -> int {
     if (p.b != tw_b || p.j < tw_0 || p.j >= tw_0 + 64) {  // uniform
       tw_b = p.b;
       tw_0 = p.j & ~63;
       const int jj = tw_0 + lane;
       tw = jj < p.nb ? a.block_tables[static_cast<int64_t>(p.b) * a.max_blocks + p.blk0 + jj] : -1;
+      if constexpr (FUSED) {
+        tw_cow = a.cow_src[p.b];
+        const int raw_len = a.seq_lens[p.b];
+        tw_app = raw_len > 0 && raw_len == p.len;
+      }
       // consume the window inside the reload branch: the wait for it stays on this
       // (rare) path instead of being merged into every step
-      asm volatile("" ::"v"(tw));
+      asm volatile("" ::"v"(tw), "s"(tw_cow), "s"(static_cast<int>(tw_app)));
     }
     return __builtin_amdgcn_readlane(tw, p.j - tw_0);
   };
@@ -300,14 +317,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   // scores (token r + (c / G) * ROWS), the other path all TPB of its tokens
   constexpr bool RS = LPT == 16 && TPB * G == 16;
   constexpr int NS = RS ? 1 : TPB;
+  // FUSED, per pipeline buffer: the new token of the block's row when the block is
+  // the row's last (dst >= 0: its id; row: the token's row in it; cow: rows before it
+  // were read from the copy-on-write source), with the lane's part of its K/V
+  struct NewTok {
+    u32x4 k[VPL], v[VPL];
+    int dst, row;
+    bool cow;
+  };
   auto load_block = [&](const Cursor& p, KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL], float(&ks)[NS],
-                        float(&vs)[NS]) -> bool {
+                        float(&vs)[NS], NewTok& nt) -> bool {
     // the id and head are the same in every lane; readfirstlane makes that explicit so the
     // loads use a scalar base with the per-lane 32-bit offsets
     const int id = __builtin_amdgcn_readfirstlane(block_id(p));
     const int h = __builtin_amdgcn_readfirstlane(p.h);
     const bool ok = id >= 0 && static_cast<int64_t>(id) < a.num_blocks;
-    const int64_t base = (static_cast<int64_t>(ok ? id : 0) * blk_stride + static_cast<int64_t>(h) * D) * EB;
+    int rid = ok ? id : 0;  // the block read
+    if constexpr (FUSED) {
+      nt.dst = -1;
+      if (ok && tw_app && p.j == p.nb - 1) {  // uniform: the row's last block
+        nt.dst = id;
+        nt.row = p.len - 1 - (p.blk0 + p.j) * 16;
+        nt.cow = nt.row > 0 && tw_cow >= 0 && static_cast<int64_t>(tw_cow) < a.num_blocks;
+        rid = nt.cow ? tw_cow : id;
+        const int64_t nb0 = (static_cast<int64_t>(p.b) * Hkv + h) * D + c * 8;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          nt.k[v] = ld16(a.k_new + nb0 + v * LPT * 8);
+          nt.v[v] = ld16(a.v_new + nb0 + v * LPT * 8);
+        }
+      }
+    }
+    const int64_t base = (static_cast<int64_t>(rid) * blk_stride + static_cast<int64_t>(h) * D) * EB;
     const char* kb = reinterpret_cast<const char*>(a.k_pages) + base;
     const char* vb = reinterpret_cast<const char*>(a.v_pages) + base;
 #pragma unroll
@@ -454,8 +495,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
   };
 
-  auto consume_block = [&](bool ok, const u32x4(&qv)[G][VPL], const KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL],
-                           const float(&ks)[NS], const float(&vs)[NS]) {
+  auto consume_block = [&](bool ok, const u32x4(&qv)[G][VPL], KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL],
+                           const float(&ks)[NS], const float(&vs)[NS], const NewTok& nt) {
+    if constexpr (FUSED) {
+      if (nt.dst >= 0) {  // uniform: the new token replaces its row; it and the rows copied on write are stored
+        char* kd = reinterpret_cast<char*>(const_cast<uint16_t*>(a.k_pages)) +
+                   (static_cast<int64_t>(nt.dst) * blk_stride + static_cast<int64_t>(cur.h) * D) * EB;
+        char* vd = reinterpret_cast<char*>(const_cast<uint16_t*>(a.v_pages)) +
+                   (static_cast<int64_t>(nt.dst) * blk_stride + static_cast<int64_t>(cur.h) * D) * EB;
+#pragma unroll
+        for (int t = 0; t < TPB; ++t) {
+          const int tok = r + t * ROWS;
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) {
+            if (tok == nt.row) {
+              kk[t][v] = nt.k[v];
+              vv[t][v] = nt.v[v];
+            }
+            if (tok == nt.row || (nt.cow && tok < nt.row)) {
+              st16(kd + voff[t][v], kk[t][v]);
+              st16(vd + voff[t][v], vv[t][v]);
+            }
+          }
+        }
+      }
+    }
     mask_values(ok, vv);
     float sc[TPB][G];
 #pragma unroll
@@ -655,20 +719,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   float ksa[NS], vsa[NS], ksb[NS], vsb[NS], ksx[NS], vsx[NS];
   u32x4 qa[G][VPL], qb[G][VPL], qx[G][VPL];
   bool ok_a, ok_b, ok_x = false;
+  NewTok nta, ntb, ntx;
+  nta.dst = ntb.dst = ntx.dst = -1;
   load_q(pre, qa);
-  ok_a = load_block(pre, ka, va, ksa, vsa);
+  ok_a = load_block(pre, ka, va, ksa, vsa, nta);
   if constexpr (NBUF == 3) {
     if (1 < count) advance(pre, a);
     load_q(pre, qb);
-    ok_b = load_block(pre, kb, vb, ksb, vsb);
+    ok_b = load_block(pre, kb, vb, ksb, vsb, ntb);
   }
-  auto step = [&](int i, bool ok_cur, const u32x4(&q_cur)[G][VPL], const KV(&k_cur)[TPB][VPL], KV(&v_cur)[TPB][VPL],
-                  const float(&ks_cur)[NS], const float(&vs_cur)[NS], u32x4(&q_nxt)[G][VPL], KV(&k_nxt)[TPB][VPL],
-                  KV(&v_nxt)[TPB][VPL], float(&ks_nxt)[NS], float(&vs_nxt)[NS], bool& ok_nxt) {
+  auto step = [&](int i, bool ok_cur, const u32x4(&q_cur)[G][VPL], KV(&k_cur)[TPB][VPL], KV(&v_cur)[TPB][VPL],
+                  const float(&ks_cur)[NS], const float(&vs_cur)[NS], const NewTok& nt_cur, u32x4(&q_nxt)[G][VPL],
+                  KV(&k_nxt)[TPB][VPL], KV(&v_nxt)[TPB][VPL], float(&ks_nxt)[NS], float(&vs_nxt)[NS], bool& ok_nxt,
+                  NewTok& nt_nxt) {
     if (i + NBUF - 1 < count) advance(pre, a);
     load_q(pre, q_nxt);
-    ok_nxt = load_block(pre, k_nxt, v_nxt, ks_nxt, vs_nxt);
-    consume_block(ok_cur, q_cur, k_cur, v_cur, ks_cur, vs_cur);
+    ok_nxt = load_block(pre, k_nxt, v_nxt, ks_nxt, vs_nxt, nt_nxt);
+    consume_block(ok_cur, q_cur, k_cur, v_cur, ks_cur, vs_cur, nt_cur);
     if (i + 1 == count || cur.j + 1 == cur.nb) {
       finish_segment();
       if (i + 1 < count) {
@@ -682,18 +749,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   int i = 0;
   if constexpr (NBUF == 2) {
     for (; i + 1 < count; i += 2) {
-      step(i, ok_a, qa, ka, va, ksa, vsa, qb, kb, vb, ksb, vsb, ok_b);
-      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, qa, ka, va, ksa, vsa, ok_a);
+      step(i, ok_a, qa, ka, va, ksa, vsa, nta, qb, kb, vb, ksb, vsb, ok_b, ntb);
+      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, ntb, qa, ka, va, ksa, vsa, ok_a, nta);
     }
-    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, qb, kb, vb, ksb, vsb, ok_b);
+    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, nta, qb, kb, vb, ksb, vsb, ok_b, ntb);
   } else {
     for (; i + 2 < count; i += 3) {
-      step(i, ok_a, qa, ka, va, ksa, vsa, qx, kx, vx, ksx, vsx, ok_x);
-      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, qa, ka, va, ksa, vsa, ok_a);
-      step(i + 2, ok_x, qx, kx, vx, ksx, vsx, qb, kb, vb, ksb, vsb, ok_b);
+      step(i, ok_a, qa, ka, va, ksa, vsa, nta, qx, kx, vx, ksx, vsx, ok_x, ntx);
+      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, ntb, qa, ka, va, ksa, vsa, ok_a, nta);
+      step(i + 2, ok_x, qx, kx, vx, ksx, vsx, ntx, qb, kb, vb, ksb, vsb, ok_b, ntb);
     }
-    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, qx, kx, vx, ksx, vsx, ok_x);
-    if (i + 1 < count) step(i + 1, ok_b, qb, kb, vb, ksb, vsb, qa, ka, va, ksa, vsa, ok_a);
+    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, nta, qx, kx, vx, ksx, vsx, ok_x, ntx);
+    if (i + 1 < count) step(i + 1, ok_b, qb, kb, vb, ksb, vsb, ntb, qa, ka, va, ksa, vsa, ok_a, nta);
   }
 }
 
@@ -957,12 +1024,18 @@ namespace {
 #define PKV_LPT_D128 16
 #endif
 
-template <class DT, int D, int G>
-constexpr auto split_kernel_ptr() {
-  return &decode_split_kernel<DT, D, G, D == 128 ? PKV_LPT_D128 : 8>;
+// The fused-append instances exist for 16-bit pages only.
+template <class DT>
+constexpr bool can_fuse() {
+  return !is_fp8<DT>::value;
 }
 
-template <class DT, int D, int G>
+template <class DT, int D, int G, bool FUSED>
+constexpr auto split_kernel_ptr() {
+  return &decode_split_kernel<DT, D, G, D == 128 ? PKV_LPT_D128 : 8, FUSED && can_fuse<DT>()>;
+}
+
+template <class DT, int D, int G, bool FUSED>
 int split_waves_t() {
   // resident waves of this instance on the current device, cached per device
   static int cache[64] = {};
@@ -971,7 +1044,7 @@ int split_waves_t() {
   if (cache[dev] > 0) return cache[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_ptr<DT, D, G>(), 64, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_ptr<DT, D, G, FUSED>(), 64, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 8;
   cache[dev] = cus * per_cu;
@@ -982,8 +1055,16 @@ template <class DT, int D, int G>
 hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
   if (a.num_waves <= 0 || a.batch <= 0) return hipSuccess;
   constexpr int LPT = D == 128 ? PKV_LPT_D128 : 8;
-  hipLaunchKernelGGL((decode_split_kernel<DT, D, G, LPT>), dim3(static_cast<unsigned>(a.num_waves)), dim3(64), 0,
-                     stream, a);
+  if (a.k_new) {
+    if constexpr (can_fuse<DT>())
+      hipLaunchKernelGGL((decode_split_kernel<DT, D, G, LPT, true>), dim3(static_cast<unsigned>(a.num_waves)),
+                         dim3(64), 0, stream, a);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<DT, D, G, LPT, false>), dim3(static_cast<unsigned>(a.num_waves)),
+                       dim3(64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -1007,30 +1088,30 @@ hipError_t launch_split_d(int head_dim, int group, const SplitArgs& a, hipStream
   }
 }
 
-template <class DT, int D>
+template <class DT, int D, bool FUSED>
 int waves_g(int group) {
   switch (group) {
-    case 1: return split_waves_t<DT, D, 1>();
-    case 2: return split_waves_t<DT, D, 2>();
-    case 4: return split_waves_t<DT, D, 4>();
-    case 8: return split_waves_t<DT, D, 8>();
+    case 1: return split_waves_t<DT, D, 1, FUSED>();
+    case 2: return split_waves_t<DT, D, 2, FUSED>();
+    case 4: return split_waves_t<DT, D, 4, FUSED>();
+    case 8: return split_waves_t<DT, D, 8, FUSED>();
     default: return 0;
   }
 }
 
-template <class DT>
+template <class DT, bool FUSED>
 int waves_d(int head_dim, int group) {
-  return head_dim == 128 ? waves_g<DT, 128>(group) : head_dim == 64 ? waves_g<DT, 64>(group) : 0;
+  return head_dim == 128 ? waves_g<DT, 128, FUSED>(group) : head_dim == 64 ? waves_g<DT, 64, FUSED>(group) : 0;
 }
 
 }  // namespace
 
-int decode_split_waves(int dtype, int head_dim, int group) {
+int decode_split_waves(int dtype, int head_dim, int group, bool fused) {
   switch (dtype) {
-    case 0: return waves_d<F16>(head_dim, group);
-    case 1: return waves_d<BF16>(head_dim, group);
-    case 2: return waves_d<FP8<F16>>(head_dim, group);
-    case 3: return waves_d<FP8<BF16>>(head_dim, group);
+    case 0: return fused ? waves_d<F16, true>(head_dim, group) : waves_d<F16, false>(head_dim, group);
+    case 1: return fused ? waves_d<BF16, true>(head_dim, group) : waves_d<BF16, false>(head_dim, group);
+    case 2: return fused ? 0 : waves_d<FP8<F16>, false>(head_dim, group);
+    case 3: return fused ? 0 : waves_d<FP8<BF16>, false>(head_dim, group);
     default: return 0;
   }
 }

@@ -67,6 +67,11 @@ struct SplitArgs {
   float* acc;
   float2* ml;
   int32_t* counts;  // [batch][num_kv_heads] partials per segment (written for non-empty segments)
+  // fused append (16-bit pages; null otherwise): each row's new token [batch][num_kv_heads][D]
+  // and its last block's copy-on-write source (-1: none)
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* cow_src;
   int64_t num_blocks;
   int32_t batch;
   int32_t num_q_heads;
@@ -135,7 +140,7 @@ hipError_t launch_kv_append_fp8(int src_dtype, const AppendArgs& a, hipStream_t 
 // Returns hipErrorInvalidValue for shapes not built.
 hipError_t launch_decode_split(int dtype, int head_dim, int group, const SplitArgs& a, hipStream_t stream);
 // Waves the split kernel runs as for these shapes on the current device (all resident at once).
-int decode_split_waves(int dtype, int head_dim, int group);
+int decode_split_waves(int dtype, int head_dim, int group, bool fused);
 hipError_t launch_merge(int head_dim, const MergeArgs& a, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int grid, hipStream_t stream);
 hipError_t launch_cascade(int dtype, int head_dim, int group, const CascadeArgs& a, hipStream_t stream);

@@ -33,6 +33,9 @@ struct pkv_plan {
   std::vector<int32_t> node_members;
   std::vector<int32_t> row_info;  // per query row: (tokens covered by nodes, partial slots used)
   int32_t max_depth = 0;
+  // decode: every row's last token lies past its nodes (so a token appended there is
+  // read by the split pass, which the fused append needs)
+  bool last_tokens_own = true;
   std::vector<int32_t> items;  // (node, kv head, first member row, piece) in launch order; node -1 = idle
 
   // device image: one int32 array holding, in order, row_info, nodes, node_blocks, node_members, items

@@ -308,6 +308,7 @@ pkv_plan* pkv_plan_build(const int32_t* block_tables, const int32_t* seq_lens, i
   build_shared_nodes(
       p, block_tables, rows, full, min_members,
       [&](int32_t r) { p->node_members.insert(p->node_members.end(), {r, 0, INT_MAX}); }, covered);
+  for (int32_t b = 0; b < batch; ++b) p->last_tokens_own &= seq_lens[b] == 0 || covered[b] < seq_lens[b];
   finish_plan(p, covered);
   return p;
 }

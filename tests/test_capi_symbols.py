@@ -85,3 +85,25 @@ def test_library_loads_beside_torch_hip_runtime():
     code = "import torch, paged_kv_cache_21_amd as m; print(m.version())"
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_fused_append_refuses_a_plan_with_a_shared_last_token():
+    """Host-side checks of pkv_paged_decode_attn_append, before anything reaches a device:
+    a plan whose node holds a row's last token, FP8-width pages, and null new-token
+    pointers are refused."""
+    import numpy as np
+
+    bt = np.array([[1, 2], [1, 2]], dtype=np.int32)
+    lens = np.array([32, 32], dtype=np.int32)
+    plan = pkv.CascadePlan(bt, lens, 2, 2)
+    lib = pkv.lib()
+    fake = 4096  # 16-byte aligned; refused before any pointer is used
+    st = lib.pkv_paged_decode_attn_append(fake, 2, 2, 2, 64, 1, fake, fake, 4, 16, fake, 2, fake, 32, fake, fake,
+                                          fake, 1.0, plan._handle, fake, 1 << 20, fake, None)
+    assert st == -1 and b"shared node" in lib.pkv_last_error()
+    st = lib.pkv_paged_decode_attn_append(None, 2, 2, 2, 64, 1, None, None, 4, 16, None, 2, None, 32, None, None,
+                                          None, 1.0, None, None, 0, None, None)
+    assert st == -1 and b"null new-token" in lib.pkv_last_error()
+    st = lib.pkv_paged_decode_attn_append(None, 2, 2, 2, 64, 5, None, None, 4, 16, None, 2, None, 32, None, None,
+                                          None, 1.0, None, None, 0, None, None)
+    assert st == -4
