@@ -130,6 +130,12 @@ def host_rows(q_bits, k_pages, v_pages, bt, lens, rows):
     return k, v, sbt, np.asarray([lens[r] for r in rows], dtype=np.int32), qb
 
 
+def host_cores():
+    """The host's CPU count and this process's affinity, reported beside the oracle baseline
+    (which runs on one thread with one BLAS thread)."""
+    return {"host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "blas_threads": 1}
+
+
 def cpu_baseline(w, q_bits, k_pages, v_pages, bt, lens, seconds):
     """Time the fp64 oracle (one BLAS thread) over the workload's rows, row after row
     and pass after pass, until about `seconds` of oracle time has been spent."""
@@ -153,7 +159,7 @@ def cpu_baseline(w, q_bits, k_pages, v_pages, bt, lens, seconds):
                     break
             passes += 1
     gbs = tokens * w.bytes_per_token / t_total / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", **host_cores(),
             "sample": f"{rows_done} decode rows ({passes} pass(es) over the {len(lens)} rows of the workload, "
                       f"{tokens} tokens, all {w.num_q_heads} query heads), {t_total:.1f} s of fp64 numpy oracle "
                       f"time on one host thread; {rows_done / t_total:.2f} decode queries/s"}
@@ -204,7 +210,7 @@ def extend_cpu_baseline(w, q_bits, k_pages, v_pages, bt, lens, q_lens, seconds):
             flops += 4.0 * w.head_dim * (pos + 1) * w.num_q_heads
             if t_total >= seconds:
                 break
-    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle", **host_cores(),
             "sample": f"{done} query rows drawn at random from the workload's {len(where)} (all {w.num_q_heads} "
                       f"heads each), {t_total:.1f} s of fp64 numpy oracle time on one host thread"}
 
@@ -465,7 +471,7 @@ def run_radix(args):
                                               seconds=args.cpu_seconds / len(traces), meta=meta)
             c_req += done
             c_s += sec
-        cpu = {"value": round(c_req / c_s, 2), "unit": "requests/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(c_req / c_s, 2), "unit": "requests/s", "cores": 1, "kind": "oracle", **host_cores(),
                "sample": f"first {int(c_req)} requests over the three traces, about {args.cpu_seconds:.0f} s"}
     line = {"metric": "prefix_cache_requests_per_s", "value": round(value, 1), "unit": "requests/s",
             "n_gpus": 0, "steps": int(total_req), "warmup": 150, "ms_per_step": round(total_s / total_req * 1e3, 5),
@@ -912,6 +918,8 @@ def main():
         "kernels": kern,
         "ms_per_step_instrumented": round(ms_per_step_instrumented, 5),
         "cold_ms_per_step_median": round(float(np.median(cold)), 5) if cold else None,
+        "cold_ms_per_step_p10_p90": [round(float(np.percentile(cold, 10)), 5),
+                                     round(float(np.percentile(cold, 90)), 5)] if cold else None,
         "host_us": {"plan_append": round(plan_append_us, 1), "plan_build": round(plan_build_us, 1)},
         "roofline": roofline,
         "read_ceiling": ceiling,
