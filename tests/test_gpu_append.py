@@ -105,10 +105,12 @@ def test_padding_slots_are_skipped(pkv):
     assert int((k != 0).sum()) == 2 * 2 * 64
 
 
-def test_radix_backtracking_protocol(pkv):
+@pytest.mark.parametrize("fused", [False, True], ids=["two-calls", "one-launch"])
+def test_radix_backtracking_protocol(pkv, fused):
     """Tree of 256 leaves over a 4096-token root; 16 steps of append -> decode with
     pruning / forking after steps 3, 7, 11, 15 (each fork shares a partly filled tail,
-    so the next append copies it).  Pages bit-exact, sampled decode rows within tolerance."""
+    so the next append copies it).  Pages bit-exact, sampled decode rows within tolerance;
+    either kv_append then paged_decode_attn, or paged_decode_attn_append."""
     torch = __import__("torch")
     w = workloads.get(5)
     k_pages, v_pages = workloads.make_pages(w, device="cuda")
@@ -128,7 +130,8 @@ def test_radix_backtracking_protocol(pkv):
         assert [tuple(int(x) for x in c) for c in cows_l] == cows_r
         total_cow += len(cows_r)
         kn, vn = workloads.make_new_tokens(w, s, device="cuda")
-        append_on_device(pkv, k_pages, v_pages, slots_l, cows_l, kn, vn, "bf16")
+        if not fused:
+            append_on_device(pkv, k_pages, v_pages, slots_l, cows_l, kn, vn, "bf16")
         k_host, v_host = oracle.apply_append(k_host, v_host, slots_r, cows_r, bits_np(kn), bits_np(vn))
         bt, lens = lib.export_tables(st.decode_rows, w.max_blocks)
         bt_r, lens_r = ref.export_tables(st.decode_rows, w.max_blocks)
@@ -137,8 +140,14 @@ def test_radix_backtracking_protocol(pkv):
             plan = pkv.CascadePlan(bt, lens, w.num_q_heads, w.num_kv_heads).upload()
         bt_d, lens_d = tables_to_device(bt, lens)
         q = workloads.make_q(w, s, device="cuda")
-        out = pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, int(lens.max()), scale=w.scale, plan=plan,
-                                    dtype="bf16")
+        if fused:
+            assert list(st.append_rows) == list(st.decode_rows)
+            cow_src = torch.from_numpy(pkv.row_cow_sources(slots_l, cows_l, w.block_size)).cuda()
+            out = pkv.paged_decode_attn_append(q, k_pages, v_pages, bt_d, lens_d, int(lens.max()), kn, vn, cow_src,
+                                               scale=w.scale, plan=plan, dtype="bf16")
+        else:
+            out = pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, int(lens.max()), scale=w.scale,
+                                        plan=plan, dtype="bf16")
         rows = sorted(rng.choice(len(lens), size=6, replace=False).tolist())
         # make sure a row that just copied a tail is among the checked ones
         if cows_r:
