@@ -143,3 +143,25 @@ def test_radix_backtracking_steps_bit_exact():
         workloads.replay(lib, st.after_ops)
     assert total_cow == 4 * 64  # every fork after a backtrack shares a partly filled tail
     assert ref.free_list() == lib.free_list()
+
+
+def test_row_cow_sources_follow_the_append_plan():
+    """Per-row copy-on-write sources for the one-launch append + decode: a row whose new
+    token lands in a block just copied on write gets the copy's source, every other row
+    -1; the source is the block the row's table held there before the append."""
+    pool = pkv.BlockPool(32, 16, np.arange(32))
+    pool.alloc(0, 20)        # blocks 0, 1 (row 4 of block 1 next)
+    pool.fork(0, 1)          # shares both blocks, tail partly filled
+    pool.alloc(2, 32)        # blocks 2, 3 (full: the next token opens a new block)
+    pool.fork(2, 3)
+    before = {s: pool.table(s) for s in range(4)}
+    batch = [1, 2, 0, 3]
+    slots, cows = pool.plan_append(batch)
+    src = pkv.row_cow_sources(slots, cows, 16)
+    assert src.dtype == np.int32 and src.shape == (4,)
+    # row 1 copies the shared tail (block 1); then sequence 0 owns block 1 and appends in place;
+    # sequences 2 and 3 open fresh blocks (no copy)
+    assert src.tolist() == [1, -1, -1, -1]
+    assert int(slots[0]) // 16 != 1 and before[1][1] == 1
+    assert int(slots[2]) // 16 == 1
+    assert pkv.row_cow_sources(np.empty(0, np.int64), np.empty((0, 3), np.int32)).shape == (0,)
