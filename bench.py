@@ -711,7 +711,7 @@ def run_swap(args, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by rows / heads with no exchange, but nothing here launches more than one GPU).",
               file=sys.stderr)
         sys.exit(2)
