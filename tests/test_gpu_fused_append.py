@@ -159,3 +159,31 @@ def test_empty_rows_append_nothing_and_bad_plan_is_refused(pkv):
     with pytest.raises(pkv.PkvInvalid):
         pkv.paged_decode_attn_append(q, k, v, bt2_d, lens2_d, 32, kn, vn, cow, plan=plan, dtype="bf16")
     torch.cuda.synchronize()
+
+
+def test_clamped_rows_and_bad_cow_source(pkv):
+    """A row longer than max_seq_len is attended up to max_seq_len and appends nothing; a
+    copy-on-write source outside [0, num_blocks) is ignored (the row's own block is read
+    and only the new token is written)."""
+    torch = __import__("torch")
+    say("fused append: clamped row, bad copy-on-write source")
+    nblk, bs, hkv, d = 8, 16, 2, 64
+    k = torch.zeros((nblk, bs, hkv, d), dtype=torch.int16, device="cuda")
+    v = torch.zeros_like(k)
+    v[2, :3] = 0x3F80  # row 1's own block: three tokens of V = 1.0 before the new one
+    bt = np.array([[4, -1], [2, -1]], dtype=np.int32)
+    lens = np.array([10, 4], dtype=np.int32)  # row 0 is longer than max_seq_len below
+    bt_d, lens_d = tables_to_device(bt, lens)
+    kn = torch.full((2, hkv, d), 0x3F80, dtype=torch.int16, device="cuda")
+    vn = torch.full((2, hkv, d), 0x4040, dtype=torch.int16, device="cuda")  # bf16 3.0
+    q = torch.zeros((2, hkv, d), dtype=torch.int16, device="cuda")
+    cow = torch.tensor([-1, 99], dtype=torch.int32, device="cuda")
+    out = pkv.paged_decode_attn_append(q, k, v, bt_d, lens_d, 6, kn, vn, cow, dtype="bf16")
+    torch.cuda.synchronize()
+    kk, vv = k.cpu().numpy(), v.cpu().numpy()
+    assert not kk[4].any() and not vv[4].any()  # row 0 (clamped to 6 of its 10 tokens) wrote nothing
+    assert np.all(vv[2, 3] == 0x4040) and np.all(kk[2, 3] == 0x3F80)  # row 1's token 3
+    assert np.all(vv[2, :3] == 0x3F80) and not vv[2, 4:].any()
+    o = out.cpu().numpy()
+    assert np.allclose(o[0], 0.0)  # six zero tokens
+    assert np.allclose(o[1], (1.0 + 1.0 + 1.0 + 3.0) / 4)  # uniform weights (q = 0)
