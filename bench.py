@@ -746,7 +746,7 @@ def main():
     workloads.replay(pool, w.build_ops)
     step = w.steps[0]
     t0 = time.perf_counter()
-    slots, cows = pool.plan_append(step.append_rows)
+    slots, cows, row_src = pool.plan_append(step.append_rows, row_sources=True)
     plan_append_us = (time.perf_counter() - t0) * 1e6
     bt, lens = pool.export_tables(step.decode_rows, w.max_blocks)
     t0 = time.perf_counter()
@@ -772,7 +772,7 @@ def main():
     if fused and list(step.append_rows) != list(step.decode_rows):
         print("--fused needs the step to append one token to every decoded row", file=sys.stderr)
         sys.exit(2)
-    cow_src_d = torch.from_numpy(pkv.row_cow_sources(slots, cows, w.block_size)).to(dev)
+    cow_src_d = torch.from_numpy(row_src).to(dev)
 
     def one_step():
         if fused:  # append + decode in one launch

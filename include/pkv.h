@@ -236,9 +236,13 @@ pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq);
  *   slot_out[i] = t[j]*block_size + off; len += 1.
  * The batch is all-or-nothing: PKV_ERR_OOM with nothing changed if the free list
  * cannot cover it.  cow_src/cow_dst/cow_rows need room for n entries; *num_cow
- * receives the count.  PKV_ERR_NOT_FOUND for an unknown id. */
+ * receives the count.  row_cow_src (host int32 [n], may be NULL): entry i is the
+ * block sequence i's last block was copied from on write in this batch, -1 if
+ * none (the per-row form pkv_paged_decode_attn_append takes).
+ * PKV_ERR_NOT_FOUND for an unknown id. */
 pkv_status pkv_plan_append(pkv_pool* pool, const int64_t* seqs, int32_t n, int64_t* slot_out,
-                           int32_t* cow_src, int32_t* cow_dst, int32_t* cow_rows, int32_t* num_cow);
+                           int32_t* cow_src, int32_t* cow_dst, int32_t* cow_rows, int32_t* num_cow,
+                           int32_t* row_cow_src);
 
 /* Write the block tables ([n][max_blocks], padded with -1) and lengths of seqs. */
 pkv_status pkv_export_tables(const pkv_pool* pool, const int64_t* seqs, int32_t n, int32_t max_blocks,

@@ -272,6 +272,14 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
         plan->block_size != block_size || plan->max_blocks != max_blocks_per_seq)
       return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: plan was built for different shapes");
     if (!plan->device) return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn: plan not uploaded (pkv_plan_upload)");
+    // the shared nodes attend to every token they cover; a max_seq_len below that would
+    // clamp a row's own part but not its shared part
+    int32_t covered = 0;
+    for (int32_t b = 0; b < plan->batch; ++b) covered = std::max(covered, plan->row_info[2 * b]);
+    if (max_seq_len < covered)
+      return fail(PKV_ERR_INVALID,
+                  "pkv_paged_decode_attn: max_seq_len %d is below the %d tokens the plan's shared nodes cover",
+                  max_seq_len, covered);
   }
   const pkv::DecodeLayout L = pkv::decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan);
   if (batch == 0) return PKV_OK;

@@ -191,6 +191,12 @@ __device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, in
 
 }  // namespace
 
+// Register pipeline depth of the 16-bit instances (blocks held per wave: one consumed,
+// the rest in flight).
+#ifndef PKV_SPLIT_NBUF16
+#define PKV_SPLIT_NBUF16 2
+#endif
+
 #ifndef PKV_SPLIT_WAVES_PER_EU
 #define PKV_SPLIT_WAVES_PER_EU 1
 #endif
@@ -714,7 +720,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   // assume the worst of two paths, which would make the wave wait for loads it
   // does not need.  (Separately named buffers, not an indexed array of them: the
   // compiler keeps those in registers.)
-  constexpr int NBUF = Q8 ? 3 : 2;
+  constexpr int NBUF = Q8 ? 3 : (G <= 4 ? PKV_SPLIT_NBUF16 : 2);
   KV ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL], kx[TPB][VPL], vx[TPB][VPL];
   float ksa[NS], vsa[NS], ksb[NS], vsb[NS], ksx[NS], vsx[NS];
   u32x4 qa[G][VPL], qb[G][VPL], qx[G][VPL];

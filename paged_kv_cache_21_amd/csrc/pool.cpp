@@ -158,7 +158,7 @@ pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq) {
 }
 
 pkv_status pkv_plan_append(pkv_pool* pool, const int64_t* seqs, int32_t n, int64_t* slot_out, int32_t* cow_src,
-                           int32_t* cow_dst, int32_t* cow_rows, int32_t* num_cow) {
+                           int32_t* cow_dst, int32_t* cow_rows, int32_t* num_cow, int32_t* row_cow_src) {
   pkv::clear_error();
   if (!pool || n < 0 || (n > 0 && (!seqs || !slot_out || !cow_src || !cow_dst || !cow_rows)) || !num_cow)
     return pkv::fail(PKV_ERR_INVALID, "pkv_plan_append: null argument or n < 0");
@@ -202,6 +202,7 @@ pkv_status pkv_plan_append(pkv_pool* pool, const int64_t* seqs, int32_t n, int64
   for (int32_t i = 0; i < n; ++i) {
     auto& s = *ss[i];
     const int32_t pos = s.len, j = pos / bs, off = pos % bs;
+    if (row_cow_src) row_cow_src[i] = -1;
     if (off == 0) {
       const int32_t y = pool->free_list.front();
       pool->free_list.pop_front();
@@ -213,6 +214,7 @@ pkv_status pkv_plan_append(pkv_pool* pool, const int64_t* seqs, int32_t n, int64
         const int32_t y = pool->free_list.front();
         pool->free_list.pop_front();
         pool->ref[y] = 1;
+        if (row_cow_src) row_cow_src[i] = x;
         cow_src[nc] = x;
         cow_dst[nc] = y;
         cow_rows[nc] = off;

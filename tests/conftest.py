@@ -12,6 +12,11 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+def pytest_report_header(config):
+    path = os.path.join(ROOT, "paged_kv_cache_21_amd", "libpkv.so")
+    return f"libpkv: {path} ({'present' if os.path.exists(path) else 'missing'})"
+
+
 def read_golden(name):
     """key -> value (int when it parses, else float, else str) from tests/golden/<name>."""
     out = {}

@@ -86,9 +86,9 @@ static void stress_pool_and_cache(uint32_t seed) {
         if (pkv_seq_is_swapped(pool, s) == 0 && rng() % 2) b.push_back(s);
       int32_t ncow = 0;
       std::vector<int64_t> slots(b.size() + 1);
-      std::vector<int32_t> cs(b.size() + 1), cd(b.size() + 1), cr(b.size() + 1);
+      std::vector<int32_t> cs(b.size() + 1), cd(b.size() + 1), cr(b.size() + 1), rs(b.size() + 1);
       pkv_status st = pkv_plan_append(pool, b.data(), static_cast<int32_t>(b.size()), slots.data(), cs.data(),
-                                      cd.data(), cr.data(), &ncow);
+                                      cd.data(), cr.data(), &ncow, rng() % 2 ? rs.data() : nullptr);
       CHECK(st == PKV_OK || st == PKV_ERR_OOM);
       if (st == PKV_OK)
         for (int64_t s : b) toks[s].push_back(rng() % 3);

@@ -235,21 +235,25 @@ def check_worked_example(RefPool):
     assert pool.refcount(root[0]) == g["refcount_root_block"]
 
 
+def expect_error(exc, fn, *args):
+    """Pin: fn(*args) raises exc.  Any other outcome (no error, or another exception
+    type, e.g. a crash halfway through a batch) fails the pin as an assertion."""
+    try:
+        fn(*args)
+    except exc:
+        return
+    except Exception as e:  # noqa: BLE001 - a different error is a failed pin
+        raise AssertionError(f"expected {exc.__name__}, got {type(e).__name__}: {e}") from e
+    raise AssertionError(f"expected {exc.__name__}")
+
+
 def check_error_conventions(RefPool):
     pool = RefPool(4, 4)
     pool.alloc("x", 9)  # 3 blocks
     before = (pool.free_list(), pool.table("x"))
-    try:
-        pool.alloc("y", 5)  # needs 2, 1 free
-        raise AssertionError("expected MemoryError")
-    except MemoryError:
-        pass
+    expect_error(MemoryError, pool.alloc, "y", 5)  # needs 2, 1 free
     assert (pool.free_list(), pool.table("x")) == before and "y" not in pool
-    try:
-        pool.fork("nope", "z")
-        raise AssertionError("expected KeyError")
-    except KeyError:
-        pass
+    expect_error(KeyError, pool.fork, "nope", "z")
     pool.free("never-allocated")  # no-op
     assert pool.free_list() == before[0]
     # an append batch that cannot fit changes nothing
@@ -257,11 +261,7 @@ def check_error_conventions(RefPool):
     pool.fork("x", "x3")  # tail block (1 of 4 rows used) shared by three
     snap = (pool.free_list(), pool.table("x"), pool.table("x2"), pool.table("x3"),
             [pool.refcount(b) for b in range(4)], pool.length("x"))
-    try:
-        pool.plan_append(["x", "x2", "x3"])  # two copies needed, one block free
-        raise AssertionError("expected MemoryError")
-    except MemoryError:
-        pass
+    expect_error(MemoryError, pool.plan_append, ["x", "x2", "x3"])  # two copies needed, one block free
     assert snap == (pool.free_list(), pool.table("x"), pool.table("x2"), pool.table("x3"),
                     [pool.refcount(b) for b in range(4)], pool.length("x"))
 

@@ -443,6 +443,8 @@ def scenario_system_prompt(Cache, Pool, users=1000, prompt=2000, bs=16, seed=0):
             first_blocks = table[:prompt // bs]
         cache.unlock(node)
         pool.free(u)
+        # the tree keeps exactly one reference to every cached block once the request is gone
+        assert all(pool.refcount(b) == 1 for b in first_blocks), ("cached prompt blocks lost their reference", u)
     assert hits == (users - 1) * prompt
     assert cache.cached_blocks() == prompt // bs + int(sum(user_len // bs))
     for b in first_blocks:
@@ -522,6 +524,12 @@ def scenario_leaf_only_eviction(Cache, Pool, bs=4):
     assert cache.cached_blocks() == 3 + 3 * 2
     cache.match_prefix(users[0])          # user 0 becomes the most recent
     cache.lock(nodes[1])                  # user 1 is in flight
+    # a lock covers the node and every ancestor below the root ("lock_ref" on the path)
+    n = nodes[1]
+    while n != 0:
+        parent, _, lock_ref, _, _, _ = cache.node_info(n)
+        assert lock_ref == 1, ("lock does not reach node", n)
+        n = parent
     released, evicted = cache.evict(100)
     assert evicted == [nodes[2], nodes[0]] and released == 4
     assert cache.cached_blocks() == 3 + 2

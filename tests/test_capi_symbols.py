@@ -35,6 +35,16 @@ def test_binding_covers_every_declared_symbol():
     assert sorted(_SIGNATURES) == declared_functions()
 
 
+def test_the_in_tree_library_is_the_one_loaded():
+    in_tree = os.path.realpath(os.path.join(ROOT, "paged_kv_cache_21_amd", "libpkv.so"))
+    assert os.path.realpath(pkv.LIB_PATH) == in_tree
+    with open("/proc/self/maps") as f:
+        mapped = {os.path.realpath(line.split()[-1]) for line in f if line.rstrip().endswith(".so")}
+    loaded = sorted(m for m in mapped if os.path.basename(m) == "libpkv.so")
+    print("libpkv.so loaded from:", loaded)
+    assert loaded == [in_tree]
+
+
 def test_version_string():
     assert "gfx950" in pkv.version()
 

@@ -125,7 +125,7 @@ def test_radix_backtracking_protocol(pkv, fused):
     for s, st in enumerate(w.steps):
         say(f"radix step {s + 1}")
         slots_r, cows_r = ref.plan_append(st.append_rows)
-        slots_l, cows_l = lib.plan_append(st.append_rows)
+        slots_l, cows_l, row_src = lib.plan_append(st.append_rows, row_sources=True)
         assert list(slots_l) == slots_r
         assert [tuple(int(x) for x in c) for c in cows_l] == cows_r
         total_cow += len(cows_r)
@@ -142,7 +142,7 @@ def test_radix_backtracking_protocol(pkv, fused):
         q = workloads.make_q(w, s, device="cuda")
         if fused:
             assert list(st.append_rows) == list(st.decode_rows)
-            cow_src = torch.from_numpy(pkv.row_cow_sources(slots_l, cows_l, w.block_size)).cuda()
+            cow_src = torch.from_numpy(row_src).cuda()
             out = pkv.paged_decode_attn_append(q, k_pages, v_pages, bt_d, lens_d, int(lens.max()), kn, vn, cow_src,
                                                scale=w.scale, plan=plan, dtype="bf16")
         else:

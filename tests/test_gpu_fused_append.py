@@ -68,11 +68,11 @@ def test_fused_append_matches_oracle(pkv, seed, shape, plan_on):
         live = ref.sequences()
         batch = [live[i] for i in rng.permutation(len(live))]
         slots_r, cows_r = ref.plan_append(batch)
-        slots_l, cows_l = lib.plan_append(batch)
+        slots_l, cows_l, row_src = lib.plan_append(batch, row_sources=True)
         assert list(slots_l) == slots_r
         total_cow += len(cows_r)
         bt, lens = lib.export_tables(batch, 64)
-        cow_src = pkv.row_cow_sources(slots_l, cows_l, bs)
+        cow_src = row_src
         kn = torch.randn((len(batch), hkv, d), generator=gen, device="cuda").to(tdt).view(torch.int16)
         vn = torch.randn((len(batch), hkv, d), generator=gen, device="cuda").to(tdt).view(torch.int16)
         q = torch.randn((len(batch), hq, d), generator=gen, device="cuda").to(tdt).view(torch.int16)
@@ -111,7 +111,7 @@ def test_fused_equals_append_then_decode(pkv):
     v0 = torch.randn((nblk, bs, hkv, d), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
     ka, va, kb, vb = k0.clone(), v0.clone(), k0.clone(), v0.clone()
     batch = refs[0].sequences()
-    slots, cows = pools[0].plan_append(batch)
+    slots, cows, row_src = pools[0].plan_append(batch, row_sources=True)
     slots_b, cows_b = pools[1].plan_append(batch)
     assert np.array_equal(slots, slots_b) and np.array_equal(cows, cows_b) and len(cows) > 0
     bt, lens = pools[0].export_tables(batch, 64)
@@ -125,7 +125,7 @@ def test_fused_equals_append_then_decode(pkv):
     pkv.kv_append(ka, va, kn, vn, slot_d, src, dst, rows, dtype="bf16")
     two = pkv.paged_decode_attn(q, ka, va, bt_d, lens_d, int(lens.max()), dtype="bf16")
     one = pkv.paged_decode_attn_append(q, kb, vb, bt_d, lens_d, int(lens.max()), kn, vn,
-                                       torch.from_numpy(pkv.row_cow_sources(slots, cows)).cuda(), dtype="bf16")
+                                       torch.from_numpy(row_src).cuda(), dtype="bf16")
     torch.cuda.synchronize()
     assert torch.equal(ka, kb) and torch.equal(va, vb)
     assert float((one - two).abs().max()) <= 1e-5

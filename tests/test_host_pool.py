@@ -156,12 +156,16 @@ def test_row_cow_sources_follow_the_append_plan():
     pool.fork(2, 3)
     before = {s: pool.table(s) for s in range(4)}
     batch = [1, 2, 0, 3]
-    slots, cows = pool.plan_append(batch)
-    src = pkv.row_cow_sources(slots, cows, 16)
+    slots, cows, src = pool.plan_append(batch, row_sources=True)
     assert src.dtype == np.int32 and src.shape == (4,)
     # row 1 copies the shared tail (block 1); then sequence 0 owns block 1 and appends in place;
     # sequences 2 and 3 open fresh blocks (no copy)
     assert src.tolist() == [1, -1, -1, -1]
     assert int(slots[0]) // 16 != 1 and before[1][1] == 1
     assert int(slots[2]) // 16 == 1
-    assert pkv.row_cow_sources(np.empty(0, np.int64), np.empty((0, 3), np.int32)).shape == (0,)
+    # every copy's destination holds exactly the slot of the row that names its source
+    for s_, d, _ in cows:
+        rows = [i for i in range(4) if int(slots[i]) // 16 == int(d)]
+        assert [int(src[i]) for i in rows] == [int(s_)]
+    empty = pool.plan_append([], row_sources=True)
+    assert empty[2].shape == (0,)

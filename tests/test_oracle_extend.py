@@ -25,10 +25,14 @@ def _load_extend(old, new):
 
 
 EXTEND_MUTANTS = [
-    ("query sees one token too few", "K[: p + 1, kh, :] @ qr[h]", "K[:p, kh, :] @ qr[h]"),
+    ("query sees one token too few",
+     "s = scale * (K[: p + 1, kh, :] @ qr[h])\n            w = np.exp(s - s.max())\n            out[j, h] = (w @ V[: p + 1, kh, :])",
+     "s = scale * (K[: max(p, 1), kh, :] @ qr[h])\n            w = np.exp(s - s.max())\n            out[j, h] = (w @ V[: max(p, 1), kh, :])"),
     ("query sees one token too many", "out.extend((b, n - ql + i) for i in range(ql))",
      "out.extend((b, n - ql + i + 1) for i in range(ql))"),
-    ("no causal mask", "s = scale * (K[: p + 1, kh, :] @ qr[h])", "s = scale * (K[:, kh, :] @ qr[h])"),
+    ("no causal mask",
+     "s = scale * (K[: p + 1, kh, :] @ qr[h])\n            w = np.exp(s - s.max())\n            out[j, h] = (w @ V[: p + 1, kh, :])",
+     "s = scale * (K[:, kh, :] @ qr[h])\n            w = np.exp(s - s.max())\n            out[j, h] = (w @ V[:, kh, :])"),
     ("positions counted from 0", "out.extend((b, n - ql + i) for i in range(ql))", "out.extend((b, i) for i in range(ql))"),
     ("query tokens reversed", "out.extend((b, n - ql + i) for i in range(ql))", "out.extend((b, n - 1 - i) for i in range(ql))"),
     ("values not truncated", "out[j, h] = (w @ V[: p + 1, kh, :]) / w.sum()", "out[j, h] = (w @ V[-(p + 1):, kh, :]) / w.sum()"),
@@ -38,7 +42,7 @@ EXTEND_MUTANTS = [
 @pytest.mark.parametrize("label,old,new", EXTEND_MUTANTS, ids=[m[0] for m in EXTEND_MUTANTS])
 def test_extend_mutant_is_caught(label, old, new):
     mod = _load_extend(old, new)
-    with pytest.raises(Exception):
+    with pytest.raises(AssertionError):
         oc.run_extend_pins(mod.ref_extend, oracle.ref_decode, oracle.bruteforce_decode)
 
 

@@ -114,7 +114,12 @@ def test_fp8_decode_pin():
     run_fp8_decode_pin(oracle.fp8)
 
 
-def test_fp8_append_copies_and_quantizes():
+def run_fp8_append_pin(fp8):
+    """A planned append onto FP8 pages: the copy-on-write moves rows [0, rows) of the
+    source's K and V codes and scales, the token's K and V head vectors land quantized
+    in its slot (each from its own input), and nothing else changes."""
+    from oracle.attention import decode_bits
+
     rng = np.random.default_rng(2)
     nblk, bs, hkv, d = 6, 4, 2, 8
     kc = rng.integers(0, 256, (nblk, bs, hkv, d)).astype(np.uint8)
@@ -124,13 +129,28 @@ def test_fp8_append_copies_and_quantizes():
     kn = oc.bf16_bits(rng.standard_normal((2, hkv, d)) * 3)
     vn = oc.bf16_bits(rng.standard_normal((2, hkv, d)) * 0.01)
     slots, cows = [4 * 3 + 2, -1], [(1, 3, 2)]
-    k2, v2, ks2, vs2 = oracle.apply_append_fp8(kc, vc, ks, vs, slots, cows, kn, vn, "bf16")
+    k2, v2, ks2, vs2 = fp8.apply_append_fp8(kc, vc, ks, vs, slots, cows, kn, vn, "bf16")
+    # copy-on-write: rows 0, 1 of block 1 into block 3, codes and scales of K and of V
     assert np.array_equal(k2[3, :2], kc[1, :2]) and np.array_equal(ks2[3, :, :2], ks[1, :, :2])
-    assert np.array_equal(vs2[3, :, :2], vs[1, :, :2])
-    cq, sq = oracle.quantize_heads(oracle.decode_bits(kn[0], "bf16"))
-    assert np.array_equal(k2[3, 2], cq) and np.array_equal(ks2[3, :, 2], sq)
+    assert np.array_equal(v2[3, :2], vc[1, :2]) and np.array_equal(vs2[3, :, :2], vs[1, :, :2])
+    # the token in slot (3, 2): K from k_new, V from v_new, with their scales
+    kq, ksq = fp8.quantize_heads(decode_bits(kn[0], "bf16"))
+    vq, vsq = fp8.quantize_heads(decode_bits(vn[0], "bf16"))
+    assert not np.array_equal(kq, vq) and not np.array_equal(ksq, vsq)  # the inputs tell K and V apart
+    assert np.array_equal(k2[3, 2], kq) and np.array_equal(ks2[3, :, 2], ksq)
+    assert np.array_equal(v2[3, 2], vq) and np.array_equal(vs2[3, :, 2], vsq)
+    # everything else unchanged: other blocks, and row 3 of block 3 (slot -1 writes nothing)
     untouched = [b for b in range(nblk) if b != 3]
-    assert np.array_equal(k2[untouched], kc[untouched]) and np.array_equal(v2[3, 3], vc[3, 3])
+    for new_arr, old_arr in ((k2, kc), (v2, vc)):
+        assert np.array_equal(new_arr[untouched], old_arr[untouched])
+        assert np.array_equal(new_arr[3, 3], old_arr[3, 3])
+    for new_arr, old_arr in ((ks2, ks), (vs2, vs)):
+        assert np.array_equal(new_arr[untouched], old_arr[untouched])
+        assert np.array_equal(new_arr[3, :, 3], old_arr[3, :, 3])
+
+
+def test_fp8_append_copies_and_quantizes():
+    run_fp8_append_pin(oracle.fp8)
 
 
 def _load_fp8(old, new):
@@ -153,18 +173,25 @@ FP8_MUTANTS = [
      "sc = np.asarray(scales, dtype=np.float64).reshape(np.asarray(scales).shape[0], -1, np.asarray(scales).shape[1])"),
     ("sign dropped", "return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)",
      "return code.astype(np.uint8)"),
+    ("V quantized from k_new", "vq, vsc = quantize_heads(decode_bits(np.asarray(v_new), dtype))",
+     "vq, vsc = quantize_heads(decode_bits(np.asarray(k_new), dtype))"),
+    ("V scale not written", "ks[blk, :, row], vs[blk, :, row] = ksc[i], vsc[i]", "ks[blk, :, row] = ksc[i]"),
+    ("V codes not copied on write", "        vc[dst, :rows] = vc[src, :rows]\n", ""),
+    ("V scales not copied on write", "        vs[dst, :, :rows] = vs[src, :, :rows]\n", ""),
 ]
 
 
 @pytest.mark.parametrize("label,old,new", FP8_MUTANTS, ids=[m[0] for m in FP8_MUTANTS])
 def test_fp8_mutant_is_caught(label, old, new):
     mod = _load_fp8(old, new)
-    with pytest.raises(Exception):
+    with pytest.raises(AssertionError):
         run_fp8_pins(mod)
         run_fp8_decode_pin(mod)
+        run_fp8_append_pin(mod)
 
 
 def test_unmutated_fp8_copy_passes():
     mod = _load_fp8("import numpy as np", "import numpy as np")
     run_fp8_pins(mod)
     run_fp8_decode_pin(mod)
+    run_fp8_append_pin(mod)

@@ -38,7 +38,7 @@ ATTENTION_MUTANTS = [
 @pytest.mark.parametrize("label,old,new", ATTENTION_MUTANTS, ids=[m[0] for m in ATTENTION_MUTANTS])
 def test_attention_mutant_is_caught(label, old, new):
     mod = _load_mutant("attention.py", old, new)
-    with pytest.raises(Exception):
+    with pytest.raises(AssertionError):
         oc.run_attention_pins(mod.ref_decode, __import__("oracle").bruteforce_decode, mod.decode_bits)
 
 
@@ -57,7 +57,7 @@ POOL_MUTANTS = [
 @pytest.mark.parametrize("label,old,new", POOL_MUTANTS, ids=[m[0] for m in POOL_MUTANTS])
 def test_pool_mutant_is_caught(label, old, new):
     mod = _load_mutant("pool.py", old, new)
-    with pytest.raises(Exception):
+    with pytest.raises(AssertionError):
         oc.run_pool_pins(mod.RefPool, mod.apply_append)
 
 

@@ -132,14 +132,14 @@ _RADIX_IMPORTS = [("from .pool import RefPool", "from oracle.pool import RefPool
 @pytest.mark.parametrize("label,old,new", RADIX_MUTANTS, ids=[m[0] for m in RADIX_MUTANTS])
 def test_radix_mutant_is_caught(label, old, new):
     mod = _load("radix.py", old, new, _RADIX_IMPORTS)
-    with pytest.raises(Exception):
+    with pytest.raises(AssertionError):
         rc.run_radix_pins(mod.RadixCache, RefPool)
 
 
 @pytest.mark.parametrize("label,old,new", POOL_MUTANTS, ids=[m[0] for m in POOL_MUTANTS])
 def test_pool_prefix_mutant_is_caught(label, old, new):
     pool = _load("pool.py", old, new, [])
-    with pytest.raises(Exception):
+    with pytest.raises(AssertionError):
         rc.run_radix_pins(RadixCache, pool.RefPool)
 
 

@@ -48,5 +48,5 @@ def test_swap_mutant_is_caught(label, old, new):
     assert src.count(old) == 1, label
     mod = types.ModuleType("oracle_mutant_pool_swap")
     exec(compile(src.replace(old, new, 1), "pool.py", "exec"), mod.__dict__)
-    with pytest.raises(Exception):
+    with pytest.raises(AssertionError):
         sc.run_swap_pins(mod.RefPool, mod.apply_append, mod.apply_swap, ref_decode)
