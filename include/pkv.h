@@ -67,6 +67,16 @@ typedef enum {
 
 typedef enum { PKV_F16 = 0, PKV_BF16 = 1 } pkv_dtype;
 
+/* Flags a decode call or-s into its optional device status word (see
+ * pkv_paged_decode_attn): the call still returns a result, but not the definition's
+ * for the rows concerned. */
+typedef enum {
+  PKV_STATUS_LEN_CLAMPED = 1, /* some seq_lens[b] outside [0, min(max_seq_len, max_blocks_per_seq*block_size)]:
+                                 the row attended to the clamped length */
+  PKV_STATUS_BAD_BLOCK = 2    /* some block id read from a table (or a plan node) outside [0, num_blocks):
+                                 its tokens got zero weight */
+} pkv_status_flag;
+
 typedef struct pkv_pool pkv_pool;
 typedef struct pkv_plan pkv_plan;
 typedef struct pkv_radix pkv_radix;
@@ -145,10 +155,15 @@ pkv_status pkv_kv_append(void* k_pages, void* v_pages, int64_t num_blocks, int32
  *   workspace     device scratch of at least pkv_decode_workspace_bytes(...) bytes
  *                 (fp32 partial results); contents on entry are ignored.
  *   out           device, float32 [batch][num_q_heads][head_dim]
+ *   status        device int32 word, or NULL: the call or-s PKV_STATUS_* flags into it
+ *                 when an input is outside the definition's domain (a length clamped, a
+ *                 block id out of range).  Never cleared by the call: zero it first to
+ *                 see one call's flags.
  * Supported: block_size 16; head_dim 64 or 128; group in {1, 2, 4, 8}; num_blocks >= 1
  * when batch > 0.  Block ids outside [0, num_blocks) are never dereferenced: their
  * tokens get zero weight (block 0 is read in their place, so a block 0 holding
- * non-finite values could still reach the output).
+ * non-finite values could still reach the output) and PKV_STATUS_BAD_BLOCK is set.
+ * With a plan, max_seq_len below the tokens its shared nodes cover is PKV_ERR_INVALID.
  * Errors: PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
  * ---------------------------------------------------------------------------------------- */
 pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -158,7 +173,7 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
                                  const int32_t* seq_lens, int32_t max_seq_len, float scale,
                                  const pkv_plan* plan, void* workspace, size_t workspace_bytes,
-                                 float* out, void* stream);
+                                 float* out, int32_t* status, void* stream);
 
 /* Append and decode in one launch: pkv_kv_append of one new token per row (with the
  * copy-on-write of a partly filled shared last block) followed by pkv_paged_decode_attn,
@@ -185,12 +200,13 @@ pkv_status pkv_paged_decode_attn_append(const void* q, int32_t batch, int32_t nu
                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
                                         const void* k_new, const void* v_new, const int32_t* cow_src, float scale,
                                         const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out,
-                                        void* stream);
+                                        int32_t* status, void* stream);
 
 /* Bytes of device workspace pkv_paged_decode_attn needs for these sizes (and plan,
  * which may be NULL).  Returns 0 for invalid arguments (see pkv_last_error). */
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, const pkv_plan* plan);
+
 
 /* ------------------------------------------------------------------------------------------
  * Host block pool ("The Reasoning Engine Meltdown", §5 and §6).
@@ -500,7 +516,8 @@ pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q
                                      const float* k_scales, const float* v_scales, int64_t num_blocks,
                                      int32_t block_size, const int32_t* block_tables, int32_t max_blocks_per_seq,
                                      const int32_t* seq_lens, int32_t max_seq_len, float scale, const pkv_plan* plan,
-                                     void* workspace, size_t workspace_bytes, float* out, void* stream);
+                                     void* workspace, size_t workspace_bytes, float* out, int32_t* status,
+                                     void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Device operation 3: multi-token (extend) attention over a paged KV cache.

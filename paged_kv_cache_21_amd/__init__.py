@@ -26,6 +26,7 @@ __all__ = [
     "ExtendPlan", "paged_extend_attn", "extend_workspace_bytes", "kv_append_fp8", "paged_decode_attn_fp8",
     "paged_decode_attn_append",
     "timing_enable", "timing_reset", "timing_read", "stream_read", "KERNELS", "lib", "LIB_PATH", "version",
+    "STATUS_LEN_CLAMPED", "STATUS_BAD_BLOCK",
 ]
 
 # The library built in-tree next to this file (paged_kv_cache_21_amd/build.py); nothing else is loaded.
@@ -34,6 +35,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_NOT_FOUND, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP, PKV_ERR_WORKSPACE = (
     0, -1, -2, -3, -4, -5, -6)
 PKV_F16, PKV_BF16 = 0, 1
+STATUS_LEN_CLAMPED, STATUS_BAD_BLOCK = 1, 2  # flags of the decode calls' optional status word
 PKV_EVICT_LRU, PKV_EVICT_RSBCM = 0, 1
 KERNELS = {"append": 0, "decode_split": 1, "merge": 2, "cascade": 3}
 
@@ -79,9 +81,9 @@ _SIGNATURES = {
     "pkv_version": (_c.c_char_p, []),
     "pkv_kv_append": (_i32, [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pkv_paged_decode_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32,
-                                     _f32, _vp, _vp, _sz, _vp, _vp]),
+                                     _f32, _vp, _vp, _sz, _vp, _vp, _vp]),
     "pkv_paged_decode_attn_append": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp,
-                                            _i32, _vp, _vp, _vp, _f32, _vp, _vp, _sz, _vp, _vp]),
+                                            _i32, _vp, _vp, _vp, _f32, _vp, _vp, _sz, _vp, _vp, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_pool_create": (_vp, [_i32, _i32, _vp]),
     "pkv_pool_destroy": (None, [_vp]),
@@ -133,7 +135,7 @@ _SIGNATURES = {
     "pkv_kv_append_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                  _vp, _i32, _vp]),
     "pkv_paged_decode_attn_fp8": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _vp,
-                                         _i32, _vp, _i32, _f32, _vp, _vp, _sz, _vp, _vp]),
+                                         _i32, _vp, _i32, _f32, _vp, _vp, _sz, _vp, _vp, _vp]),
     "pkv_stream_read": (_i32, [_vp, _i64, _vp, _i32, _vp]),
     "pkv_pool_set_host_slots": (_i32, [_vp, _i32, _vp]),
     "pkv_seq_swap_out": (_i32, [_vp, _i64, _vp, _vp, _i32, _vp]),
@@ -275,9 +277,10 @@ def kv_append_fp8(k_pages, v_pages, k_scales, v_scales, k_new, v_new, slot_mappi
 
 
 def paged_decode_attn_fp8(q, k_pages, v_pages, k_scales, v_scales, block_tables, seq_lens, max_seq_len, scale=None,
-                          plan=None, workspace=None, out=None, q_dtype=None, stream=None):
+                          plan=None, workspace=None, out=None, q_dtype=None, stream=None, status=None):
     """Decode attention over FP8 pages (codes x per-row scales); q [B, Hq, d] fp16/bf16, fp32 output.
-    ``plan``: an uploaded CascadePlan of the same tables (shared blocks through the matrix-core pass)."""
+    ``plan``: an uploaded CascadePlan of the same tables (shared blocks through the matrix-core pass).
+    ``status``: as for paged_decode_attn."""
     import torch
 
     _require(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape and k_pages.dtype == torch.uint8,
@@ -304,8 +307,19 @@ def paged_decode_attn_fp8(q, k_pages, v_pages, k_scales, v_scales, block_tables,
                                           _ptr(block_tables), int(block_tables.shape[1]), _ptr(seq_lens),
                                           int(max_seq_len), float(scale), plan._handle if plan is not None else None,
                                           _ptr(workspace),
-                                          workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream, q)))
+                                          workspace.numel() * workspace.element_size(), _ptr(out),
+                                          _status_ptr(status), _stream(stream, q)))
     return out
+
+
+def _status_ptr(status):
+    """Device address of an optional int32 status word (a one-element int32 device tensor)."""
+    if status is None:
+        return None
+    import torch
+
+    _require(status.dtype == torch.int32 and status.numel() >= 1 and status.is_cuda, "status: int32 device tensor")
+    return status.data_ptr()
 
 
 def decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan=None):
@@ -319,12 +333,14 @@ def decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_seq_l
 
 
 def paged_decode_attn(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len, scale=None, plan=None,
-                      workspace=None, out=None, dtype=None, stream=None):
+                      workspace=None, out=None, dtype=None, stream=None, status=None):
     """o[b, h] = softmax(scale * q[b, h] . K_b^T) V_b over the row's seq_lens[b] tokens (fp32 output).
 
     q: [B, Hq, d]; pages [num_blocks, 16, Hkv, d]; block_tables int32 [B, max_blocks];
     seq_lens int32 [B] (all device tensors).  ``plan``: an uploaded CascadePlan or None.
     ``workspace``: a device tensor of at least decode_workspace_bytes(...) bytes (allocated if None).
+    ``status``: optional one-element int32 device tensor; the call or-s STATUS_LEN_CLAMPED /
+    STATUS_BAD_BLOCK into it for inputs outside the definition's domain (never cleared by the call).
     """
     import torch
 
@@ -349,13 +365,13 @@ def paged_decode_attn(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len, 
     _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, hq, d), "bad out tensor")
     _check(_lib.pkv_paged_decode_attn(_ptr(q), B, hq, hkv, d, _dtype_code(q, dtype), _ptr(k_pages), _ptr(v_pages),
                                       nblk, bs, _ptr(block_tables), max_blocks, _ptr(seq_lens), int(max_seq_len),
-                                      float(scale), hplan, _ptr(workspace), ws_bytes, _ptr(out),
+                                      float(scale), hplan, _ptr(workspace), ws_bytes, _ptr(out), _status_ptr(status),
                                       _stream(stream, q)))
     return out
 
 
 def paged_decode_attn_append(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len, k_new, v_new, cow_src,
-                             scale=None, plan=None, workspace=None, out=None, dtype=None, stream=None):
+                             scale=None, plan=None, workspace=None, out=None, dtype=None, stream=None, status=None):
     """kv_append of one new token per row followed by paged_decode_attn, in one launch.
 
     The tables are those after the append; row b's new token (k_new/v_new [B, Hkv, d]) is
@@ -390,7 +406,8 @@ def paged_decode_attn_append(q, k_pages, v_pages, block_tables, seq_lens, max_se
     _check(_lib.pkv_paged_decode_attn_append(_ptr(q), B, hq, hkv, d, _dtype_code(q, dtype), _ptr(k_pages),
                                              _ptr(v_pages), nblk, bs, _ptr(block_tables), max_blocks, _ptr(seq_lens),
                                              int(max_seq_len), _ptr(k_new), _ptr(v_new), _ptr(cow_src), float(scale),
-                                             hplan, _ptr(workspace), ws_bytes, _ptr(out), _stream(stream, q)))
+                                             hplan, _ptr(workspace), ws_bytes, _ptr(out), _status_ptr(status),
+                                             _stream(stream, q)))
     return out
 
 

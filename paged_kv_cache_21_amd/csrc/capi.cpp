@@ -248,8 +248,9 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
                        int32_t head_dim, const void* k_pages, const void* v_pages, const float* k_scales,
                        const float* v_scales, int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float scale,
-                       const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out, void* stream,
-                       const void* k_new = nullptr, const void* v_new = nullptr, const int32_t* cow_src = nullptr) {
+                       const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out, int32_t* status,
+                       void* stream, const void* k_new = nullptr, const void* v_new = nullptr,
+                       const int32_t* cow_src = nullptr) {
   const int dtype = kdtype;
   const bool fused = k_new != nullptr;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0 ||
@@ -318,7 +319,8 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
                        scale_log2,
                        plan->rows_per_item,
                        k_scales,
-                       v_scales};
+                       v_scales,
+                       status};
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
     if (st != PKV_OK) return st;
@@ -349,13 +351,14 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
                       L.slots,
                       PKV_MIN_CHUNK,
                       waves,
-                      scale_log2};
+                      scale_log2,
+                      status};
     pkv_status st = pkv::launch(PKV_KERNEL_DECODE_SPLIT, "decode_split", s,
                                 [&] { return pkv::launch_decode_split(dtype, head_dim, group, sa, s); });
     if (st != PKV_OK) return st;
   }
   pkv::MergeArgs ma{seq_lens, row_info, counts, acc, ml, out, batch, num_q_heads, num_kv_heads, max_blocks_per_seq,
-                    max_seq_len, L.slots};
+                    max_seq_len, L.slots, status};
   return pkv::launch(PKV_KERNEL_MERGE, "merge", s, [&] { return pkv::launch_merge(head_dim, ma, s); });
 }
 
@@ -368,12 +371,12 @@ pkv_status pkv_paged_decode_attn(const void* q, int32_t batch, int32_t num_q_hea
                                  int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
                                  int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len, float scale,
                                  const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out,
-                                 void* stream) {
+                                 int32_t* status, void* stream) {
   pkv::clear_error();
   if (dtype != PKV_F16 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn: dtype %d", dtype);
   return decode_impl(dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, nullptr, nullptr,
                      num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
-                     workspace, workspace_bytes, out, stream);
+                     workspace, workspace_bytes, out, status, stream);
 }
 
 pkv_status pkv_paged_decode_attn_append(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -382,7 +385,7 @@ pkv_status pkv_paged_decode_attn_append(const void* q, int32_t batch, int32_t nu
                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
                                         const void* k_new, const void* v_new, const int32_t* cow_src, float scale,
                                         const pkv_plan* plan, void* workspace, size_t workspace_bytes, float* out,
-                                        void* stream) {
+                                        int32_t* status, void* stream) {
   pkv::clear_error();
   if (dtype != PKV_F16 && dtype != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn_append: dtype %d", dtype);
@@ -397,7 +400,7 @@ pkv_status pkv_paged_decode_attn_append(const void* q, int32_t batch, int32_t nu
   if (batch == 0) return PKV_OK;
   return decode_impl(dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, nullptr, nullptr,
                      num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
-                     workspace, workspace_bytes, out, stream, k_new, v_new, cow_src);
+                     workspace, workspace_bytes, out, status, stream, k_new, v_new, cow_src);
 }
 
 pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -405,7 +408,8 @@ pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q
                                      const float* k_scales, const float* v_scales, int64_t num_blocks,
                                      int32_t block_size, const int32_t* block_tables, int32_t max_blocks_per_seq,
                                      const int32_t* seq_lens, int32_t max_seq_len, float scale, const pkv_plan* plan,
-                                     void* workspace, size_t workspace_bytes, float* out, void* stream) {
+                                     void* workspace, size_t workspace_bytes, float* out, int32_t* status,
+                                     void* stream) {
   pkv::clear_error();
   if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn_fp8: q dtype %d", q_dtype);
@@ -414,7 +418,7 @@ pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q
     return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: scales must be 4-byte aligned (16 with a plan)");
   return decode_impl(2 + q_dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, k_scales, v_scales,
                      num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
-                     workspace, workspace_bytes, out, stream);
+                     workspace, workspace_bytes, out, status, stream);
 }
 
 size_t pkv_extend_workspace_bytes(const pkv_plan* plan, int32_t head_dim) {
@@ -487,13 +491,14 @@ pkv_status extend_impl(int kdtype, const void* q, int32_t num_query_rows, int32_
                        scale_log2,
                        plan->rows_per_item,
                        k_scales,
-                       v_scales};
+                       v_scales,
+                       nullptr};
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
     if (st != PKV_OK) return st;
   }
   pkv::MergeArgs ma{nullptr, plan->device + plan->off_row_info, nullptr, acc, ml, out, num_query_rows, num_q_heads,
-                    num_kv_heads, 0, 0, slots};
+                    num_kv_heads, 0, 0, slots, nullptr};
   return pkv::launch(PKV_KERNEL_MERGE, "merge", s, [&] { return pkv::launch_merge(head_dim, ma, s); });
 }
 

@@ -254,6 +254,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     Stage st = st_in;
     // block_id reads a lane of a register: its argument must be wave-uniform
     const bool ok0 = block_id(2 * ch) >= 0, ok1 = block_id(2 * ch + 1) >= 0;
+    // an entry that names a block outside the pool (not the piece's odd end) is reported
+    if (a.status && tid == 0 &&
+        ((!ok0 && 2 * ch < nblk) || (!ok1 && 2 * ch + 1 < nblk)))
+      __hip_atomic_fetch_or(a.status, PKV_STATUS_BAD_BLOCK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (vthread && (ch * 32 + 32 > piece_valid || !ok0 || !ok1)) {  // uniform
       const int t = ch * 32 + 2 * vpair;
       const bool blk_ok = vhi ? ok1 : ok0;

@@ -12,6 +12,8 @@
 //   M = max_i m_i,  o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
 // Scores are kept in log2 units (scale * log2(e) folded into one multiply) so
 // every exponential is a single v_exp_f32.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -42,7 +44,8 @@ namespace pkv {
 
 namespace {
 
-// A position in the (row, KV head, block) work order.
+// A position in the (row, KV head, block) work order.  Every field is the same in
+// all lanes (the compiler keeps cursors in scalar registers).
 struct Cursor {
   int b;        // row
   int h;        // KV head
@@ -50,42 +53,71 @@ struct Cursor {
   int nb;       // own blocks of the row
   int blk0;     // logical block index where the row's own part starts
   int depth;    // partials the cascade pass wrote for this row
-  int len;      // row length (tokens)
+  int len;      // row length (tokens, clamped)
+  int cow;      // FUSED: the row's copy-on-write source block (-1: none)
+  int app;      // FUSED: 1 if the row's new token is attended (its length was not clamped)
   int64_t seg;  // index of block 0 of segment (b, h) in the work order
 };
 
-struct RowInfo {
-  int nb, blk0, depth, len;
+// The row information of 64 consecutive rows [base, base + 64), lane l holding row
+// base + l, kept in registers so a cursor moving to the next row reads it with a
+// lane read instead of a memory round trip (a load younger than the K/V loads in
+// flight would make the wave wait for all of them).
+struct RowWindow {
+  int base;  // uniform
+  int len;   // clamped length
+  int beg;   // tokens covered by the row's shared nodes (0 without a plan)
+  int dep;   // node partial slots of the row
+  int cow;   // FUSED: copy-on-write source of the row's last block
+  int app;   // FUSED: new token attended
 };
 
-__device__ __forceinline__ RowInfo load_row(const SplitArgs& a, int b) {
-  int len = a.seq_lens[b];
-  len = min(len, a.max_seq_len);
-  len = min(len, a.max_blocks * 16);
-  // branch-free: without a plan, read seq_lens[b] in place of the plan entry and drop it
-  const bool plan = a.row_info != nullptr;
-  const int32_t* info = plan ? a.row_info + 2 * b : a.seq_lens + b;
-  const int i0 = info[0];
-  const int i1 = info[plan ? 1 : 0];
-  const int begin = plan ? i0 : 0;
-  const int depth = plan ? i1 : 0;
-  RowInfo r;
-  r.nb = len > begin ? (len - begin + 15) >> 4 : 0;
-  r.blk0 = begin >> 4;
-  r.depth = depth;
-  r.len = len;
-  return r;
+__device__ __forceinline__ int clamp_len(const SplitArgs& a, int raw) {
+  return max(0, min(min(raw, a.max_seq_len), a.max_blocks * 16));
 }
 
-__device__ __forceinline__ void set_row(Cursor& c, const RowInfo& r) {
-  c.nb = r.nb;
-  c.blk0 = r.blk0;
-  c.depth = r.depth;
-  c.len = r.len;
+// Loads the window of rows [base, base + 64) (rows past the batch read as empty).
+template <bool FUSED>
+__device__ __forceinline__ void load_window(const SplitArgs& a, int base, RowWindow& win) {
+  const int b = base + __lane_id();
+  const int bb = min(b, a.batch - 1);
+  const bool plan = a.row_info != nullptr;
+  const int raw = a.seq_lens[bb];
+  const int32_t* info = plan ? a.row_info + 2 * bb : a.seq_lens + bb;
+  const int i0 = info[0];
+  const int i1 = info[plan ? 1 : 0];
+  win.base = base;
+  win.len = b < a.batch ? clamp_len(a, raw) : 0;
+  win.beg = plan ? i0 : 0;
+  win.dep = plan ? i1 : 0;
+  if constexpr (FUSED) {
+    win.cow = a.cow_src[bb];
+    win.app = raw > 0 && raw == win.len;
+  } else {
+    win.cow = -1;
+    win.app = 0;
+  }
+}
+
+// Fills the row fields of cursor c for row c.b from the window (reloaded when c.b
+// lies outside it: at most once per 64 rows).
+template <bool FUSED>
+__device__ __forceinline__ void set_row(Cursor& c, const SplitArgs& a, RowWindow& win) {
+  if (c.b - win.base >= 64) load_window<FUSED>(a, c.b & ~63, win);  // uniform; rows only move forward
+  const int k = c.b - win.base;
+  const int len = __builtin_amdgcn_readlane(win.len, k);
+  const int beg = __builtin_amdgcn_readlane(win.beg, k);
+  c.len = len;
+  c.nb = len > beg ? (len - beg + 15) >> 4 : 0;
+  c.blk0 = beg >> 4;
+  c.depth = __builtin_amdgcn_readlane(win.dep, k);
+  c.cow = FUSED ? __builtin_amdgcn_readlane(win.cow, k) : -1;
+  c.app = FUSED ? __builtin_amdgcn_readlane(win.app, k) : 0;
 }
 
 // next block in the work order (the caller guarantees one exists)
-__device__ __forceinline__ void advance(Cursor& c, const SplitArgs& a) {
+template <bool FUSED>
+__device__ __forceinline__ void advance(Cursor& c, const SplitArgs& a, RowWindow& win) {
   if (++c.j < c.nb) return;
   c.j = 0;
   c.seg += c.nb;
@@ -93,7 +125,7 @@ __device__ __forceinline__ void advance(Cursor& c, const SplitArgs& a) {
   c.h = 0;
   do {
     ++c.b;
-    set_row(c, load_row(a, c.b));
+    set_row<FUSED>(c, a, win);
   } while (c.nb == 0);
 }
 
@@ -108,24 +140,27 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
   return x;
 }
 
+// sum over the wave, in every lane (returned as a wave-uniform value so that what is
+// derived from it stays in scalar registers)
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
   for (int d = 1; d < 64; d *= 2) x += __builtin_amdgcn_ds_bpermute((__lane_id() ^ d) << 2, x);
-  return x;
+  return __builtin_amdgcn_readfirstlane(x);
 }
 
 // This wave's share of the work order and its first position, for batches of at
 // most 64 * KW rows.  Every row's length and plan entry are loaded at once (clamped
 // indices, no branches, so the loads are all in flight together and the wave pays
-// one round of memory latency); the sums and the search then run on registers.
-// Returns false when the wave has no work.
-template <int KW>
+// one round of memory latency); the sums and the search then run on registers, and
+// the 64-row window holding the first position stays in registers as the row
+// window.  Returns false when the wave has no work.
+template <int KW, bool FUSED>
 __device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, int64_t& chunk, int& count,
-                                                   Cursor& cur) {
+                                                   Cursor& cur, RowWindow& win) {
   const int lane = __lane_id();
   const int Hkv = a.num_kv_heads;
   const bool plan = a.row_info != nullptr;
-  int raw_len[KW], raw_beg[KW], raw_dep[KW];
+  int raw_len[KW], raw_beg[KW], raw_dep[KW], raw_cow[KW];
 #pragma unroll
   for (int k = 0; k < KW; ++k) {
     const int b = min(k * 64 + lane, a.batch - 1);
@@ -133,20 +168,19 @@ __device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, in
     raw_len[k] = a.seq_lens[b];
     raw_beg[k] = info[0];
     raw_dep[k] = info[plan ? 1 : 0];
+    raw_cow[k] = FUSED ? a.cow_src[b] : -1;
   }
 #pragma unroll
-  for (int k = 0; k < KW; ++k) asm volatile("" ::"v"(raw_len[k]), "v"(raw_beg[k]), "v"(raw_dep[k]));
-  int nbk[KW], wsum[KW];
+  for (int k = 0; k < KW; ++k) asm volatile("" ::"v"(raw_len[k]), "v"(raw_beg[k]), "v"(raw_dep[k]), "v"(raw_cow[k]));
+  int nbk[KW], wsum[KW], lenk[KW];
   int64_t total = 0;
 #pragma unroll
   for (int k = 0; k < KW; ++k) {
     const bool in = k * 64 + lane < a.batch;
-    int len = min(min(raw_len[k], a.max_seq_len), a.max_blocks * 16);
-    const int begin = plan ? raw_beg[k] : 0;
-    raw_len[k] = len;
-    raw_beg[k] = begin;
+    lenk[k] = in ? clamp_len(a, raw_len[k]) : 0;
+    raw_beg[k] = plan ? raw_beg[k] : 0;
     raw_dep[k] = plan ? raw_dep[k] : 0;
-    nbk[k] = (in && len > begin) ? (len - begin + 15) >> 4 : 0;
+    nbk[k] = lenk[k] > raw_beg[k] ? (lenk[k] - raw_beg[k] + 15) >> 4 : 0;
     wsum[k] = wave_sum(nbk[k]);
     total += wsum[k];
   }
@@ -164,29 +198,72 @@ __device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, in
     kw = here ? k : kw;
     run += (kw < 0) ? wk : 0;
   }
-  int s_nb = nbk[0], s_len = raw_len[0], s_beg = raw_beg[0], s_dep = raw_dep[0];
+  int s_nb = nbk[0];
+  win.len = lenk[0];
+  win.beg = raw_beg[0];
+  win.dep = raw_dep[0];
+  win.cow = raw_cow[0];
+  win.app = raw_len[0] > 0 && raw_len[0] == lenk[0];
 #pragma unroll
   for (int k = 1; k < KW; ++k) {
     s_nb = k == kw ? nbk[k] : s_nb;
-    s_len = k == kw ? raw_len[k] : s_len;
-    s_beg = k == kw ? raw_beg[k] : s_beg;
-    s_dep = k == kw ? raw_dep[k] : s_dep;
+    win.len = k == kw ? lenk[k] : win.len;
+    win.beg = k == kw ? raw_beg[k] : win.beg;
+    win.dep = k == kw ? raw_dep[k] : win.dep;
+    win.cow = k == kw ? raw_cow[k] : win.cow;
+    win.app = k == kw ? (raw_len[k] > 0 && raw_len[k] == lenk[k]) : win.app;
   }
+  win.base = kw * 64;
   const int u = s_nb * Hkv;
   const int incl = wave_inclusive_scan(u);
   const uint64_t hit = __ballot(run + incl > start);
   const int k = __builtin_ctzll(hit);
   const int64_t row_start = run + __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(u, k);
   cur.b = kw * 64 + k;
-  cur.nb = __builtin_amdgcn_readlane(s_nb, k);
-  cur.blk0 = __builtin_amdgcn_readlane(s_beg, k) >> 4;
-  cur.depth = __builtin_amdgcn_readlane(s_dep, k);
-  cur.len = __builtin_amdgcn_readlane(s_len, k);
+  set_row<FUSED>(cur, a, win);
   const int off = static_cast<int>(start - row_start);
   cur.h = off / cur.nb;
   cur.j = off - cur.h * cur.nb;
   cur.seg = row_start + static_cast<int64_t>(cur.h) * cur.nb;
   return true;
+}
+
+// The same for any batch size: the rows are scanned 64 at a time (one round of
+// memory latency per 64 rows), then the window of the first row is loaded.
+template <bool FUSED>
+__device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64_t& chunk, int& count, Cursor& cur,
+                                                RowWindow& win) {
+  const int Hkv = a.num_kv_heads;
+  int64_t total = 0;
+  for (int base = 0; base < a.batch; base += 64) {
+    load_window<FUSED>(a, base, win);
+    const int nb = win.len > win.beg ? (win.len - win.beg + 15) >> 4 : 0;
+    total += wave_sum(nb);
+  }
+  total *= Hkv;
+  chunk = max(static_cast<int64_t>(a.min_chunk), (total + a.num_waves - 1) / a.num_waves);
+  const int64_t start = static_cast<int64_t>(w) * chunk;
+  if (start >= total) return false;
+  count = static_cast<int>(min(chunk, total - start));
+  int64_t run = 0;
+  for (int base = 0;; base += 64) {
+    load_window<FUSED>(a, base, win);
+    const int u = (win.len > win.beg ? (win.len - win.beg + 15) >> 4 : 0) * Hkv;
+    const int incl = wave_inclusive_scan(u);
+    const uint64_t hit = __ballot(run + incl > start);
+    if (hit) {
+      const int k = __builtin_ctzll(hit);
+      const int64_t row_start = run + __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(u, k);
+      cur.b = base + k;
+      set_row<FUSED>(cur, a, win);
+      const int off = static_cast<int>(start - row_start);
+      cur.h = off / cur.nb;
+      cur.j = off - cur.h * cur.nb;
+      cur.seg = row_start + static_cast<int64_t>(cur.h) * cur.nb;
+      return true;
+    }
+    run += __builtin_amdgcn_readlane(incl, 63);
+  }
 }
 
 }  // namespace
@@ -195,6 +272,12 @@ __device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, in
 // the rest in flight).
 #ifndef PKV_SPLIT_NBUF16
 #define PKV_SPLIT_NBUF16 2
+#endif
+
+// Partial results of finished segment pieces staged in LDS and stored after the
+// wave's last block (1) or stored as each piece finishes (0).
+#ifndef PKV_SPLIT_STAGE
+#define PKV_SPLIT_STAGE 1
 #endif
 
 #ifndef PKV_SPLIT_WAVES_PER_EU
@@ -234,45 +317,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   int64_t chunk = 0;
   int count = 0;
   Cursor cur;
+  RowWindow win;
   const int nwin = (a.batch + 63) >> 6;
-  if (nwin <= 16) {
-    const bool any = nwin == 1   ? find_start_windows<1>(a, w, chunk, count, cur)
-                     : nwin <= 4 ? find_start_windows<4>(a, w, chunk, count, cur)
-                                 : find_start_windows<16>(a, w, chunk, count, cur);
-    if (!any) return;
-  } else {
-    int64_t total = 0;
-    for (int base = 0; base < a.batch; base += 64) {
-      const int b = base + lane;
-      const int nb = b < a.batch ? load_row(a, b).nb : 0;
-      total += wave_sum(nb);
-    }
-    total *= Hkv;
-    chunk = max(static_cast<int64_t>(a.min_chunk), (total + a.num_waves - 1) / a.num_waves);
-    const int64_t start = static_cast<int64_t>(w) * chunk;
-    if (start >= total) return;
-    count = static_cast<int>(min(chunk, total - start));
-    int64_t run = 0;
-    for (int base = 0;; base += 64) {
-      const int b = base + lane;
-      const int u = b < a.batch ? load_row(a, b).nb * Hkv : 0;
-      const int incl = wave_inclusive_scan(u);
-      const uint64_t hit = __ballot(run + incl > start);
-      if (hit) {
-        const int k = __builtin_ctzll(hit);
-        const int64_t row_start = run + __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(u, k);
-        cur.b = base + k;
-        set_row(cur, load_row(a, cur.b));
-        const int off = static_cast<int>(start - row_start);
-        cur.h = off / cur.nb;
-        cur.j = off - cur.h * cur.nb;
-        cur.seg = row_start + static_cast<int64_t>(cur.h) * cur.nb;
-        break;
-      }
-      run += __builtin_amdgcn_readlane(incl, 63);
-    }
-  }
-  Cursor pre = cur;  // position of the next block to load
+  const bool any = nwin == 1   ? find_start_windows<1, FUSED>(a, w, chunk, count, cur, win)
+                   : nwin <= 4 ? find_start_windows<4, FUSED>(a, w, chunk, count, cur, win)
+                   : nwin <= 16 ? find_start_windows<16, FUSED>(a, w, chunk, count, cur, win)
+                                : find_start_scan<FUSED>(a, w, chunk, count, cur, win);
+  if (!any) return;
 
   const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;  // elements between consecutive tokens
   const int64_t blk_stride = 16 * tok_stride;
@@ -285,31 +336,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     for (int v = 0; v < VPL; ++v)
       voff[t][v] = static_cast<uint32_t>(((r + t * ROWS) * tok_stride + (v * LPT + c) * 8) * EB);
 
-  // Block ids come from a 64-entry window of the row's table held one per lane, so
-  // the K/V loads of the next block are addressed without a memory round trip
-  // (which, younger than the loads in flight, would make the wave wait for all of
-  // them); the window is reloaded when the cursor leaves it.
-  int tw = -1, tw_b = -1, tw_0 = 0;
-  // FUSED: the window's row's copy-on-write source and whether its new token lies in
-  // the attended range (its length not clamped), loaded with the window
-  int tw_cow = -1;
-  bool tw_app = false;
-  auto block_id = [&](const Cursor& p) -> int {
-    if (p.b != tw_b || p.j < tw_0 || p.j >= tw_0 + 64) {  // uniform
-      tw_b = p.b;
-      tw_0 = p.j & ~63;
-      const int jj = tw_0 + lane;
-      tw = jj < p.nb ? a.block_tables[static_cast<int64_t>(p.b) * a.max_blocks + p.blk0 + jj] : -1;
-      if constexpr (FUSED) {
-        tw_cow = a.cow_src[p.b];
-        const int raw_len = a.seq_lens[p.b];
-        tw_app = raw_len > 0 && raw_len == p.len;
-      }
-      // consume the window inside the reload branch: the wait for it stays on this
-      // (rare) path instead of being merged into every step
-      asm volatile("" ::"v"(tw), "s"(tw_cow), "s"(static_cast<int>(tw_app)));
-    }
-    return __builtin_amdgcn_readlane(tw, p.j - tw_0);
+  // Block ids are scalar loads issued one pipeline step before the block's K/V loads
+  // need them: they wait on the scalar counter, never behind the K/V loads in flight.
+  // (The tables are read-only during the call; reading them through the constant
+  // address space is what lets the compiler use scalar loads beside this kernel's
+  // stores.)
+  typedef const int32_t __attribute__((address_space(4))) const_i32;
+  auto fetch_id = [&](const Cursor& p) -> int {
+    const int row = __builtin_amdgcn_readfirstlane(p.b);
+    const int col = __builtin_amdgcn_readfirstlane(p.blk0 + p.j);
+    const_i32* t = (const_i32*)(a.block_tables);  // address-space cast
+    return t[static_cast<int64_t>(row) * a.max_blocks + col];
   };
   auto load_q = [&](const Cursor& p, u32x4(&qq)[G][VPL]) {
 #pragma unroll
@@ -331,21 +368,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     int dst, row;
     bool cow;
   };
-  auto load_block = [&](const Cursor& p, KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL], float(&ks)[NS],
+  auto load_block = [&](const Cursor& p, int id_in, KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL], float(&ks)[NS],
                         float(&vs)[NS], NewTok& nt) -> bool {
     // the id and head are the same in every lane; readfirstlane makes that explicit so the
     // loads use a scalar base with the per-lane 32-bit offsets
-    const int id = __builtin_amdgcn_readfirstlane(block_id(p));
+    const int id = __builtin_amdgcn_readfirstlane(id_in);
     const int h = __builtin_amdgcn_readfirstlane(p.h);
     const bool ok = id >= 0 && static_cast<int64_t>(id) < a.num_blocks;
+    if (!ok && a.status && lane == 0) __hip_atomic_fetch_or(a.status, PKV_STATUS_BAD_BLOCK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int rid = ok ? id : 0;  // the block read
     if constexpr (FUSED) {
       nt.dst = -1;
-      if (ok && tw_app && p.j == p.nb - 1) {  // uniform: the row's last block
+      if (ok && p.app && p.j == p.nb - 1) {  // uniform: the row's last block
         nt.dst = id;
         nt.row = p.len - 1 - (p.blk0 + p.j) * 16;
-        nt.cow = nt.row > 0 && tw_cow >= 0 && static_cast<int64_t>(tw_cow) < a.num_blocks;
-        rid = nt.cow ? tw_cow : id;
+        nt.cow = nt.row > 0 && p.cow >= 0 && static_cast<int64_t>(p.cow) < a.num_blocks;
+        rid = nt.cow ? p.cow : id;
         const int64_t nb0 = (static_cast<int64_t>(p.b) * Hkv + h) * D + c * 8;
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
@@ -627,6 +665,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
   };
 
+  // Partial results of finished segment pieces wait in LDS until the wave's last block
+  // is consumed (a store issued while K/V loads are in flight joins their wait
+  // counter and holds up the next block's wait); pieces beyond kStage are stored
+  // directly.
+  constexpr bool STAGE = PKV_SPLIT_STAGE != 0;
+  constexpr int kStage = G >= 8 ? 3 : G == 4 ? 6 : G == 2 ? 10 : 16;
+  __shared__ __attribute__((aligned(16))) float stg_acc[STAGE ? kStage : 1][G][D];
+  __shared__ float2 stg_ml[STAGE ? kStage : 1][G];
+  __shared__ int4 stg_meta[STAGE ? kStage : 1];
+  int nst = 0;
+
   // merge the token rows and store this segment piece's partial.  Rows are merged
   // pairwise (distance 8 by DPP, 16 and 32 by the permlane swaps, all on the VALU);
   // both rows of a pair compute the same combination of (lower, upper), so every
@@ -691,24 +740,64 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
     }
     const int64_t first_wave = cur.seg / chunk;
     const int k = static_cast<int>(w - first_wave);
+    const int64_t rec0 = (static_cast<int64_t>(cur.b) * a.slots + cur.depth + k) * a.num_q_heads + cur.h * G;
+    const int cnt = k == 0 ? static_cast<int>((cur.seg + cur.nb - 1) / chunk - first_wave + 1) : 0;
+    const int cidx = cur.b * Hkv + cur.h;
+    if (STAGE && nst < kStage) {  // uniform: park the piece in LDS, stored after the wave's last block
+      if (r == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) {
+            f32x4* d4 = reinterpret_cast<f32x4*>(&stg_acc[nst][g][(v * LPT + c) * 8]);
+            d4[0] = f32x4{acc[g][v * 8 + 0], acc[g][v * 8 + 1], acc[g][v * 8 + 2], acc[g][v * 8 + 3]};
+            d4[1] = f32x4{acc[g][v * 8 + 4], acc[g][v * 8 + 5], acc[g][v * 8 + 6], acc[g][v * 8 + 7]};
+          }
+          if (c == 0) stg_ml[nst][g] = make_float2(m[g], l[g]);
+        }
+      }
+      if (lane == 0) stg_meta[nst] = make_int4(static_cast<int>(rec0), static_cast<int>(rec0 >> 32), cnt, cidx);
+      ++nst;
+      return;
+    }
     if (r == 0) {
-      const int slot = cur.depth + k;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const int64_t rec = (static_cast<int64_t>(cur.b) * a.slots + slot) * a.num_q_heads + cur.h * G + g;
-        float* dst = a.acc + rec * D;
+        float* dst = a.acc + (rec0 + g) * D;
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
           float4* d4 = reinterpret_cast<float4*>(dst + (v * LPT + c) * 8);
           d4[0] = make_float4(acc[g][v * 8 + 0], acc[g][v * 8 + 1], acc[g][v * 8 + 2], acc[g][v * 8 + 3]);
           d4[1] = make_float4(acc[g][v * 8 + 4], acc[g][v * 8 + 5], acc[g][v * 8 + 6], acc[g][v * 8 + 7]);
         }
-        if (c == 0) a.ml[rec] = make_float2(m[g], l[g]);
+        if (c == 0) a.ml[rec0 + g] = make_float2(m[g], l[g]);
       }
     }
-    if (k == 0 && lane == 0) {
-      const int64_t last_wave = (cur.seg + cur.nb - 1) / chunk;
-      a.counts[static_cast<int64_t>(cur.b) * Hkv + cur.h] = static_cast<int>(last_wave - first_wave + 1);
+    if (cnt > 0 && lane == 0) a.counts[cidx] = cnt;
+  };
+
+  // The staged pieces, stored once the wave has consumed its last block (nothing is
+  // in flight then, so no wait for a store holds up a load).
+  auto flush_staged = [&]() {
+    for (int p = 0; p < nst; ++p) {  // uniform
+      const int4 meta = stg_meta[p];
+      const int64_t rec0 = static_cast<int64_t>(static_cast<uint32_t>(meta.x)) |
+                           (static_cast<int64_t>(meta.y) << 32);
+      if (r == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float* dst = a.acc + (rec0 + g) * D;
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) {
+            const f32x4* s4 = reinterpret_cast<const f32x4*>(&stg_acc[p][g][(v * LPT + c) * 8]);
+            f32x4* d4 = reinterpret_cast<f32x4*>(dst + (v * LPT + c) * 8);
+            d4[0] = s4[0];
+            d4[1] = s4[1];
+          }
+          if (c == 0) a.ml[rec0 + g] = stg_ml[p][g];
+        }
+      }
+      if (meta.z > 0 && lane == 0) a.counts[meta.w] = meta.z;
     }
   };
 
@@ -727,47 +816,56 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WA
   bool ok_a, ok_b, ok_x = false;
   NewTok nta, ntb, ntx;
   nta.dst = ntb.dst = ntx.dst = -1;
-  load_q(pre, qa);
-  ok_a = load_block(pre, ka, va, ksa, vsa, nta);
-  if constexpr (NBUF == 3) {
-    if (1 < count) advance(pre, a);
-    load_q(pre, qb);
-    ok_b = load_block(pre, kb, vb, ksb, vsb, ntb);
-  }
+  Cursor ca = cur, cb = cur, cx = cur;  // the position of the block each buffer holds
+
+  // The producer: nxt is the next block to issue and id_nxt its table entry, already
+  // requested.  Issuing a block records its position with the buffer, moves nxt on
+  // and requests the following entry; once every block of the range is issued, the
+  // last one is issued again (an L2 hit) so every step has the same loads.
+  Cursor nxt = cur;
+  int id_nxt = fetch_id(nxt);
+  int issued = 0;
+  auto issue = [&](u32x4(&qq)[G][VPL], KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL], float(&ks)[NS], float(&vs)[NS],
+                   NewTok& nt, Cursor& pos, bool& ok) {
+    pos = nxt;
+    load_q(nxt, qq);
+    ok = load_block(nxt, id_nxt, kk, vv, ks, vs, nt);
+    if (++issued < count) {  // uniform
+      advance<FUSED>(nxt, a, win);
+      id_nxt = fetch_id(nxt);
+    }
+  };
+  issue(qa, ka, va, ksa, vsa, nta, ca, ok_a);
+  if constexpr (NBUF == 3) issue(qb, kb, vb, ksb, vsb, ntb, cb, ok_b);
   auto step = [&](int i, bool ok_cur, const u32x4(&q_cur)[G][VPL], KV(&k_cur)[TPB][VPL], KV(&v_cur)[TPB][VPL],
-                  const float(&ks_cur)[NS], const float(&vs_cur)[NS], const NewTok& nt_cur, u32x4(&q_nxt)[G][VPL],
-                  KV(&k_nxt)[TPB][VPL], KV(&v_nxt)[TPB][VPL], float(&ks_nxt)[NS], float(&vs_nxt)[NS], bool& ok_nxt,
-                  NewTok& nt_nxt) {
-    if (i + NBUF - 1 < count) advance(pre, a);
-    load_q(pre, q_nxt);
-    ok_nxt = load_block(pre, k_nxt, v_nxt, ks_nxt, vs_nxt, nt_nxt);
+                  const float(&ks_cur)[NS], const float(&vs_cur)[NS], const NewTok& nt_cur, const Cursor& c_cur,
+                  u32x4(&q_nxt)[G][VPL], KV(&k_nxt)[TPB][VPL], KV(&v_nxt)[TPB][VPL], float(&ks_nxt)[NS],
+                  float(&vs_nxt)[NS], bool& ok_nxt, NewTok& nt_nxt, Cursor& c_nxt) {
+    issue(q_nxt, k_nxt, v_nxt, ks_nxt, vs_nxt, nt_nxt, c_nxt, ok_nxt);
+    cur = c_cur;
     consume_block(ok_cur, q_cur, k_cur, v_cur, ks_cur, vs_cur, nt_cur);
-    if (i + 1 == count || cur.j + 1 == cur.nb) {
+    if (i + 1 == count || cur.j + 1 == cur.nb) {  // the end of a segment piece
       finish_segment();
-      if (i + 1 < count) {
-        advance(cur, a);
-        reset_state();
-      }
-    } else {
-      ++cur.j;
+      reset_state();
     }
   };
   int i = 0;
   if constexpr (NBUF == 2) {
     for (; i + 1 < count; i += 2) {
-      step(i, ok_a, qa, ka, va, ksa, vsa, nta, qb, kb, vb, ksb, vsb, ok_b, ntb);
-      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, ntb, qa, ka, va, ksa, vsa, ok_a, nta);
+      step(i, ok_a, qa, ka, va, ksa, vsa, nta, ca, qb, kb, vb, ksb, vsb, ok_b, ntb, cb);
+      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, ntb, cb, qa, ka, va, ksa, vsa, ok_a, nta, ca);
     }
-    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, nta, qb, kb, vb, ksb, vsb, ok_b, ntb);
+    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, nta, ca, qb, kb, vb, ksb, vsb, ok_b, ntb, cb);
   } else {
     for (; i + 2 < count; i += 3) {
-      step(i, ok_a, qa, ka, va, ksa, vsa, nta, qx, kx, vx, ksx, vsx, ok_x, ntx);
-      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, ntb, qa, ka, va, ksa, vsa, ok_a, nta);
-      step(i + 2, ok_x, qx, kx, vx, ksx, vsx, ntx, qb, kb, vb, ksb, vsb, ok_b, ntb);
+      step(i, ok_a, qa, ka, va, ksa, vsa, nta, ca, qx, kx, vx, ksx, vsx, ok_x, ntx, cx);
+      step(i + 1, ok_b, qb, kb, vb, ksb, vsb, ntb, cb, qa, ka, va, ksa, vsa, ok_a, nta, ca);
+      step(i + 2, ok_x, qx, kx, vx, ksx, vsx, ntx, cx, qb, kb, vb, ksb, vsb, ok_b, ntb, cb);
     }
-    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, nta, qx, kx, vx, ksx, vsx, ok_x, ntx);
-    if (i + 1 < count) step(i + 1, ok_b, qb, kb, vb, ksb, vsb, ntb, qa, ka, va, ksa, vsa, ok_a, nta);
+    if (i < count) step(i, ok_a, qa, ka, va, ksa, vsa, nta, ca, qx, kx, vx, ksx, vsx, ok_x, ntx, cx);
+    if (i + 1 < count) step(i + 1, ok_b, qb, kb, vb, ksb, vsb, ntb, cb, qa, ka, va, ksa, vsa, ok_a, nta, ca);
   }
+  if constexpr (STAGE) flush_staged();
 }
 
 // ---------------------------------------------------------------------------
@@ -796,12 +894,13 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   }
   int nsplit = 0;  // no split pieces without lengths (the extend pass)
   if (a.seq_lens) {
-    int len = a.seq_lens[b];
+    const int raw = a.seq_lens[b];
     const int hkv = h / (a.num_q_heads / a.num_kv_heads);
     const int counted = a.counts[static_cast<int64_t>(b) * a.num_kv_heads + hkv];  // valid when the row has own tokens
-    len = min(len, a.max_seq_len);
-    len = min(len, a.max_blocks * 16);
+    const int len = max(0, min(min(raw, a.max_seq_len), a.max_blocks * 16));
     nsplit = len > begin ? counted : 0;
+    if (len != raw && a.status && blockIdx.x % groups == 0 && lane == 0)
+      __hip_atomic_fetch_or(a.status, PKV_STATUS_LEN_CLAMPED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int np = min(depth + nsplit, a.slots);
   const int64_t rec0 = static_cast<int64_t>(b) * a.slots * a.num_q_heads + h;
@@ -1041,6 +1140,14 @@ constexpr auto split_kernel_ptr() {
   return &decode_split_kernel<DT, D, G, D == 128 ? PKV_LPT_D128 : 8, FUSED && can_fuse<DT>()>;
 }
 
+// Waves per SIMD the split kernel is launched with at most: more resident waves than
+// this add contention without adding bandwidth (measured on the 70B-MHA layer: 3 waves
+// per SIMD 653 us, 4 waves 670 us).
+#ifndef PKV_SPLIT_MAX_WAVES_PER_SIMD
+#define PKV_SPLIT_MAX_WAVES_PER_SIMD 3
+#endif
+constexpr int split_max_waves_per_simd(int /*group*/) { return PKV_SPLIT_MAX_WAVES_PER_SIMD; }
+
 template <class DT, int D, int G, bool FUSED>
 int split_waves_t() {
   // resident waves of this instance on the current device, cached per device
@@ -1053,6 +1160,7 @@ int split_waves_t() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_ptr<DT, D, G, FUSED>(), 64, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 8;
+  per_cu = std::min(per_cu, 4 * split_max_waves_per_simd(G));
   cache[dev] = cus * per_cu;
   return cache[dev];
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pkv.h"
+
 namespace pkv {
 
 // Block copies: for i < n and array k < num_arrays, block dst_ids[i] of dst[k]
@@ -82,6 +84,7 @@ struct SplitArgs {
   int32_t min_chunk;  // c >= min_chunk bounds the partials per segment
   int32_t num_waves;  // W
   float scale_log2;
+  int32_t* status;    // optional device word: PKV_STATUS_BAD_BLOCK is or-ed in for block ids out of range
 };
 
 // Merge of all partials of a query row into the normalised output.  Decode:
@@ -100,6 +103,7 @@ struct MergeArgs {
   int32_t max_blocks;
   int32_t max_seq_len;
   int32_t slots;
+  int32_t* status;  // optional device word: PKV_STATUS_LEN_CLAMPED is or-ed in for lengths outside [0, limit]
 };
 
 // Shared-prefix (cascade) pass over the plan's work items.
@@ -125,6 +129,7 @@ struct CascadeArgs {
   int32_t rows_per_item;     // query rows per work item: kCascadeRowsPerItem or kExtendRowsPerItem
   const float* k_scales;     // FP8 pages: [num_blocks][num_kv_heads][16] per-row scales (else null)
   const float* v_scales;
+  int32_t* status;           // optional device word: PKV_STATUS_BAD_BLOCK for node block ids out of range
 };
 
 constexpr int kCascadeRowsPerItem = 64;     // decode plans: 4 waves x 16 rows

@@ -53,25 +53,25 @@ def test_host_side_argument_errors_need_no_gpu():
     # validation happens before any HIP call
     lib = pkv.lib()
     st = lib.pkv_paged_decode_attn(None, 1, 32, 8, 96, 1, None, None, 1, 16, None, 1, None, 16, 0.1, None, None, 0,
-                                   None, None)
+                                   None, None, None)
     assert st == pkv.PKV_ERR_UNSUPPORTED and b"head_dim" in lib.pkv_last_error()
     st = lib.pkv_paged_decode_attn(None, 1, 30, 8, 128, 1, None, None, 1, 16, None, 1, None, 16, 0.1, None, None, 0,
-                                   None, None)
+                                   None, None, None)
     assert st == pkv.PKV_ERR_INVALID
     st = lib.pkv_paged_decode_attn(None, 1, 32, 8, 128, 7, None, None, 1, 16, None, 1, None, 16, 0.1, None, None, 0,
-                                   None, None)
+                                   None, None, None)
     assert st == pkv.PKV_ERR_UNSUPPORTED
     st = lib.pkv_paged_decode_attn(None, 1, 32, 8, 128, 1, None, None, 1, 32, None, 1, None, 16, 0.1, None, None, 0,
-                                   None, None)
+                                   None, None, None)
     assert st == pkv.PKV_ERR_UNSUPPORTED and b"block_size" in lib.pkv_last_error()
     st = lib.pkv_paged_decode_attn(None, 1, 48, 8, 128, 1, None, None, 1, 16, None, 1, None, 16, 0.1, None, None, 0,
-                                   None, None)
+                                   None, None, None)
     assert st == pkv.PKV_ERR_UNSUPPORTED and b"group" in lib.pkv_last_error()
     st = lib.pkv_paged_decode_attn(None, 1, 32, 8, 128, 1, None, None, 1, 16, None, 1, None, 16, 0.1, None, None, 0,
-                                   None, None)
+                                   None, None, None)
     assert st == pkv.PKV_ERR_INVALID and b"null" in lib.pkv_last_error()
     # workspace too small is reported before any launch
-    st = lib.pkv_paged_decode_attn(16, 1, 32, 8, 128, 1, 16, 16, 1, 16, 16, 1, 16, 16, 0.1, None, 16, 8, 16, None)
+    st = lib.pkv_paged_decode_attn(16, 1, 32, 8, 128, 1, 16, 16, 1, 16, 16, 1, 16, 16, 0.1, None, 16, 8, 16, None, None)
     assert st == pkv.PKV_ERR_WORKSPACE
     st = lib.pkv_kv_append(None, None, 4, 16, 1, 3, 1, None, None, 1, None, None, None, None, 0, None)
     assert st == pkv.PKV_ERR_UNSUPPORTED
@@ -109,11 +109,11 @@ def test_fused_append_refuses_a_plan_with_a_shared_last_token():
     lib = pkv.lib()
     fake = 4096  # 16-byte aligned; refused before any pointer is used
     st = lib.pkv_paged_decode_attn_append(fake, 2, 2, 2, 64, 1, fake, fake, 4, 16, fake, 2, fake, 32, fake, fake,
-                                          fake, 1.0, plan._handle, fake, 1 << 20, fake, None)
+                                          fake, 1.0, plan._handle, fake, 1 << 20, fake, None, None)
     assert st == -1 and b"shared node" in lib.pkv_last_error()
     st = lib.pkv_paged_decode_attn_append(None, 2, 2, 2, 64, 1, None, None, 4, 16, None, 2, None, 32, None, None,
-                                          None, 1.0, None, None, 0, None, None)
+                                          None, 1.0, None, None, 0, None, None, None)
     assert st == -1 and b"null new-token" in lib.pkv_last_error()
     st = lib.pkv_paged_decode_attn_append(None, 2, 2, 2, 64, 5, None, None, 4, 16, None, 2, None, 32, None, None,
-                                          None, 1.0, None, None, 0, None, None)
+                                          None, 1.0, None, None, 0, None, None, None)
     assert st == -4

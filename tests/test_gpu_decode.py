@@ -316,3 +316,58 @@ def test_all_empty_batch(pkv):
     zeros = np.zeros_like(lens)
     got, _ = run_decode(pkv, w, q, k_pages, v_pages, bt, zeros, False, max_seq_len=0)
     assert np.all(got == 0)
+
+
+def test_status_word_reports_clamped_lengths_and_bad_ids(pkv):
+    """The optional status word: zero for in-domain inputs (with and without a plan);
+    STATUS_LEN_CLAMPED when a length exceeds max_seq_len (the row then attends to its
+    first max_seq_len tokens, as the oracle computes for the cut row); STATUS_BAD_BLOCK
+    for a table entry outside the pool, through the split pass and through the shared-
+    prefix pass; a plan covering more than max_seq_len is refused on the host."""
+    torch = __import__("torch")
+    w = workloads.get(1)  # 4 rows: 256 shared + 32 own tokens each
+    pool, k_pages, v_pages, bt, lens, q = setup_workload(w)
+    k_host, v_host, q_host = bits_np(k_pages), bits_np(v_pages), bits_np(q)
+    bt_d, lens_d = tables_to_device(bt, lens)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan = pkv.CascadePlan(bt, lens, w.num_q_heads, w.num_kv_heads).upload()
+    ref = oracle.ref_decode(q_host, k_host, v_host, bt, lens, w.scale, w.dtype)
+    for p in (None, plan):
+        status.zero_()
+        out = pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, int(lens.max()), scale=w.scale, plan=p,
+                                    dtype=w.dtype, status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert max_err(out.cpu().numpy(), ref) <= ATOL
+    # lengths above max_seq_len: clamped and reported
+    cut = 270
+    ref_cut = oracle.ref_decode(q_host, k_host, v_host, bt, np.minimum(lens, cut), w.scale, w.dtype)
+    for p in (None, plan):
+        status.zero_()
+        out = pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, cut, scale=w.scale, plan=p, dtype=w.dtype,
+                                    status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == pkv.STATUS_LEN_CLAMPED
+        assert max_err(out.cpu().numpy(), ref_cut) <= ATOL
+    with pytest.raises(pkv.PkvInvalid):
+        pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, 200, scale=w.scale, plan=plan, dtype=w.dtype)
+    # an own block out of range (split pass): flagged, the other rows unaffected
+    bad = bt.copy()
+    bad[2, 17] = w.num_blocks + 5
+    status.zero_()
+    out = pkv.paged_decode_attn(q, k_pages, v_pages, *tables_to_device(bad, lens), int(lens.max()), scale=w.scale,
+                                dtype=w.dtype, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == pkv.STATUS_BAD_BLOCK
+    keep = [0, 1, 3]
+    assert max_err(out.cpu().numpy()[keep], ref[keep]) <= ATOL
+    # a shared block out of range (the shared-prefix pass reads it)
+    bad = bt.copy()
+    bad[:, 3] = w.num_blocks + 7
+    bad_plan = pkv.CascadePlan(bad, lens, w.num_q_heads, w.num_kv_heads).upload()
+    assert bad_plan.num_nodes >= 1
+    status.zero_()
+    pkv.paged_decode_attn(q, k_pages, v_pages, *tables_to_device(bad, lens), int(lens.max()), scale=w.scale,
+                          plan=bad_plan, dtype=w.dtype, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == pkv.STATUS_BAD_BLOCK

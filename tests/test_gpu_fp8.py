@@ -221,7 +221,7 @@ def test_errors(pkv):
         pkv.paged_decode_attn_fp8(q.float(), k, k, s, s, bt, ln, 1)  # fp32 q
     lib = pkv.lib()
     assert lib.pkv_paged_decode_attn_fp8(q.data_ptr(), 1, 2, 2, 64, 1, k.data_ptr(), k.data_ptr(), None, None, 4, 16,
-                                         bt.data_ptr(), 1, ln.data_ptr(), 1, 0.1, None, None, 0, None, None) == -1
+                                         bt.data_ptr(), 1, ln.data_ptr(), 1, 0.1, None, None, 0, None, None, None) == -1
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}-hq{s[1]}-hkv{s[2]}-d{s[3]}" for s in SHAPES])
