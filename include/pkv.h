@@ -207,6 +207,27 @@ pkv_status pkv_paged_decode_attn_append(const void* q, int32_t batch, int32_t nu
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_seq_len, const pkv_plan* plan);
 
+/* pkv_paged_decode_attn for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation and kernels, with the partial results in a fixed scratch array of
+ * PKV_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on (from
+ * its first use on that device until the process ends) instead of a caller workspace.
+ * The caller still passes q, pages, tables, lengths, out (and the optional status
+ * word); the call allocates nothing and calls no allocating routine.
+ *   Limit: sizes whose pkv_decode_workspace_bytes(...) exceeds the scratch are refused
+ *   with PKV_ERR_WORKSPACE before anything is enqueued.
+ *   Sharing: every call on one device uses that device's one scratch array; calls whose
+ *   execution overlaps on one device (other streams, other threads) race and must be
+ *   ordered by the caller.  Nothing in the scratch needs clearing between calls.
+ * Errors: as pkv_paged_decode_attn (PKV_ERR_HIP also when the scratch address cannot be
+ * resolved). */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pkv_status pkv_paged_decode_attn_noalloc(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
+                                         int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                         float scale, const pkv_plan* plan, float* out, int32_t* status,
+                                         void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * Host block pool ("The Reasoning Engine Meltdown", §5 and §6).

@@ -26,7 +26,7 @@ __all__ = [
     "ExtendPlan", "paged_extend_attn", "extend_workspace_bytes", "kv_append_fp8", "paged_decode_attn_fp8",
     "paged_decode_attn_append",
     "timing_enable", "timing_reset", "timing_read", "stream_read", "KERNELS", "lib", "LIB_PATH", "version",
-    "STATUS_LEN_CLAMPED", "STATUS_BAD_BLOCK",
+    "STATUS_LEN_CLAMPED", "STATUS_BAD_BLOCK", "paged_decode_attn_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 # The library built in-tree next to this file (paged_kv_cache_21_amd/build.py); nothing else is loaded.
@@ -36,6 +36,7 @@ PKV_OK, PKV_ERR_INVALID, PKV_ERR_OOM, PKV_ERR_NOT_FOUND, PKV_ERR_UNSUPPORTED, PK
     0, -1, -2, -3, -4, -5, -6)
 PKV_F16, PKV_BF16 = 0, 1
 STATUS_LEN_CLAMPED, STATUS_BAD_BLOCK = 1, 2  # flags of the decode calls' optional status word
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PKV_NOALLOC_SCRATCH_BYTES
 PKV_EVICT_LRU, PKV_EVICT_RSBCM = 0, 1
 KERNELS = {"append": 0, "decode_split": 1, "merge": 2, "cascade": 3}
 
@@ -85,6 +86,8 @@ _SIGNATURES = {
     "pkv_paged_decode_attn_append": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp,
                                             _i32, _vp, _vp, _vp, _f32, _vp, _vp, _sz, _vp, _vp, _vp]),
     "pkv_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_paged_decode_attn_noalloc": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _i32, _vp,
+                                             _i32, _f32, _vp, _vp, _vp, _vp]),
     "pkv_pool_create": (_vp, [_i32, _i32, _vp]),
     "pkv_pool_destroy": (None, [_vp]),
     "pkv_seq_alloc": (_i32, [_vp, _i64, _i32]),
@@ -367,6 +370,33 @@ def paged_decode_attn(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len, 
                                       nblk, bs, _ptr(block_tables), max_blocks, _ptr(seq_lens), int(max_seq_len),
                                       float(scale), hplan, _ptr(workspace), ws_bytes, _ptr(out), _status_ptr(status),
                                       _stream(stream, q)))
+    return out
+
+
+def paged_decode_attn_noalloc(q, k_pages, v_pages, block_tables, seq_lens, max_seq_len, out, scale=None, plan=None,
+                              dtype=None, stream=None, status=None):
+    """paged_decode_attn with the partial results in the library's fixed per-device scratch
+    (NOALLOC_SCRATCH_BYTES) instead of a workspace: the call allocates nothing.  ``out``
+    (float32 [B, Hq, d]) must be given.  Calls that overlap on one device race."""
+    import torch
+
+    _require(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape, "bad q / page ranks")
+    _require(q.is_contiguous() and k_pages.is_contiguous() and v_pages.is_contiguous(), "inputs must be contiguous")
+    _require(block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables and lengths must be int32")
+    _require(block_tables.is_contiguous() and seq_lens.is_contiguous(), "tables and lengths must be contiguous")
+    B, hq, d = q.shape
+    nblk, bs, hkv, dk = k_pages.shape
+    _require(dk == d, "head_dim of q and pages differ")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] == B and seq_lens.numel() == B, "bad table shape")
+    _require(out is not None and out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, hq, d),
+             "out: float32 [B, Hq, d] contiguous tensor required")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    _check(_lib.pkv_paged_decode_attn_noalloc(_ptr(q), B, hq, hkv, d, _dtype_code(q, dtype), _ptr(k_pages),
+                                              _ptr(v_pages), nblk, bs, _ptr(block_tables),
+                                              int(block_tables.shape[1]), _ptr(seq_lens), int(max_seq_len),
+                                              float(scale), plan._handle if plan is not None else None, _ptr(out),
+                                              _status_ptr(status), _stream(stream, q)))
     return out
 
 

@@ -421,6 +421,35 @@ pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q
                      workspace, workspace_bytes, out, status, stream);
 }
 
+pkv_status pkv_paged_decode_attn_noalloc(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t dtype, const void* k_pages, const void* v_pages,
+                                         int64_t num_blocks, int32_t block_size, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                         float scale, const pkv_plan* plan, float* out, int32_t* status,
+                                         void* stream) {
+  pkv::clear_error();
+  if (dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn_noalloc: dtype %d", dtype);
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_noalloc: invalid sizes");
+  if (plan && (plan->kind != pkv_plan::kDecode || plan->batch != batch))
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_noalloc: plan not a decode plan for batch %d", batch);
+  const size_t need = pkv::decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, plan).bytes;
+  if (need > pkv::kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE,
+                "pkv_paged_decode_attn_noalloc: these sizes need %zu bytes of scratch; the fixed scratch holds %zu "
+                "(use pkv_paged_decode_attn with a workspace)",
+                need, pkv::kScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = pkv::scratch_address(&scratch);
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "pkv_paged_decode_attn_noalloc: scratch address: %s", hipGetErrorString(e));
+  return decode_impl(dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, nullptr, nullptr,
+                     num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
+                     scratch, pkv::kScratchBytes, out, status, stream);
+}
+
 size_t pkv_extend_workspace_bytes(const pkv_plan* plan, int32_t head_dim) {
   pkv::clear_error();
   if (!plan || plan->kind != pkv_plan::kExtend || head_dim <= 0) {

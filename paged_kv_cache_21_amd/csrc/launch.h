@@ -150,4 +150,10 @@ hipError_t launch_merge(int head_dim, const MergeArgs& a, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int grid, hipStream_t stream);
 hipError_t launch_cascade(int dtype, int head_dim, int group, const CascadeArgs& a, hipStream_t stream);
 
+// Size of the fixed per-device scratch the no-allocation decode uses in place of a
+// caller workspace, and its device address on the current device (taken once per
+// device; an error if the runtime cannot resolve it).
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+hipError_t scratch_address(void** out);
+
 }  // namespace pkv
