@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5, 6],
+                    help="time this workload alone (default: the 8B-shaped layer as the headline, then a line "
+                         "per other workload)")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 (E4M3) pages with per-row scales: quantizing append + FP8 decode (configs 2 and 4)")
     ap.add_argument("--protocol", action="store_true",
@@ -58,8 +60,8 @@ def parse():
     ap.add_argument("--no-cascade", action="store_true", help="decode every row on its own (no shared-prefix pass)")
     ap.add_argument("--fused", action="store_true",
                     help="step = the one-launch paged_decode_attn_append (default: kv_append then paged_decode_attn)")
-    ap.add_argument("--cold-iters", type=int, default=10,
-                    help="extra steps each preceded by a 1 GiB write that evicts L2 and MALL (0 = skip)")
+    ap.add_argument("--cold-iters", type=int, default=50,
+                    help="decode calls (and steps) each preceded by a 1 GiB write that evicts L2 and MALL (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget for the oracle baseline (0 = skip)")
     ap.add_argument("--read-ceiling-gib", type=int, default=4,
                     help="also time a plain streaming read of this many GiB (the read-bandwidth yardstick; 0 = skip)")
@@ -708,6 +710,194 @@ def run_swap(args, dev):
     print(json.dumps(line))
 
 
+# The decode step timed for each workload: the first step, except for the radix tree,
+# where it is the first step after a backtrack (its append copies 64 shared tails on write).
+TIMED_STEP = {1: 0, 2: 0, 3: 0, 4: 0, 5: 3}
+HEADLINE_CONFIG = 2
+EXTRA_CONFIGS = (1, 3, 4, 5)
+
+
+def setup_step(w, dev, step_index, cascade):
+    """Pages, the library pool replayed to the timed step, that step's append plan and
+    tables, and the cascade plan (None when off or when nothing is shared)."""
+    import types
+
+    import torch
+
+    import paged_kv_cache_21_amd as pkv
+    import workloads
+
+    r = types.SimpleNamespace()
+    r.k_pages, r.v_pages = workloads.make_pages(w, device=dev)
+    pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(pool, w.build_ops)
+    for s_ in range(step_index):  # earlier steps on the host pool only (values do not matter for timing)
+        pool.plan_append(w.steps[s_].append_rows)
+        if w.steps[s_].after_ops:
+            workloads.replay(pool, w.steps[s_].after_ops)
+    step = w.steps[step_index]
+    t0 = time.perf_counter()
+    r.slots, r.cows, r.row_src = pool.plan_append(step.append_rows, row_sources=True)
+    r.plan_append_us = (time.perf_counter() - t0) * 1e6
+    r.fused_ok = list(step.append_rows) == list(step.decode_rows)
+    r.bt, r.lens = pool.export_tables(step.decode_rows, w.max_blocks)
+    t0 = time.perf_counter()
+    plan = pkv.CascadePlan(r.bt, r.lens, w.num_q_heads, w.num_kv_heads) if cascade else None
+    r.plan_build_us = (time.perf_counter() - t0) * 1e6
+    if plan is not None and plan.num_nodes == 0:
+        plan = None
+    if plan is not None:
+        plan.upload(device=dev)
+    r.plan = plan
+    r.q = workloads.make_q(w, step_index, device=dev)
+    r.k_new, r.v_new = workloads.make_new_tokens(w, step_index, device=dev)
+    r.slot_d = torch.from_numpy(r.slots).to(dev)
+    cow = np.asarray(r.cows, dtype=np.int32).reshape(-1, 3)
+    r.cow_d = ([torch.from_numpy(np.ascontiguousarray(cow[:, i])).to(dev) for i in range(3)] if len(cow)
+               else [None] * 3)
+    r.cow_src_d = torch.from_numpy(r.row_src).to(dev)
+    r.bt_d = torch.from_numpy(r.bt).to(dev)
+    r.lens_d = torch.from_numpy(r.lens).to(dev)
+    r.max_len = int(r.lens.max())
+    need = max(pkv.decode_workspace_bytes(len(r.lens), w.num_q_heads, w.num_kv_heads, w.head_dim, r.max_len, plan),
+               pkv.decode_workspace_bytes(len(r.lens), w.num_q_heads, w.num_kv_heads, w.head_dim, r.max_len))
+    r.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    r.out = torch.empty((len(r.lens), w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    r.stream = torch.cuda.current_stream(dev)
+    B = len(r.lens)
+    r.kv_unique = unique_bytes(r.bt, r.lens, w)
+    r.kv_logical = int(r.lens.sum()) * w.bytes_per_token
+    r.q_bytes = B * w.num_q_heads * w.head_dim * 2
+    r.o_bytes = B * w.num_q_heads * w.head_dim * 4
+    r.tbl_bytes = r.bt.nbytes + r.lens.nbytes
+    r.U = r.kv_unique + r.q_bytes + r.o_bytes + r.tbl_bytes
+    return r
+
+
+def step_fns(w, r, fused, use_plan=True):
+    """(one step = append + decode, the decode call alone) for the set-up r."""
+    import paged_kv_cache_21_amd as pkv
+
+    plan = r.plan if use_plan else None
+
+    def attn_call():
+        pkv.paged_decode_attn(r.q, r.k_pages, r.v_pages, r.bt_d, r.lens_d, r.max_len, scale=w.scale, plan=plan,
+                              workspace=r.ws, out=r.out, dtype=w.dtype, stream=r.stream)
+
+    def one_step():
+        if fused:  # append + decode in one launch
+            pkv.paged_decode_attn_append(r.q, r.k_pages, r.v_pages, r.bt_d, r.lens_d, r.max_len, r.k_new, r.v_new,
+                                         r.cow_src_d, scale=w.scale, plan=plan, workspace=r.ws, out=r.out,
+                                         dtype=w.dtype, stream=r.stream)
+            return
+        pkv.kv_append(r.k_pages, r.v_pages, r.k_new, r.v_new, r.slot_d, r.cow_d[0], r.cow_d[1], r.cow_d[2],
+                      dtype=w.dtype, stream=r.stream)
+        attn_call()
+
+    return one_step, attn_call
+
+
+def time_back_to_back(fn, stream, steps, warmup):
+    """ms per call over `steps` back-to-back calls after `warmup` untimed ones (inputs resident)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / max(steps, 1)
+
+
+def time_flushed(fn, stream, iters, dev, flush=None):
+    """Per-call ms, each call preceded by a 1 GiB write that evicts L2 and the 256 MB MALL
+    (the first call untimed): list of `iters` times."""
+    import torch
+
+    own = flush is None
+    if own:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    out = []
+    for it in range(iters + 1):
+        flush.fill_(it & 0xff)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if it:
+            out.append(e0.elapsed_time(e1))
+    if own:
+        del flush
+    return out
+
+
+def pct(xs):
+    """(median, p10, p90) of a list of ms, in us."""
+    a = np.asarray(xs) * 1e3
+    return round(float(np.median(a)), 3), round(float(np.percentile(a, 10)), 3), round(float(np.percentile(a, 90)), 3)
+
+
+def kernel_times(fn, steps):
+    """Per-kernel average us from the library's event timing over `steps` calls."""
+    import torch
+
+    import paged_kv_cache_21_amd as pkv
+
+    pkv.timing_reset()
+    pkv.timing_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    pkv.timing_enable(False)
+    kern = {}
+    for name in ("append", "decode_split", "merge", "cascade"):
+        total, count = pkv.timing_read(name)
+        kern[name] = {"avg_us": round(total / count * 1e3, 3) if count else 0.0, "launches": count}
+    return kern
+
+
+def summarize_config(w, dev, steps, warmup, flush_iters, flush):
+    """One workload's line in the default run: warm step and decode-call times, the flushed
+    decode call (median, p10, p90), per-kernel times, bytes, with and without the cascade
+    pass when the workload shares blocks."""
+    import torch
+
+    r = setup_step(w, dev, TIMED_STEP[w.number], cascade=True)
+    one_step, attn_call = step_fns(w, r, fused=False)
+    step_ms = time_back_to_back(one_step, r.stream, steps, warmup)
+    attn_ms = time_back_to_back(attn_call, r.stream, steps, warmup)
+    fl = pct(time_flushed(attn_call, r.stream, flush_iters, dev, flush))
+    kern = kernel_times(one_step, steps)
+    out = {"workload": f"{w.name}: {w.description}", "timed_step": TIMED_STEP[w.number] + 1, "rows": len(r.lens),
+           "copy_on_write": len(r.cows), "step_us": round(step_ms * 1e3, 3), "decode_call_us": round(attn_ms * 1e3, 3),
+           "decode_call_flushed_us_median_p10_p90": list(fl),
+           "effective_gb_per_s": round(r.U / (attn_ms * 1e-3) / 1e9, 1),
+           "effective_gb_per_s_flushed_median": round(r.U / (fl[0] * 1e-6) / 1e9, 1),
+           "hbm_peak_frac": round(r.U / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "decode_queries_per_s": round(len(r.lens) / (attn_ms * 1e-3), 1),
+           "bytes": {"unique_U": r.U, "kv_unique": r.kv_unique, "kv_logical": r.kv_logical},
+           "kernels_us": {k: v["avg_us"] for k, v in kern.items() if v["launches"]},
+           "cascade": r.plan is not None, "shared_nodes": r.plan.num_nodes if r.plan is not None else 0,
+           "host_us": {"plan_append": round(r.plan_append_us, 1), "plan_build": round(r.plan_build_us, 1)}}
+    if r.plan is not None:  # the same call with every row decoded on its own
+        _, attn_off = step_fns(w, r, fused=False, use_plan=False)
+        off_ms = time_back_to_back(attn_off, r.stream, steps, warmup)
+        off_fl = pct(time_flushed(attn_off, r.stream, flush_iters, dev, flush))
+        kern_off = kernel_times(attn_off, steps)
+        out["cascade_off"] = {"decode_call_us": round(off_ms * 1e3, 3),
+                              "decode_call_flushed_us_median_p10_p90": list(off_fl),
+                              "kernels_us": {k: v["avg_us"] for k, v in kern_off.items() if v["launches"]},
+                              "speedup_of_cascade": round(off_ms / attn_ms, 3)}
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -731,82 +921,37 @@ def main():
     torch.cuda.set_device(dev)
     if args.swap:
         return run_swap(args, dev)
-    w = workloads.get(args.config)
+    default_run = args.config is None
+    w = workloads.get(HEADLINE_CONFIG if default_run else args.config)
     print(f"[bench] workload {w.number} {w.name}: {w.description}", file=sys.stderr, flush=True)
     if args.protocol:
         return run_protocol(args, w, dev)
-    if args.extend or args.config == 6:
+    if args.extend or w.number == 6:
         return run_extend(args, w, dev)
     if args.fp8:
         return run_fp8(args, w, dev)
 
     # ---- set-up (not timed): pages, pool, the step's append plan, tables, cascade plan
-    k_pages, v_pages = workloads.make_pages(w, device=dev)
-    pool = pkv.BlockPool(w.num_blocks, w.block_size, w.free_order)
-    workloads.replay(pool, w.build_ops)
-    step = w.steps[0]
-    t0 = time.perf_counter()
-    slots, cows, row_src = pool.plan_append(step.append_rows, row_sources=True)
-    plan_append_us = (time.perf_counter() - t0) * 1e6
-    bt, lens = pool.export_tables(step.decode_rows, w.max_blocks)
-    t0 = time.perf_counter()
-    plan = None if args.no_cascade else pkv.CascadePlan(bt, lens, w.num_q_heads, w.num_kv_heads)
-    plan_build_us = (time.perf_counter() - t0) * 1e6
-    if plan is not None:
-        plan.upload(device=dev)
-    n_nodes = plan.num_nodes if plan is not None else 0
-
-    q = workloads.make_q(w, 0, device=dev)
-    k_new, v_new = workloads.make_new_tokens(w, 0, device=dev)
-    slot_d = torch.from_numpy(slots).to(dev)
-    cow = np.asarray(cows, dtype=np.int32).reshape(-1, 3)
-    cow_d = [torch.from_numpy(np.ascontiguousarray(cow[:, i])).to(dev) for i in range(3)] if len(cow) else [None] * 3
-    bt_d = torch.from_numpy(bt).to(dev)
-    lens_d = torch.from_numpy(lens).to(dev)
-    max_len = int(lens.max())
-    ws = torch.empty(max(pkv.decode_workspace_bytes(len(lens), w.num_q_heads, w.num_kv_heads, w.head_dim, max_len,
-                                                    plan), 16), dtype=torch.uint8, device=dev)
-    out = torch.empty((len(lens), w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    r = setup_step(w, dev, TIMED_STEP[w.number], cascade=not args.no_cascade)
     fused = args.fused
-    if fused and list(step.append_rows) != list(step.decode_rows):
+    if fused and not r.fused_ok:
         print("--fused needs the step to append one token to every decoded row", file=sys.stderr)
         sys.exit(2)
-    cow_src_d = torch.from_numpy(row_src).to(dev)
-
-    def one_step():
-        if fused:  # append + decode in one launch
-            pkv.paged_decode_attn_append(q, k_pages, v_pages, bt_d, lens_d, max_len, k_new, v_new, cow_src_d,
-                                         scale=w.scale, plan=plan, workspace=ws, out=out, dtype=w.dtype,
-                                         stream=stream)
-            return
-        pkv.kv_append(k_pages, v_pages, k_new, v_new, slot_d, cow_d[0], cow_d[1], cow_d[2], dtype=w.dtype,
-                      stream=stream)
-        pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, max_len, scale=w.scale, plan=plan, workspace=ws,
-                              out=out, dtype=w.dtype, stream=stream)
-
-    for _ in range(args.warmup):
-        one_step()
-    torch.cuda.synchronize()
+    one_step, attn_call = step_fns(w, r, fused)
+    plan, lens, bt, cows = r.plan, r.lens, r.bt, r.cows
 
     # ---- timed region 1: K back-to-back steps (the reported value)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        one_step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / max(args.steps, 1)
+    ms_per_step = time_back_to_back(one_step, r.stream, args.steps, args.warmup)
 
     # ---- timed region 2: the same K steps with per-kernel HIP events (library timing, same stream)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     pkv.timing_reset()
     pkv.timing_enable(True)
     torch.cuda.synchronize()
-    ev0.record(stream)
+    ev0.record(r.stream)
     for _ in range(args.steps):
         one_step()
-    ev1.record(stream)
+    ev1.record(r.stream)
     torch.cuda.synchronize()
     pkv.timing_enable(False)
     ms_per_step_instrumented = ev0.elapsed_time(ev1) / max(args.steps, 1)
@@ -815,19 +960,10 @@ def main():
         total, count = pkv.timing_read(name)
         kern[name] = {"avg_us": round(total / count * 1e3, 3) if count else 0.0, "launches": count}
 
-    # ---- cold steps: evict L2 / MALL with a 1 GiB write before each step
-    cold = []
-    if args.cold_iters > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        for _ in range(args.cold_iters):
-            flush.fill_(1)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            one_step()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1))
-        del flush
+    # ---- flushed: each call after a 1 GiB write that evicts L2 and the 256 MB MALL
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold_iters > 0 else None
+    cold = time_flushed(one_step, r.stream, args.cold_iters, dev, flush) if args.cold_iters > 0 else []
+    attn_cold = time_flushed(attn_call, r.stream, args.cold_iters, dev, flush) if args.cold_iters > 0 else []
 
     if args.copy_calibration_mib > 0:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
@@ -840,12 +976,7 @@ def main():
 
     # ---- bytes
     B = len(lens)
-    kv_unique = unique_bytes(bt, lens, w)
-    kv_logical = int(lens.sum()) * w.bytes_per_token
-    q_bytes = B * w.num_q_heads * w.head_dim * 2
-    o_bytes = B * w.num_q_heads * w.head_dim * 4
-    tbl_bytes = bt.nbytes + lens.nbytes
-    U = kv_unique + q_bytes + o_bytes + tbl_bytes
+    U = r.U
     value = U / (ms_per_step * 1e-3) / 1e9
 
     # roofline of the dominant kernel: split-K decode; algorithmic bytes = the K/V of every row's own
@@ -854,7 +985,7 @@ def main():
         own_tokens = sum(int(lens[b]) - plan.row(b)[0] for b in range(B))
     else:
         own_tokens = int(lens.sum())
-    split_bytes = own_tokens * w.bytes_per_token + q_bytes
+    split_bytes = own_tokens * w.bytes_per_token + r.q_bytes
     if fused:  # the split kernel also reads the new tokens and writes them and the copied-on-write rows
         split_bytes += (2 * B + sum(int(c[2]) for c in cows)) * w.bytes_per_token
     t_split = kern["decode_split"]["avg_us"] * 1e-6
@@ -865,28 +996,22 @@ def main():
                 "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
                 "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": kern["decode_split"]["avg_us"]}
 
-    # the paged_decode_attn call alone (no append): K back-to-back calls on the same
-    # inputs, bracketed by events; the same unique bytes over the time per call
-    def attn_call():
-        pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, max_len, scale=w.scale, plan=plan, workspace=ws,
-                              out=out, dtype=w.dtype, stream=stream)
-
-    for _ in range(args.warmup):
-        attn_call()
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        attn_call()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t_attn = ev0.elapsed_time(ev1) / max(args.steps, 1) * 1e-3
+    # the paged_decode_attn call alone (no append): K back-to-back calls on the same inputs
+    t_attn = time_back_to_back(attn_call, r.stream, args.steps, args.warmup) * 1e-3
     attn_gbs = U / t_attn / 1e9 if t_attn > 0 else 0.0
     attn_only = {"us": round(t_attn * 1e6, 3), "gb_per_s": round(attn_gbs, 1),
                  "hbm_peak_frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
+    flushed = None
+    if attn_cold:
+        med, p10, p90 = pct(attn_cold)
+        flushed = {"decode_call_us_median": med, "decode_call_us_p10": p10, "decode_call_us_p90": p90,
+                   "gb_per_s_median": round(U / (med * 1e-6) / 1e9, 1),
+                   "hbm_peak_frac_median": round(U / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "decode_queries_per_s_median": round(B / (med * 1e-6), 1), "iterations": len(attn_cold)}
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, q, k_pages, v_pages, bt, lens, args.cpu_seconds)
+        cpu = cpu_baseline(w, r.q, r.k_pages, r.v_pages, bt, lens, args.cpu_seconds)
     ceiling = read_ceiling(args.read_ceiling_gib, dev) if args.read_ceiling_gib > 0 else None
     if ceiling:
         roofline["frac_of_measured_read_ceiling"] = round(achieved / ceiling["gbs"], 4)
@@ -906,25 +1031,40 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "batch": B, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-                   "mean_seq_len": round(float(lens.mean()), 1), "max_seq_len": max_len, "accumulate": "f32",
-                   "cascade": plan is not None, "shared_nodes": n_nodes,
+                   "mean_seq_len": round(float(lens.mean()), 1), "max_seq_len": r.max_len, "accumulate": "f32",
+                   "cascade": plan is not None, "shared_nodes": plan.num_nodes if plan is not None else 0,
                    "step": "paged_decode_attn_append (one launch)" if fused else "kv_append + paged_decode_attn",
                    "parallelism": "single GPU"},
+        "headline": "value = unique bytes U / ms_per_step, warm back-to-back steps (kv_append + paged_decode_attn) "
+                    "with inputs resident in HBM; decode_attn_only = the decode call alone, warm; flushed = the "
+                    "decode call after a 1 GiB write each time (median, p10, p90)",
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "decode_queries_per_s": round(B / (ms_per_step * 1e-3), 1),
         "decode_attn_only": attn_only,
-        "bytes": {"kv_unique": kv_unique, "kv_logical": kv_logical, "q": q_bytes, "out": o_bytes,
-                  "tables": tbl_bytes, "step_total_U": U},
+        "flushed": flushed,
+        "bytes": {"kv_unique": r.kv_unique, "kv_logical": r.kv_logical, "q": r.q_bytes, "out": r.o_bytes,
+                  "tables": r.tbl_bytes, "step_total_U": U},
         "kernels": kern,
         "ms_per_step_instrumented": round(ms_per_step_instrumented, 5),
         "cold_ms_per_step_median": round(float(np.median(cold)), 5) if cold else None,
         "cold_ms_per_step_p10_p90": [round(float(np.percentile(cold, 10)), 5),
                                      round(float(np.percentile(cold, 90)), 5)] if cold else None,
-        "host_us": {"plan_append": round(plan_append_us, 1), "plan_build": round(plan_build_us, 1)},
+        "host_us": {"plan_append": round(r.plan_append_us, 1), "plan_build": round(r.plan_build_us, 1)},
         "roofline": roofline,
         "read_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
+    if default_run and not args.no_cascade and not fused:
+        del r
+        torch.cuda.empty_cache()
+        configs = {}
+        for n in EXTRA_CONFIGS:
+            wx = workloads.get(n)
+            print(f"[bench] workload {n} {wx.name}", file=sys.stderr, flush=True)
+            configs[f"config{n}"] = summarize_config(wx, dev, steps=max(args.steps // 2, 10),
+                                                    warmup=max(args.warmup // 2, 3),
+                                                    flush_iters=max(args.cold_iters, 10), flush=flush)
+        res["configs"] = configs
     print(json.dumps(res), flush=True)
 
 

@@ -109,7 +109,8 @@ def test_padding_slots_are_skipped(pkv):
 def test_radix_backtracking_protocol(pkv, fused):
     """Tree of 256 leaves over a 4096-token root; 16 steps of append -> decode with
     pruning / forking after steps 3, 7, 11, 15 (each fork shares a partly filled tail,
-    so the next append copies it).  Pages bit-exact, sampled decode rows within tolerance;
+    so the next append copies it).  Pages bit-exact; every leaf compared at step 4 (the first
+    after a backtrack, 64 copies on write) and step 16, sampled leaves at the other steps;
     either kv_append then paged_decode_attn, or paged_decode_attn_append."""
     torch = __import__("torch")
     w = workloads.get(5)
@@ -148,15 +149,19 @@ def test_radix_backtracking_protocol(pkv, fused):
         else:
             out = pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, int(lens.max()), scale=w.scale,
                                         plan=plan, dtype="bf16")
-        rows = sorted(rng.choice(len(lens), size=6, replace=False).tolist())
-        # make sure a row that just copied a tail is among the checked ones
-        if cows_r:
-            touched = [i for i, sl in enumerate(slots_r) if sl // 16 == cows_r[0][1]]
-            rows = sorted(set(rows + touched[:1]))
+        if s in (3, 15):  # the first step after a backtrack (64 copies on write) and the last: every leaf
+            assert s != 3 or len(cows_r) == 64
+            rows = list(range(len(lens)))
+        else:
+            rows = sorted(rng.choice(len(lens), size=6, replace=False).tolist())
+            # make sure a row that just copied a tail is among the checked ones
+            if cows_r:
+                touched = [i for i, sl in enumerate(slots_r) if sl // 16 == cows_r[0][1]]
+                rows = sorted(set(rows + touched[:1]))
         got = out.cpu().numpy()[rows]
         refo = oracle.ref_decode_rows(bits_np(q), k_host, v_host, bt_r, lens_r, w.scale, "bf16", rows=rows)
         err = max_err(got, refo)
-        say(f"  cows={len(cows_r)} max_err={err:.3e}")
+        say(f"  cows={len(cows_r)} rows={len(rows)} max_err={err:.3e}")
         assert err <= ATOL
         if s in (0, 3, 15):
             torch.cuda.synchronize()
