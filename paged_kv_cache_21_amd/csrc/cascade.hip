@@ -54,6 +54,14 @@ __device__ __forceinline__ f32x4 mfma16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
                                                 0);
 }
 
+// 4 x 16-bit transpose read from LDS (gfx950 ds_read_b64_tr_b16): see the V^T
+// operand reads for the lane mapping
+typedef short s16x4 __attribute__((vector_size(8)));
+__device__ __forceinline__ u32x2 tr_read16(const uint16_t* p) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p)));
+}
+
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
   return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
 }
@@ -79,8 +87,8 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
 // read from LDS then feeds RB products; the registers it costs lower the
 // occupancy (3 waves per SIMD at RB = 1, 2 at RB = 2).
 template <class DT, int D, int G, int NW, int RB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3 : 2))) void cascade_kernel(
-    CascadeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3 : RB == 2 ? 2 : 1))) void
+cascade_kernel(CascadeArgs a) {
   // FP8 pages: E4M3 codes widened to the 16-bit type of q on their way into LDS
   // (exact), the per-token K scale applied to each score and the V scale folded
   // into each weight
@@ -88,8 +96,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
   constexpr bool Q8 = is_fp8<DT>::value;
   constexpr int EB = Q8 ? 1 : 2;  // bytes per page element
   typedef typename std::conditional<Q8, u32x2, u32x4>::type KV;  // 8 page elements
-  constexpr int KPITCH = D + 8;  // K row pitch in LDS (elements); the pad spreads rows over banks
-  constexpr int VPITCH = 18;     // V^T row pitch in LDS (32-bit words = 2 tokens each; 16 used)
+  constexpr int KPITCH = D + 8;   // K row pitch in LDS (elements); the pad spreads rows over banks
+  constexpr int VPITCH = D + 16;  // V row pitch (elements): the transpose reads of a half-wave
+                                  // (8 rows x 32 bytes) then land in distinct banks
   constexpr int NKS = D / 32;    // k-steps of the QK product
   constexpr int NDT = D / 16;    // 16-wide d tiles of the PV product
   constexpr int KVEC = 32 * D / 8;             // 16-byte vectors per K chunk
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
   static_assert(KVEC_PER_THREAD >= 1, "unsupported head_dim");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][32 * KPITCH];
-  __shared__ __attribute__((aligned(16))) uint32_t vt_lds[2][D * VPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][32 * VPITCH];
   // FP8: the chunk's 32 K scales, then its 32 V scales (zero for tokens without data)
   __shared__ __attribute__((aligned(16))) float sc_lds[2][Q8 ? 64 : 1];
 
@@ -178,10 +187,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     for (int dt = 0; dt < NDT; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int vpair = tid & 15;  // tokens 2*vpair, 2*vpair+1
-  const int vcol = tid >> 4;   // 8-element column group
-  const bool vthread = vcol < D / 8;
-
   // the piece's block ids, lane j of register w holding block 64 w + j (a piece has
   // at most 64 NW blocks); read with readlane so the chunk loop issues no scalar
   // memory loads, which would share a wait counter with the LDS reads
@@ -200,9 +205,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     return (id >= 0 && static_cast<int64_t>(id) < a.num_blocks) ? id : -1;
   };
 
+  // K and V take the same thread mapping: vector i of thread tid is token
+  // (tid + 256 i) / (D / 8) of the chunk, 8-element column (tid + 256 i) % (D / 8)
   struct Stage {
     KV k[KVEC_PER_THREAD];
-    KV v0, v1;
+    KV v[KVEC_PER_THREAD];
     f32x4 sc;  // FP8, threads 0..15: four scales of the chunk
   };
   const int nchunks = (nblk + 1) / 2;
@@ -219,8 +226,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     koff[i] = static_cast<int>((tok & 15) * tok_stride + static_cast<int64_t>(hkv) * D + col * 8);
     khi[i] = tok >= 16;
   }
-  const int voff = static_cast<int>(((2 * vpair) & 15) * tok_stride + static_cast<int64_t>(hkv) * D + vcol * 8);
-  const bool vhi = 2 * vpair >= 16;
   // global -> registers (cached loads: the other row tiles of this piece read the
   // same K/V from L2); past the last chunk the last one is read again (an L2 hit)
   auto load_chunk = [&](int ch, Stage& st) {
@@ -231,12 +236,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     const char* kbase = reinterpret_cast<const char*>(a.k_pages);
     const char* vbase = reinterpret_cast<const char*>(a.v_pages);
 #pragma unroll
-    for (int i = 0; i < KVEC_PER_THREAD; ++i)
-      st.k[i] = *reinterpret_cast<const KV*>(kbase + (khi[i] ? b1 : b0) + static_cast<int64_t>(koff[i]) * EB);
-    if (vthread) {
-      const char* vp = vbase + (vhi ? b1 : b0) + static_cast<int64_t>(voff) * EB;
-      st.v0 = *reinterpret_cast<const KV*>(vp);
-      st.v1 = *reinterpret_cast<const KV*>(vp + tok_stride * EB);
+    for (int i = 0; i < KVEC_PER_THREAD; ++i) {
+      const int64_t off = (khi[i] ? b1 : b0) + static_cast<int64_t>(koff[i]) * EB;
+      st.k[i] = *reinterpret_cast<const KV*>(kbase + off);
+      st.v[i] = *reinterpret_cast<const KV*>(vbase + off);
     }
     if constexpr (Q8) {
       if (tid < 16) {  // (K | V) x (block 0 | 1) x rows 4 p .. 4 p + 3
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
       }
     }
   };
-  // registers -> LDS buffer: K as is, V transposed to [d][token] pairs; the values
+  // registers -> LDS buffer, K and V token-major as in the pages; the values
   // of tokens without data (past the node's valid length, or in a block with a bad
   // id) are zeroed, so their zero weights never meet stale Inf / NaN bits
   auto store_chunk = [&](const Stage& st_in, int ch, int buf) {
@@ -258,11 +261,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     if (a.status && tid == 0 &&
         ((!ok0 && 2 * ch < nblk) || (!ok1 && 2 * ch + 1 < nblk)))
       __hip_atomic_fetch_or(a.status, PKV_STATUS_BAD_BLOCK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (vthread && (ch * 32 + 32 > piece_valid || !ok0 || !ok1)) {  // uniform
-      const int t = ch * 32 + 2 * vpair;
-      const bool blk_ok = vhi ? ok1 : ok0;
-      if (!(blk_ok && t < piece_valid)) st.v0 = KV{};
-      if (!(blk_ok && t + 1 < piece_valid)) st.v1 = KV{};
+    if (ch * 32 + 32 > piece_valid || !ok0 || !ok1) {  // uniform
+#pragma unroll
+      for (int i = 0; i < KVEC_PER_THREAD; ++i) {
+        const int tok = (tid + 256 * i) / (D / 8);
+        const bool blk_ok = khi[i] ? ok1 : ok0;
+        if (!(blk_ok && ch * 32 + tok < piece_valid)) st.v[i] = KV{};
+      }
     }
     if constexpr (Q8) {
       if (tid < 16) {
@@ -287,24 +292,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
         kw = st.k[i];
       *reinterpret_cast<u32x4*>(&k_lds[buf][tok * KPITCH + col * 8]) = kw;
     }
-    if (vthread) {
-      u32x4 v0w, v1w;
-      if constexpr (Q8) {
-        v0w = widen8<CT>(st.v0);
-        v1w = widen8<CT>(st.v1);
-      } else {
-        v0w = st.v0;
-        v1w = st.v1;
-      }
-      const uint32_t w0[4] = {v0w.x, v0w.y, v0w.z, v0w.w};
-      const uint32_t w1[4] = {v1w.x, v1w.y, v1w.z, v1w.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // elements 2e and 2e+1 of the column group, for tokens 2*vpair (low half) and
-        // 2*vpair+1 (high half): one byte permute each
-        vt_lds[buf][(vcol * 8 + 2 * e) * VPITCH + vpair] = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-        vt_lds[buf][(vcol * 8 + 2 * e + 1) * VPITCH + vpair] = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
-      }
+    for (int i = 0; i < KVEC_PER_THREAD; ++i) {
+      const int vi = tid + 256 * i;
+      const int tok = vi / (D / 8);
+      const int col = vi % (D / 8);
+      u32x4 vw;
+      if constexpr (Q8)
+        vw = widen8<CT>(st.v[i]);
+      else
+        vw = st.v[i];
+      *reinterpret_cast<u32x4*>(&v_lds[buf][tok * VPITCH + col * 8]) = vw;
     }
   };
   // evaluate chunk ch from LDS buffer buf for this wave's RB x 16 rows
@@ -312,6 +310,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     if (!wave_active) return;
     const bool valid0 = block_id(2 * ch) >= 0;
     const bool valid1 = block_id(2 * ch + 1) >= 0;
+    // Every LDS operand of the chunk is requested up front, K first, then V^T: the
+    // reads' latencies overlap one another, the V^T reads complete under the QK
+    // products and the softmax, and no matrix instruction waits on a read issued just
+    // before it.
+    // (With one row block per wave the registers this takes would cost a resident
+    // wave per SIMD, so that instance reads each operand where it is used.)
+    constexpr bool BATCH = RB >= 2;
+    u32x4 kop[NKS][2], vop[NDT];
+    auto k_operand = [&](int ks, int tt) {
+      return *reinterpret_cast<const u32x4*>(&k_lds[buf][(tt * 16 + lrow) * KPITCH + ks * 32 + lgrp * 8]);
+    };
+    const int trow = lrow >> 2, tcol = 4 * (lrow & 3);
+    auto v_operand = [&](int dt) {
+      const uint16_t* v0p = &v_lds[buf][(4 * lgrp + trow) * VPITCH + dt * 16 + tcol];
+      const u32x2 t0 = tr_read16(v0p);                // tokens 4*lgrp .. +3
+      const u32x2 t1 = tr_read16(v0p + 16 * VPITCH);  // tokens 16 + 4*lgrp .. +3
+      return u32x4{t0.x, t0.y, t1.x, t1.y};
+    };
+    if constexpr (BATCH) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) kop[ks][tt] = k_operand(ks, tt);
+    }
+    // V^T operands by transpose reads of the token-major V: in each 16-lane group, the
+    // lane 4 j + q supplies the address of token row tok_j, columns 4 q .. 4 q + 3 of
+    // the d tile, and lane 4 q + e receives column 4 q + e of rows tok_0 .. tok_3, i.e.
+    // its own d (the MFMA row) for four consecutive tokens.  Group g's k slots hold
+    // tokens 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3, the order the weights leave
+    // the S^T accumulator in.
+    if constexpr (BATCH) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vop[dt] = v_operand(dt);
+    }
     // S^T tiles: st[rb][tt][j] = score of token 16*tt + 4*lgrp + j for this lane's row of
     // block rb; each K operand read from LDS feeds RB products
     f32x4 st[RB][2];
@@ -321,7 +353,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(&k_lds[buf][(tt * 16 + lrow) * KPITCH + ks * 32 + lgrp * 8]);
+        const u32x4 kv = BATCH ? kop[ks][tt] : k_operand(ks, tt);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) st[rb][tt] = mfma16x16x32<CT>(kv, qb[rb][ks], st[rb][tt]);
       }
@@ -397,10 +429,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 3
     // each V^T operand read from LDS feeds 2 x RB products
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const uint32_t* vrow = &vt_lds[buf][(dt * 16 + lrow) * VPITCH];
-      const uint2 t0 = *reinterpret_cast<const uint2*>(vrow + 2 * lgrp);      // tokens 4*lgrp .. +3
-      const uint2 t1 = *reinterpret_cast<const uint2*>(vrow + 8 + 2 * lgrp);  // tokens 16 + 4*lgrp .. +3
-      const u32x4 av = u32x4{t0.x, t0.y, t1.x, t1.y};
+      const u32x4 av = BATCH ? vop[dt] : v_operand(dt);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         o[rb][dt] = mfma16x16x32<CT>(av, bh[rb], o[rb][dt]);
@@ -465,8 +494,9 @@ template <class DT, int D, int G>
 hipError_t launch_cascade_t(const CascadeArgs& a, hipStream_t stream) {
   if (a.num_items <= 0) return hipSuccess;
   if (a.max_piece_blocks > kCascadeMaxPieceBlocks) return hipErrorInvalidValue;
-  if (a.rows_per_item == kCascadeRowsPerItem) return launch_cascade_rb<DT, D, G, 1>(a, stream);
-  if (a.rows_per_item == 2 * kCascadeRowsPerItem) return launch_cascade_rb<DT, D, G, 2>(a, stream);
+  if (a.rows_per_item == 64) return launch_cascade_rb<DT, D, G, 1>(a, stream);
+  if (a.rows_per_item == 128) return launch_cascade_rb<DT, D, G, 2>(a, stream);
+  if (a.rows_per_item == 256) return launch_cascade_rb<DT, D, G, 4>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -132,7 +132,10 @@ struct CascadeArgs {
   int32_t* status;           // optional device word: PKV_STATUS_BAD_BLOCK for node block ids out of range
 };
 
-constexpr int kCascadeRowsPerItem = 64;     // decode plans: 4 waves x 16 rows
+#ifndef PKV_CASCADE_ROWS
+#define PKV_CASCADE_ROWS 64
+#endif
+constexpr int kCascadeRowsPerItem = PKV_CASCADE_ROWS;  // decode plans: 4 waves x (rows / 64) blocks of 16 rows
 constexpr int kExtendRowsPerItem = 128;     // extend plans: 4 waves x 2 x 16 rows
 constexpr int kCascadeMaxPieceBlocks = 256;  // blocks of one work item's token piece
 constexpr int kNodeInts = 8;             // ints per node record of a plan image

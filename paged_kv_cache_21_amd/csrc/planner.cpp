@@ -77,7 +77,9 @@ int32_t tile_pieces(const pkv_plan* p, int32_t n, int32_t t) {
 // kMinPieceBlocks blocks per piece: every piece costs each member row one more
 // fp32 partial per query head, written and read back once.
 void split_pieces(pkv_plan* p) {
-  constexpr int64_t kTargetItems = 1024;
+  // items the chip runs at once: one work-group of the 256-row instance per CU, about
+  // four of the smaller ones; aim at two rounds
+  const int64_t kTargetItems = p->rows_per_item >= 256 ? 512 : 1024;
   constexpr int32_t kMinPieceBlocks = 32;
   constexpr int32_t kMaxPieceBlocks = pkv::kCascadeMaxPieceBlocks;
   const int rows_per_item = p->rows_per_item;
