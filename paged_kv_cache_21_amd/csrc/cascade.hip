@@ -397,13 +397,16 @@ cascade_kernel(CascadeArgs a) {
           sv[j] = ok ? sv[j] : kNegInf;
         }
       }
-      float cmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      cmax = xor_max<16>(cmax);
-      cmax = xor_max<32>(cmax);
-      const float cm = cmax * c;  // chunk max in log2 units
-      // Rescale only when some row's max grows by more than 2^8: until then the
-      // weights 2^(s - m) stay <= 256, harmless in fp32 and in the 16-bit terms.
-      if (__any(cm > m[rb] + 8.f)) {
+      // this lane's largest score of the chunk, in log2 units
+      const float lmax =
+          fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]))) * c;
+      // Rescale only when some score outgrows its row's running max by more than 2^8:
+      // until then the weights 2^(s - m) stay <= 256, harmless in fp32 and in the 16-bit
+      // terms.  The row's max over its four lane groups is needed only then, so the
+      // cross-lane reduction stays on that (rare) path.
+      if (__any(lmax > m[rb] + 8.f)) {
+        float cm = xor_max<16>(lmax);
+        cm = xor_max<32>(cm);  // the chunk max of the lane's row
         const float mn = fmaxf(m[rb], cm);
         const float alpha = exp2_diff(m[rb], mn);
         lsum[rb] *= alpha;

@@ -79,7 +79,7 @@ int32_t tile_pieces(const pkv_plan* p, int32_t n, int32_t t) {
 void split_pieces(pkv_plan* p) {
   // items the chip runs at once: one work-group of the 256-row instance per CU, about
   // four of the smaller ones; aim at two rounds
-  const int64_t kTargetItems = p->rows_per_item >= 256 ? 512 : 1024;
+  const int64_t kTargetItems = p->rows_per_item >= 128 ? 512 : 1024;
   constexpr int32_t kMinPieceBlocks = 32;
   constexpr int32_t kMaxPieceBlocks = pkv::kCascadeMaxPieceBlocks;
   const int rows_per_item = p->rows_per_item;
@@ -274,6 +274,17 @@ pkv_plan* new_plan(pkv_plan::Kind kind, int32_t batch, int32_t max_blocks_per_se
 }
 
 void finish_plan(pkv_plan* p, const std::vector<int32_t>& covered_per_query_row) {
+  // A decode plan whose every node has at least 128 query rows takes 128-row work
+  // items (two 16-row blocks per wave share each LDS operand; two work-groups per
+  // CU); one with smaller nodes keeps 64-row items, four work-groups per CU, so the
+  // many small items still overlap (tree search 79 -> 74 us with 128 rows, radix tree
+  // 68 -> 93 us).
+  if (p->kind == pkv_plan::kDecode && !p->nodes.empty()) {
+    int32_t min_rows = INT32_MAX;
+    for (const auto& n : p->nodes) min_rows = std::min(min_rows, n.num_members * p->group);
+    p->rows_per_item = min_rows >= 2 * pkv::kCascadeRowsPerItem ? 2 * pkv::kCascadeRowsPerItem
+                                                                  : pkv::kCascadeRowsPerItem;
+  }
   p->row_info.assign(2 * static_cast<size_t>(p->num_query_rows), 0);
   for (int32_t r = 0; r < p->num_query_rows; ++r) p->row_info[2 * r] = covered_per_query_row[r];
   split_pieces(p);
