@@ -297,7 +297,7 @@ __device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64
 // depend on this launch's writes (no other segment reads a row's last block: it is
 // private to the row), so no wave waits for another.
 template <class DT, int D, int G, int LPT, bool FUSED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(is_fp8<DT>::value || G >= 8 ? 1 : PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
   typedef typename is_fp8<DT>::compute CT;  // type of q and of the dot products
   constexpr bool Q8 = is_fp8<DT>::value;
   constexpr int EB = Q8 ? 1 : 2;  // bytes per stored element

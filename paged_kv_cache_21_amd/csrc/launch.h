@@ -136,7 +136,10 @@ struct CascadeArgs {
 #define PKV_CASCADE_ROWS 64
 #endif
 constexpr int kCascadeRowsPerItem = PKV_CASCADE_ROWS;  // decode plans: 4 waves x (rows / 64) blocks of 16 rows
-constexpr int kExtendRowsPerItem = 128;     // extend plans: 4 waves x 2 x 16 rows
+#ifndef PKV_EXTEND_ROWS
+#define PKV_EXTEND_ROWS 128
+#endif
+constexpr int kExtendRowsPerItem = PKV_EXTEND_ROWS;  // extend plans: 4 waves x 2 x 16 rows
 constexpr int kCascadeMaxPieceBlocks = 256;  // blocks of one work item's token piece
 constexpr int kNodeInts = 8;             // ints per node record of a plan image
 constexpr int kMemberInts = 3;           // ints per member entry of a plan image
