@@ -188,22 +188,35 @@ cascade_kernel(CascadeArgs a) {
   }
 
   // the piece's block ids, lane j of register w holding block 64 w + j (a piece has
-  // at most 64 NW blocks); read with readlane so the chunk loop issues no scalar
-  // memory loads, which would share a wait counter with the LDS reads
+  // at most 64 NW blocks), -1 past the piece's end and for an id outside the pool; read
+  // with readlane so the chunk loop issues no scalar memory loads, which would share a
+  // wait counter with the LDS reads
   int blk_win[NW];
+  int first_bad = nblk;  // the piece's first block with an id outside the pool (uniform)
 #pragma unroll
   for (int w4 = 0; w4 < NW; ++w4) {
     const int j = 64 * w4 + lane;
-    blk_win[w4] = j < nblk ? a.node_blocks[blk_off + pb0 + j] : -1;
+    const int id = j < nblk ? a.node_blocks[blk_off + pb0 + j] : -1;
+    const bool bad = j < nblk && !(id >= 0 && static_cast<int64_t>(id) < a.num_blocks);
+    blk_win[w4] = bad ? -1 : id;
+    const uint64_t badm = __ballot(bad);
+    if (badm != 0 && first_bad == nblk) first_bad = 64 * w4 + __builtin_ctzll(badm);
   }
-  auto block_id = [&](int j) -> int {  // j: block within the piece (uniform)
-    if (j >= nblk) return -1;
+  // an entry that names a block outside the pool is reported (its tokens get no weight)
+  if (first_bad < nblk && a.status && tid == 0)
+    __hip_atomic_fetch_or(a.status, PKV_STATUS_BAD_BLOCK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto block_id = [&](int j) -> int {  // j: block within the piece (uniform, < 64 NW); -1: none
     int v = blk_win[0];
 #pragma unroll
     for (int w4 = 1; w4 < NW; ++w4) v = (j >> 6) == w4 ? blk_win[w4] : v;
-    const int id = __builtin_amdgcn_readlane(v, j & 63);
-    return (id >= 0 && static_cast<int64_t>(id) < a.num_blocks) ? id : -1;
+    return __builtin_amdgcn_readlane(v, j & 63);
   };
+  // Chunks [0, clean_store) are whole, readable and inside the node's filled tokens: their
+  // K/V go to LDS unmasked.  Chunks [0, clean_wave) also lie at or before every one of the
+  // wave's rows' last attended positions: their scores need no mask.  Both uniform.
+  const int clean_store = min(min(first_bad, nblk) / 2, piece_valid < 0 ? 0 : piece_valid / 32);
+  const int clean_wave =
+      wave_min_limit == INT_MAX ? clean_store : min(clean_store, wave_min_limit < 0 ? 0 : (wave_min_limit + 1) / 32);
 
   // K and V take the same thread mapping: vector i of thread tid is token
   // (tid + 256 i) / (D / 8) of the chunk, 8-element column (tid + 256 i) % (D / 8)
@@ -257,11 +270,7 @@ cascade_kernel(CascadeArgs a) {
     Stage st = st_in;
     // block_id reads a lane of a register: its argument must be wave-uniform
     const bool ok0 = block_id(2 * ch) >= 0, ok1 = block_id(2 * ch + 1) >= 0;
-    // an entry that names a block outside the pool (not the piece's odd end) is reported
-    if (a.status && tid == 0 &&
-        ((!ok0 && 2 * ch < nblk) || (!ok1 && 2 * ch + 1 < nblk)))
-      __hip_atomic_fetch_or(a.status, PKV_STATUS_BAD_BLOCK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (ch * 32 + 32 > piece_valid || !ok0 || !ok1) {  // uniform
+    if (ch >= clean_store) {  // uniform
 #pragma unroll
       for (int i = 0; i < KVEC_PER_THREAD; ++i) {
         const int tok = (tid + 256 * i) / (D / 8);
@@ -308,8 +317,6 @@ cascade_kernel(CascadeArgs a) {
   // evaluate chunk ch from LDS buffer buf for this wave's RB x 16 rows
   auto compute_chunk = [&](int ch, int buf) {
     if (!wave_active) return;
-    const bool valid0 = block_id(2 * ch) >= 0;
-    const bool valid1 = block_id(2 * ch + 1) >= 0;
     // Every LDS operand of the chunk is requested up front, K first, then V^T: the
     // reads' latencies overlap one another, the V^T reads complete under the QK
     // products and the softmax, and no matrix instruction waits on a read issued just
@@ -362,7 +369,7 @@ cascade_kernel(CascadeArgs a) {
     const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
     // uniform: a piece's odd end, bad ids, the node's partly filled end, or a
     // chunk past some row's last attended position
-    const bool mask_chunk = !(valid0 && valid1) || ch * 32 + 31 > wave_min_limit || ch * 32 + 32 > piece_valid;
+    const bool mask_chunk = ch >= clean_wave;
     u32x4 bh[RB], bl[RB];
     float ksc[8], vsc[8];  // FP8: this lane's tokens' scales
     if constexpr (Q8) {
@@ -390,6 +397,8 @@ cascade_kernel(CascadeArgs a) {
         for (int j = 0; j < 8; ++j) sv[j] *= ksc[j];
       }
       if (mask_chunk) {
+        const bool valid0 = block_id(2 * ch) >= 0;
+        const bool valid1 = block_id(2 * ch + 1) >= 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = ch * 32 + 16 * (j / 4) + 4 * lgrp + (j % 4);  // piece-local token of score j
