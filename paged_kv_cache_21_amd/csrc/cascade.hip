@@ -229,15 +229,19 @@ cascade_kernel(CascadeArgs a) {
   // Per-thread element offsets inside a block (32-bit: a block is 16 * Hkv * D
   // elements); per chunk only the two block bases change, and those are uniform.
   const int64_t blk_stride = 16 * tok_stride;
-  int koff[KVEC_PER_THREAD];
-  bool khi[KVEC_PER_THREAD];  // token in the chunk's second block
+  uint32_t koff[KVEC_PER_THREAD];  // bytes
+  // token in the chunk's second block: the same for a whole wave (a wave's 64 vectors
+  // cover 512 / D consecutive tokens of one block), so each load takes one block base
+  // for the wave and a 32-bit offset per lane
+  bool khi[KVEC_PER_THREAD];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
   for (int i = 0; i < KVEC_PER_THREAD; ++i) {
     const int vi = tid + 256 * i;
     const int tok = vi / (D / 8);
     const int col = vi % (D / 8);
-    koff[i] = static_cast<int>((tok & 15) * tok_stride + static_cast<int64_t>(hkv) * D + col * 8);
-    khi[i] = tok >= 16;
+    koff[i] = static_cast<uint32_t>(((tok & 15) * tok_stride + static_cast<int64_t>(hkv) * D + col * 8) * EB);
+    khi[i] = (64 * wave_u + 256 * i) / (D / 8) >= 16;
   }
   // global -> registers (cached loads: the other row tiles of this piece read the
   // same K/V from L2); past the last chunk the last one is read again (an L2 hit)
@@ -248,11 +252,22 @@ cascade_kernel(CascadeArgs a) {
     const int64_t b1 = static_cast<int64_t>(id1 < 0 ? 0 : id1) * blk_stride * EB;
     const char* kbase = reinterpret_cast<const char*>(a.k_pages);
     const char* vbase = reinterpret_cast<const char*>(a.v_pages);
+    // the block bases go to scalar registers as they are, so each load is one scalar base
+    // plus the lane's 32-bit offset (no 64-bit address arithmetic per lane)
+    typedef const char __attribute__((address_space(1))) gchar;
+    auto sbase = [](const char* p) {
+      const uint64_t u = reinterpret_cast<uint64_t>(p);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+      return (gchar*)((static_cast<uint64_t>(hi) << 32) | lo);  // global address space
+    };
+    typedef const KV __attribute__((address_space(1))) gKV;
 #pragma unroll
     for (int i = 0; i < KVEC_PER_THREAD; ++i) {
-      const int64_t off = (khi[i] ? b1 : b0) + static_cast<int64_t>(koff[i]) * EB;
-      st.k[i] = *reinterpret_cast<const KV*>(kbase + off);
-      st.v[i] = *reinterpret_cast<const KV*>(vbase + off);
+      gchar* kb = sbase(kbase + (khi[i] ? b1 : b0));
+      gchar* vb = sbase(vbase + (khi[i] ? b1 : b0));
+      st.k[i] = *(gKV*)(kb + koff[i]);
+      st.v[i] = *(gKV*)(vb + koff[i]);
     }
     if constexpr (Q8) {
       if (tid < 16) {  // (K | V) x (block 0 | 1) x rows 4 p .. 4 p + 3
@@ -263,9 +278,9 @@ cascade_kernel(CascadeArgs a) {
       }
     }
   };
-  // registers -> LDS buffer, K and V token-major as in the pages; the values
-  // of tokens without data (past the node's valid length, or in a block with a bad
-  // id) are zeroed, so their zero weights never meet stale Inf / NaN bits
+  // registers -> LDS buffer, K and V token-major as in the pages; K and V of tokens
+  // without data (past the node's valid length, or in a block with a bad id) are
+  // zeroed, so stale Inf / NaN bits meet neither a score's -inf bias nor a zero weight
   auto store_chunk = [&](const Stage& st_in, int ch, int buf) {
     Stage st = st_in;
     // block_id reads a lane of a register: its argument must be wave-uniform
@@ -275,7 +290,7 @@ cascade_kernel(CascadeArgs a) {
       for (int i = 0; i < KVEC_PER_THREAD; ++i) {
         const int tok = (tid + 256 * i) / (D / 8);
         const bool blk_ok = khi[i] ? ok1 : ok0;
-        if (!(blk_ok && ch * 32 + tok < piece_valid)) st.v[i] = KV{};
+        if (!(blk_ok && ch * 32 + tok < piece_valid)) st.k[i] = st.v[i] = KV{};
       }
     }
     if constexpr (Q8) {
@@ -365,13 +380,7 @@ cascade_kernel(CascadeArgs a) {
         for (int rb = 0; rb < RB; ++rb) st[rb][tt] = mfma16x16x32<CT>(kv, qb[rb][ks], st[rb][tt]);
       }
     }
-    // c > 0, so a masked (-inf) score gives exp2(-inf) = 0 with no test per score
-    const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
-    // uniform: a piece's odd end, bad ids, the node's partly filled end, or a
-    // chunk past some row's last attended position
-    const bool mask_chunk = ch >= clean_wave;
-    u32x4 bh[RB], bl[RB];
-    float ksc[8], vsc[8];  // FP8: this lane's tokens' scales
+    float vsc[8];  // FP8: this lane's tokens' V scales; the K scales go onto the scores here
     if constexpr (Q8) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -379,11 +388,37 @@ cascade_kernel(CascadeArgs a) {
         const f32x4 vq = *reinterpret_cast<const f32x4*>(&sc_lds[buf][32 + 16 * tt + 4 * lgrp]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          ksc[4 * tt + j] = kq[j];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) st[rb][tt][j] *= kq[j];
           vsc[4 * tt + j] = vq[j];
         }
       }
     }
+    // Scores that must not count (a piece's odd end, bad ids, the node's partly filled
+    // end, a row's last attended position) become -inf, in place (uniform branch; K is
+    // zeroed where there is no data, so no stale bits are in play).
+    if (ch >= clean_wave) {
+      const bool valid0 = block_id(2 * ch) >= 0;
+      const bool valid1 = block_id(2 * ch + 1) >= 0;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = ch * 32 + 16 * tt + 4 * lgrp + j;  // piece-local token
+            const bool ok = (tt ? valid1 : valid0) && t <= my_limit[rb] && t < piece_valid;
+            st[rb][tt][j] = ok ? st[rb][tt][j] : kNegInf;
+          }
+    }
+    // c > 0, so a masked (-inf) score gives exp2(-inf) = 0 with no test per score
+    const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
+    u32x4 bh[RB], bl[RB];
+    // max(x, y) as med3(x, y, +inf), with +inf opaque to the compiler so the median is
+    // not turned back into a max that first quiets NaNs in both operands
+    float pinf = __builtin_inff();
+    asm volatile("" : "+v"(pinf));
+    auto max2 = [pinf](float x, float y) { return __builtin_amdgcn_fmed3f(x, y, pinf); };
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float sv[8];
@@ -392,23 +427,9 @@ cascade_kernel(CascadeArgs a) {
         sv[j] = st[rb][0][j];
         sv[4 + j] = st[rb][1][j];
       }
-      if constexpr (Q8) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) sv[j] *= ksc[j];
-      }
-      if (mask_chunk) {
-        const bool valid0 = block_id(2 * ch) >= 0;
-        const bool valid1 = block_id(2 * ch + 1) >= 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int t = ch * 32 + 16 * (j / 4) + 4 * lgrp + (j % 4);  // piece-local token of score j
-          const bool ok = (j < 4 ? valid0 : valid1) && t <= my_limit[rb] && t < piece_valid;
-          sv[j] = ok ? sv[j] : kNegInf;
-        }
-      }
       // this lane's largest score of the chunk, in log2 units
       const float lmax =
-          fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]))) * c;
+          max2(max2(max2(sv[0], sv[1]), max2(sv[2], sv[3])), max2(max2(sv[4], sv[5]), max2(sv[6], sv[7]))) * c;
       // Rescale only when some score outgrows its row's running max by more than 2^8:
       // until then the weights 2^(s - m) stay <= 256, harmless in fp32 and in the 16-bit
       // terms.  The row's max over its four lane groups is needed only then, so the
