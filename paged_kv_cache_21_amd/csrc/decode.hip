@@ -507,7 +507,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(is_fp8<DT>::
     // max over the block's tokens of this lane's head: lanes c, c-4, c-8, c-12 of the row
     float mx = fmaxf(sv, dpp_f32<kDppRowRor4>(sv));
     mx = fmaxf(mx, dpp_f32<kDppRowRor8>(mx));
-    const bool grow = mx > m1;
+    // Rescale only when a score outgrows the running max by more than 2^8 (log2 units):
+    // until then the weights 2^(s - m) stay <= 256, harmless in the fp32 sums, and the
+    // (m, l, acc) triple stays consistent for the merge whichever m it is taken against.
+    const bool grow = mx > m1 + 8.f;
     if (__any(grow)) {
       const float mn = fmaxf(m1, mx);
       const float alpha = exp2_diff(m1, mn);
@@ -635,7 +638,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(is_fp8<DT>::
       mx[g] = m[g];
 #pragma unroll
       for (int t = 0; t < TPB; ++t) mx[g] = fmaxf(mx[g], sc[t][g]);
-      grow |= mx[g] > m[g];
+      grow |= mx[g] > m[g] + 8.f;  // rescale only past 2^8 (as in the reduce-scatter path)
     }
     if (__any(grow)) {
 #pragma unroll
