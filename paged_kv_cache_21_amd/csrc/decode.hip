@@ -297,7 +297,7 @@ __device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64
 // depend on this launch's writes (no other segment reads a row's last block: it is
 // private to the row), so no wave waits for another.
 template <class DT, int D, int G, int LPT, bool FUSED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(is_fp8<DT>::value || G >= 8 ? 1 : PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(is_fp8<DT>::value ? 3 : G >= 8 ? 1 : PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
   typedef typename is_fp8<DT>::compute CT;  // type of q and of the dot products
   constexpr bool Q8 = is_fp8<DT>::value;
   constexpr int EB = Q8 ? 1 : 2;  // bytes per stored element
@@ -806,13 +806,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(is_fp8<DT>::
 
   // The pipeline: NBUF register buffers, each holding one block's K/V (and FP8
   // scales) plus the q of that block's segment; step i consumes block i and loads
-  // block i + NBUF - 1 (FP8 blocks are half the bytes, so they keep one more block
-  // in flight).  Every load is issued on every path (past the last block, the last
+  // block i + NBUF - 1.  (FP8 pages keep two blocks in flight too: with a third the
+  // G = 4 instance needs more than 168 VGPRs and runs two waves per SIMD instead of
+  // three, which loses more than the deeper prefetch gains.)  Every load is issued on every path (past the last block, the last
   // one is read again: an L2 hit), so the compiler's wait counts never have to
   // assume the worst of two paths, which would make the wave wait for loads it
   // does not need.  (Separately named buffers, not an indexed array of them: the
   // compiler keeps those in registers.)
-  constexpr int NBUF = Q8 ? 3 : (G <= 4 ? PKV_SPLIT_NBUF16 : 2);
+  constexpr int NBUF = Q8 ? 2 : (G <= 4 ? PKV_SPLIT_NBUF16 : 2);
   KV ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL], kx[TPB][VPL], vx[TPB][VPL];
   float ksa[NS], vsa[NS], ksb[NS], vsb[NS], ksx[NS], vsx[NS];
   u32x4 qa[G][VPL], qb[G][VPL], qx[G][VPL];
