@@ -90,38 +90,30 @@ struct is_fp8<FP8<CT>> {
   typedef CT compute;
 };
 
-// Two E4M3 codes (byte pair 0,1 or 2,3 of a word) converted to fp32, as floats and
-// as bit patterns.  Each consumer below uses the one view that hipcc compiles
-// correctly for it: bit-casting one element of the float pair was miscompiled
-// (element 1 read as element 0) in both directions we tried, so the bf16 packing
-// takes the pair through a 2 x u32 view and fp32 consumers take the floats as is.
+// Two E4M3 codes (byte pair 0,1 or 2,3 of a word) converted to fp32.  Consumers
+// take the floats as returned: bit-casting one element of the pair was miscompiled
+// (element 1 read as element 0) in both directions we tried.
 template <bool HIGH>
 __device__ __forceinline__ f32x2 fp8_pair_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH);
-}
-template <bool HIGH>
-__device__ __forceinline__ u32x2 fp8_pair_bits(uint32_t w) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH));
 }
 
 // four E4M3 codes (one word) -> two words of CT pairs (codes 0,1 and 2,3)
 template <class CT>
 __device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi);
 
+// gfx950 converts a pair of codes straight to a 16-bit pair (times a scale, here 1:
+// every E4M3 value is exact in bf16 and in f16, so the conversion is exact)
 template <>
 __device__ __forceinline__ void widen4<BF16>(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  const u32x2 a = fp8_pair_bits<false>(w), b = fp8_pair_bits<true>(w);
-  // the values have at most 4 significant bits: the upper half of each fp32 is exact
-  lo = __builtin_amdgcn_perm(a.y, a.x, 0x07060302u);
-  hi = __builtin_amdgcn_perm(b.y, b.x, 0x07060302u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 template <>
 __device__ __forceinline__ void widen4<F16>(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  const f32x2 a = fp8_pair_f32<false>(w), b = fp8_pair_f32<true>(w);
-  // every E4M3 value is exact in f16, so the round-toward-zero packing is exact
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
-  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
 }
 
 // eight E4M3 codes -> eight CT values packed as in a 16-bit page vector
