@@ -56,8 +56,22 @@ struct Cursor {
   int len;      // row length (tokens, clamped)
   int cow;      // FUSED: the row's copy-on-write source block (-1: none)
   int app;      // FUSED: 1 if the row's new token is attended (its length was not clamped)
-  int64_t seg;  // index of block 0 of segment (b, h) in the work order
+  int64_t seg;  // position of block 0 of segment (b, h) in the work order
 };
+
+// Work-order units per segment beyond its blocks.  A segment costs its wave a fixed
+// amount besides its blocks (the row merge and partial store at its end, the new
+// row's state), so each segment is followed by kSegUnits units that hold no block:
+// waves whose share falls on many short segments get correspondingly fewer blocks.
+// (Measured on 1,024 rows with the tree-search suffix lengths: equal shares of blocks
+// left the waves on short rows about 7 % behind.)
+constexpr int kSegUnits = 1;
+
+// position of the block after c's in the work order (the next segment's block 0 when
+// c holds its segment's last block)
+__device__ __forceinline__ int64_t next_pos(const Cursor& c) {
+  return c.j + 1 < c.nb ? c.seg + c.j + 1 : c.seg + c.nb + kSegUnits;
+}
 
 // The row information of 64 consecutive rows [base, base + 64), lane l holding row
 // base + l, kept in registers so a cursor moving to the next row reads it with a
@@ -120,7 +134,7 @@ template <bool FUSED>
 __device__ __forceinline__ void advance(Cursor& c, const SplitArgs& a, RowWindow& win) {
   if (++c.j < c.nb) return;
   c.j = 0;
-  c.seg += c.nb;
+  c.seg += c.nb + kSegUnits;
   if (++c.h < a.num_kv_heads) return;
   c.h = 0;
   do {
@@ -148,6 +162,47 @@ __device__ __forceinline__ int wave_sum(int x) {
   return __builtin_amdgcn_readfirstlane(x);
 }
 
+// Places c (its row already set, the row's units starting at row_start) on the first
+// block at or after position start; false if the wave's range [start, end) holds no
+// block (it starts in the units after some segment's last block and ends there).
+template <bool FUSED>
+__device__ __forceinline__ bool place_cursor(Cursor& c, const SplitArgs& a, RowWindow& win, int64_t row_start,
+                                             int64_t start, int64_t end) {
+  const int ext = c.nb + kSegUnits;
+  const int off = static_cast<int>(start - row_start);
+  c.h = off / ext;
+  c.j = off - c.h * ext;
+  c.seg = row_start + static_cast<int64_t>(c.h) * ext;
+  if (c.j < c.nb) return true;
+  c.j = c.nb - 1;
+  if (next_pos(c) >= end) return false;
+  advance<FUSED>(c, a, win);  // a next block exists: its position is below end <= the total
+  return true;
+}
+
+// Number of blocks at positions [position of c, end), walked segment by segment on
+// copies of the cursor and the row window (rows only move forward).
+template <bool FUSED>
+__device__ __forceinline__ int count_blocks(const SplitArgs& a, Cursor t, RowWindow tw, int64_t end) {
+  int count = 0;
+  int64_t p = t.seg + t.j;
+  for (;;) {  // uniform
+    const int64_t stop = t.seg + t.nb;  // the position after the segment's last block
+    if (end <= stop) return count + static_cast<int>(end - p);
+    count += static_cast<int>(stop - p);
+    p = stop + kSegUnits;
+    if (p >= end) return count;
+    if (++t.h == a.num_kv_heads) {
+      t.h = 0;
+      do {
+        ++t.b;
+        set_row<FUSED>(t, a, tw);
+      } while (t.nb == 0);
+    }
+    t.seg = p;
+  }
+}
+
 // This wave's share of the work order and its first position, for batches of at
 // most 64 * KW rows.  Every row's length and plan entry are loaded at once (clamped
 // indices, no branches, so the loads are all in flight together and the wave pays
@@ -155,7 +210,7 @@ __device__ __forceinline__ int wave_sum(int x) {
 // the 64-row window holding the first position stays in registers as the row
 // window.  Returns false when the wave has no work.
 template <int KW, bool FUSED>
-__device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, int64_t& chunk, int& count,
+__device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, int64_t& chunk, int64_t& end,
                                                    Cursor& cur, RowWindow& win) {
   const int lane = __lane_id();
   const int Hkv = a.num_kv_heads;
@@ -181,14 +236,14 @@ __device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, in
     raw_beg[k] = plan ? raw_beg[k] : 0;
     raw_dep[k] = plan ? raw_dep[k] : 0;
     nbk[k] = lenk[k] > raw_beg[k] ? (lenk[k] - raw_beg[k] + 15) >> 4 : 0;
-    wsum[k] = wave_sum(nbk[k]);
+    wsum[k] = wave_sum(nbk[k] > 0 ? nbk[k] + kSegUnits : 0);
     total += wsum[k];
   }
   total *= Hkv;
   chunk = max(static_cast<int64_t>(a.min_chunk), (total + a.num_waves - 1) / a.num_waves);
   const int64_t start = static_cast<int64_t>(w) * chunk;
   if (start >= total) return false;
-  count = static_cast<int>(min(chunk, total - start));
+  end = min(start + chunk, total);
   int64_t run = 0;
   int kw = -1;
 #pragma unroll
@@ -214,41 +269,38 @@ __device__ __forceinline__ bool find_start_windows(const SplitArgs& a, int w, in
     win.app = k == kw ? (raw_len[k] > 0 && raw_len[k] == lenk[k]) : win.app;
   }
   win.base = kw * 64;
-  const int u = s_nb * Hkv;
+  const int u = (s_nb > 0 ? s_nb + kSegUnits : 0) * Hkv;
   const int incl = wave_inclusive_scan(u);
   const uint64_t hit = __ballot(run + incl > start);
   const int k = __builtin_ctzll(hit);
   const int64_t row_start = run + __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(u, k);
   cur.b = kw * 64 + k;
   set_row<FUSED>(cur, a, win);
-  const int off = static_cast<int>(start - row_start);
-  cur.h = off / cur.nb;
-  cur.j = off - cur.h * cur.nb;
-  cur.seg = row_start + static_cast<int64_t>(cur.h) * cur.nb;
-  return true;
+  return place_cursor<FUSED>(cur, a, win, row_start, start, end);
 }
 
 // The same for any batch size: the rows are scanned 64 at a time (one round of
 // memory latency per 64 rows), then the window of the first row is loaded.
 template <bool FUSED>
-__device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64_t& chunk, int& count, Cursor& cur,
+__device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64_t& chunk, int64_t& end, Cursor& cur,
                                                 RowWindow& win) {
   const int Hkv = a.num_kv_heads;
   int64_t total = 0;
   for (int base = 0; base < a.batch; base += 64) {
     load_window<FUSED>(a, base, win);
     const int nb = win.len > win.beg ? (win.len - win.beg + 15) >> 4 : 0;
-    total += wave_sum(nb);
+    total += wave_sum(nb > 0 ? nb + kSegUnits : 0);
   }
   total *= Hkv;
   chunk = max(static_cast<int64_t>(a.min_chunk), (total + a.num_waves - 1) / a.num_waves);
   const int64_t start = static_cast<int64_t>(w) * chunk;
   if (start >= total) return false;
-  count = static_cast<int>(min(chunk, total - start));
+  end = min(start + chunk, total);
   int64_t run = 0;
   for (int base = 0;; base += 64) {
     load_window<FUSED>(a, base, win);
-    const int u = (win.len > win.beg ? (win.len - win.beg + 15) >> 4 : 0) * Hkv;
+    const int nb = win.len > win.beg ? (win.len - win.beg + 15) >> 4 : 0;
+    const int u = (nb > 0 ? nb + kSegUnits : 0) * Hkv;
     const int incl = wave_inclusive_scan(u);
     const uint64_t hit = __ballot(run + incl > start);
     if (hit) {
@@ -256,11 +308,7 @@ __device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64
       const int64_t row_start = run + __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(u, k);
       cur.b = base + k;
       set_row<FUSED>(cur, a, win);
-      const int off = static_cast<int>(start - row_start);
-      cur.h = off / cur.nb;
-      cur.j = off - cur.h * cur.nb;
-      cur.seg = row_start + static_cast<int64_t>(cur.h) * cur.nb;
-      return true;
+      return place_cursor<FUSED>(cur, a, win, row_start, start, end);
     }
     run += __builtin_amdgcn_readlane(incl, 63);
   }
@@ -297,7 +345,7 @@ __device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64
 // depend on this launch's writes (no other segment reads a row's last block: it is
 // private to the row), so no wave waits for another.
 template <class DT, int D, int G, int LPT, bool FUSED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(is_fp8<DT>::value ? 3 : G >= 8 ? 1 : PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 : is_fp8<DT>::value ? 3 : PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
   typedef typename is_fp8<DT>::compute CT;  // type of q and of the dot products
   constexpr bool Q8 = is_fp8<DT>::value;
   constexpr int EB = Q8 ? 1 : 2;  // bytes per stored element
@@ -315,15 +363,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(is_fp8<DT>::
 
   // ---- this wave's range of the work order, and its first position
   int64_t chunk = 0;
-  int count = 0;
+  int64_t end = 0;  // the wave's range of the work order is [w * chunk, end)
   Cursor cur;
   RowWindow win;
   const int nwin = (a.batch + 63) >> 6;
-  const bool any = nwin == 1   ? find_start_windows<1, FUSED>(a, w, chunk, count, cur, win)
-                   : nwin <= 4 ? find_start_windows<4, FUSED>(a, w, chunk, count, cur, win)
-                   : nwin <= 16 ? find_start_windows<16, FUSED>(a, w, chunk, count, cur, win)
-                                : find_start_scan<FUSED>(a, w, chunk, count, cur, win);
+  const bool any = nwin == 1   ? find_start_windows<1, FUSED>(a, w, chunk, end, cur, win)
+                   : nwin <= 4 ? find_start_windows<4, FUSED>(a, w, chunk, end, cur, win)
+                   : nwin <= 16 ? find_start_windows<16, FUSED>(a, w, chunk, end, cur, win)
+                                : find_start_scan<FUSED>(a, w, chunk, end, cur, win);
   if (!any) return;
+  const int count = count_blocks<FUSED>(a, cur, win, end);
 
   const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;  // elements between consecutive tokens
   const int64_t blk_stride = 16 * tok_stride;

@@ -52,11 +52,14 @@ struct AppendArgs {
 // work spread evenly over a fixed number of persistent waves.
 //
 // Work order: rows b, then KV heads, then the row's own blocks j; a row-head
-// "segment" (b, h) holds n_b = ceil((len_b - shared_b) / 16) blocks.  With T the
-// total number of blocks and W waves, wave w takes blocks [w*c, (w+1)*c),
+// "segment" (b, h) holds n_b = ceil((len_b - shared_b) / 16) blocks and spans
+// n_b + kSegUnits positions of the order (the extra positions hold no block and
+// stand for the segment's fixed cost).  With T the total number of positions and W
+// waves, wave w takes the blocks at positions [w*c, (w+1)*c),
 // c = max(min_chunk, ceil(T / W)).  Partial k of segment (b, h) comes from wave
-// floor(S_bh / c) + k (S_bh = the segment's first index) and goes to partial slot
-// depth_b + k; the wave that starts a segment also stores its partial count.
+// floor(S_bh / c) + k (S_bh = the position of the segment's block 0) and goes to
+// partial slot depth_b + k; the wave that starts a segment also stores its partial
+// count.
 struct SplitArgs {
   const uint16_t* q;
   const uint16_t* k_pages;
