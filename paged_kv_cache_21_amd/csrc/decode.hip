@@ -926,14 +926,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
 //   M = max_i m_i,  o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i,
 // and gives rows with no tokens 0.  A wave covers 64 / (D / 8) query heads of one
 // row, lanes split as (head, 8 output dims).  The row's length, plan entry and
-// partial counts are read together, then the partials in batches of 8 with all
+// partial counts are read together, then the partials in batches of 4 with all
 // their loads in flight at once: two dependent rounds of memory latency in all
-// for up to 8 partials.
+// for up to 4 partials.  A partial slot's records start at a wave-uniform address,
+// so every load is a scalar base plus the lane's fixed 32-bit offset; with 4 in a
+// batch the kernel stays under 72 VGPRs (7 waves per SIMD, against 3 with 8 in a
+// batch and per-lane 64-bit addresses).
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   constexpr int LPH = D / 8;     // lanes per query head
   constexpr int HPP = 64 / LPH;  // query heads per wave
-  constexpr int BATCH = 8;       // partials loaded together
+  constexpr int BATCH = 4;       // partials loaded together
   const int lane = threadIdx.x;
   const int groups = (a.num_q_heads + HPP - 1) / HPP;
   const int b = blockIdx.x / groups;
@@ -956,7 +959,14 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
       __hip_atomic_fetch_or(a.status, PKV_STATUS_LEN_CLAMPED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int np = min(depth + nsplit, a.slots);
-  const int64_t rec0 = static_cast<int64_t>(b) * a.slots * a.num_q_heads + h;
+  // slot p of row b: acc records at acc_row + p * slot_bytes, (m, l) at ml_row + p * Hq
+  const int64_t recs_row = static_cast<int64_t>(b) * a.slots * a.num_q_heads;
+  const char* acc_row = reinterpret_cast<const char*>(a.acc + recs_row * D);
+  const char* ml_row = reinterpret_cast<const char*>(a.ml + recs_row);
+  const int64_t slot_bytes = static_cast<int64_t>(a.num_q_heads) * D * sizeof(float);
+  const int64_t slot_ml_bytes = static_cast<int64_t>(a.num_q_heads) * sizeof(float2);
+  const uint32_t aoff = static_cast<uint32_t>((h * D + c * 8) * sizeof(float));
+  const uint32_t moff = static_cast<uint32_t>(h * sizeof(float2));
 
   float M = kNegInf, L = 0.f;
   float o[8];
@@ -970,11 +980,10 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
       ml[i] = make_float2(kNegInf, 0.f);
       x0[i] = x1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (p0 + i < np) {
-        const int64_t rec = rec0 + static_cast<int64_t>(p0 + i) * a.num_q_heads;
-        ml[i] = a.ml[rec];
-        const float4* src = reinterpret_cast<const float4*>(a.acc + rec * D + c * 8);
-        x0[i] = src[0];
-        x1[i] = src[1];
+        const char* ab = acc_row + (p0 + i) * slot_bytes + aoff;
+        ml[i] = *reinterpret_cast<const float2*>(ml_row + (p0 + i) * slot_ml_bytes + moff);
+        x0[i] = *reinterpret_cast<const float4*>(ab);
+        x1[i] = *reinterpret_cast<const float4*>(ab + 16);
       }
     }
 #pragma unroll
