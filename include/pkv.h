@@ -615,6 +615,21 @@ int64_t pkv_plan_image(const pkv_plan* plan, int32_t* out, int64_t capacity, int
  * row is a multiple of it): 64 for decode plans, 128 for extend plans. -1 for NULL. */
 int32_t pkv_plan_rows_per_item(const pkv_plan* plan);
 
+/* Where the plan's device image holds the work-item records the matrix-core pass
+ * reads (the same work items as the items section, each made self-contained so that
+ * a work-group's first K/V and query loads need one read of its record): returns the
+ * record section's offset in int32 entries (a multiple of 4) and stores the ints per
+ * record in *ints_per_item (if non-NULL); -1 for NULL.  A record is a 16-int header
+ * (KV head or -1 for an idle item, first tile row, piece, index of the piece's first
+ * block in the node-block section, blocks in the piece, query rows of the node, logical
+ * position of the piece's first token, tokens of the piece holding data, the ids of the
+ * piece's first 4 blocks or -1, 4 zeros), then 4 ints per member row of the tile
+ * (query row or -1 past the node's members, partial slot of this piece, last attended
+ * position or INT32_MAX, 0).  An idle item's record has head -1, no blocks, no rows,
+ * ids -1 and every member row -1.  For inspection; the layout follows the plan's kind and
+ * may change with the library version. */
+int64_t pkv_plan_item_records(const pkv_plan* plan, int32_t* ints_per_item);
+
 /* ------------------------------------------------------------------------------------------
  * Kernel timing (for measurement).  When enabled, every kernel launch of the
  * library is bracketed with HIP events on its own stream; pkv_timing_read()

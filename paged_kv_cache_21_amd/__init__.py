@@ -131,6 +131,7 @@ _SIGNATURES = {
     "pkv_plan_num_query_rows": (_i32, [_vp]),
     "pkv_plan_rows_per_item": (_i32, [_vp]),
     "pkv_plan_image": (_i64, [_vp, _vp, _i64, _vp]),
+    "pkv_plan_item_records": (_i64, [_vp, _vp]),
     "pkv_paged_extend_attn": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _i32, _f32, _vp, _vp, _sz,
                                      _vp, _vp]),
     "pkv_paged_extend_attn_fp8": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _i32, _f32,
@@ -814,13 +815,19 @@ class CascadePlan:
         return int(_lib.pkv_plan_rows_per_item(self._handle))
 
     def image(self):
-        """(int32 image, {section: offset}, partial slots per query row) as uploaded to the device."""
+        """(int32 image, {section: offset}, partial slots per query row) as uploaded to the device;
+        the sections are row_info, nodes, blocks, members, items and item_recs (the work-item
+        records, ``item_ints`` ints each)."""
         offs = np.zeros(6, dtype=np.int64)
         n = int(_lib.pkv_plan_image(self._handle, None, 0, _ptr(offs)))
         img = np.zeros(max(n, 1), dtype=np.int32)
         _lib.pkv_plan_image(self._handle, _ptr(img), n, _ptr(offs))
         names = ("row_info", "nodes", "blocks", "members", "items")
-        return img[:n], dict(zip(names, offs[:5].tolist())), int(offs[5])
+        sections = dict(zip(names, offs[:5].tolist()))
+        ints = np.zeros(1, dtype=np.int32)
+        sections["item_recs"] = int(_lib.pkv_plan_item_records(self._handle, _ptr(ints)))
+        sections["item_ints"] = int(ints[0])
+        return img[:n], sections, int(offs[5])
 
     def row(self, b):
         """(shared tokens, partial slots used by the row's nodes) of row b."""

@@ -301,26 +301,26 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
   const int32_t* row_info = plan ? plan->device + plan->off_row_info : nullptr;
 
   if (plan && plan->num_items() > 0) {
-    pkv::CascadeArgs c{static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k_pages),
-                       static_cast<const uint16_t*>(v_pages),
-                       plan->device + plan->off_items,
-                       plan->device + plan->off_nodes,
-                       plan->device + plan->off_blocks,
-                       plan->device + plan->off_members,
-                       acc,
-                       ml,
-                       num_blocks,
-                       plan->num_items(),
-                       num_q_heads,
-                       num_kv_heads,
-                       L.slots,
-                       plan->max_piece_blocks(),
-                       scale_log2,
-                       plan->rows_per_item,
-                       k_scales,
-                       v_scales,
-                       status};
+    pkv::CascadeArgs c{};
+    c.q = static_cast<const uint16_t*>(q);
+    c.k_pages = static_cast<const uint16_t*>(k_pages);
+    c.v_pages = static_cast<const uint16_t*>(v_pages);
+    c.item_recs = plan->device + plan->off_item_recs;
+    c.item_ints = plan->item_ints;
+    c.node_blocks = plan->device + plan->off_blocks;
+    c.acc = acc;
+    c.ml = ml;
+    c.num_blocks = num_blocks;
+    c.num_items = plan->num_items();
+    c.num_q_heads = num_q_heads;
+    c.num_kv_heads = num_kv_heads;
+    c.slots = L.slots;
+    c.max_piece_blocks = plan->max_piece_blocks();
+    c.scale_log2 = scale_log2;
+    c.rows_per_item = plan->rows_per_item;
+    c.k_scales = k_scales;
+    c.v_scales = v_scales;
+    c.status = status;
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
     if (st != PKV_OK) return st;
@@ -502,26 +502,26 @@ pkv_status extend_impl(int kdtype, const void* q, int32_t num_query_rows, int32_
                                          ((recs * head_dim * sizeof(float) + 255) & ~static_cast<size_t>(255)));
   const float scale_log2 = scale * 1.4426950408889634f;
   if (plan->num_items() > 0) {
-    pkv::CascadeArgs c{static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k_pages),
-                       static_cast<const uint16_t*>(v_pages),
-                       plan->device + plan->off_items,
-                       plan->device + plan->off_nodes,
-                       plan->device + plan->off_blocks,
-                       plan->device + plan->off_members,
-                       acc,
-                       ml,
-                       num_blocks,
-                       plan->num_items(),
-                       num_q_heads,
-                       num_kv_heads,
-                       slots,
-                       plan->max_piece_blocks(),
-                       scale_log2,
-                       plan->rows_per_item,
-                       k_scales,
-                       v_scales,
-                       nullptr};
+    pkv::CascadeArgs c{};
+    c.q = static_cast<const uint16_t*>(q);
+    c.k_pages = static_cast<const uint16_t*>(k_pages);
+    c.v_pages = static_cast<const uint16_t*>(v_pages);
+    c.item_recs = plan->device + plan->off_item_recs;
+    c.item_ints = plan->item_ints;
+    c.node_blocks = plan->device + plan->off_blocks;
+    c.acc = acc;
+    c.ml = ml;
+    c.num_blocks = num_blocks;
+    c.num_items = plan->num_items();
+    c.num_q_heads = num_q_heads;
+    c.num_kv_heads = num_kv_heads;
+    c.slots = slots;
+    c.max_piece_blocks = plan->max_piece_blocks();
+    c.scale_log2 = scale_log2;
+    c.rows_per_item = plan->rows_per_item;
+    c.k_scales = k_scales;
+    c.v_scales = v_scales;
+    c.status = nullptr;
     pkv_status st = pkv::launch(PKV_KERNEL_CASCADE, "cascade", s,
                                 [&] { return pkv::launch_cascade(dtype, head_dim, group, c, s); });
     if (st != PKV_OK) return st;

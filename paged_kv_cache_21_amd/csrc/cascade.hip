@@ -110,113 +110,40 @@ cascade_kernel(CascadeArgs a) {
   // FP8: the chunk's 32 K scales, then its 32 V scales (zero for tokens without data)
   __shared__ __attribute__((aligned(16))) float sc_lds[2][Q8 ? 64 : 1];
 
+  // The work item's record holds everything needed before the first K/V loads (the
+  // piece's first block ids, its member rows), so they issue one read after launch.
+  // The header is read through the constant address space (scalar loads: the record is
+  // never written while the kernel runs).  An idle item has no blocks and no member rows.
+  typedef const int32_t __attribute__((address_space(4))) const_i32;
   const int item = blockIdx.x;
-  const int node = a.items[4 * item];
-  if (node < 0) return;  // padding item (uniform for the work-group)
-  const int hkv = a.items[4 * item + 1];
-  const int row0 = a.items[4 * item + 2];
-  const int piece = a.items[4 * item + 3];
-  const int32_t* nrec = a.nodes + kNodeInts * node;
-  const int blk_off = nrec[0];
-  const int node_blocks = nrec[1];
-  const int mem_off = nrec[2];
-  const int nmem = nrec[3];
-  const int piece_blocks = nrec[5];
-  const int pb0 = piece * piece_blocks;
-  const int piece_tok0 = nrec[6] + pb0 * 16;  // logical position of the piece's first token
-  const int piece_valid = nrec[7] - pb0 * 16;  // tokens of the piece holding data (may exceed the piece)
-  const int nblk = min(piece_blocks, node_blocks - pb0);
-  const int R = nmem * G;
-  const int Hkv = a.num_kv_heads;
-  const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;
-
+  const int32_t* irec = a.item_recs + static_cast<int64_t>(item) * a.item_ints;
+  const_i32* hrec = (const_i32*)(irec);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int lrow = lane & 15;  // MFMA row / column index
   const int lgrp = lane >> 4;  // MFMA k group
+  // this lane's member entries, one per row block (query row -1 past the node's members):
+  // at a fixed place in the record, so they load alongside the header
+  int my_b[RB], my_slot[RB], my_limit_raw[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int32_t* mrec = irec + kItemHeadInts + kItemMemberInts * ((wave * 16 * RB + rb * 16 + lrow) / G);
+    my_b[rb] = mrec[0];
+    my_slot[rb] = mrec[1];
+    my_limit_raw[rb] = mrec[2];
+  }
+  const int hkv = max(hrec[0], 0);  // -1 (idle item) reads as head 0
+  const int row0 = hrec[1];
+  const int blk_start = hrec[3];  // the piece's first id in node_blocks
+  const int nblk = hrec[4];
+  const int R = hrec[5];
+  const int piece_tok0 = hrec[6];   // logical position of the piece's first token
+  const int piece_valid = hrec[7];  // tokens of the piece holding data (may exceed the piece)
+  const int Hkv = a.num_kv_heads;
+  const int64_t tok_stride = static_cast<int64_t>(Hkv) * D;
+
   const bool wave_active = row0 + wave * 16 * RB < R;
-
-  // queries of this lane's rows (one per row block), as B operands
-  u32x4 qb[RB][NKS];
-  int my_row[RB], my_b[RB], my_slot[RB], my_h[RB];
-  int my_limit[RB];  // last attended position, piece-local (rows past R attend to nothing)
-  int wave_min_limit = INT_MAX;
-  // a negative scale is applied as |scale| on -q (flipping sign bits is exact), so the
-  // running max can be taken on the unscaled scores
-  const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    my_row[rb] = row0 + wave * 16 * RB + rb * 16 + lrow;
-    my_b[rb] = -1;
-    my_slot[rb] = 0;
-    my_h[rb] = 0;
-    my_limit[rb] = -1;
-    if (my_row[rb] < R) {
-      const int32_t* mrec = a.node_members + kMemberInts * (mem_off + my_row[rb] / G);
-      my_b[rb] = mrec[0];
-      my_slot[rb] = mrec[1] + piece;
-      const int limit = mrec[2];
-      my_limit[rb] = limit == INT_MAX ? INT_MAX : limit - piece_tok0;
-      my_h[rb] = hkv * G + my_row[rb] % G;
-      const uint16_t* qp = a.q + (static_cast<int64_t>(my_b[rb]) * a.num_q_heads + my_h[rb]) * D + lgrp * 8;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qb[rb][ks] = ld16(qp + ks * 32) ^ flip;
-      wave_min_limit = min(wave_min_limit, my_limit[rb]);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qb[rb][ks] = u32x4{0, 0, 0, 0};
-    }
-  }
-  // the earliest last-attended position over the wave's rows (rows past R count as
-  // unlimited: their results are never stored); chunks entirely at or before it
-  // need no causal mask
-  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 1));
-  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 2));
-  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 4));
-  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 8));
-  wave_min_limit = __builtin_amdgcn_readfirstlane(wave_min_limit);
-
-  float m[RB], lsum[RB];
-  f32x4 o[RB][NDT];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = kNegInf;
-    lsum[rb] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // the piece's block ids, lane j of register w holding block 64 w + j (a piece has
-  // at most 64 NW blocks), -1 past the piece's end and for an id outside the pool; read
-  // with readlane so the chunk loop issues no scalar memory loads, which would share a
-  // wait counter with the LDS reads
-  int blk_win[NW];
-  int first_bad = nblk;  // the piece's first block with an id outside the pool (uniform)
-#pragma unroll
-  for (int w4 = 0; w4 < NW; ++w4) {
-    const int j = 64 * w4 + lane;
-    const int id = j < nblk ? a.node_blocks[blk_off + pb0 + j] : -1;
-    const bool bad = j < nblk && !(id >= 0 && static_cast<int64_t>(id) < a.num_blocks);
-    blk_win[w4] = bad ? -1 : id;
-    const uint64_t badm = __ballot(bad);
-    if (badm != 0 && first_bad == nblk) first_bad = 64 * w4 + __builtin_ctzll(badm);
-  }
-  // an entry that names a block outside the pool is reported (its tokens get no weight)
-  if (first_bad < nblk && a.status && tid == 0)
-    __hip_atomic_fetch_or(a.status, PKV_STATUS_BAD_BLOCK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  auto block_id = [&](int j) -> int {  // j: block within the piece (uniform, < 64 NW); -1: none
-    int v = blk_win[0];
-#pragma unroll
-    for (int w4 = 1; w4 < NW; ++w4) v = (j >> 6) == w4 ? blk_win[w4] : v;
-    return __builtin_amdgcn_readlane(v, j & 63);
-  };
-  // Chunks [0, clean_store) are whole, readable and inside the node's filled tokens: their
-  // K/V go to LDS unmasked.  Chunks [0, clean_wave) also lie at or before every one of the
-  // wave's rows' last attended positions: their scores need no mask.  Both uniform.
-  const int clean_store = min(min(first_bad, nblk) / 2, piece_valid < 0 ? 0 : piece_valid / 32);
-  const int clean_wave =
-      wave_min_limit == INT_MAX ? clean_store : min(clean_store, wave_min_limit < 0 ? 0 : (wave_min_limit + 1) / 32);
 
   // K and V take the same thread mapping: vector i of thread tid is token
   // (tid + 256 i) / (D / 8) of the chunk, 8-element column (tid + 256 i) % (D / 8)
@@ -245,9 +172,7 @@ cascade_kernel(CascadeArgs a) {
   }
   // global -> registers (cached loads: the other row tiles of this piece read the
   // same K/V from L2); past the last chunk the last one is read again (an L2 hit)
-  auto load_chunk = [&](int ch, Stage& st) {
-    ch = min(ch, nchunks - 1);
-    const int id0 = block_id(2 * ch), id1 = block_id(2 * ch + 1);
+  auto load_ids = [&](int id0, int id1, Stage& st) {
     const int64_t b0 = static_cast<int64_t>(id0 < 0 ? 0 : id0) * blk_stride * EB;  // bytes
     const int64_t b1 = static_cast<int64_t>(id1 < 0 ? 0 : id1) * blk_stride * EB;
     const char* kbase = reinterpret_cast<const char*>(a.k_pages);
@@ -277,6 +202,94 @@ cascade_kernel(CascadeArgs a) {
         st.sc = *reinterpret_cast<const f32x4*>(sb + (static_cast<int64_t>(id < 0 ? 0 : id) * Hkv + hkv) * 16 + 4 * part);
       }
     }
+  };
+  // The first two chunks' K/V loads go out as soon as the header is in (an idle item
+  // reads block 0 and discards it), then the queries and the piece's block-id window;
+  // nothing waits for them before the first chunk is staged.
+  Stage s0, s1;
+  {
+    int fid[kItemFirstIds];  // the record's copy of the piece's first ids, checked as the window's are
+#pragma unroll
+    for (int j = 0; j < kItemFirstIds; ++j) {
+      const int id = hrec[8 + j];
+      fid[j] = id >= 0 && static_cast<int64_t>(id) < a.num_blocks ? id : -1;
+    }
+    const bool two = nchunks > 1;  // else chunk 1 is chunk 0 again, as load_chunk would read it
+    load_ids(fid[0], fid[1], s0);
+    load_ids(two ? fid[2] : fid[0], two ? fid[3] : fid[1], s1);
+  }
+
+  // queries of this lane's rows (one per row block), as B operands: loaded for every lane
+  // (a lane past the node's rows reads its item's row 0 of q) and made final (zeroed past
+  // the rows, sign-flipped for a negative scale) after the first chunk is staged
+  u32x4 qb[RB][NKS];
+  int my_h[RB];
+  int my_limit[RB];  // last attended position, piece-local (rows past R attend to nothing)
+  int wave_min_limit = INT_MAX;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const bool in = my_b[rb] >= 0;  // the lane's row rb is one of the node's rows
+    const int limit = my_limit_raw[rb];
+    my_limit[rb] = !in ? -1 : limit == INT_MAX ? INT_MAX : limit - piece_tok0;
+    my_h[rb] = hkv * G + (wave * 16 * RB + rb * 16 + lrow) % G;  // tile rows start at a multiple of G
+    const uint16_t* qp = a.q + (static_cast<int64_t>(in ? my_b[rb] : 0) * a.num_q_heads + my_h[rb]) * D + lgrp * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qb[rb][ks] = ld16(qp + ks * 32);
+    if (in) wave_min_limit = min(wave_min_limit, my_limit[rb]);
+  }
+  // the earliest last-attended position over the wave's rows (rows past R count as
+  // unlimited: their results are never stored); chunks entirely at or before it
+  // need no causal mask
+  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 1));
+  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 2));
+  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 4));
+  wave_min_limit = min(wave_min_limit, __shfl_xor(wave_min_limit, 8));
+  wave_min_limit = __builtin_amdgcn_readfirstlane(wave_min_limit);
+
+  float m[RB], lsum[RB];
+  f32x4 o[RB][NDT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegInf;
+    lsum[rb] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[rb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // the piece's block ids, lane j of register w holding block 64 w + j (a piece has
+  // at most 64 NW blocks), -1 past the piece's end and for an id outside the pool; read
+  // with readlane so the chunk loop issues no scalar memory loads, which would share a
+  // wait counter with the LDS reads
+  int blk_win[NW];
+  int first_bad = nblk;  // the piece's first block with an id outside the pool (uniform)
+#pragma unroll
+  for (int w4 = 0; w4 < NW; ++w4) {
+    const int j = 64 * w4 + lane;
+    const int id = j < nblk ? a.node_blocks[blk_start + j] : -1;
+    const bool bad = j < nblk && !(id >= 0 && static_cast<int64_t>(id) < a.num_blocks);
+    blk_win[w4] = bad ? -1 : id;
+    const uint64_t badm = __ballot(bad);
+    if (badm != 0 && first_bad == nblk) first_bad = 64 * w4 + __builtin_ctzll(badm);
+  }
+  // an entry that names a block outside the pool is reported (its tokens get no weight)
+  if (first_bad < nblk && a.status && tid == 0)
+    __hip_atomic_fetch_or(a.status, PKV_STATUS_BAD_BLOCK, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto block_id = [&](int j) -> int {  // j: block within the piece (uniform, < 64 NW); -1: none
+    int v = blk_win[0];
+#pragma unroll
+    for (int w4 = 1; w4 < NW; ++w4) v = (j >> 6) == w4 ? blk_win[w4] : v;
+    return __builtin_amdgcn_readlane(v, j & 63);
+  };
+  // Chunks [0, clean_store) are whole, readable and inside the node's filled tokens: their
+  // K/V go to LDS unmasked.  Chunks [0, clean_wave) also lie at or before every one of the
+  // wave's rows' last attended positions: their scores need no mask.  Both uniform.
+  const int clean_store = min(min(first_bad, nblk) / 2, piece_valid < 0 ? 0 : piece_valid / 32);
+  const int clean_wave =
+      wave_min_limit == INT_MAX ? clean_store : min(clean_store, wave_min_limit < 0 ? 0 : (wave_min_limit + 1) / 32);
+
+  auto load_chunk = [&](int ch, Stage& st) {
+    ch = min(ch, nchunks - 1);
+    load_ids(block_id(2 * ch), block_id(2 * ch + 1), st);
   };
   // registers -> LDS buffer, K and V token-major as in the pages; K and V of tokens
   // without data (past the node's valid length, or in a block with a bad id) are
@@ -472,12 +485,16 @@ cascade_kernel(CascadeArgs a) {
   };
 
   if (nchunks > 0) {
-    Stage s0, s1;
-    load_chunk(0, s0);
-    load_chunk(1, s1);
     store_chunk(s0, 0, 0);
     load_chunk(2, s0);
     __syncthreads();
+    // a negative scale is applied as |scale| on -q (flipping sign bits is exact), so the
+    // running max can be taken on the unscaled scores; lanes past the node's rows get q = 0
+    const uint32_t flip = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qb[rb][ks] = my_b[rb] >= 0 ? qb[rb][ks] ^ flip : u32x4{0, 0, 0, 0};
     for (int ch = 0; ch < nchunks; ch += 2) {
       compute_chunk(ch, 0);
       store_chunk(s1, ch + 1, 1);
@@ -499,7 +516,7 @@ cascade_kernel(CascadeArgs a) {
     float ls = lo + hi;
     pair_values<32>(ls, lo, hi);
     ls = lo + hi;
-    if (my_row[rb] < R) {
+    if (my_b[rb] >= 0) {
       const int64_t rec = (static_cast<int64_t>(my_b[rb]) * a.slots + my_slot[rb]) * a.num_q_heads + my_h[rb];
       float* dst = a.acc + rec * D + lgrp * 4;
 #pragma unroll

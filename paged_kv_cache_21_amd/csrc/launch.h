@@ -114,12 +114,15 @@ struct CascadeArgs {
   const uint16_t* q;
   const uint16_t* k_pages;
   const uint16_t* v_pages;
-  const int32_t* items;         // [num_items][4] = (node, kv head, first tile row, piece); node < 0: idle
-  const int32_t* nodes;         // [num_nodes][kNodeInts] = (block offset, blocks, member offset, members,
-                                //   pieces, blocks per piece, first token position, tokens holding data)
+  // [num_items][item_ints] self-contained work items: header (kv head or -1 = idle, first
+  // tile row, piece, index of the piece's first id in node_blocks, blocks in the piece,
+  // query rows of the node, logical position of the piece's first token, tokens of the
+  // piece holding data, ids of the piece's first kItemFirstIds blocks or -1, padding),
+  // then kItemMemberInts ints per member row of the tile (query row or -1, partial slot
+  // of this piece, last token position it attends to or INT_MAX, 0)
+  const int32_t* item_recs;
+  int32_t item_ints;
   const int32_t* node_blocks;   // physical block ids
-  const int32_t* node_members;  // [..][kMemberInts] = (query row, partial slot of piece 0 (piece p uses
-                                //   slot + p), last token position it attends to, INT_MAX: all)
   float* acc;
   float2* ml;
   int64_t num_blocks;
@@ -144,8 +147,9 @@ constexpr int kCascadeRowsPerItem = PKV_CASCADE_ROWS;  // decode plans: 4 waves 
 #endif
 constexpr int kExtendRowsPerItem = PKV_EXTEND_ROWS;  // extend plans: 4 waves x 2 x 16 rows
 constexpr int kCascadeMaxPieceBlocks = 256;  // blocks of one work item's token piece
-constexpr int kNodeInts = 8;             // ints per node record of a plan image
-constexpr int kMemberInts = 3;           // ints per member entry of a plan image
+constexpr int kItemHeadInts = 16;       // header ints of a work-item record
+constexpr int kItemFirstIds = 4;        // block ids of a piece's first two chunks in the header
+constexpr int kItemMemberInts = 4;      // ints per member entry of a work-item record
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // FP8 pages: quantize each new token's head vectors; src_dtype 0 f16, 1 bf16 for k_new / v_new.

@@ -38,9 +38,23 @@ struct pkv_plan {
   bool last_tokens_own = true;
   std::vector<int32_t> items;  // (node, kv head, first member row, piece) in launch order; node -1 = idle
 
-  // device image: one int32 array holding, in order, row_info, nodes, node_blocks, node_members, items
+  // Self-contained work-item records, the form the matrix-core kernel reads: per item a
+  // header of kItemHeadInts ints (kv head or -1 = idle, first tile row, piece, index of
+  // the piece's first id in node_blocks, blocks in the piece, query rows of the node,
+  // logical position of the piece's first token, tokens of the piece holding data, the
+  // ids of the piece's first kItemFirstIds blocks or -1, zero padding), then one entry
+  // of kItemMemberInts ints per member row of the tile (query row or -1 past the node's
+  // members, partial slot of this piece, last attended position or INT32_MAX, 0).
+  // Everything an item needs before its first K/V loads is one read away.
+  static constexpr int kItemHeadInts = 16;
+  static constexpr int kItemFirstIds = 4;
+  static constexpr int kItemMemberInts = 4;
+  int32_t item_ints = 0;  // ints per record: kItemHeadInts + kItemMemberInts * rows_per_item / group
+
+  // device image: one int32 array holding, in order, row_info, nodes, node_blocks, node_members,
+  // items, then (from a multiple of 4 ints) the item records
   std::vector<int32_t> image;
-  size_t off_row_info = 0, off_nodes = 0, off_blocks = 0, off_members = 0, off_items = 0;
+  size_t off_row_info = 0, off_nodes = 0, off_blocks = 0, off_members = 0, off_items = 0, off_item_recs = 0;
   const int32_t* device = nullptr;  // bound by pkv_plan_upload
 
   int32_t num_items() const { return static_cast<int32_t>(items.size() / 4); }

@@ -28,6 +28,10 @@
 #include "launch.h"
 #include "plan.h"
 
+static_assert(pkv_plan::kItemHeadInts == pkv::kItemHeadInts && pkv_plan::kItemFirstIds == pkv::kItemFirstIds &&
+                  pkv_plan::kItemMemberInts == pkv::kItemMemberInts,
+              "work-item record layout shared by the planner and the matrix-core kernel");
+
 namespace {
 
 struct Group {
@@ -51,6 +55,50 @@ void build_image(pkv_plan* p) {
   im.insert(im.end(), p->node_members.begin(), p->node_members.end());
   p->off_items = im.size();
   im.insert(im.end(), p->items.begin(), p->items.end());
+  while (im.size() % 4) im.push_back(0);
+  p->off_item_recs = im.size();
+  const int32_t per_tile = p->rows_per_item / p->group;  // member rows of a tile
+  p->item_ints = pkv_plan::kItemHeadInts + pkv_plan::kItemMemberInts * per_tile;
+  for (size_t it = 0; it + 4 <= p->items.size(); it += 4) {
+    const int32_t node = p->items[it], head = p->items[it + 1], row0 = p->items[it + 2], piece = p->items[it + 3];
+    const size_t base = im.size();
+    im.resize(base + p->item_ints, 0);
+    int32_t* r = im.data() + base;
+    if (node < 0) {  // idle item: no blocks, no member rows
+      r[0] = -1;
+      for (int32_t j = 0; j < pkv_plan::kItemFirstIds; ++j) r[8 + j] = -1;
+      for (int32_t li = 0; li < per_tile; ++li) {
+        r[pkv_plan::kItemHeadInts + pkv_plan::kItemMemberInts * li] = -1;
+        r[pkv_plan::kItemHeadInts + pkv_plan::kItemMemberInts * li + 2] = -1;
+      }
+      continue;
+    }
+    const auto& n = p->nodes[node];
+    const int32_t pb0 = piece * n.piece_blocks;
+    const int32_t nblk = std::min(n.piece_blocks, n.num_blocks - pb0);
+    r[0] = head;
+    r[1] = row0;
+    r[2] = piece;
+    r[3] = n.block_off + pb0;
+    r[4] = nblk;
+    r[5] = n.num_members * p->group;
+    r[6] = n.start_tok + pb0 * p->block_size;
+    r[7] = n.valid_tokens - pb0 * p->block_size;
+    for (int32_t j = 0; j < pkv_plan::kItemFirstIds; ++j) r[8 + j] = j < nblk ? p->node_blocks[n.block_off + pb0 + j] : -1;
+    for (int32_t li = 0; li < per_tile; ++li) {
+      int32_t* e = r + pkv_plan::kItemHeadInts + pkv_plan::kItemMemberInts * li;
+      const int32_t m = row0 / p->group + li;  // member index inside the node
+      if (m < n.num_members) {
+        const int32_t* mrec = &p->node_members[pkv_plan::kMemberInts * (n.member_off + m)];
+        e[0] = mrec[0];
+        e[1] = mrec[1] + piece;
+        e[2] = mrec[2];
+      } else {
+        e[0] = -1;
+        e[2] = -1;
+      }
+    }
+  }
   if (im.empty()) im.push_back(0);
 }
 
@@ -395,6 +443,12 @@ int32_t pkv_plan_num_nodes(const pkv_plan* plan) { return plan ? static_cast<int
 int32_t pkv_plan_num_query_rows(const pkv_plan* plan) { return plan ? plan->num_query_rows : -1; }
 
 int32_t pkv_plan_rows_per_item(const pkv_plan* plan) { return plan ? plan->rows_per_item : -1; }
+
+int64_t pkv_plan_item_records(const pkv_plan* plan, int32_t* ints_per_item) {
+  if (!plan) return -1;
+  if (ints_per_item) *ints_per_item = plan->item_ints;
+  return static_cast<int64_t>(plan->off_item_recs);
+}
 
 int64_t pkv_plan_image(const pkv_plan* plan, int32_t* out, int64_t capacity, int64_t* offsets) {
   if (!plan) return -1;

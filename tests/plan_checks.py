@@ -20,10 +20,20 @@ def check_plan_image(plan, num_q_heads, num_kv_heads, num_blocks):
     nodes = img[off["nodes"]:off["blocks"]].reshape(-1, NODE_INTS)
     blocks = img[off["blocks"]:off["members"]]
     members = img[off["members"]:off["items"]].reshape(-1, MEMBER_INTS)
-    items = img[off["items"]:].reshape(-1, 4) if len(img) > off["items"] else np.zeros((0, 4), np.int32)
+    seg = img[off["items"]:off["item_recs"]]
+    items = seg[:len(seg) // 4 * 4].reshape(-1, 4)
+    assert off["item_recs"] % 4 == 0 and off["item_recs"] - off["items"] - 4 * len(items) < 4
+    ints = off["item_ints"]
+    per_tile = ROWS_PER_ITEM // group
+    assert ints == 16 + 4 * per_tile
+    recs = img[off["item_recs"]:off["item_recs"] + ints * len(items)].reshape(-1, ints)
+    assert len(recs) == len(items)
     written = {}
     for it, (node, hkv, row0, piece) in enumerate(items.tolist()):
-        if node < 0:
+        rec = recs[it].tolist()
+        if node < 0:  # idle: no blocks, no member rows
+            assert rec[:8] == [-1, 0, 0, 0, 0, 0, 0, 0] and rec[8:12] == [-1] * 4 and rec[12:16] == [0] * 4
+            assert all(rec[16 + 4 * li: 20 + 4 * li] == [-1, 0, -1, 0] for li in range(per_tile))
             continue
         assert 0 <= node < len(nodes), (it, node)
         assert 0 <= hkv < num_kv_heads
@@ -39,6 +49,18 @@ def check_plan_image(plan, num_q_heads, num_kv_heads, num_blocks):
         R = nmem * group
         assert 0 <= row0 < R and row0 % ROWS_PER_ITEM == 0
         assert 0 <= mem_off and mem_off + nmem <= len(members)
+        # the work item's record: the same item with its node's and members' fields inline
+        assert rec[:8] == [hkv, row0, piece, blk_off + pb0, nblk, R, start_tok + 16 * pb0, valid - 16 * pb0], (it, rec[:8])
+        assert rec[8:12] == [int(blocks[blk_off + pb0 + j]) if j < nblk else -1 for j in range(4)], (it, rec[8:12])
+        assert rec[12:16] == [0, 0, 0, 0]
+        for li in range(per_tile):
+            e = rec[16 + 4 * li: 20 + 4 * li]
+            m = row0 // group + li
+            if m < nmem:
+                qr, slot0, limit = members[mem_off + m].tolist()
+                assert e == [qr, slot0 + piece, limit, 0], (it, li, e)
+            else:
+                assert e[0] == -1 and e[2] == -1, (it, li, e)
         for row in range(row0, min(row0 + ROWS_PER_ITEM, R)):
             qr, slot0, limit = members[mem_off + row // group].tolist()
             h = hkv * group + row % group
