@@ -40,8 +40,10 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense matrix-core p
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: a few hundred bring the GPU to its steady clocks (with 10 the "
+                         "8B step timed 4-7 %% slower)")
     ap.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5, 6],
                     help="time this workload alone (default: the 8B-shaped layer as the headline, then a line "
                          "per other workload)")
@@ -217,7 +219,7 @@ def extend_cpu_baseline(w, q_bits, k_pages, v_pages, bt, lens, q_lens, seconds):
                       f"heads each), {t_total:.1f} s of fp64 numpy oracle time on one host thread"}
 
 
-def run_extend(args, w, dev):
+def run_extend(args, w, dev, emit=True):
     """Multi-token pass: one paged_extend_attn call per step over the workload's query tokens."""
     import torch
 
@@ -311,10 +313,12 @@ def run_extend(args, w, dev):
                      "algorithmic_flops_per_launch": flops, "avg_launch_us": kern["cascade"]["avg_us"]},
         "cpu_baseline": cpu,
     }
-    print(json.dumps(res), flush=True)
+    if emit:
+        print(json.dumps(res), flush=True)
+    return res
 
 
-def run_fp8(args, w, dev):
+def run_fp8(args, w, dev, emit=True):
     """Append + decode over FP8 pages (with the shared-prefix pass when the workload shares
     blocks): the decode's K/V bytes halve."""
     import torch
@@ -399,7 +403,9 @@ def run_fp8(args, w, dev):
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": kern["decode_split"]["avg_us"]},
         "cpu_baseline": None,
     }
-    print(json.dumps(res), flush=True)
+    if emit:
+        print(json.dumps(res), flush=True)
+    return res
 
 
 def radix_replay(Pool, Cache, reqs, num_blocks, policy, block_size=16, batch=32, seconds=None, meta=None):
@@ -884,6 +890,9 @@ def summarize_config(w, dev, steps, warmup, flush_iters, flush):
            "kernels_us": {k: v["avg_us"] for k, v in kern.items() if v["launches"]},
            "cascade": r.plan is not None, "shared_nodes": r.plan.num_nodes if r.plan is not None else 0,
            "host_us": {"plan_append": round(r.plan_append_us, 1), "plan_build": round(r.plan_build_us, 1)}}
+    if r.fused_ok:  # the same step as one launch (pkv_paged_decode_attn_append)
+        fused_step, _ = step_fns(w, r, fused=True)
+        out["step_us_one_launch"] = round(time_back_to_back(fused_step, r.stream, steps, warmup) * 1e3, 3)
     if r.plan is not None:  # the same call with every row decoded on its own
         _, attn_off = step_fns(w, r, fused=False, use_plan=False)
         off_ms = time_back_to_back(attn_off, r.stream, steps, warmup)
@@ -1065,6 +1074,21 @@ def main():
                                                     warmup=max(args.warmup // 2, 3),
                                                     flush_iters=max(args.cold_iters, 10), flush=flush)
         res["configs"] = configs
+        # the FP8 and multi-token passes, timed in the same run (shorter loops, no oracle)
+        import argparse as _ap
+        sub = _ap.Namespace(**vars(args))
+        sub.steps, sub.warmup, sub.cpu_seconds = max(args.steps // 5, 10), max(args.warmup // 2, 3), 0.0
+        extras = {}
+        for key, n, kind in (("fp8_decode_8b", 2, "fp8"), ("fp8_decode_70b_mha", 4, "fp8"),
+                             ("extend_tree_verify", 3, "extend"), ("extend_chunked_prefill", 6, "extend")):
+            wx = workloads.get(n)
+            print(f"[bench] {key}: workload {n} {wx.name}", file=sys.stderr, flush=True)
+            sub.fp8 = kind == "fp8"
+            rx = run_fp8(sub, wx, dev, emit=False) if kind == "fp8" else run_extend(sub, wx, dev, emit=False)
+            extras[key] = {k: rx[k] for k in ("value", "unit", "ms_per_step", "dtype", "kernels", "roofline")}
+            extras[key]["workload"] = rx["config"]["workload"]
+            torch.cuda.empty_cache()
+        res["extras"] = extras
     print(json.dumps(res), flush=True)
 
 

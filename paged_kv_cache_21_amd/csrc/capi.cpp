@@ -359,6 +359,15 @@ pkv_status decode_impl(int kdtype, const void* q, int32_t batch, int32_t num_q_h
   }
   pkv::MergeArgs ma{seq_lens, row_info, counts, acc, ml, out, batch, num_q_heads, num_kv_heads, max_blocks_per_seq,
                     max_seq_len, L.slots, status};
+  if (fused) {  // the merge writes the new tokens (and copied rows) once every read is done
+    ma.k_pages = static_cast<uint16_t*>(const_cast<void*>(k_pages));
+    ma.v_pages = static_cast<uint16_t*>(const_cast<void*>(v_pages));
+    ma.block_tables = block_tables;
+    ma.k_new = static_cast<const uint16_t*>(k_new);
+    ma.v_new = static_cast<const uint16_t*>(v_new);
+    ma.cow_src = cow_src;
+    ma.num_blocks = num_blocks;
+  }
   return pkv::launch(PKV_KERNEL_MERGE, "merge", s, [&] { return pkv::launch_merge(head_dim, ma, s); });
 }
 

@@ -594,11 +594,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   auto consume_block = [&](bool ok, const u32x4(&qv)[G][VPL], KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL],
                            const float(&ks)[NS], const float(&vs)[NS], const NewTok& nt) {
     if constexpr (FUSED) {
-      if (nt.dst >= 0) {  // uniform: the new token replaces its row; it and the rows copied on write are stored
-        char* kd = reinterpret_cast<char*>(const_cast<uint16_t*>(a.k_pages)) +
-                   (static_cast<int64_t>(nt.dst) * blk_stride + static_cast<int64_t>(cur.h) * D) * EB;
-        char* vd = reinterpret_cast<char*>(const_cast<uint16_t*>(a.v_pages)) +
-                   (static_cast<int64_t>(nt.dst) * blk_stride + static_cast<int64_t>(cur.h) * D) * EB;
+      if (nt.dst >= 0) {  // uniform: the new token replaces its row (the merge kernel stores it)
 #pragma unroll
         for (int t = 0; t < TPB; ++t) {
           const int tok = r + t * ROWS;
@@ -607,10 +603,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
             if (tok == nt.row) {
               kk[t][v] = nt.k[v];
               vv[t][v] = nt.v[v];
-            }
-            if (tok == nt.row || (nt.cow && tok < nt.row)) {
-              st16(kd + voff[t][v], kk[t][v]);
-              st16(vd + voff[t][v], vv[t][v]);
             }
           }
         }
@@ -932,6 +924,49 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
 // so every load is a scalar base plus the lane's fixed 32-bit offset; with 4 in a
 // batch the kernel stays under 72 VGPRs (7 waves per SIMD, against 3 with 8 in a
 // batch and per-lane 64-bit addresses).
+// One-launch append, run by the merge kernel once the split pass has read everything:
+// writes row b's new token (token len - 1, from k_new / v_new) into its own last
+// block and, when that block was just copied on write, rows [0, new row) from the
+// copy's source, for the KV heads whose first query head lies in [h0, h0 + nh) (so
+// each KV head of a row is written by exactly one wave).  Rows with no tokens, with a
+// length outside the table or max_seq_len, or with an out-of-range block id are left
+// alone, as the split pass left them out of its append.
+template <int D>
+__device__ __forceinline__ void append_row_tail(const MergeArgs& a, int b, int h0, int nh, int lane) {
+  const int raw = a.seq_lens[b];
+  const int len = max(0, min(min(raw, a.max_seq_len), a.max_blocks * 16));
+  if (raw <= 0 || raw != len) return;  // uniform
+  const int pos = len - 1;
+  const int row = pos & 15;
+  const int id = a.block_tables[static_cast<int64_t>(b) * a.max_blocks + (pos >> 4)];
+  if (id < 0 || static_cast<int64_t>(id) >= a.num_blocks) return;
+  const int src = a.cow_src[b];
+  const bool cow = row > 0 && src >= 0 && static_cast<int64_t>(src) < a.num_blocks;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  constexpr int VPR = D / 8;           // 16-byte vectors per (token, head) row
+  constexpr int RPI = 64 / (2 * VPR);  // token rows per pass (K and V)
+  const int hk0 = (h0 + G - 1) / G;
+  const int hk1 = min((h0 + nh - 1) / G, a.num_kv_heads - 1);
+  const int64_t tok_stride = static_cast<int64_t>(a.num_kv_heads) * D;
+  const int v = lane % VPR;
+  const bool is_v = (lane / VPR) & 1;
+  const int sub = lane / (2 * VPR);
+  for (int hk = hk0; hk <= hk1; ++hk) {
+    const int64_t col = static_cast<int64_t>(hk) * D + v * 8;
+    uint16_t* pages = is_v ? a.v_pages : a.k_pages;
+    uint16_t* dst = pages + static_cast<int64_t>(id) * 16 * tok_stride + col;
+    // the copied rows (none without a copy), then the new token's row
+    for (int r0 = cow ? 0 : row; r0 <= row; r0 += RPI) {
+      const int r = r0 + sub;
+      if (r <= row) {
+        const uint16_t* from = r == row ? (is_v ? a.v_new : a.k_new) + static_cast<int64_t>(b) * tok_stride + col
+                                        : pages + static_cast<int64_t>(src) * 16 * tok_stride + r * tok_stride + col;
+        st16(dst + r * tok_stride, ld16(from));
+      }
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   constexpr int LPH = D / 8;     // lanes per query head
@@ -942,6 +977,7 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
   const int b = blockIdx.x / groups;
   const int h = (blockIdx.x % groups) * HPP + lane / LPH;
   const int c = lane % LPH;
+  if (a.k_new) append_row_tail<D>(a, b, (blockIdx.x % groups) * HPP, HPP, lane);
   if (h >= a.num_q_heads) return;
   int begin = 0, depth = 0;
   if (a.row_info) {

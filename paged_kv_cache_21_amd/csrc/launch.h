@@ -107,6 +107,16 @@ struct MergeArgs {
   int32_t max_seq_len;
   int32_t slots;
   int32_t* status;  // optional device word: PKV_STATUS_LEN_CLAMPED is or-ed in for lengths outside [0, limit]
+  // One-launch append (k_new non-null): after every read of the call, each row's new token
+  // (token len - 1) and, when its last block was copied on write, rows [0, its row) of the
+  // copy's source are written into the row's own last block (16-bit pages).
+  uint16_t* k_pages = nullptr;
+  uint16_t* v_pages = nullptr;
+  const int32_t* block_tables = nullptr;
+  const uint16_t* k_new = nullptr;  // [batch][num_kv_heads][D]
+  const uint16_t* v_new = nullptr;
+  const int32_t* cow_src = nullptr;  // per row: copy-on-write source of the last block, or -1
+  int64_t num_blocks = 0;
 };
 
 // Shared-prefix (cascade) pass over the plan's work items.
