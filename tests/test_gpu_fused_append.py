@@ -44,8 +44,9 @@ def _forest(rng, ref, lib, roots, forks, max_len):
 
 
 @pytest.mark.parametrize("plan_on", [False, True], ids=["split", "cascade"])
-@pytest.mark.parametrize("shape", [("bf16", 32, 8, 128), ("f16", 8, 8, 64), ("bf16", 8, 2, 64)],
-                         ids=["bf16-g4-d128", "f16-g1-d64", "bf16-g4-d64"])
+@pytest.mark.parametrize("shape", [("bf16", 32, 8, 128), ("f16", 8, 8, 64), ("bf16", 8, 2, 64), ("bf16", 32, 4, 128),
+                                   ("f16", 16, 8, 128)],
+                         ids=["bf16-g4-d128", "f16-g1-d64", "bf16-g4-d64", "bf16-g8-d128", "f16-g2-d128"])
 @pytest.mark.parametrize("seed", range(2))
 def test_fused_append_matches_oracle(pkv, seed, shape, plan_on):
     torch = __import__("torch")
