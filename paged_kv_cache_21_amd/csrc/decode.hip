@@ -1076,13 +1076,26 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     return;
   }
   const int t = blockIdx.x - a.num_cow;
-  const int64_t slot = a.slot_mapping[t];
-  if (slot < 0 || slot >= a.num_blocks * a.block_size) return;
   const u32x4* kn = reinterpret_cast<const u32x4*>(a.k_new) + static_cast<int64_t>(t) * vec_per_row;
   const u32x4* vn = reinterpret_cast<const u32x4*>(a.v_new) + static_cast<int64_t>(t) * vec_per_row;
+  // The token's first vectors are read together with its slot (they do not depend on it;
+  // a clamped index keeps the loads unconditional), so the launch pays one round of
+  // memory latency before its stores instead of two.
+  const int64_t i0 = threadIdx.x;
+  const int64_t ic = i0 < vec_per_row ? i0 : vec_per_row - 1;
+  const u32x4 k0 = kn[ic], v0 = vn[ic];
+  const int64_t slot = a.slot_mapping[t];
+  // an empty asm taking the values keeps the loads ahead of the slot test (the compiler
+  // would otherwise sink them past it and wait for the slot first)
+  asm volatile("" ::"v"(k0.x), "v"(k0.y), "v"(k0.z), "v"(k0.w), "v"(v0.x), "v"(v0.y), "v"(v0.z), "v"(v0.w));
+  if (slot < 0 || slot >= a.num_blocks * a.block_size) return;
   u32x4* kd = reinterpret_cast<u32x4*>(a.k_pages) + slot * vec_per_row;
   u32x4* vd = reinterpret_cast<u32x4*>(a.v_pages) + slot * vec_per_row;
-  for (int64_t i = threadIdx.x; i < vec_per_row; i += blockDim.x) {
+  if (i0 < vec_per_row) {
+    kd[i0] = k0;
+    vd[i0] = v0;
+  }
+  for (int64_t i = i0 + blockDim.x; i < vec_per_row; i += blockDim.x) {
     kd[i] = kn[i];
     vd[i] = vn[i];
   }
