@@ -212,6 +212,28 @@ def test_mha70b_all_rows(pkv):
     assert err <= ATOL
 
 
+def test_long_shared_prefix_wide_pieces(pkv):
+    """Two MHA rows (64 heads, d 128) sharing a ~32K-token prefix: the decode plan cuts the
+    shared node into pieces of more than 64 blocks, so the matrix-core pass keeps the
+    piece's block ids in four 64-lane registers; parity with the cascade on and off."""
+    w = workloads.random_forest(11, num_rows=2, max_len=33000, dtype="f16", num_q_heads=64, num_kv_heads=64,
+                                head_dim=128, share_prob=1.0, min_len=32768)
+    pool, k_pages, v_pages, bt, lens, q = setup_workload(w)
+    got_off, _ = run_decode(pkv, w, q, k_pages, v_pages, bt, lens, False)
+    got_on, plan = run_decode(pkv, w, q, k_pages, v_pages, bt, lens, True)
+    assert plan.num_nodes == 1
+    blocks = len(plan.node(0)[0])
+    pieces = plan.node_pieces(0)
+    piece_blocks = -(-blocks // pieces)
+    say(f"wide pieces: {blocks} shared blocks in {pieces} pieces of {piece_blocks}")
+    assert piece_blocks > 64
+    t0 = time.perf_counter()
+    ref = oracle_rows(q, k_pages, v_pages, bt, lens, [0, 1], w.scale, "f16")
+    err_on, err_off = max_err(got_on, ref), max_err(got_off, ref)
+    say(f"  max_err cascade on {err_on:.3e} off {err_off:.3e}, oracle {time.perf_counter() - t0:.1f} s")
+    assert err_on <= ATOL and err_off <= ATOL
+
+
 def test_radix_tree_build_state(pkv):
     w = workloads.get(5)
     pool, k_pages, v_pages, bt, lens, q = setup_workload(w)
