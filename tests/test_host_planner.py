@@ -178,3 +178,23 @@ def test_plan_image_indices_in_bounds(seed, extend):
         plan = pkv.CascadePlan(bt, lens, 16, 4)
     items, written = check_plan_image(plan, 16, 4, w.num_blocks)
     assert items > 0 and written > 0
+
+
+@pytest.mark.parametrize("cfg,extend_tokens", [(5, 0), (3, 8), (6, 4096)])
+def test_plan_image_full_size_workloads(cfg, extend_tokens):
+    """The same bounds and write-once checks on plans at full size: the radix-tree decode step
+    (more work items than one wave of work-groups), tree verify (8 query tokens per branch) and
+    chunked prefill (4,096 query tokens per row)."""
+    from plan_checks import check_plan_image
+
+    w = workloads.get(cfg)
+    ref = oracle.RefPool(w.num_blocks, w.block_size, w.free_order)
+    workloads.replay(ref, w.build_ops, allow_cow=True)
+    bt, lens = ref.export_tables(w.steps[0].decode_rows, w.max_blocks)
+    if extend_tokens:
+        q_lens = np.minimum(lens, extend_tokens).astype(np.int32)
+        plan = pkv.ExtendPlan(bt, lens, q_lens, w.num_q_heads, w.num_kv_heads)
+    else:
+        plan = pkv.CascadePlan(bt, lens, w.num_q_heads, w.num_kv_heads)
+    items, written = check_plan_image(plan, w.num_q_heads, w.num_kv_heads, w.num_blocks)
+    assert items > 256 and written > 0
