@@ -511,8 +511,7 @@ pkv_status pkv_plan_row(const pkv_plan* plan, int32_t row, int32_t* shared_token
  *   - an appended token's head vector x is stored as round-to-nearest-even(x / 2^k)
  *     (exact scaling, then the nearest E4M3 value, ties to even), so appending never
  *     re-quantizes earlier rows.
- * Halves the KV bytes the decode streams.  The cascade and extend passes take
- * 16-bit pages only.
+ * Halves the KV bytes the decode streams.
  * ---------------------------------------------------------------------------------------- */
 
 /* As pkv_kv_append, for FP8 pages: copy-on-write copies codes and scales of rows
@@ -529,9 +528,10 @@ pkv_status pkv_kv_append_fp8(void* k_pages, void* v_pages, float* k_scales, floa
  * q is q_dtype (PKV_F16 or PKV_BF16) and the arithmetic is that of the 16-bit path
  * (every E4M3 value is exact in both 16-bit types).  With a cascade plan the shared
  * blocks go through the matrix-core pass, their codes widened to q's type in LDS, the
- * K scale applied to each score and the V scale folded into each weight; the scales
- * must then be 16-byte aligned (else 4).  Workspace: pkv_decode_workspace_bytes(...,
- * plan).  Errors as pkv_paged_decode_attn. */
+ * K scale applied to each score and the V scale folded into each weight.  The scale
+ * arrays must be 16-byte aligned (a token group's four scales are read as one
+ * vector).  Workspace: pkv_decode_workspace_bytes(..., plan).  Errors as
+ * pkv_paged_decode_attn. */
 pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t q_dtype, const void* k_pages, const void* v_pages,
                                      const float* k_scales, const float* v_scales, int64_t num_blocks,

@@ -423,8 +423,8 @@ pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q
   if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "pkv_paged_decode_attn_fp8: q dtype %d", q_dtype);
   if (batch > 0 && (!k_scales || !v_scales)) return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: null scales");
-  if ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & (plan ? 15u : 3u))
-    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: scales must be 4-byte aligned (16 with a plan)");
+  if ((reinterpret_cast<uintptr_t>(k_scales) | reinterpret_cast<uintptr_t>(v_scales)) & 15u)
+    return fail(PKV_ERR_INVALID, "pkv_paged_decode_attn_fp8: scales must be 16-byte aligned");
   return decode_impl(2 + q_dtype, q, batch, num_q_heads, num_kv_heads, head_dim, k_pages, v_pages, k_scales, v_scales,
                      num_blocks, block_size, block_tables, max_blocks_per_seq, seq_lens, max_seq_len, scale, plan,
                      workspace, workspace_bytes, out, status, stream);

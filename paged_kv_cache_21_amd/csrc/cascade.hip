@@ -39,29 +39,6 @@ namespace pkv {
 
 namespace {
 
-template <class DT>
-__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c);
-
-template <>
-__device__ __forceinline__ f32x4 mfma16x16x32<BF16>(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
-                                                 0, 0);
-}
-
-template <>
-__device__ __forceinline__ f32x4 mfma16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
-                                                0);
-}
-
-// 4 x 16-bit transpose read from LDS (gfx950 ds_read_b64_tr_b16): see the V^T
-// operand reads for the lane mapping
-typedef short s16x4 __attribute__((vector_size(8)));
-__device__ __forceinline__ u32x2 tr_read16(const uint16_t* p) {
-  return __builtin_bit_cast(
-      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p)));
-}
-
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
   return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
 }

@@ -328,6 +328,12 @@ __device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64
 #define PKV_SPLIT_STAGE 1
 #endif
 
+// Matrix-core instances (head_dim 128, GQA group 4 or 8, not fused): q.k and the PV
+// update on MFMA instead of the VALU (1), or the VALU path for every shape (0).
+#ifndef PKV_SPLIT_MFMA
+#define PKV_SPLIT_MFMA 1
+#endif
+
 #ifndef PKV_SPLIT_WAVES_PER_EU
 #define PKV_SPLIT_WAVES_PER_EU 1
 #endif
@@ -344,8 +350,38 @@ __device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64
 // then writes those rows and the new token into the row's own block.  Reads never
 // depend on this launch's writes (no other segment reads a row's last block: it is
 // private to the row), so no wave waits for another.
+// Whether an instance takes the matrix-core path (see the kernel).
+template <int D, int G, int LPT, bool FUSED>
+constexpr bool split_mfma() {
+  return PKV_SPLIT_MFMA != 0 && !FUSED && D == 128 && (G == 4 || G == 8) && LPT == 16;
+}
+
+// Register pipeline depth of the matrix-core instances (a third block in flight
+// measured slower).
+#ifndef PKV_SPLIT_MFMA_NBUF
+#define PKV_SPLIT_MFMA_NBUF 2
+#endif
+
+// Waves per SIMD of the matrix-core instances: three for FP8 pages (their blocks are
+// half the bytes, so more of them must be in flight), two for 16-bit pages (three
+// measured slower, as for the VALU instances), two for G = 8 (registers).
+#ifndef PKV_SPLIT_MFMA_WAVES_FP8
+#define PKV_SPLIT_MFMA_WAVES_FP8 3
+#endif
+#ifndef PKV_SPLIT_MFMA_WAVES16
+#define PKV_SPLIT_MFMA_WAVES16 2
+#endif
 template <class DT, int D, int G, int LPT, bool FUSED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 : is_fp8<DT>::value ? 3 : PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
+constexpr int split_mfma_waves() {
+  return G >= 8 ? 2 : is_fp8<DT>::value ? PKV_SPLIT_MFMA_WAVES_FP8 : PKV_SPLIT_MFMA_WAVES16;
+}
+
+template <class DT, int D, int G, int LPT, bool FUSED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
+    split_mfma<D, G, LPT, FUSED>() ? split_mfma_waves<DT, D, G, LPT, FUSED>()
+    : G >= 8                       ? 1
+    : is_fp8<DT>::value            ? 3
+                                   : PKV_SPLIT_WAVES_PER_EU))) void decode_split_kernel(SplitArgs a) {
   typedef typename is_fp8<DT>::compute CT;  // type of q and of the dot products
   constexpr bool Q8 = is_fp8<DT>::value;
   constexpr int EB = Q8 ? 1 : 2;  // bytes per stored element
@@ -354,10 +390,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   constexpr int VPL = D / (8 * LPT);  // 8-element vectors per token per lane
   constexpr int TPB = 16 / ROWS;      // tokens per lane per 16-token block
   static_assert(VPL >= 1 && TPB >= 1 && ROWS * TPB == 16, "unsupported lane split");
+  // Matrix-core instance: the block's K and V are loaded as in the VALU path (each
+  // load instruction covers 4 whole token rows) and written token-major to a per-wave
+  // LDS tile.  Then S^T = K q^T on v_mfma_f32_16x16x32 (K read back as the A
+  // operand: lane l holds token l % 16, dims 32 t + 8 (l / 16) .. + 7 of slice t; q
+  // is the B operand, one column per query head of the group, read from LDS too),
+  // the online softmax on the accumulator (lane l holds the scores of tokens
+  // 4 (l / 16) .. + 3 for head l % 16), and O^T += V^T P^T on v_mfma_f32_16x16x32
+  // (V read back transposed; P^T is the score accumulator's layout, as two 16-bit
+  // terms p = p_hi + p_lo so the weights keep ~16 bits).  Loading K straight into
+  // the A layout instead makes every load instruction touch 16 token rows in 64-byte
+  // (FP8: 32-byte) pieces, which measured 10-30 % slower.
+  constexpr bool MF = split_mfma<D, G, LPT, FUSED>();
+  constexpr int NDT = D / 16;  // 16-wide d tiles of the MF accumulator
 
   const int lane = threadIdx.x;
   const int r = lane / LPT;
   const int c = lane % LPT;
+  const int lgrp = lane >> 4;  // MF: MFMA k group
+  const int lrow = lane & 15;  // MF: MFMA row / column
   const int Hkv = a.num_kv_heads;
   const int w = blockIdx.x;
 
@@ -398,6 +449,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
     return t[static_cast<int64_t>(row) * a.max_blocks + col];
   };
   auto load_q = [&](const Cursor& p, u32x4(&qq)[G][VPL]) {
+    if constexpr (MF) {  // qq[k][0]: head 4 k + l / 16, dims 8 (l % 16) .. + 7 (one 16-byte load per 4 heads)
+      const uint16_t* qh = a.q + (static_cast<int64_t>(p.b) * a.num_q_heads + p.h * G + lgrp) * D + 8 * lrow;
+#pragma unroll
+      for (int k = 0; k < G / 4; ++k) qq[k][0] = ld16(qh + 4 * k * D);
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const uint16_t* qh = a.q + (static_cast<int64_t>(p.b) * a.num_q_heads + p.h * G + g) * D + c * 8;
@@ -408,7 +465,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   // FP8 scales the lane needs per block: the reduce-scatter path owns one token's
   // scores (token r + (c / G) * ROWS), the other path all TPB of its tokens
   constexpr bool RS = LPT == 16 && TPB * G == 16;
-  constexpr int NS = RS ? 1 : TPB;
+  constexpr int NS = MF ? 4 : RS ? 1 : TPB;  // MF: tokens 4 (l / 16) .. + 3
   // FUSED, per pipeline buffer: the new token of the block's row when the block is
   // the row's last (dst >= 0: its id; row: the token's row in it; cow: rows before it
   // were read from the copy-on-write source), with the lane's part of its K/V
@@ -459,11 +516,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
     }
     if constexpr (Q8) {
       const int64_t sbase = (static_cast<int64_t>(ok ? id : 0) * Hkv + h) * 16;
+      if constexpr (MF) {  // tokens 4 (l / 16) .. + 3: one 16-byte load each (scales are 16-byte aligned)
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(a.k_scales + sbase + 4 * lgrp);
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(a.v_scales + sbase + 4 * lgrp);
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        const int row = r + (RS ? c / G : t) * ROWS;
-        ks[t] = a.k_scales[sbase + row];
-        vs[t] = a.v_scales[sbase + row];
+        for (int t = 0; t < NS; ++t) {
+          ks[t] = k4[t];
+          vs[t] = v4[t];
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          const int row = r + (RS ? c / G : t) * ROWS;
+          ks[t] = a.k_scales[sbase + row];
+          vs[t] = a.v_scales[sbase + row];
+        }
       }
     }
     return ok;
@@ -477,7 +544,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   // (RS and NS are defined with load_block.)
   float m[G], l[G], acc[G][VPL * 8];
   float m1 = kNegInf, l1 = 0.f;  // reduce-scatter state: head c % G of this token row
+                                 // (MF: head lrow; l1 sums this lane's tokens only)
+  f32x4 o[MF ? NDT : 1];         // MF: O^T tiles, lane l holds dims 16 dt + 4 (l / 16) .. + 3 of head lrow
   auto reset_state = [&]() {
+    if constexpr (MF) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m1 = kNegInf;
+      l1 = 0.f;
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       m[g] = kNegInf;
@@ -591,8 +667,81 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
     }
   };
 
+  // MF: one token-major tile holds the block's K, then its V (written once K's
+  // operand reads are issued: a wave's LDS operations run in order); its row pitch
+  // spreads a half-wave's transpose reads over distinct banks.  q_lds holds the
+  // block's G query heads, read as the B operand with column h taking head h % G (the
+  // columns past G repeat real heads: finite, and never stored).
+  constexpr int VPITCH = D + 16;
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[MF ? 16 * VPITCH : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[MF ? G * D : 8];
+  auto consume_mf = [&](bool ok, const u32x4(&qv)[G][VPL], KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL],
+                        const float(&ks)[NS], const float(&vs)[NS]) {
+    mask_values(ok, vv);
+#pragma unroll
+    for (int k = 0; k < G / 4; ++k) *reinterpret_cast<u32x4*>(&q_lds[(4 * k + lgrp) * D + 8 * lrow]) = qv[k][0];
+#pragma unroll
+    for (int t = 0; t < TPB; ++t) *reinterpret_cast<u32x4*>(&kv_lds[(r + t * ROWS) * VPITCH + c * 8]) = as16(kk[t][0]);
+    // (one wave's LDS operations run in order, so the reads below see these writes)
+    u32x4 ka[D / 32], qb[D / 32];
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      ka[t] = *reinterpret_cast<const u32x4*>(&kv_lds[lrow * VPITCH + 32 * t + 8 * lgrp]);
+      qb[t] = *reinterpret_cast<const u32x4*>(&q_lds[(lrow % G) * D + 32 * t + 8 * lgrp]);
+    }
+#pragma unroll
+    for (int t = 0; t < TPB; ++t) *reinterpret_cast<u32x4*>(&kv_lds[(r + t * ROWS) * VPITCH + c * 8]) = as16(vv[t][0]);
+    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) st = mfma16x16x32<CT>(ka[t], qb[t], st);
+    float sv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sv[j] = st[j] * (Q8 ? a.scale_log2 * ks[j] : a.scale_log2);
+    const int tok0 = (cur.blk0 + cur.j) * 16;
+    if (!ok || tok0 + 16 > cur.len) {  // uniform: only a row's last block can be partial
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sv[j] = ok && tok0 + 4 * lgrp + j < cur.len ? sv[j] : kNegInf;
+    }
+    const float lmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    // rescale only past 2^8 (as in the VALU paths); the column's max over its four
+    // lane groups is needed only then
+    if (__any(lmax > m1 + 8.f)) {
+      float cm = xor_max<16>(lmax);
+      cm = xor_max<32>(cm);
+      const float mn = fmaxf(m1, cm);
+      const float alpha = exp2_diff(m1, mn);
+      l1 *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      m1 = mn;
+    }
+    const float mref = fmaxf(m1, -3.0e38f);
+    float pw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p = fast_exp2(sv[j] - mref);
+      l1 += p;
+      pw[j] = Q8 ? (p == 0.f ? 0.f : p * vs[j]) : p;  // FP8: the token's V scale
+    }
+    // One 16x16x32 product per d tile takes both terms: k slots 8 (l / 16) .. + 3 hold
+    // tokens 4 (l / 16) .. + 3 with p_hi, slots + 4 .. + 7 the same tokens with p_lo.
+    const uint32_t h0 = CT::pack2(pw[0], pw[1]), h1 = CT::pack2(pw[2], pw[3]);
+    const u32x4 bp = u32x4{h0, h1, CT::pack2(pw[0] - CT::lo(h0), pw[1] - CT::hi(h0)),
+                           CT::pack2(pw[2] - CT::lo(h1), pw[3] - CT::hi(h1))};
+    const uint16_t* vp = &kv_lds[(4 * lgrp + (lrow >> 2)) * VPITCH + 4 * (lrow & 3)];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const u32x2 av = tr_read16(vp + dt * 16);  // V^T rows 16 dt + lrow, tokens 4 (l / 16) .. + 3
+      o[dt] = mfma16x16x32<CT>(u32x4{av.x, av.y, av.x, av.y}, bp, o[dt]);
+    }
+  };
+
   auto consume_block = [&](bool ok, const u32x4(&qv)[G][VPL], KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL],
                            const float(&ks)[NS], const float(&vs)[NS], const NewTok& nt) {
+    if constexpr (MF) {
+      consume_mf(ok, qv, kk, vv, ks, vs);
+      return;
+    }
     if constexpr (FUSED) {
       if (nt.dst >= 0) {  // uniform: the new token replaces its row (the merge kernel stores it)
 #pragma unroll
@@ -714,7 +863,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   // counter and holds up the next block's wait); pieces beyond kStage are stored
   // directly.
   constexpr bool STAGE = PKV_SPLIT_STAGE != 0;
-  constexpr int kStage = G >= 8 ? 3 : G == 4 ? 6 : G == 2 ? 10 : 16;
+  // (MF with FP8 pages: three waves per SIMD leave LDS for fewer staged pieces)
+  constexpr int kStage = MF ? (G >= 8 ? (Q8 ? 1 : 2) : Q8 ? 3 : 6) : G >= 8 ? 3 : G == 4 ? 6 : G == 2 ? 10 : 16;
   __shared__ __attribute__((aligned(16))) float stg_acc[STAGE ? kStage : 1][G][D];
   __shared__ float2 stg_ml[STAGE ? kStage : 1][G];
   __shared__ int4 stg_meta[STAGE ? kStage : 1];
@@ -725,6 +875,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   // both rows of a pair compute the same combination of (lower, upper), so every
   // row ends with the same merged state.
   auto finish_segment = [&]() {
+    if constexpr (MF) {
+      // the column's weight sum over its four lane groups (m1 is already common to them)
+      float la, lb;
+      pair_values<16>(l1, la, lb);
+      l1 = la + lb;
+      pair_values<32>(l1, la, lb);
+      l1 = la + lb;
+      const int64_t first_wave = cur.seg / chunk;
+      const int k = static_cast<int>(w - first_wave);
+      const int64_t rec0 = (static_cast<int64_t>(cur.b) * a.slots + cur.depth + k) * a.num_q_heads + cur.h * G;
+      const int cnt = k == 0 ? static_cast<int>((cur.seg + cur.nb - 1) / chunk - first_wave + 1) : 0;
+      const int cidx = cur.b * Hkv + cur.h;
+      if (STAGE && nst < kStage) {  // uniform
+        if (lrow < G) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            *reinterpret_cast<f32x4*>(&stg_acc[nst][lrow][16 * dt + 4 * lgrp]) = o[dt];
+          if (lgrp == 0) stg_ml[nst][lrow] = make_float2(m1, l1);
+        }
+        if (lane == 0) stg_meta[nst] = make_int4(static_cast<int>(rec0), static_cast<int>(rec0 >> 32), cnt, cidx);
+        ++nst;
+        return;
+      }
+      if (lrow < G) {
+        float* dst = a.acc + (rec0 + lrow) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<float4*>(dst + 16 * dt + 4 * lgrp) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+        if (lgrp == 0) a.ml[rec0 + lrow] = make_float2(m1, l1);
+      }
+      if (cnt > 0 && lane == 0) a.counts[cidx] = cnt;
+      return;
+    }
     if constexpr (RS) {
       // the row's weight sum of head c % G: over the lanes c, c-4, c-8, c-12
       l1 += dpp_f32<kDppRowRor4>(l1);
@@ -854,7 +1037,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 1 :
   // assume the worst of two paths, which would make the wave wait for loads it
   // does not need.  (Separately named buffers, not an indexed array of them: the
   // compiler keeps those in registers.)
-  constexpr int NBUF = Q8 ? 2 : (G <= 4 ? PKV_SPLIT_NBUF16 : 2);
+  constexpr int NBUF = MF ? PKV_SPLIT_MFMA_NBUF : Q8 ? 2 : (G <= 4 ? PKV_SPLIT_NBUF16 : 2);
   KV ka[TPB][VPL], va[TPB][VPL], kb[TPB][VPL], vb[TPB][VPL], kx[TPB][VPL], vx[TPB][VPL];
   float ksa[NS], vsa[NS], ksb[NS], vsb[NS], ksx[NS], vsx[NS];
   u32x4 qa[G][VPL], qb[G][VPL], qx[G][VPL];
@@ -1271,7 +1454,9 @@ int split_waves_t() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_ptr<DT, D, G, FUSED>(), 64, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 8;
-  per_cu = std::min(per_cu, 4 * split_max_waves_per_simd(G));
+  constexpr int LPT = D == 128 ? PKV_LPT_D128 : 8;
+  constexpr bool mf = split_mfma<D, G, LPT, FUSED && can_fuse<DT>()>();
+  per_cu = std::min(per_cu, 4 * (mf ? split_mfma_waves<DT, D, G, LPT, false>() : split_max_waves_per_simd(G)));
   cache[dev] = cus * per_cu;
   return cache[dev];
 }

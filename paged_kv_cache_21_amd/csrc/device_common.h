@@ -231,6 +231,35 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // exp2(a - b) with exp2(-inf - anything) = 0 (an empty running state has m = -inf)
 __device__ __forceinline__ float exp2_diff(float a, float b) { return a == kNegInf ? 0.f : fast_exp2(a - b); }
 
+// Matrix-core product D = A B + C on a 16 x 16 tile with k = 32 (lane l, element j of
+// 8: A row l % 16, k = 8 (l / 16) + j; B column l % 16, same k; accumulator element j
+// of lane l is row 4 (l / 16) + j, column l % 16).
+template <class DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c);
+
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<BF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 4 x 16-bit transpose read from LDS (gfx950 ds_read_b64_tr_b16).  In each 16-lane
+// group, lane 4 j + q supplies the address of row j's 4 consecutive 16-bit values
+// (columns 4 q .. 4 q + 3 of a 16-column tile), and lane 4 q + e receives column
+// 4 q + e of rows 0 .. 3: a row-major 4 x 16 tile comes back column by column.
+__device__ __forceinline__ u32x2 tr_read16(const uint16_t* p) {
+  return __builtin_bit_cast(u32x2,
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p)));
+}
+
 // 16-byte global load / store helpers
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
