@@ -671,15 +671,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   // operand reads are issued: a wave's LDS operations run in order); its row pitch
   // spreads a half-wave's transpose reads over distinct banks.  q_lds holds the
   // block's G query heads, read as the B operand with column h taking head h % G (the
-  // columns past G repeat real heads: finite, and never stored).
+  // columns past G repeat real heads: finite, and never stored); its padded rows put
+  // the heads' reads on different banks.
   constexpr int VPITCH = D + 16;
+  constexpr int QPITCH = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[MF ? 16 * VPITCH : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[MF ? G * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[MF ? G * QPITCH : 8];
   auto consume_mf = [&](bool ok, const u32x4(&qv)[G][VPL], KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL],
                         const float(&ks)[NS], const float(&vs)[NS]) {
     mask_values(ok, vv);
 #pragma unroll
-    for (int k = 0; k < G / 4; ++k) *reinterpret_cast<u32x4*>(&q_lds[(4 * k + lgrp) * D + 8 * lrow]) = qv[k][0];
+    for (int k = 0; k < G / 4; ++k) *reinterpret_cast<u32x4*>(&q_lds[(4 * k + lgrp) * QPITCH + 8 * lrow]) = qv[k][0];
 #pragma unroll
     for (int t = 0; t < TPB; ++t) *reinterpret_cast<u32x4*>(&kv_lds[(r + t * ROWS) * VPITCH + c * 8]) = as16(kk[t][0]);
     // (one wave's LDS operations run in order, so the reads below see these writes)
@@ -687,7 +689,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
       ka[t] = *reinterpret_cast<const u32x4*>(&kv_lds[lrow * VPITCH + 32 * t + 8 * lgrp]);
-      qb[t] = *reinterpret_cast<const u32x4*>(&q_lds[(lrow % G) * D + 32 * t + 8 * lgrp]);
+      qb[t] = *reinterpret_cast<const u32x4*>(&q_lds[(lrow % G) * QPITCH + 32 * t + 8 * lgrp]);
     }
 #pragma unroll
     for (int t = 0; t < TPB; ++t) *reinterpret_cast<u32x4*>(&kv_lds[(r + t * ROWS) * VPITCH + c * 8]) = as16(vv[t][0]);
