@@ -328,10 +328,15 @@ __device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64
 #define PKV_SPLIT_STAGE 1
 #endif
 
-// Matrix-core instances (head_dim 128, GQA group 4 or 8, not fused): q.k and the PV
+// Matrix-core instances (head_dim 128, GQA group 4 or 8): q.k and the PV
 // update on MFMA instead of the VALU (1), or the VALU path for every shape (0).
 #ifndef PKV_SPLIT_MFMA
 #define PKV_SPLIT_MFMA 1
+#endif
+// ... and for the one-launch append + decode instances too (their new-token rows are
+// substituted in the load layout, before the block goes to LDS)
+#ifndef PKV_SPLIT_MFMA_FUSED
+#define PKV_SPLIT_MFMA_FUSED 1
 #endif
 
 #ifndef PKV_SPLIT_WAVES_PER_EU
@@ -353,7 +358,8 @@ __device__ __forceinline__ bool find_start_scan(const SplitArgs& a, int w, int64
 // Whether an instance takes the matrix-core path (see the kernel).
 template <int D, int G, int LPT, bool FUSED>
 constexpr bool split_mfma() {
-  return PKV_SPLIT_MFMA != 0 && !FUSED && D == 128 && (G == 4 || G == 8) && LPT == 16;
+  return PKV_SPLIT_MFMA != 0 && (!FUSED || PKV_SPLIT_MFMA_FUSED != 0) && D == 128 && (G == 4 || G == 8) &&
+         LPT == 16;
 }
 
 // Register pipeline depth of the matrix-core instances (a third block in flight
@@ -740,10 +746,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
 
   auto consume_block = [&](bool ok, const u32x4(&qv)[G][VPL], KV(&kk)[TPB][VPL], KV(&vv)[TPB][VPL],
                            const float(&ks)[NS], const float(&vs)[NS], const NewTok& nt) {
-    if constexpr (MF) {
-      consume_mf(ok, qv, kk, vv, ks, vs);
-      return;
-    }
     if constexpr (FUSED) {
       if (nt.dst >= 0) {  // uniform: the new token replaces its row (the merge kernel stores it)
 #pragma unroll
@@ -758,6 +760,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
           }
         }
       }
+    }
+    if constexpr (MF) {
+      consume_mf(ok, qv, kk, vv, ks, vs);
+      return;
     }
     mask_values(ok, vv);
     float sc[TPB][G];
@@ -1458,7 +1464,7 @@ int split_waves_t() {
     per_cu = 8;
   constexpr int LPT = D == 128 ? PKV_LPT_D128 : 8;
   constexpr bool mf = split_mfma<D, G, LPT, FUSED && can_fuse<DT>()>();
-  per_cu = std::min(per_cu, 4 * (mf ? split_mfma_waves<DT, D, G, LPT, false>() : split_max_waves_per_simd(G)));
+  per_cu = std::min(per_cu, 4 * (mf ? split_mfma_waves<DT, D, G, LPT, FUSED>() : split_max_waves_per_simd(G)));
   cache[dev] = cus * per_cu;
   return cache[dev];
 }
