@@ -65,7 +65,10 @@ struct Cursor {
 // waves whose share falls on many short segments get correspondingly fewer blocks.
 // (Measured on 1,024 rows with the tree-search suffix lengths: equal shares of blocks
 // left the waves on short rows about 7 % behind.)
-constexpr int kSegUnits = 1;
+#ifndef PKV_SPLIT_SEG_UNITS
+#define PKV_SPLIT_SEG_UNITS 1
+#endif
+constexpr int kSegUnits = PKV_SPLIT_SEG_UNITS;
 
 // position of the block after c's in the work order (the next segment's block 0 when
 // c holds its segment's last block)

@@ -407,3 +407,54 @@ def test_status_word_reports_clamped_lengths_and_bad_ids(pkv):
                           plan=bad_plan, dtype=w.dtype, status=status)
     torch.cuda.synchronize()
     assert int(status.item()) == pkv.STATUS_BAD_BLOCK
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["decode", "append-decode"])
+def test_status_word_matrix_core_path(pkv, fused):
+    """The same out-of-domain handling on the matrix-core instances (head_dim 128, GQA 4): a length
+    above max_seq_len is clamped and reported, an own block id outside the pool is reported and read
+    at zero weight without touching the other rows; in-domain calls report nothing."""
+    torch = __import__("torch")
+    w = workloads.random_forest(6, num_rows=9, max_len=700, dtype="bf16", num_q_heads=32, num_kv_heads=8,
+                                head_dim=128, share_prob=0.0, min_len=100)
+    pool, k_pages, v_pages, bt, lens, q = setup_workload(w)
+    k_host, v_host, q_host = bits_np(k_pages), bits_np(v_pages), bits_np(q)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def call(tables, cut):
+        status.zero_()
+        bt_d, lens_d = tables_to_device(tables, lens)
+        if fused:  # the new token is already in the pages: append it again, unchanged, in the same call
+            slots = np.array([int(tables[b, (lens[b] - 1) // 16]) * 16 + (lens[b] - 1) % 16
+                              if 0 <= tables[b, (lens[b] - 1) // 16] < w.num_blocks else -1
+                              for b in range(len(lens))], dtype=np.int64)
+            kv = k_pages.view(-1, w.num_kv_heads, w.head_dim)
+            vv = v_pages.view(-1, w.num_kv_heads, w.head_dim)
+            safe = torch.from_numpy(np.maximum(slots, 0)).cuda()
+            k_new, v_new = kv[safe].contiguous(), vv[safe].contiguous()
+            cow = torch.full((len(lens),), -1, dtype=torch.int32, device="cuda")
+            out = pkv.paged_decode_attn_append(q, k_pages, v_pages, bt_d, lens_d, cut, k_new, v_new, cow,
+                                               scale=w.scale, dtype=w.dtype, status=status)
+        else:
+            out = pkv.paged_decode_attn(q, k_pages, v_pages, bt_d, lens_d, cut, scale=w.scale, dtype=w.dtype,
+                                        status=status)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), int(status.item())
+
+    ref = oracle.ref_decode(q_host, k_host, v_host, bt, lens, w.scale, w.dtype)
+    out, st = call(bt, int(lens.max()))
+    assert st == 0 and max_err(out, ref) <= ATOL
+    cut = int(np.sort(lens)[len(lens) // 2])
+    if not fused:  # (the one-launch call appends nothing for rows past max_seq_len)
+        out, st = call(bt, cut)
+        assert st == pkv.STATUS_LEN_CLAMPED
+        ref_cut = oracle.ref_decode(q_host, k_host, v_host, bt, np.minimum(lens, cut), w.scale, w.dtype)
+        assert max_err(out, ref_cut) <= ATOL
+    bad = bt.copy()
+    b_bad = int(np.argmax(lens))
+    bad[b_bad, 1] = w.num_blocks + 3
+    out, st = call(bad, int(lens.max()))
+    assert st == pkv.STATUS_BAD_BLOCK
+    keep = [b for b in range(len(lens)) if b != b_bad]
+    assert max_err(out[keep], ref[keep]) <= ATOL
+    assert np.all(np.isfinite(out[b_bad]))
