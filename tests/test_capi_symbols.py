@@ -117,3 +117,18 @@ def test_fused_append_refuses_a_plan_with_a_shared_last_token():
     st = lib.pkv_paged_decode_attn_append(None, 2, 2, 2, 64, 5, None, None, 4, 16, None, 2, None, 32, None, None,
                                           None, 1.0, None, None, 0, None, None, None)
     assert st == -4
+
+
+def test_fp8_decode_refuses_misaligned_scales():
+    """pkv_paged_decode_attn_fp8 reads each lane's four token scales as one 16-byte vector, so
+    scale arrays that are not 16-byte aligned are refused on the host, with or without a plan,
+    before any pointer is used; null scales are refused too."""
+    lib = pkv.lib()
+    fake = 4096  # 16-byte aligned
+    for ks, vs in ((fake + 4, fake), (fake, fake + 8), (fake + 12, fake + 12)):
+        st = lib.pkv_paged_decode_attn_fp8(fake, 2, 8, 2, 128, 1, fake, fake, ks, vs, 4, 16, fake, 2, fake, 32, 1.0,
+                                           None, fake, 1 << 20, fake, None, None)
+        assert st == -1 and b"16-byte aligned" in lib.pkv_last_error(), lib.pkv_last_error()
+    st = lib.pkv_paged_decode_attn_fp8(fake, 2, 8, 2, 128, 1, fake, fake, None, fake, 4, 16, fake, 2, fake, 32, 1.0,
+                                       None, fake, 1 << 20, fake, None, None)
+    assert st == -1 and b"null scales" in lib.pkv_last_error()
