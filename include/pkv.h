@@ -528,8 +528,11 @@ pkv_status pkv_kv_append_fp8(void* k_pages, void* v_pages, float* k_scales, floa
  * q is q_dtype (PKV_F16 or PKV_BF16) and the arithmetic is that of the 16-bit path
  * (every E4M3 value is exact in both 16-bit types).  With a cascade plan the shared
  * blocks go through the matrix-core pass, their codes widened to q's type in LDS, the
- * K scale applied to each score and the V scale folded into each weight.  The scale
- * arrays must be 16-byte aligned (a token group's four scales are read as one
+ * K scale applied to each score and the V scale folded into each weight.  With q in
+ * f16 that weight (at most 2^8 times the V scale) is held in f16 for the matrix-core
+ * products: V scales up to 2^8, which is what pkv_kv_append_fp8 writes from f16 data,
+ * keep it finite, and a product above the largest finite f16 is clamped to it.  The
+ * scale arrays must be 16-byte aligned (a token group's four scales are read as one
  * vector).  Workspace: pkv_decode_workspace_bytes(..., plan).  Errors as
  * pkv_paged_decode_attn. */
 pkv_status pkv_paged_decode_attn_fp8(const void* q, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -441,8 +441,8 @@ cascade_kernel(CascadeArgs a) {
         float p1 = fast_exp2(fmaf(sv[2 * j2 + 1], c, -mref));
         lsum[rb] += p0 + p1;
         if constexpr (Q8) {  // the V scale rides on the weight
-          p0 *= vsc[2 * j2];
-          p1 *= vsc[2 * j2 + 1];
+          p0 = CT::finite_weight(p0 * vsc[2 * j2]);
+          p1 = CT::finite_weight(p1 * vsc[2 * j2 + 1]);
         }
         const uint32_t h = CT::pack2(p0, p1);  // the 16-bit terms, then what they leave
         bh[rb][j2] = h;

@@ -732,7 +732,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     for (int j = 0; j < 4; ++j) {
       const float p = fast_exp2(sv[j] - mref);
       l1 += p;
-      pw[j] = Q8 ? (p == 0.f ? 0.f : p * vs[j]) : p;  // FP8: the token's V scale
+      pw[j] = Q8 ? (p == 0.f ? 0.f : CT::finite_weight(p * vs[j])) : p;  // FP8: the token's V scale
     }
     // One 16x16x32 product per d tile takes both terms: k slots 8 (l / 16) .. + 3 hold
     // tokens 4 (l / 16) .. + 3 with p_hi, slots + 4 .. + 7 the same tokens with p_lo.

@@ -44,6 +44,8 @@ struct BF16 {
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
   }
+  // a non-negative weight that must stay finite when packed (bf16 has fp32's range)
+  static __device__ __forceinline__ float finite_weight(float x) { return x; }
 };
 
 struct F16 {
@@ -66,6 +68,9 @@ struct F16 {
   static __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
   }
+  // a non-negative weight that must stay finite when packed: at most the largest
+  // finite f16 (a weight <= 2^8 times an FP8 V scale <= 2^8 can reach 2^16)
+  static __device__ __forceinline__ float finite_weight(float x) { return fminf(x, 65504.f); }
 };
 
 // FP8 pages: OCP E4M3 codes, one byte per element, with a power-of-two scale per
