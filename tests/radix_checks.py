@@ -248,7 +248,7 @@ class PinnedCache:
             self.unlock(node)
             self.free(seq)
 
-    # pool calls the driver makes
+    # pool calls the request traces make
     def alloc_with_prefix(self, seq, blocks, n):
         self.pool.alloc_with_prefix(seq, blocks, n)
         self.live.add(seq)
