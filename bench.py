@@ -94,8 +94,10 @@ def read_ceiling(gib, dev):
                 times.append(e0.elapsed_time(e1))
         gbs = buf.numel() / (float(np.median(times)) * 1e-3) / 1e9
         best = max(best, (gbs, grid))
+    # freed into torch's cache, not back to the driver: device memory mapped again after a
+    # release measured 2-4 % slower under the same kernels (FP8 8B split 63.7 -> 66.1 us),
+    # so no workload of this run is timed on memory the driver has just handed back
     del buf
-    torch.cuda.empty_cache()
     return {"gbs": round(best[0], 1), "grid": best[1], "bytes": gib << 30,
             "kernel": "stream_read_kernel (16-byte non-temporal loads, 4 in flight per thread)"}
 
@@ -902,8 +904,7 @@ def summarize_config(w, dev, steps, warmup, flush_iters, flush):
                               "decode_call_flushed_us_median_p10_p90": list(off_fl),
                               "kernels_us": {k: v["avg_us"] for k, v in kern_off.items() if v["launches"]},
                               "speedup_of_cascade": round(off_ms / attn_ms, 3)}
-    del r
-    torch.cuda.empty_cache()
+    del r  # (kept in torch's cache: see read_ceiling)
     return out
 
 
@@ -1064,8 +1065,7 @@ def main():
         "cpu_baseline": cpu,
     }
     if default_run and not args.no_cascade and not fused:
-        del r
-        torch.cuda.empty_cache()
+        del r  # (kept in torch's cache: see read_ceiling)
         configs = {}
         for n in EXTRA_CONFIGS:
             wx = workloads.get(n)
@@ -1087,7 +1087,6 @@ def main():
             rx = run_fp8(sub, wx, dev, emit=False) if kind == "fp8" else run_extend(sub, wx, dev, emit=False)
             extras[key] = {k: rx[k] for k in ("value", "unit", "ms_per_step", "dtype", "kernels", "roofline")}
             extras[key]["workload"] = rx["config"]["workload"]
-            torch.cuda.empty_cache()
         res["extras"] = extras
     print(json.dumps(res), flush=True)
 
