@@ -15,8 +15,9 @@
 //   O^T += V_n^T P^T       (V staged transposed in LDS as the A operand; P^T comes
 //                           straight out of the S^T accumulator layout)
 //
-// P is fed to the matrix core as two 16-bit terms, p = p_hi + p_lo, so the
-// product keeps ~16 bits of the fp32 weights rather than 8.
+// For bf16 (and FP8) pages P is fed to the matrix core as two 16-bit terms,
+// p = p_hi + p_lo, so the product keeps ~16 bits of the fp32 weights rather than 8;
+// for f16 pages one f16 term (11 bits) is exact enough.
 //
 // Each (query row, query head) gets one partial (m, l, acc) per node piece, in
 // the same log2-scaled form as the split-K partials, and the merge kernel
@@ -44,6 +45,12 @@ __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
 }
 
 }  // namespace
+
+// One f16 weight term in the PV products of f16 pages (see the kernel): 1, or two
+// 16-bit terms for every page type: 0.
+#ifndef PKV_CASCADE_F16P
+#define PKV_CASCADE_F16P 1
+#endif
 
 // Work-group: 4 waves, 64 x RB query rows (16 x RB per wave), one token piece of
 // one node for one KV head.  Row rho of a node is (member rho / G, query head
@@ -84,6 +91,11 @@ cascade_kernel(CascadeArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][32 * KPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][32 * VPITCH];
+  // f16 pages: the weights enter the PV products as one f16 term (11 significant bits,
+  // exact enough); bf16 and FP8 pages as two 16-bit terms.  (Staging bf16 V a second
+  // time as f16 for one term, with the two-term path kept for chunks beyond the f16
+  // range, measured much slower: the copy and the registers cost more than the products.)
+  constexpr bool P16 = PKV_CASCADE_F16P != 0 && !Q8 && std::is_same<CT, F16>::value;
   // FP8: the chunk's 32 K scales, then its 32 V scales (zero for tokens without data)
   __shared__ __attribute__((aligned(16))) float sc_lds[2][Q8 ? 64 : 1];
 
@@ -330,12 +342,13 @@ cascade_kernel(CascadeArgs a) {
     // wave per SIMD, so that instance reads each operand where it is used.)
     constexpr bool BATCH = RB >= 2;
     u32x4 kop[NKS][2], vop[NDT];
+    const uint16_t* vsrc = &v_lds[buf][0];
     auto k_operand = [&](int ks, int tt) {
       return *reinterpret_cast<const u32x4*>(&k_lds[buf][(tt * 16 + lrow) * KPITCH + ks * 32 + lgrp * 8]);
     };
     const int trow = lrow >> 2, tcol = 4 * (lrow & 3);
     auto v_operand = [&](int dt) {
-      const uint16_t* v0p = &v_lds[buf][(4 * lgrp + trow) * VPITCH + dt * 16 + tcol];
+      const uint16_t* v0p = vsrc + (4 * lgrp + trow) * VPITCH + dt * 16 + tcol;
       const u32x2 t0 = tr_read16(v0p);                // tokens 4*lgrp .. +3
       const u32x2 t1 = tr_read16(v0p + 16 * VPITCH);  // tokens 16 + 4*lgrp .. +3
       return u32x4{t0.x, t0.y, t1.x, t1.y};
@@ -444,9 +457,13 @@ cascade_kernel(CascadeArgs a) {
           p0 = CT::finite_weight(p0 * vsc[2 * j2]);
           p1 = CT::finite_weight(p1 * vsc[2 * j2 + 1]);
         }
-        const uint32_t h = CT::pack2(p0, p1);  // the 16-bit terms, then what they leave
-        bh[rb][j2] = h;
-        bl[rb][j2] = CT::pack2(p0 - CT::lo(h), p1 - CT::hi(h));
+        if constexpr (P16) {  // one f16 term
+          bh[rb][j2] = F16::pack2(p0, p1);
+        } else {
+          const uint32_t h = CT::pack2(p0, p1);  // the 16-bit terms, then what they leave
+          bh[rb][j2] = h;
+          bl[rb][j2] = CT::pack2(p0 - CT::lo(h), p1 - CT::hi(h));
+        }
       }
     }
     // each V^T operand read from LDS feeds 2 x RB products
@@ -455,8 +472,12 @@ cascade_kernel(CascadeArgs a) {
       const u32x4 av = BATCH ? vop[dt] : v_operand(dt);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        o[rb][dt] = mfma16x16x32<CT>(av, bh[rb], o[rb][dt]);
-        o[rb][dt] = mfma16x16x32<CT>(av, bl[rb], o[rb][dt]);
+        if constexpr (P16) {
+          o[rb][dt] = mfma16x16x32<F16>(av, bh[rb], o[rb][dt]);
+        } else {
+          o[rb][dt] = mfma16x16x32<CT>(av, bh[rb], o[rb][dt]);
+          o[rb][dt] = mfma16x16x32<CT>(av, bl[rb], o[rb][dt]);
+        }
       }
     }
   };
